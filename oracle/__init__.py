@@ -1,0 +1,210 @@
+"""fp64 CPU oracle for YOCO's cross-decoder hot path -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The HIP library never imports, links or
+calls it, and it shares no code with that library.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, OpenMP over independent
+query rows and heads).  This module only marshals numpy arrays to it:
+
+* ``rmsnorm``     -- RMSNorm in fp64.
+* ``project``     -- RMSNorm then ``@ W`` (the shared K^/V^ projection of the
+                     YOCO reading notes, section 2.1, Eq. 2, and the per-layer
+                     query projection of Eq. 3).
+* ``attention``   -- causal GQA softmax attention of one query block over one
+                     shared K/V slab (Eq. 3; the blog's section 2 formula).
+* ``prefill`` / ``decode`` -- position bookkeeping around ``attention``.
+
+Inputs are the stored values: float32 arrays, or bf16 kept as ``uint16`` bits.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_DIR, "oracle.c")
+_LIB = os.path.join(_DIR, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+F32, BF16 = 0, 1
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile ``oracle.c`` (or a copy of it) with gcc: fp64, no fast-math,
+    no contraction of multiply-add, OpenMP for the independent task loops."""
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
+        return out
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC",
+           "-shared", "-std=c11", "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"oracle inputs are float32 or bf16 bits (uint16), got {a.dtype}")
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Oracle:
+    """Marshalling around one compiled copy of ``oracle.c``."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        lib.oracle_num_threads.restype = i32
+        lib.oracle_set_num_threads.argtypes = [i32]
+        lib.oracle_rmsnorm.argtypes = [vp, i32, i64, i64, vp, dbl, vp]
+        lib.oracle_matmul.argtypes = [vp, i64, i64, vp, i32, i64, vp]
+        lib.oracle_project.argtypes = [vp, i32, i64, i64, vp, dbl, vp, i32, i64, vp]
+        lib.oracle_project.restype = i32
+        lib.oracle_attention.argtypes = [vp, i32, i64, vp, i32, vp, vp, i32, i64, i32, i32,
+                                         dbl, vp, vp]
+        lib.oracle_attention.restype = i32
+        self.lib = lib
+        self.path = path
+
+    def num_threads(self) -> int:
+        return int(self.lib.oracle_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        self.lib.oracle_set_num_threads(int(n))
+
+    def rmsnorm(self, x: np.ndarray, gain=None, eps: float = 1e-6) -> np.ndarray:
+        """RMSNorm of the rows of ``x`` ([n, d]), fp64 result."""
+        x = np.ascontiguousarray(x)
+        n, d = x.shape
+        y = np.empty((n, d), dtype=np.float64)
+        g = None if gain is None else np.ascontiguousarray(gain, dtype=np.float32)
+        self.lib.oracle_rmsnorm(_ptr(x), _code(x), n, d, None if g is None else _ptr(g),
+                                eps, _ptr(y))
+        return y
+
+    def matmul(self, y: np.ndarray, w: np.ndarray) -> np.ndarray:
+        """``y @ w``: y fp64 [n, d], w stored [d, ncols]; fp64 result."""
+        y = np.ascontiguousarray(y, dtype=np.float64)
+        w = np.ascontiguousarray(w)
+        n, d = y.shape
+        if w.shape[0] != d:
+            raise ValueError("w must be [d, ncols]")
+        out = np.empty((n, w.shape[1]), dtype=np.float64)
+        self.lib.oracle_matmul(_ptr(y), n, d, _ptr(w), _code(w), w.shape[1], _ptr(out))
+        return out
+
+    def project(self, x: np.ndarray, w: np.ndarray, gain=None, eps: float = 1e-6) -> np.ndarray:
+        """``RMSNorm(x) @ w`` in fp64: x [n, d], w [d, ncols] -> [n, ncols]."""
+        x = np.ascontiguousarray(x)
+        w = np.ascontiguousarray(w)
+        n, d = x.shape
+        if w.shape[0] != d:
+            raise ValueError("w must be [d_model, ncols]")
+        out = np.empty((n, w.shape[1]), dtype=np.float64)
+        g = None if gain is None else np.ascontiguousarray(gain, dtype=np.float32)
+        rc = self.lib.oracle_project(_ptr(x), _code(x), n, d, None if g is None else _ptr(g),
+                                     eps, _ptr(w), _code(w), w.shape[1], _ptr(out))
+        if rc != 0:
+            raise MemoryError("oracle_project could not allocate scratch")
+        return out
+
+    def attention(self, q: np.ndarray, pos, k: np.ndarray, v: np.ndarray, scale: float,
+                  want_lse: bool = False):
+        """Causal GQA attention.
+
+        q: [n_q, H_q, d_h] stored values; pos: [n_q] absolute positions (query
+        i reads rows 0..pos[i]); k, v: [rows, H_kv, d_h] stored values of one
+        sequence.  Returns o [n_q, H_q, d_h] fp64 (and lse [n_q, H_q]).
+        """
+        q = np.ascontiguousarray(q)
+        k = np.ascontiguousarray(k)
+        v = np.ascontiguousarray(v)
+        if k.dtype != v.dtype:
+            raise TypeError("k and v must share a storage type")
+        n_q, hq, dh = q.shape
+        rows, hkv, dhk = k.shape
+        if v.shape != k.shape or dhk != dh:
+            raise ValueError("shape mismatch between q, k and v")
+        pos = np.ascontiguousarray(pos, dtype=np.int64).reshape(-1)
+        if pos.shape[0] != n_q:
+            raise ValueError("one position per query row")
+        o = np.empty((n_q, hq, dh), dtype=np.float64)
+        lse = np.empty((n_q, hq), dtype=np.float64) if want_lse else None
+        rc = self.lib.oracle_attention(_ptr(q), _code(q), n_q, _ptr(pos), hq, _ptr(k), _ptr(v),
+                                       _code(k), rows, hkv, dh, float(scale), _ptr(o),
+                                       None if lse is None else _ptr(lse))
+        if rc == -1:
+            raise ValueError("bad attention arguments (H_q % H_kv, or a position outside the slab)")
+        if rc != 0:
+            raise MemoryError("oracle_attention could not allocate scratch")
+        return (o, lse) if want_lse else o
+
+    def prefill(self, q: np.ndarray, q_start: int, k: np.ndarray, v: np.ndarray,
+                scale: float, rows=None, want_lse: bool = False):
+        """Causal prefill: query row i sits at position q_start + i.  ``rows``
+        optionally selects which query rows to evaluate (sampled parity)."""
+        if rows is None:
+            rows = np.arange(q.shape[0], dtype=np.int64)
+        rows = np.asarray(rows, dtype=np.int64)
+        return self.attention(q[rows], q_start + rows, k, v, scale, want_lse)
+
+    def decode(self, q: np.ndarray, length: int, k: np.ndarray, v: np.ndarray,
+               scale: float, want_lse: bool = False):
+        """Decode: every query row (e.g. one per cross layer) sits at position
+        length - 1 and reads cache rows 0..length-1."""
+        pos = np.full(q.shape[0], length - 1, dtype=np.int64)
+        return self.attention(q, pos, k[:length], v[:length], scale, want_lse)
+
+
+def default() -> Oracle:
+    """The oracle built from ``oracle.c`` beside this file (built if stale)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            build(force=False)
+            _lib = Oracle(_LIB)
+        return _lib
+
+
+def num_threads() -> int:
+    return default().num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    default().set_num_threads(n)
+
+
+def rmsnorm(x, gain=None, eps: float = 1e-6):
+    return default().rmsnorm(x, gain, eps)
+
+
+def matmul(y, w):
+    return default().matmul(y, w)
+
+
+def project(x, w, gain=None, eps: float = 1e-6):
+    return default().project(x, w, gain, eps)
+
+
+def attention(q, pos, k, v, scale, want_lse: bool = False):
+    return default().attention(q, pos, k, v, scale, want_lse)
+
+
+def prefill(q, q_start, k, v, scale, rows=None, want_lse: bool = False):
+    return default().prefill(q, q_start, k, v, scale, rows, want_lse)
+
+
+def decode(q, length, k, v, scale, want_lse: bool = False):
+    return default().decode(q, length, k, v, scale, want_lse)

@@ -1,0 +1,356 @@
+"""Pins for the fp64 oracle: facts fixed by the pages and by mathematics.
+
+Every pin takes an ``oracle.Oracle`` instance and raises ``AssertionError``
+when the instance disagrees.  ``test_oracle.py`` runs them against the real
+oracle; ``test_oracle_mutations.py`` runs them against copies of ``oracle.c``
+with a plausible mistake planted, and requires each copy to fail at least one.
+
+None of these re-types the oracle's formula.  They use closed forms
+(constant and one-hot rows, one or two visible keys, identical keys),
+invariants the pages fix (causality, GQA == MHA with repeated heads, prefix
+invariance, shared == per-layer copies), invariances of softmax (shift of the
+keys, affine V, row permutation) and independent library routines
+(``torch.nn.functional.rms_norm`` and ``scaled_dot_product_attention`` in
+fp64 on the CPU, numpy fp64 matmul).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from workloads import BF16, F32, as_f32, store
+
+
+def _rng(seed):
+    return np.random.default_rng(1000 + seed)
+
+
+def _grid(rng, shape, step=1.0 / 64, lim=4.0):
+    """fp32 values on a coarse grid, so that sums of a few of them are exact."""
+    return (np.round(rng.uniform(-lim, lim, size=shape) / step) * step).astype(np.float32)
+
+
+def _close(a, b, rtol, atol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if not np.all(np.isfinite(a)):
+        raise AssertionError(f"{what}: non-finite oracle output")
+    if not np.allclose(a, b, rtol=rtol, atol=atol):
+        err = np.max(np.abs(a - b))
+        raise AssertionError(f"{what}: max abs err {err:.3e}")
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm
+# ---------------------------------------------------------------------------
+def pin_rmsnorm_constant_row(orc):
+    """x = c*1 gives y = c*g / sqrt(c^2 + eps) (mean of squares is c^2)."""
+    rng = _rng(1)
+    d = 16
+    g = (1.0 + 0.5 * rng.standard_normal(d)).astype(np.float32)
+    eps = 0.25
+    for c in (0.5, -3.0, 2.0):
+        x = np.full((1, d), c, dtype=np.float32)
+        y = orc.rmsnorm(x, g, eps)
+        want = c * g.astype(np.float64) / math.sqrt(c * c + eps)
+        _close(y[0], want, 1e-13, 0, f"rmsnorm constant row c={c}")
+
+
+def pin_rmsnorm_one_hot(orc):
+    """x = a*e_k gives y_k = a*g_k / sqrt(a^2/d + eps) and zeros elsewhere."""
+    d, k, a, eps = 32, 5, 3.0, 0.5
+    g = np.linspace(0.5, 2.0, d).astype(np.float32)
+    x = np.zeros((1, d), dtype=np.float32)
+    x[0, k] = a
+    y = orc.rmsnorm(x, g, eps)
+    want = np.zeros(d)
+    want[k] = a * float(g[k]) / math.sqrt(a * a / d + eps)
+    _close(y[0], want, 1e-13, 0, "rmsnorm one-hot")
+
+
+def pin_rmsnorm_library(orc):
+    """Agrees with torch.nn.functional.rms_norm in fp64 (fp32 and bf16 storage)."""
+    rng = _rng(2)
+    for dtype in (F32, BF16):
+        x = store(rng.standard_normal((7, 96)).astype(np.float32) * 3, dtype)
+        g = (1 + 0.2 * rng.standard_normal(96)).astype(np.float32)
+        eps = 1e-3
+        got = orc.rmsnorm(x, g, eps)
+        xt = torch.from_numpy(as_f32(x).astype(np.float64))
+        want = torch.nn.functional.rms_norm(xt, (96,), torch.from_numpy(g.astype(np.float64)), eps)
+        _close(got, want.numpy(), 1e-12, 1e-14, f"rmsnorm vs torch ({dtype})")
+
+
+# ---------------------------------------------------------------------------
+# Projections (RMSNorm then @ W)
+# ---------------------------------------------------------------------------
+def pin_project_identity(orc):
+    """With W = I the projection is the normalised input."""
+    rng = _rng(3)
+    x = rng.standard_normal((5, 24)).astype(np.float32)
+    g = (1 + 0.3 * rng.standard_normal(24)).astype(np.float32)
+    out = orc.project(x, np.eye(24, dtype=np.float32), g, 1e-6)
+    _close(out, orc.rmsnorm(x, g, 1e-6), 1e-14, 0, "project with identity W")
+
+
+def pin_project_column_selector(orc):
+    """Column j of W = e_{c_j} picks normalised feature c_j (orientation of W)."""
+    rng = _rng(4)
+    d, ncols = 40, 12
+    x = rng.standard_normal((6, d)).astype(np.float32)
+    cols = rng.choice(d, ncols, replace=False)
+    w = np.zeros((d, ncols), dtype=np.float32)
+    w[cols, np.arange(ncols)] = 1.0
+    out = orc.project(x, w, None, 1e-6)
+    xt = torch.from_numpy(x.astype(np.float64))
+    y = torch.nn.functional.rms_norm(xt, (d,), None, 1e-6).numpy()
+    _close(out, y[:, cols], 1e-13, 0, "project column selector")
+
+
+def pin_project_library(orc):
+    """Agrees with torch rms_norm followed by numpy fp64 matmul (non-square W)."""
+    rng = _rng(5)
+    for dtype in (F32, BF16):
+        d, ncols = 48, 20
+        x = store(rng.standard_normal((9, d)).astype(np.float32), dtype)
+        w = store((rng.standard_normal((d, ncols)) / math.sqrt(d)).astype(np.float32), dtype)
+        g = (1 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+        got = orc.project(x, w, g, 1e-6)
+        xt = torch.from_numpy(as_f32(x).astype(np.float64))
+        y = torch.nn.functional.rms_norm(xt, (d,), torch.from_numpy(g.astype(np.float64)), 1e-6)
+        want = y.numpy() @ as_f32(w).astype(np.float64)
+        _close(got, want, 1e-12, 1e-14, f"project vs torch+numpy ({dtype})")
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+def _torch_reference(q, q_pos, k, v, scale):
+    """fp64 SDPA with an explicit causal mask built from absolute positions and
+    repeat-interleaved K/V heads (query head h reads KV head h // G)."""
+    qf = torch.from_numpy(as_f32(q).astype(np.float64))       # [n_q, hq, dh]
+    kf = torch.from_numpy(as_f32(k).astype(np.float64))       # [rows, hkv, dh]
+    vf = torch.from_numpy(as_f32(v).astype(np.float64))
+    hq, hkv = qf.shape[1], kf.shape[1]
+    kr = kf.repeat_interleave(hq // hkv, dim=1).permute(1, 0, 2).contiguous()
+    vr = vf.repeat_interleave(hq // hkv, dim=1).permute(1, 0, 2).contiguous()
+    qh = qf.permute(1, 0, 2).contiguous()
+    rows = kf.shape[0]
+    mask = torch.arange(rows)[None, :] <= torch.as_tensor(np.asarray(q_pos))[:, None]
+    o = torch.nn.functional.scaled_dot_product_attention(qh, kr, vr, attn_mask=mask, scale=scale)
+    logits = (qh @ kr.transpose(1, 2)) * scale
+    logits = logits.masked_fill(~mask, float("-inf"))
+    lse = torch.logsumexp(logits, dim=-1)
+    return o.permute(1, 0, 2).numpy(), lse.permute(1, 0).numpy()
+
+
+def pin_attn_single_visible_key(orc):
+    """Position 0 sees only row 0: the output is V_0 exactly and lse is the
+    one logit."""
+    rng = _rng(6)
+    q = rng.standard_normal((1, 4, 16)).astype(np.float32)
+    k = rng.standard_normal((5, 2, 16)).astype(np.float32)
+    v = rng.standard_normal((5, 2, 16)).astype(np.float32)
+    o, lse = orc.attention(q, [0], k, v, 0.3, want_lse=True)
+    for h in range(4):
+        g = h // 2
+        if not np.array_equal(o[0, h], v[0, g].astype(np.float64)):
+            raise AssertionError("single visible key must return V_0 exactly")
+        want = 0.3 * float(np.dot(q[0, h].astype(np.float64), k[0, g].astype(np.float64)))
+        _close(lse[0, h], want, 1e-13, 1e-15, "lse with one visible key")
+
+
+def pin_attn_identical_keys(orc):
+    """All keys equal: uniform weights, output = mean of visible V rows,
+    lse = logit + ln(t+1)."""
+    rng = _rng(7)
+    rows, dh = 9, 8
+    k = np.tile(rng.standard_normal((1, 1, dh)).astype(np.float32), (rows, 1, 1))
+    v = rng.standard_normal((rows, 1, dh)).astype(np.float32)
+    q = rng.standard_normal((rows, 1, dh)).astype(np.float32)
+    pos = np.arange(rows)
+    o, lse = orc.attention(q, pos, k, v, 0.7, want_lse=True)
+    for t in range(rows):
+        want = v[: t + 1, 0].astype(np.float64).mean(axis=0)
+        _close(o[t, 0], want, 1e-13, 1e-15, f"identical keys, position {t}")
+        x = 0.7 * float(np.dot(q[t, 0].astype(np.float64), k[0, 0].astype(np.float64)))
+        _close(lse[t, 0], x + math.log(t + 1), 1e-13, 1e-15, "lse with identical keys")
+
+
+def pin_attn_two_keys_closed_form(orc):
+    """Two visible keys: weights are a logistic pair in s*(q.k0 - q.k1)."""
+    q = np.array([[[1.0, 2.0, -1.0, 0.5]]], dtype=np.float32)
+    k = np.array([[[0.5, 1.0, 0.0, 2.0]], [[-1.0, 0.25, 1.5, 1.0]]], dtype=np.float32)
+    v = np.array([[[1.0, -2.0, 3.0, 0.0]], [[4.0, 0.5, -1.0, 2.0]]], dtype=np.float32)
+    s = 0.37
+    x0 = s * (0.5 + 2.0 + 0.0 + 1.0)          # s * q.k0 = s * 3.5
+    x1 = s * (-1.0 + 0.5 - 1.5 + 0.5)         # s * q.k1 = s * -1.5
+    w0 = 1.0 / (1.0 + math.exp(x1 - x0))
+    want = w0 * v[0, 0].astype(np.float64) + (1 - w0) * v[1, 0].astype(np.float64)
+    o, lse = orc.attention(q, [1], k, v, s, want_lse=True)
+    _close(o[0, 0], want, 1e-14, 1e-15, "two-key closed form")
+    _close(lse[0, 0], x0 + math.log1p(math.exp(x1 - x0)), 1e-14, 1e-15, "two-key lse")
+
+
+def pin_attn_gqa_head_mapping(orc):
+    """H_q=6, H_kv=3: query head h reads KV head h // 2.  V of KV head g is the
+    constant g+1, so each output is that constant."""
+    rng = _rng(8)
+    rows, dh = 7, 8
+    q = rng.standard_normal((rows, 6, dh)).astype(np.float32)
+    k = rng.standard_normal((rows, 3, dh)).astype(np.float32)
+    v = np.zeros((rows, 3, dh), dtype=np.float32)
+    for g in range(3):
+        v[:, g, :] = g + 1
+    o = orc.attention(q, np.arange(rows), k, v, 0.5)
+    for h in range(6):
+        _close(o[:, h, :], np.full((rows, dh), h // 2 + 1.0), 1e-13, 1e-13, f"GQA head {h}")
+
+
+def pin_attn_gqa_equals_mha(orc):
+    """Repeating each KV head G times and running MHA gives the GQA result."""
+    rng = _rng(9)
+    rows, hq, hkv, dh = 11, 6, 2, 16
+    q = rng.standard_normal((rows, hq, dh)).astype(np.float32)
+    k = rng.standard_normal((rows, hkv, dh)).astype(np.float32)
+    v = rng.standard_normal((rows, hkv, dh)).astype(np.float32)
+    pos = np.arange(rows)
+    gqa = orc.attention(q, pos, k, v, 0.25)
+    mha = orc.attention(q, pos, np.repeat(k, hq // hkv, axis=1), np.repeat(v, hq // hkv, axis=1), 0.25)
+    if not np.array_equal(gqa, mha):
+        raise AssertionError("GQA must equal MHA over repeated KV heads")
+
+
+def pin_attn_prefix_invariance(orc):
+    """The output at position t does not change when rows after t exist."""
+    rng = _rng(10)
+    rows, dh = 20, 8
+    q = rng.standard_normal((rows, 2, dh)).astype(np.float32)
+    k = rng.standard_normal((rows, 1, dh)).astype(np.float32)
+    v = rng.standard_normal((rows, 1, dh)).astype(np.float32)
+    full = orc.attention(q, np.arange(rows), k, v, 0.4)
+    for t in (0, 3, 12, rows - 1):
+        part = orc.attention(q[t:t + 1], [t], k[: t + 1], v[: t + 1], 0.4)
+        if not np.array_equal(part[0], full[t]):
+            raise AssertionError(f"prefix invariance fails at position {t}")
+
+
+def pin_attn_causal_boundary(orc):
+    """Position p depends on row p (inclusive mask) and not on row p+1."""
+    rng = _rng(11)
+    rows, dh, p = 10, 8, 5
+    q = rng.standard_normal((1, 1, dh)).astype(np.float32)
+    k = rng.standard_normal((rows, 1, dh)).astype(np.float32)
+    v = rng.standard_normal((rows, 1, dh)).astype(np.float32)
+    base = orc.attention(q, [p], k, v, 0.5)
+    k2, v2 = k.copy(), v.copy()
+    k2[p + 1] += 3.0
+    v2[p + 1] += 3.0
+    if not np.array_equal(orc.attention(q, [p], k2, v2, 0.5), base):
+        raise AssertionError("row p+1 must be invisible at position p")
+    v3 = v.copy()
+    v3[p] += 3.0
+    if np.allclose(orc.attention(q, [p], k, v3, 0.5), base, rtol=0, atol=1e-9):
+        raise AssertionError("row p must be visible at position p")
+
+
+def pin_attn_shift_invariance(orc):
+    """Adding one vector u to every key of a head shifts all logits by s*q.u,
+    which softmax ignores.  Keys and u sit on a 1/64 grid so k+u is stored
+    exactly.  The large shift pushes logits past 1000, where exp overflows in
+    fp64 without the max subtraction."""
+    rng = _rng(12)
+    rows, dh = 16, 8
+    q = _grid(rng, (rows, 1, dh), lim=2.0)
+    q[:, 0, 0] = 2.0
+    k = _grid(rng, (rows, 1, dh))
+    v = _grid(rng, (rows, 1, dh))
+    base = orc.attention(q, np.arange(rows), k, v, 1.0)
+    for shift in (3.0, 1200.0):
+        u = np.zeros((1, 1, dh), dtype=np.float32)
+        u[0, 0, 0] = shift
+        got = orc.attention(q, np.arange(rows), k + u, v, 1.0)
+        _close(got, base, 1e-11, 1e-12, f"shift invariance (shift {shift})")
+
+
+def pin_attn_v_affine(orc):
+    """V -> a*V + b gives O -> a*O + b; a constant V gives that constant."""
+    rng = _rng(13)
+    rows, dh = 12, 8
+    q = rng.standard_normal((rows, 2, dh)).astype(np.float32)
+    k = rng.standard_normal((rows, 2, dh)).astype(np.float32)
+    v = _grid(rng, (rows, 2, dh))
+    b = _grid(rng, (1, 2, dh))
+    base = orc.attention(q, np.arange(rows), k, v, 0.3)
+    got = orc.attention(q, np.arange(rows), k, 2.0 * v + b, 0.3)
+    _close(got, 2.0 * base + b.astype(np.float64), 1e-12, 1e-12, "V affine")
+
+
+def pin_attn_row_permutation(orc):
+    """Decode over all rows is invariant to permuting the cache rows (K and V
+    together)."""
+    rng = _rng(14)
+    rows, dh = 33, 16
+    q = rng.standard_normal((3, 4, dh)).astype(np.float32)
+    k = rng.standard_normal((rows, 2, dh)).astype(np.float32)
+    v = rng.standard_normal((rows, 2, dh)).astype(np.float32)
+    perm = rng.permutation(rows)
+    a = orc.decode(q, rows, k, v, 0.25)
+    b = orc.decode(q, rows, k[perm], v[perm], 0.25)
+    _close(a, b, 1e-12, 1e-14, "row permutation")
+
+
+def pin_attn_library(orc):
+    """Agrees with torch SDPA in fp64 (explicit position mask, repeated KV
+    heads) for prefill blocks with q_start > 0 and for decode, fp32 and bf16."""
+    rng = _rng(15)
+    for dtype, (rows, q_start, hq, hkv, dh) in (
+            (F32, (37, 0, 4, 2, 16)), (BF16, (45, 13, 6, 2, 32)), (BF16, (29, 28, 3, 1, 8))):
+        t = rows - q_start
+        q = store(rng.standard_normal((t, hq, dh)).astype(np.float32), dtype)
+        k = store(rng.standard_normal((rows, hkv, dh)).astype(np.float32) * 2, dtype)
+        v = store(rng.standard_normal((rows, hkv, dh)).astype(np.float32), dtype)
+        s = 1 / math.sqrt(dh)
+        pos = q_start + np.arange(t)
+        o, lse = orc.prefill(q, q_start, k, v, s, want_lse=True)
+        ro, rlse = _torch_reference(q, pos, k, v, s)
+        _close(o, ro, 1e-11, 1e-13, f"attention vs torch SDPA ({dtype}, q_start={q_start})")
+        _close(lse, rlse, 1e-12, 1e-13, f"lse vs torch logsumexp ({dtype})")
+
+
+def pin_decode_is_last_prefill_row(orc):
+    """Decode at length n equals prefill row n-1 (the last prompt position
+    runs the cross layer, as the reading notes' section 2.5 describes)."""
+    rng = _rng(16)
+    rows, dh = 19, 16
+    q = rng.standard_normal((rows, 4, dh)).astype(np.float32)
+    k = rng.standard_normal((rows, 2, dh)).astype(np.float32)
+    v = rng.standard_normal((rows, 2, dh)).astype(np.float32)
+    pre = orc.prefill(q, 0, k, v, 0.25)
+    dec = orc.decode(q[rows - 1:rows], rows, k, v, 0.25)
+    if not np.array_equal(pre[rows - 1], dec[0]):
+        raise AssertionError("decode must equal the last prefill row")
+
+
+ALL_PINS = [
+    pin_rmsnorm_constant_row,
+    pin_rmsnorm_one_hot,
+    pin_rmsnorm_library,
+    pin_project_identity,
+    pin_project_column_selector,
+    pin_project_library,
+    pin_attn_single_visible_key,
+    pin_attn_identical_keys,
+    pin_attn_two_keys_closed_form,
+    pin_attn_gqa_head_mapping,
+    pin_attn_gqa_equals_mha,
+    pin_attn_prefix_invariance,
+    pin_attn_causal_boundary,
+    pin_attn_shift_invariance,
+    pin_attn_v_affine,
+    pin_attn_row_permutation,
+    pin_attn_library,
+    pin_decode_is_last_prefill_row,
+]

@@ -1,0 +1,54 @@
+"""Plant a plausible mistake in a copy of oracle.c and require the pins to
+catch it.  Each mutation is a dropped term, a wrong sign or index, a transposed
+operand or a misplaced constant; the unmodified oracle passes every pin
+(test_oracle.py), so a pin failure here is caused by the planted mistake."""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+from tests.oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTATIONS = {
+    "dropped_softmax_scale": ("logits[j] = scale * dot;", "logits[j] = dot;"),
+    "causal_mask_leaks_next_row": (
+        "const int64_t n_keys = pos[i] + 1;",
+        "const int64_t n_keys = (pos[i] + 2 < kv_rows) ? pos[i] + 2 : kv_rows;"),
+    "gqa_modulo_mapping": ("const int g = h / group;", "const int g = h % hkv;"),
+    "eps_outside_root": ("sqrt(sum_sq / (double)d + eps)", "(sqrt(sum_sq / (double)d) + eps)"),
+    "rms_sum_not_mean": ("sqrt(sum_sq / (double)d + eps)", "sqrt(sum_sq + eps)"),
+    "rms_divides_by_d_minus_1": ("sqrt(sum_sq / (double)d + eps)",
+                                 "sqrt(sum_sq / (double)(d - 1) + eps)"),
+    "gain_dropped": ("* g / rms;", "/ rms;"),
+    "weight_transposed": ("read_elem(w, w_dtype, c * ncols + j)", "read_elem(w, w_dtype, j * d + c)"),
+    "no_max_subtraction": ("logits[j] = exp(logits[j] - m);", "logits[j] = exp(logits[j]);"),
+    "missing_normalisation": ("o[q_base + e] = acc[e] / l;", "o[q_base + e] = acc[e];"),
+    "lse_without_max": ("lse[i * hq + h] = m + log(l);", "lse[i * hq + h] = log(l);"),
+    "v_reads_k": ("acc[e] += logits[j] * read_elem(v, kv_dtype, v_base + e);",
+                  "acc[e] += logits[j] * read_elem(k, kv_dtype, v_base + e);"),
+    "dot_skips_last_element": ("for (int e = 0; e < dh; ++e) {\n          dot +=",
+                               "for (int e = 0; e < dh - 1; ++e) {\n          dot +="),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name):
+    old, new = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    with tempfile.TemporaryDirectory() as tmp:
+        path = os.path.join(tmp, f"oracle_{name}.c")
+        with open(path, "w") as f:
+            f.write(src.replace(old, new))
+        lib = oracle.build(force=True, src=path, out=os.path.join(tmp, f"lib_{name}.so"))
+        mutant = oracle.Oracle(lib)
+        caught = []
+        for pin in ALL_PINS:
+            try:
+                pin(mutant)
+            except (AssertionError, ValueError, MemoryError) as exc:
+                caught.append((pin.__name__, str(exc)[:80]))
+        assert caught, f"no pin caught the planted mistake {name}"
