@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the shared-KV cross-decoder hot path on one MI355X.
+
+One *step* is one generation step of the cross-decoder over the shared cache
+at N = 131072 rows (YOCO-3B shapes: H_q=24, H_kv=8, d_h=128, 13 cross layers,
+d_model=3072, bf16 storage, fp32 accumulation):
+
+  1. append: RMSNorm of the new self-decoder row and its K^/V^ projection,
+     written once into cache row 131071 (``yoco_kv_append``);
+  2. for each of the 13 cross layers, one split-N decode call over all
+     131072 rows with that layer's own query (``yoco_cross_attn_decode``).
+
+The cache length is set back to 131071 before each step (a host-side
+truncation), so every step decodes exactly 131072 rows.  Inputs are resident
+in HBM before timing starts.  ``value`` is the whole step's time divided by
+13 (microseconds per token per layer).
+
+The same run also times causal prefill on the 32768-token workload (bf16
+MFMA) and reports its TFLOP/s, and times the fp64 CPU oracle on the host
+cores for the same decode step (``cpu_baseline``).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--no-prefill]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E, AMD published
+BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, AMD published
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--prefill-reps", type=int, default=5)
+    return p.parse_args()
+
+
+def to_dev(a, torch):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def bench_decode(args, torch, y, W):
+    cfg = W.DECODE_128K
+    n, hq, hkv, dh, layers = cfg["n_rows"], cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["layers"]
+    d_model = 3072
+    log(f"generating decode workload N={n}")
+    case = W.make_decode(**cfg)
+    proj = W.make_project(n=args.warmup + args.steps, d_model=d_model, n_kv_heads=hkv, head_dim=dh, seed=1)
+
+    cache = y.KVCache(1, n, hkv, dh, torch.bfloat16)
+    cache.k[0] = to_dev(case.k[0], torch)
+    cache.v[0] = to_dev(case.v[0], torch)
+    q_layers = [to_dev(case.q[l], torch) for l in range(layers)]          # each [1, 24, 128]
+    m_rows = to_dev(proj.m, torch)                                        # [steps, 3072]
+    w_k, w_v = to_dev(proj.w_k, torch), to_dev(proj.w_v, torch)
+    gain = torch.ones(d_model, dtype=torch.float32, device="cuda")
+    ws = y.decode_workspace(cache, hq)
+    outs = [torch.empty((1, hq, dh), dtype=torch.float32, device="cuda") for _ in range(layers)]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    n_ev = layers * args.steps
+    ev_start = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ev_end = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+
+    def step(i, record):
+        cache.len[0] = n - 1
+        y.kv_append(cache, m_rows[i:i + 1], w_k, w_v, gain, 1e-6, stream=stream)
+        for l in range(layers):
+            if record is not None:
+                ev_start[record * layers + l].record(stream)
+            y.cross_attn_decode(q_layers[l], cache, workspace=ws, out=outs[l], stream=stream)
+            if record is not None:
+                ev_end[record * layers + l].record(stream)
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i, None)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kern_ms = [s.elapsed_time(e) for s, e in zip(ev_start, ev_end)]
+    kern_avg_ms = float(np.mean(kern_ms))
+    bytes_per_launch = 2 * n * hkv * dh * 2            # K^ + V^ read once per layer call
+    achieved_gbps = bytes_per_launch / (kern_avg_ms * 1e-3) / 1e9
+    us_per_token_layer = ms_per_step * 1e3 / layers
+    step_bytes = layers * bytes_per_launch + 2 * d_model * hkv * dh * 2
+    log(f"decode step {ms_per_step:.3f} ms; {us_per_token_layer:.2f} us/token/layer; "
+        f"decode kernel avg {kern_avg_ms * 1e3:.2f} us -> {achieved_gbps:.0f} GB/s")
+    return dict(case=case, cache=cache, q_layers=q_layers, outs=outs, ms_per_step=ms_per_step,
+                us_per_token_layer=us_per_token_layer, kern_avg_us=kern_avg_ms * 1e3,
+                kern_p10_us=float(np.percentile(kern_ms, 10)) * 1e3,
+                kern_p90_us=float(np.percentile(kern_ms, 90)) * 1e3,
+                achieved_gbps=achieved_gbps, bytes_per_launch=bytes_per_launch,
+                step_gbps=step_bytes / (ms_per_step * 1e-3) / 1e9)
+
+
+def bench_prefill(args, torch, y, W):
+    cfg = W.PREFILL_32K
+    n, hq, hkv, dh = cfg["n"], cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    log(f"generating prefill workload N={n}")
+    c = W.make_prefill(**cfg)
+    cache = y.KVCache(1, n, hkv, dh, torch.bfloat16)
+    cache.k[0] = to_dev(c.k, torch)
+    cache.v[0] = to_dev(c.v, torch)
+    cache.len[0] = n
+    q = to_dev(c.q, torch)
+    o = torch.empty((n, hq, dh), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    y.cross_attn_prefill(q, cache, out=o, stream=stream)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.prefill_reps)]
+    for s, e in evs:
+        s.record(stream)
+        y.cross_attn_prefill(q, cache, out=o, stream=stream)
+        e.record(stream)
+    torch.cuda.synchronize()
+    ms = [s.elapsed_time(e) for s, e in evs]
+    flops = 2.0 * dh * hq * n * (n + 1)                # causal QK^T and PV, diagonal included
+    avg = float(np.mean(ms))
+    tflops = flops / (avg * 1e-3) / 1e12
+    log(f"prefill {avg:.3f} ms -> {tflops:.1f} TFLOP/s")
+    return dict(ms=avg, ms_min=float(np.min(ms)), tflops=tflops, flops=flops,
+                frac=tflops / BF16_DENSE_PEAK_TFLOPS)
+
+
+def cpu_baseline(dec, W):
+    import oracle
+    case = dec["case"]
+    n = int(case.lens[0])
+    threads = oracle.num_threads()
+    log(f"cpu baseline: fp64 oracle decode, 13 layers x 24 heads over {n} rows, {threads} threads")
+    t0 = time.perf_counter()
+    oracle.decode(case.q[:, 0], n, case.k[0], case.v[0], case.softmax_scale)
+    dt = time.perf_counter() - t0
+    return {"value": dt * 1e6 / case.layers, "unit": "us/token/layer", "cores": threads,
+            "kind": "oracle",
+            "sample": f"one full decode step: 13 layers x 24 query heads over all {n} cache rows "
+                      f"(fp64, {dt:.2f} s wall)"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              f"(each box has a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import workloads as W
+    import yoco_shared_kv_amd as y
+
+    dec = bench_decode(args, torch, y, W)
+    pre = None if args.no_prefill else bench_prefill(args, torch, y, W)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(dec, W)
+
+    result = {
+        "metric": "cross-attn decode us/token/layer at N=128K (shared bf16 K^/V^, 13 layers)",
+        "value": round(dec["us_per_token_layer"], 3),
+        "unit": "us/token/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), no weights)",
+        "config": {
+            "workload": "decode, shared cache N=131072, H_q=24, H_kv=8, d_h=128, bf16, batch 1, "
+                        "13 cross layers, plus one appended row (d_model=3072)",
+            "n_rows": 131072, "layers": 13, "n_q_heads": 24, "n_kv_heads": 8, "head_dim": 128,
+            "d_model": 3072, "batch": 1,
+        },
+        "decode_hbm_GBps": round(dec["achieved_gbps"], 1),
+        "step_GBps": round(dec["step_gbps"], 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_kernel<bf16, d_h=128, G=3>",
+            "achieved": round(dec["achieved_gbps"], 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(dec["achieved_gbps"] / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(dec["kern_avg_us"], 2),
+            "p10_launch_us": round(dec["kern_p10_us"], 2),
+            "p90_launch_us": round(dec["kern_p90_us"], 2),
+            "bytes_per_launch": dec["bytes_per_launch"],
+        },
+        "cpu_baseline": cpu,
+    }
+    if pre is not None:
+        result["prefill"] = {
+            "workload": "causal prefill N=32768, H_q=24, H_kv=8, d_h=128, bf16 MFMA, fp32 out",
+            "ms": round(pre["ms"], 3), "tflops": round(pre["tflops"], 1),
+            "roofline": {"bound": "mfma", "achieved": round(pre["tflops"], 1),
+                         "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(pre["frac"], 4), "flops_per_launch": pre["flops"]},
+        }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,224 @@
+/*
+ * yoco.h -- C ABI of the MI355X (gfx950) shared-KV cross-decoder library.
+ *
+ * YOCO ("You Only Cache Once") splits a decoder into a self-decoder and a
+ * cross-decoder.  The self-decoder output M is projected ONCE into a global
+ * K^/V^ cache, and every one of the L/2 cross-decoder layers brings its own
+ * query Q^l = RMSNorm_l(X^l) W_Q^l to that single cache through causal GQA
+ * softmax attention.  Sources (page title, section, equation):
+ *   [Notes] "YOCO：You Only Cache Once 中文精读笔记", section 2.1, Eq. 2
+ *           (K^ = LN(M) W_K, V^ = LN(M) W_V, projected once at the boundary)
+ *           and Eq. 3 (Q^l = LN(X^l) W_Q^l; Attention(Q^l, K^, V^) with a
+ *           causal mask, position n reads rows m <= n; GQA).
+ *   [Blog]  "NeurIPS'24 | YOCO: 长上下文 LLM 为什么不必每层都存一份 KV Cache?",
+ *           section 2 (o_t = softmax(q_t K_{<=t}^T / sqrt(d_h)) V_{<=t}),
+ *           section 6 (prefill skips history cross outputs; the last prompt
+ *           token still runs every cross layer), section 7 (CrossDecoder
+ *           projects the shared K/V once and writes the cache before the
+ *           skip branch; each CrossAttention projects only its own Q and
+ *           calls causal attention on the K/V passed to it; shapes K, V
+ *           [B,S,8,128], Q [B,T,24,128]).
+ *   [Deep]  "You Only Cache Once: Decoder-Decoder Architectures for Language
+ *           Models" (papercache deep notes), section 2.2 Cross-Decoder.
+ *
+ * Conventions for every function:
+ *   - Data pointers are DEVICE pointers unless marked HOST.  The caller owns
+ *     all memory; the library allocates, frees and retains nothing.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and the library never synchronizes.  Buffers must stay alive until the
+ *     stream work completes.
+ *   - All validation happens on the host before anything is enqueued.  On any
+ *     status other than YOCO_OK nothing was enqueued and every host-side
+ *     length is unchanged; yoco_last_error() gives the reason.
+ *   - Row-major layouts; element [a][b][c] of an [A][B][C] array sits at
+ *     offset (a*B + b)*C + c.
+ *   - head_dim is 64 or 128; H_q must be a multiple of H_kv with group size
+ *     G = H_q / H_kv in {1, 2, 3, 4, 6, 8}.  Query head h reads KV head
+ *     floor(h / G).
+ *   - RMSNorm is y = x * g / sqrt(mean(x^2) + eps) per row, statistics in
+ *     fp32; the projections accumulate in fp32 and store with
+ *     round-to-nearest-even when the destination is bf16.
+ *   - Functions are re-entrant.  The only library state is the per-thread
+ *     error text and a per-device record that the device is gfx950.
+ */
+#ifndef YOCO_H
+#define YOCO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define YOCO_ABI_VERSION 1
+#define YOCO_MAX_SEQ 256
+
+/* Storage types. */
+typedef enum yoco_dtype {
+  YOCO_DT_F32 = 0,  /* IEEE binary32 */
+  YOCO_DT_BF16 = 1  /* bfloat16: the upper 16 bits of a binary32 */
+} yoco_dtype;
+
+typedef enum yoco_status {
+  YOCO_OK = 0,
+  YOCO_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
+  YOCO_ERR_BAD_SHAPE = 2,    /* unsupported head_dim / group size / counts */
+  YOCO_ERR_BAD_DTYPE = 3,    /* unsupported or mismatched storage type */
+  YOCO_ERR_OUT_OF_RANGE = 4, /* rows or positions outside the cache */
+  YOCO_ERR_WORKSPACE = 5,    /* decode workspace too small */
+  YOCO_ERR_HIP = 6,          /* HIP runtime error, or the device is not gfx950 */
+  YOCO_ERR_BAD_VALUE = 7     /* bad scalar argument (eps, scale, split rows) */
+} yoco_status;
+
+/* The shared global K^/V^ cache ([Notes] Eq. 2; [Blog] section 7): ONE copy,
+ * read by every cross layer.  k and v are each
+ * [n_seq][seq_capacity][n_kv_heads][head_dim] in `dtype`.  len_host[b]
+ * (HOST memory) is the number of valid rows of sequence b; the project and
+ * append calls advance it when they enqueue their writes.  Lowering
+ * len_host[b] truncates a sequence (e.g. to roll back speculative tokens). */
+typedef struct yoco_kv_cache {
+  void *k;
+  void *v;
+  int64_t *len_host;    /* HOST [n_seq] */
+  int64_t seq_capacity; /* rows per sequence slab, >= 1 */
+  int32_t n_seq;        /* 1 .. YOCO_MAX_SEQ */
+  int32_t n_kv_heads;   /* >= 1 */
+  int32_t head_dim;     /* 64 or 128 */
+  int32_t dtype;        /* yoco_dtype of k and v */
+} yoco_kv_cache;
+
+/* Returns YOCO_ABI_VERSION of the built library. */
+int yoco_abi_version(void);
+
+/* Text describing the last non-OK status returned on the calling thread
+ * ("" if none).  The pointer stays valid until the next call on the thread. */
+const char *yoco_last_error(void);
+
+/* Host-only helper: bytes of ONE of the k / v tensors of a cache with these
+ * dimensions (2 * this value for the whole cache).  For 131072 rows, 8 KV
+ * heads, head dim 128 in bf16 the pair is 2*131072*8*128*2 B = 0.5 GiB, the
+ * size [Blog] section 7 prints for the shared cache.  Errors: NULL bytes ->
+ * NULL_POINTER; non-positive sizes -> BAD_SHAPE; unknown dtype -> BAD_DTYPE. */
+yoco_status yoco_kv_cache_bytes(int32_t n_seq, int64_t seq_capacity, int32_t n_kv_heads,
+                                int32_t head_dim, int32_t dtype, size_t *bytes);
+
+/* Shared K^/V^ projection with one cache write ([Notes] Eq. 2; [Blog]
+ * section 7: computed once in the cross-decoder front and written before the
+ * early-exit return, so prefill of history tokens needs only this call).
+ *
+ *   r_n       = sqrt(mean_c m[n][c]^2 + eps)                  (fp32)
+ *   K^[n][j]  = sum_c (m[n][c] * gain[c] / r_n) * w_k[c][j]   (fp32 accumulate)
+ *   V^[n][j]  = likewise with w_v; one norm is shared by K and V.
+ *   column j = g*head_dim + e is stored at cache row (row_start + n), head g,
+ *   element e of sequence `seq`.
+ *
+ * m:     [n][d_model], m_dtype (f32 or bf16).
+ * gain:  [d_model] fp32, or NULL for unit gain.
+ * w_k, w_v: [d_model][n_kv_heads*head_dim], w_dtype (f32 or bf16).
+ * Writes k/v rows row_start .. row_start+n-1 of `seq` in the cache dtype,
+ * then sets len_host[seq] = max(len_host[seq], row_start + n).
+ * n == 0 is a successful no-op.
+ * Errors: NULL m/w_k/w_v/cache/cache->k/v/len_host -> NULL_POINTER;
+ * d_model < 1, bad cache dims, seq outside [0, n_seq) -> BAD_SHAPE;
+ * dtype codes -> BAD_DTYPE; row_start < 0 or row_start + n > seq_capacity ->
+ * OUT_OF_RANGE; eps < 0 or not finite -> BAD_VALUE. */
+yoco_status yoco_kv_project(const void *m, int32_t m_dtype, int64_t n, int32_t d_model,
+                            const float *gain, float eps, const void *w_k, const void *w_v,
+                            int32_t w_dtype, yoco_kv_cache *cache, int32_t seq,
+                            int64_t row_start, void *stream);
+
+/* Generation-time append ([Notes] section 2.1 and section 2.5: each new token
+ * goes through the self-decoder and its K/V row is appended to the shared
+ * cache; then every cross layer reads the whole cache).
+ * m_new: [n_seq][d_model], one new self-decoder output row per sequence.
+ * Projects each row exactly as yoco_kv_project does and writes it at row
+ * len_host[b] of sequence b, then increments every len_host[b].
+ * Errors as yoco_kv_project; any len_host[b] + 1 > seq_capacity or
+ * len_host[b] < 0 -> OUT_OF_RANGE (and nothing is written). */
+yoco_status yoco_kv_append(const void *m_new, int32_t m_dtype, int32_t d_model,
+                           const float *gain, float eps, const void *w_k, const void *w_v,
+                           int32_t w_dtype, yoco_kv_cache *cache, void *stream);
+
+/* Per-layer query projection ([Notes] Eq. 3: Q^l = LN(X^l) W_Q^l with the
+ * layer's own norm; [Blog] section 7: each cross layer projects only its Q).
+ * x: [n][d_model] (f32 or bf16); gain: [d_model] fp32 or NULL;
+ * w_q: [d_model][n_q_heads*head_dim]; q_out: [n][n_q_heads][head_dim] in
+ * q_dtype (f32 or bf16).  n == 0 is a no-op.
+ * Errors: NULL_POINTER, BAD_SHAPE (head_dim not 64/128, counts < 1),
+ * BAD_DTYPE, BAD_VALUE (eps). */
+yoco_status yoco_q_project(const void *x, int32_t x_dtype, int64_t n, int32_t d_model,
+                           const float *gain, float eps, const void *w_q, int32_t w_dtype,
+                           int32_t n_q_heads, int32_t head_dim, void *q_out, int32_t q_dtype,
+                           void *stream);
+
+/* Causal cross-attention over the shared cache for a block of query rows
+ * (prefill / training forward: [Notes] Eq. 3 with the causal mask; [Blog]
+ * section 2 formula; [Notes] Table 2: the quadratic term the early exit
+ * skips at inference but training still pays).
+ *
+ * Query row i sits at absolute position p = q_start + i and reads cache rows
+ * 0..p of sequence `seq` (inclusive).  For head h with KV head g = h / G:
+ *   x_j = softmax_scale * <q[i][h], K^[j][g]>,  j = 0..p
+ *   o[i][h] = sum_j softmax(x)_j V^[j][g];   lse[i][h] = ln sum_j exp(x_j)
+ * q:   [t][n_q_heads][head_dim] in the cache dtype.
+ * o:   [t][n_q_heads][head_dim] in o_dtype (f32 or bf16).
+ * lse: [t][n_q_heads] fp32, or NULL.
+ * No W_O and no residual: the output is the concatenated heads.
+ * The bf16 path runs both contractions on bf16 MFMA with fp32 accumulation
+ * (probabilities are rounded to bf16 for the second); the f32 path uses
+ * fp32 arithmetic throughout.  t == 0 is a no-op.
+ * Errors: NULL_POINTER; BAD_SHAPE (head/group/head_dim, seq); BAD_DTYPE
+ * (q dtype != cache dtype, o dtype); OUT_OF_RANGE (q_start < 0, t < 0,
+ * q_start + t > len_host[seq]); BAD_VALUE (scale not finite or <= 0). */
+yoco_status yoco_cross_attn_prefill(const void *q, int32_t q_dtype, int64_t q_start, int64_t t,
+                                    int32_t n_q_heads, const yoco_kv_cache *cache, int32_t seq,
+                                    float softmax_scale, void *o, int32_t o_dtype, float *lse,
+                                    void *stream);
+
+/* Bytes of device workspace yoco_cross_attn_decode needs for this cache,
+ * query head count and split size, valid for any len_host up to
+ * seq_capacity.  rows_per_split: 0 selects the library's split size;
+ * otherwise a positive multiple of 256.  Errors: NULL_POINTER, BAD_SHAPE,
+ * BAD_DTYPE, BAD_VALUE (rows_per_split). */
+yoco_status yoco_cross_attn_decode_workspace(const yoco_kv_cache *cache, int32_t n_q_heads,
+                                             int64_t rows_per_split, size_t *bytes);
+
+/* One generation step of one cross layer over the shared cache: split-N
+ * flash decoding ([Notes] section 2.5 and [Blog] section 7: every cross layer
+ * re-reads the whole global cache; sharing storage does not merge the
+ * layers' queries, so each layer is its own call).
+ *
+ * For every sequence b (with len_host[b] >= 1) the single query row sits at
+ * position len_host[b] - 1 and reads rows 0..len_host[b]-1 (the appended
+ * row included).  q: [n_seq][n_q_heads][head_dim] in the cache dtype;
+ * o: [n_seq][n_q_heads][head_dim] fp32; lse: [n_seq][n_q_heads] fp32 or NULL.
+ *
+ * The rows of each (sequence, KV head) are cut into splits of
+ * rows_per_split rows (0 = library choice from the current lengths); one
+ * workgroup streams one split with 128-bit loads, all G query heads of the
+ * group sharing each row it reads, and keeps a running (max, sum, weighted
+ * V) per head; the last workgroup of each (sequence, KV head) to finish
+ * merges the splits in a fixed order, so results are bitwise reproducible
+ * for a fixed split size.
+ *
+ * workspace: device memory of at least the size yoco_cross_attn_decode_workspace
+ * reports for the same cache, n_q_heads and rows_per_split.  Its first
+ * YOCO_DECODE_COUNTER_BYTES bytes are arrival counters that must be zero
+ * before the first call; every completed call leaves them zero again, so
+ * zero-filling a workspace once at allocation is enough.  Calls that share a
+ * workspace must not overlap in time (same stream, or synchronized).
+ * Errors: NULL_POINTER; BAD_SHAPE; BAD_DTYPE (q dtype != cache dtype);
+ * OUT_OF_RANGE (some len_host[b] < 1 or > seq_capacity); WORKSPACE (too
+ * small); BAD_VALUE (scale, rows_per_split). */
+#define YOCO_DECODE_COUNTER_BYTES (YOCO_MAX_SEQ * 64 * 4)
+yoco_status yoco_cross_attn_decode(const void *q, int32_t q_dtype, int32_t n_q_heads,
+                                   const yoco_kv_cache *cache, float softmax_scale, float *o,
+                                   float *lse, void *workspace, size_t workspace_bytes,
+                                   int64_t rows_per_split, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* YOCO_H */

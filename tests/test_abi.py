@@ -1,0 +1,224 @@
+"""The C ABI on the host: the library loads, exports every declared symbol,
+and rejects bad arguments before it touches the GPU (no compute calls)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from tests.conftest import ROOT, gpu_available
+
+HEADER = os.path.join(ROOT, "include", "yoco.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "cache_sizes.txt")
+
+
+def _lib():
+    from yoco_shared_kv_amd._native import lib
+    return lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(yoco_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    names = _declared_functions()
+    assert len(names) == 9, names
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in yoco.h but not exported"
+
+
+def test_abi_version_matches_header():
+    ver = int(re.search(r"#define YOCO_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert _lib().yoco_abi_version() == ver
+
+
+def test_kv_cache_bytes_matches_printed_size():
+    import yoco_shared_kv_amd as y
+    import torch
+    per_tensor = y.kv_cache_bytes(1, 131072, 8, 128, torch.bfloat16)
+    golden = {}
+    for line in open(GOLDEN):
+        if line.strip() and not line.startswith("#"):
+            name, value, unit = line.split()
+            golden[name] = float(value) * {"GiB": 2 ** 30, "MiB": 2 ** 20}[unit]
+    assert 2 * per_tensor == golden["yoco_shared_kv"]
+    assert y.kv_cache_bytes(1, 1, 1, 64, torch.float32) == 256
+    with pytest.raises(y.YocoError) as e:
+        y.kv_cache_bytes(0, 1, 1, 64)
+    assert e.value.name == "YOCO_ERR_BAD_SHAPE"
+
+
+# ---- error paths with placeholder pointers (never dereferenced) ----------
+FAKE = ctypes.c_void_p(0x1000)
+
+
+def _cache(n_seq=2, cap=64, hkv=2, dh=64, dtype=1, lens=(10, 20)):
+    from yoco_shared_kv_amd._native import KVCacheStruct
+    lens_arr = np.array(lens, dtype=np.int64)
+    c = KVCacheStruct()
+    c.k, c.v = 0x2000, 0x3000
+    c.len_host = lens_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    c.seq_capacity, c.n_seq, c.n_kv_heads, c.head_dim, c.dtype = cap, n_seq, hkv, dh, dtype
+    return c, lens_arr
+
+
+def _status(name):
+    from yoco_shared_kv_amd._native import STATUS
+    return {v: k for k, v in STATUS.items()}[name]
+
+
+def _project(c, **kw):
+    args = dict(m=FAKE, m_dt=1, n=4, d=32, gain=None, eps=1e-6, wk=FAKE, wv=FAKE, w_dt=1, seq=0, row_start=0)
+    args.update(kw)
+    return _lib().yoco_kv_project(args["m"], args["m_dt"], args["n"], args["d"], args["gain"], args["eps"],
+                                  args["wk"], args["wv"], args["w_dt"], ctypes.byref(c), args["seq"],
+                                  args["row_start"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(m=None), "YOCO_ERR_NULL_POINTER"),
+    (dict(wv=None), "YOCO_ERR_NULL_POINTER"),
+    (dict(d=0), "YOCO_ERR_BAD_SHAPE"),
+    (dict(seq=2), "YOCO_ERR_BAD_SHAPE"),
+    (dict(m_dt=5), "YOCO_ERR_BAD_DTYPE"),
+    (dict(eps=-1.0), "YOCO_ERR_BAD_VALUE"),
+    (dict(eps=float("nan")), "YOCO_ERR_BAD_VALUE"),
+    (dict(row_start=61), "YOCO_ERR_OUT_OF_RANGE"),
+    (dict(row_start=-1), "YOCO_ERR_OUT_OF_RANGE"),
+    (dict(n=65), "YOCO_ERR_OUT_OF_RANGE"),
+])
+def test_kv_project_rejects(kw, status):
+    c, lens = _cache()
+    assert _project(c, **kw) == _status(status)
+    assert lens.tolist() == [10, 20]
+    assert len(_lib().yoco_last_error()) > 0
+
+
+def test_kv_project_zero_rows_is_noop():
+    c, lens = _cache()
+    assert _project(c, n=0) == 0
+    assert lens.tolist() == [10, 20]
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 96, "YOCO_ERR_BAD_SHAPE"),
+    ("n_seq", 0, "YOCO_ERR_BAD_SHAPE"),
+    ("n_seq", 257, "YOCO_ERR_BAD_SHAPE"),
+    ("n_kv_heads", 0, "YOCO_ERR_BAD_SHAPE"),
+    ("n_kv_heads", 65, "YOCO_ERR_BAD_SHAPE"),
+    ("dtype", 3, "YOCO_ERR_BAD_DTYPE"),
+    ("seq_capacity", 0, "YOCO_ERR_BAD_SHAPE"),
+])
+def test_bad_cache_descriptor(field, value, status):
+    c, lens = _cache()
+    setattr(c, field, value)
+    assert _project(c) == _status(status)
+    assert lens.tolist() == [10, 20]
+
+
+def test_cache_pointers_required():
+    c, _ = _cache()
+    c.k = None
+    assert _project(c) == _status("YOCO_ERR_NULL_POINTER")
+    assert _lib().yoco_kv_project(FAKE, 1, 4, 32, None, 1e-6, FAKE, FAKE, 1, None, 0, 0, None) == \
+        _status("YOCO_ERR_NULL_POINTER")
+
+
+def test_append_at_capacity_rejected_and_lengths_kept():
+    c, lens = _cache(lens=(10, 64))
+    st = _lib().yoco_kv_append(FAKE, 1, 32, None, 1e-6, FAKE, FAKE, 1, ctypes.byref(c), None)
+    assert st == _status("YOCO_ERR_OUT_OF_RANGE")
+    assert lens.tolist() == [10, 64]
+
+
+def _prefill(c, q_start=0, t=4, hq=4, q_dt=1, o_dt=0, scale=0.125, seq=0):
+    return _lib().yoco_cross_attn_prefill(FAKE, q_dt, q_start, t, hq, ctypes.byref(c), seq, scale, FAKE,
+                                          o_dt, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q_start=8, t=3), "YOCO_ERR_OUT_OF_RANGE"),     # 8 + 3 > len 10
+    (dict(q_start=-1), "YOCO_ERR_OUT_OF_RANGE"),
+    (dict(t=-1), "YOCO_ERR_OUT_OF_RANGE"),
+    (dict(hq=3), "YOCO_ERR_BAD_SHAPE"),                  # 3 % 2 != 0
+    (dict(hq=10), "YOCO_ERR_BAD_SHAPE"),                 # group 5 unsupported
+    (dict(q_dt=0), "YOCO_ERR_BAD_DTYPE"),                # q f32, cache bf16
+    (dict(o_dt=4), "YOCO_ERR_BAD_DTYPE"),
+    (dict(scale=0.0), "YOCO_ERR_BAD_VALUE"),
+    (dict(scale=float("inf")), "YOCO_ERR_BAD_VALUE"),
+    (dict(seq=5), "YOCO_ERR_BAD_SHAPE"),
+])
+def test_prefill_rejects(kw, status):
+    c, _ = _cache()
+    assert _prefill(c, **kw) == _status(status)
+
+
+def test_prefill_zero_rows_is_noop():
+    c, _ = _cache()
+    assert _prefill(c, q_start=10, t=0) == 0
+
+
+def _ws_bytes(c, hq=4, rows=0):
+    out = ctypes.c_size_t(0)
+    st = _lib().yoco_cross_attn_decode_workspace(ctypes.byref(c), hq, rows, ctypes.byref(out))
+    return st, out.value
+
+
+def test_decode_workspace_sizes():
+    c, _ = _cache(n_seq=1, cap=131072, hkv=8, dh=128, lens=(131072,))
+    st, auto = _ws_bytes(c, hq=24)
+    assert st == 0
+    counters = 256 * 64 * 4
+    # library split size: at most 64 splits per KV head plus one per sequence
+    assert auto == counters + (64 + 1) * 8 * 3 * (128 + 4) * 4
+    st, fixed = _ws_bytes(c, hq=24, rows=256)
+    assert st == 0 and fixed == counters + 512 * 8 * 3 * 132 * 4
+    assert _ws_bytes(c, hq=24, rows=100)[0] == _status("YOCO_ERR_BAD_VALUE")
+    assert _ws_bytes(c, hq=20)[0] == _status("YOCO_ERR_BAD_SHAPE")
+
+
+def _decode(c, ws_bytes=1 << 30, hq=4, rows=0, q_dt=1):
+    return _lib().yoco_cross_attn_decode(FAKE, q_dt, hq, ctypes.byref(c), 0.125, FAKE, None, FAKE,
+                                         ws_bytes, rows, None)
+
+
+def test_decode_rejects():
+    c, _ = _cache(lens=(10, 0))
+    assert _decode(c) == _status("YOCO_ERR_OUT_OF_RANGE")       # empty sequence
+    c, _ = _cache(lens=(10, 65))
+    assert _decode(c) == _status("YOCO_ERR_OUT_OF_RANGE")       # past capacity
+    c, _ = _cache()
+    assert _decode(c, ws_bytes=16) == _status("YOCO_ERR_WORKSPACE")
+    assert _decode(c, rows=300) == _status("YOCO_ERR_BAD_VALUE")
+    assert _decode(c, q_dt=0) == _status("YOCO_ERR_BAD_DTYPE")
+    assert _lib().yoco_cross_attn_decode(FAKE, 1, 4, ctypes.byref(c), 0.125, FAKE, None, None, 1 << 30, 0,
+                                         None) == _status("YOCO_ERR_NULL_POINTER")
+
+
+def test_q_project_rejects():
+    L = _lib()
+    assert L.yoco_q_project(FAKE, 1, 4, 32, None, 1e-6, FAKE, 1, 4, 96, FAKE, 1, None) == _status("YOCO_ERR_BAD_SHAPE")
+    assert L.yoco_q_project(None, 1, 4, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 1, None) == _status("YOCO_ERR_NULL_POINTER")
+    assert L.yoco_q_project(FAKE, 1, 4, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 2, None) == _status("YOCO_ERR_BAD_DTYPE")
+    assert L.yoco_q_project(FAKE, 1, 0, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 1, None) == 0
+
+
+@pytest.mark.skipif(gpu_available(), reason="checks the no-GPU failure mode")
+def test_valid_call_without_gpu_fails_loudly():
+    c, lens = _cache()
+    st = _project(c)
+    assert st == _status("YOCO_ERR_HIP")
+    assert lens.tolist() == [10, 20]
+    assert b"hip" in _lib().yoco_last_error().lower()
+
+
+def test_python_binding_refuses_host_tensors():
+    import torch
+    import yoco_shared_kv_amd as y
+    with pytest.raises(ValueError):
+        y.q_project(torch.zeros(2, 32), torch.zeros(32, 256), 4, 64)

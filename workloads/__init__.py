@@ -6,7 +6,12 @@ and the HIP library consume exactly the values it returns.
 
 Conventions
 -----------
-* Generator: ``numpy.random.default_rng(seed)`` (PCG64), seed 0 unless stated.
+* Generator: PCG64 (numpy), seed 0 unless stated.  Each tensor is a numbered
+  *stream*; its elements (row-major) are drawn in chunks of 2**22, chunk i of
+  stream s from ``PCG64(SeedSequence(seed, spawn_key=(s, i)))`` with
+  ``standard_normal(dtype=float32)``.  Chunks are filled on several threads;
+  the values do not depend on the thread count.  Small integer draws (ragged
+  lengths, needle rows, peaked rows) use their own numbered streams.
 * Values are drawn in float32 and then stored in the workload's dtype.  For
   bf16 the stored value is the round-to-nearest-even bf16 of the float32 draw,
   kept as raw ``uint16`` bits; the oracle reads those bits, never the draw.
@@ -19,11 +24,25 @@ every stored value, so it is part of the contract.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import Optional
 
 import numpy as np
+
+_CHUNK = 1 << 22
+_THREADS = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 4))
+
+
+def _pool_map(fn, n):
+    if n <= 1:
+        for i in range(n):
+            fn(i)
+        return
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(_THREADS, n)) as ex:
+        list(ex.map(fn, range(n)))
 
 F32 = "f32"
 BF16 = "bf16"
@@ -40,15 +59,15 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
         raise ValueError("non-finite value in a synthetic input")
     out = np.empty(x.shape, dtype=np.uint16)
     flat_in, flat_out = x.reshape(-1).view(np.uint32), out.reshape(-1)
-    step = 1 << 22
-    for s in range(0, flat_in.size, step):
+
+    for s in range(0, flat_in.size, _CHUNK):
         # finite values are <= 0xFF7FFFFF, so adding at most 0x8000 stays in uint32
-        u = flat_in[s:s + step].copy()
+        u = flat_in[s:s + _CHUNK].copy()
         lsb = (u >> 16) & 1
         u += 0x7FFF
         u += lsb
         u >>= 16
-        flat_out[s:s + step] = u
+        flat_out[s:s + _CHUNK] = u
     return out
 
 
@@ -74,11 +93,23 @@ def as_f32(x: np.ndarray) -> np.ndarray:
     return np.asarray(x, dtype=np.float32)
 
 
-def _normal(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
-    x = rng.standard_normal(size=shape, dtype=np.float32)
-    if std != 1.0:
-        x *= np.float32(std)
+def _normal(seed: int, stream: int, shape, std: float = 1.0) -> np.ndarray:
+    """N(0, std^2) float32 draws of one numbered stream (see module notes)."""
+    x = np.empty(shape, dtype=np.float32)
+    flat = x.reshape(-1)
+
+    def fill(i):
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(stream, i))))
+        g.standard_normal(out=flat[i * _CHUNK:(i + 1) * _CHUNK], dtype=np.float32)
+        if std != 1.0:
+            flat[i * _CHUNK:(i + 1) * _CHUNK] *= np.float32(std)
+
+    _pool_map(fill, (flat.size + _CHUNK - 1) // _CHUNK)
     return x
+
+
+def _int_rng(seed: int, stream: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(stream,))))
 
 
 # ---------------------------------------------------------------------------
@@ -90,7 +121,8 @@ class TinyCase:
 
     d_model=256, H_q=4, H_kv=2 (GQA group 2), d_h=64.  M, X ~ N(0,1);
     W_K, W_V, W_Q ~ N(0, 1/d_model); RMSNorm gain 1, eps 1e-6.
-    Draw order: M[257,256], X[257,256], W_K[256,128], W_V[256,128], W_Q[256,256].
+    Streams: 1 M[257,256], 2 X[257,256], 3 W_K[256,128], 4 W_V[256,128],
+    5 W_Q[256,256].
     Row 256 of M and X is the generated token (position 257 counted from 1).
     """
     m: np.ndarray
@@ -114,14 +146,13 @@ class TinyCase:
 
 
 def make_tiny(seed: int = 0) -> TinyCase:
-    rng = np.random.default_rng(seed)
     d, hq, hkv, dh, n = 256, 4, 2, 64, 256
-    m = _normal(rng, (n + 1, d))
-    x = _normal(rng, (n + 1, d))
+    m = _normal(seed, 1, (n + 1, d))
+    x = _normal(seed, 2, (n + 1, d))
     std = 1.0 / math.sqrt(d)
-    w_k = _normal(rng, (d, hkv * dh), std)
-    w_v = _normal(rng, (d, hkv * dh), std)
-    w_q = _normal(rng, (d, hq * dh), std)
+    w_k = _normal(seed, 3, (d, hkv * dh), std)
+    w_v = _normal(seed, 4, (d, hkv * dh), std)
+    w_q = _normal(seed, 5, (d, hq * dh), std)
     ones = np.ones(d, dtype=np.float32)
     return TinyCase(m=m, x=x, w_k=w_k, w_v=w_v, w_q=w_q, gain_kv=ones, gain_q=ones.copy())
 
@@ -160,16 +191,15 @@ class DecodeCase:
 def make_decode(n_rows: int = 131072, n_q_heads: int = 24, n_kv_heads: int = 8,
                 head_dim: int = 128, layers: int = 13, dtype: str = BF16,
                 seed: int = 0) -> DecodeCase:
-    """Single-sequence decode: K, V ``[n_rows, H_kv, d_h]`` then Q
-    ``[layers, 1, H_q, d_h]``, all N(0,1).  Draw order: K, V, Q.
+    """Single-sequence decode: K, V ``[n_rows, H_kv, d_h]`` and Q
+    ``[layers, 1, H_q, d_h]``, all N(0,1).  Streams: 1 K, 2 V, 3 Q.
 
     The default sizes are the 128 Ki-token decode workload (cache
     2*131072*8*128*2 B = 512 MiB in bf16).
     """
-    rng = np.random.default_rng(seed)
-    k = store(_normal(rng, (n_rows, n_kv_heads, head_dim)), dtype)
-    v = store(_normal(rng, (n_rows, n_kv_heads, head_dim)), dtype)
-    q = store(_normal(rng, (layers, 1, n_q_heads, head_dim)), dtype)
+    k = store(_normal(seed, 1, (n_rows, n_kv_heads, head_dim)), dtype)
+    v = store(_normal(seed, 2, (n_rows, n_kv_heads, head_dim)), dtype)
+    q = store(_normal(seed, 3, (layers, 1, n_q_heads, head_dim)), dtype)
     return DecodeCase(k=[k], v=[v], q=q, lens=np.array([n_rows], dtype=np.int64),
                       n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, head_dim=head_dim,
                       layers=layers, dtype=dtype)
@@ -189,16 +219,15 @@ def ragged_lengths(n_seq: int = 16, lo: int = RAGGED_LO, hi: int = RAGGED_HI,
 def make_ragged_decode(n_seq: int = 16, lo: int = RAGGED_LO, hi: int = RAGGED_HI,
                        n_q_heads: int = 24, n_kv_heads: int = 8, head_dim: int = 128,
                        layers: int = 13, dtype: str = BF16, seed: int = 0) -> DecodeCase:
-    """Ragged batched decode.  Draw order: lengths (16 integers on [lo, hi]);
-    then for b = 0..n_seq-1: K_b ``[L_b, H_kv, d_h]``, V_b; then Q
-    ``[layers, n_seq, H_q, d_h]``.  All values N(0,1)."""
-    rng = np.random.default_rng(seed)
-    lens = rng.integers(lo, hi, n_seq, endpoint=True).astype(np.int64)
+    """Ragged batched decode.  Lengths: ``ragged_lengths`` (the first draw of
+    ``default_rng(seed)``).  Streams: 1 Q ``[layers, n_seq, H_q, d_h]``;
+    100 + 2b K_b ``[L_b, H_kv, d_h]``; 101 + 2b V_b.  All values N(0,1)."""
+    lens = ragged_lengths(n_seq, lo, hi, seed)
+    q = store(_normal(seed, 1, (layers, n_seq, n_q_heads, head_dim)), dtype)
     ks, vs = [], []
     for b in range(n_seq):
-        ks.append(store(_normal(rng, (int(lens[b]), n_kv_heads, head_dim)), dtype))
-        vs.append(store(_normal(rng, (int(lens[b]), n_kv_heads, head_dim)), dtype))
-    q = store(_normal(rng, (layers, n_seq, n_q_heads, head_dim)), dtype)
+        ks.append(store(_normal(seed, 100 + 2 * b, (int(lens[b]), n_kv_heads, head_dim)), dtype))
+        vs.append(store(_normal(seed, 101 + 2 * b, (int(lens[b]), n_kv_heads, head_dim)), dtype))
     return DecodeCase(k=ks, v=vs, q=q, lens=lens, n_q_heads=n_q_heads,
                       n_kv_heads=n_kv_heads, head_dim=head_dim, layers=layers, dtype=dtype)
 
@@ -211,8 +240,9 @@ def make_needle_decode(n_rows: int = 1 << 20, n_q_heads: int = 24, n_kv_heads: i
                        seed: int = 0, sigmas: float = NEEDLE_SIGMAS) -> DecodeCase:
     """Long-context decode with one planted needle key per KV head.
 
-    Draw order: K, V ``[n_rows, H_kv, d_h]``, Q ``[layers, 1, H_q, d_h]`` (all
-    N(0,1)); then for g = 0..H_kv-1 a row p_g = integers(0, n_rows).
+    Streams: 1 K, 2 V ``[n_rows, H_kv, d_h]``, 3 Q ``[layers, 1, H_q, d_h]``
+    (all N(0,1)); stream 4 draws, for g = 0..H_kv-1 in turn, the needle row
+    p_g = integers(0, n_rows).
 
     The needle for KV head g replaces K[p_g, g] by the minimum-norm vector k
     with q.k = sigmas * ||q|| for every stored query q of that group (all
@@ -222,10 +252,10 @@ def make_needle_decode(n_rows: int = 1 << 20, n_q_heads: int = 24, n_kv_heads: i
     those queries.  The solve runs in float64 on the stored queries; the result
     is stored like every other value.
     """
-    rng = np.random.default_rng(seed)
-    kf = _normal(rng, (n_rows, n_kv_heads, head_dim))
-    vf = _normal(rng, (n_rows, n_kv_heads, head_dim))
-    q = store(_normal(rng, (layers, 1, n_q_heads, head_dim)), dtype)
+    kf = _normal(seed, 1, (n_rows, n_kv_heads, head_dim))
+    vf = _normal(seed, 2, (n_rows, n_kv_heads, head_dim))
+    q = store(_normal(seed, 3, (layers, 1, n_q_heads, head_dim)), dtype)
+    rng = _int_rng(seed, 4)
     qf = as_f32(q).astype(np.float64)
     g_size = n_q_heads // n_kv_heads
     pos = np.zeros((1, n_kv_heads), dtype=np.int64)
@@ -281,19 +311,20 @@ def make_prefill(n: int = 32768, n_q_heads: int = 24, n_kv_heads: int = 8,
                  q_start: int = 0, t: Optional[int] = None) -> PrefillCase:
     """Causal full-sequence cross-attention input.
 
-    Draw order: Q ``[t, H_q, d_h]``, K ``[n, H_kv, d_h]``, V (all N(0,1)); then
-    floor(peak_fraction*n) distinct rows ``choice(n, ., replace=False)`` whose
+    Streams: 1 Q ``[t, H_q, d_h]``, 2 K ``[n, H_kv, d_h]``, 3 V (all N(0,1));
+    stream 4 draws floor(peak_fraction*n) distinct rows
+    ``choice(n, ., replace=False)`` whose
     keys (all KV heads) are multiplied by ``peak_scale`` to make peaked softmax
     rows.  A power-of-two scale is exact in bf16, so scaling before or after
     rounding stores the same value.  ``t`` defaults to ``n - q_start``.
     """
     if t is None:
         t = n - q_start
-    rng = np.random.default_rng(seed)
-    qf = _normal(rng, (t, n_q_heads, head_dim))
-    kf = _normal(rng, (n, n_kv_heads, head_dim))
-    vf = _normal(rng, (n, n_kv_heads, head_dim))
+    qf = _normal(seed, 1, (t, n_q_heads, head_dim))
+    kf = _normal(seed, 2, (n, n_kv_heads, head_dim))
+    vf = _normal(seed, 3, (n, n_kv_heads, head_dim))
     n_peak = int(math.floor(peak_fraction * n))
+    rng = _int_rng(seed, 4)
     peaked = np.sort(rng.choice(n, n_peak, replace=False)) if n_peak > 0 else np.zeros(0, np.int64)
     kf[peaked] *= np.float32(peak_scale)
     return PrefillCase(q=store(qf, dtype), k=store(kf, dtype), v=store(vf, dtype),
@@ -320,17 +351,16 @@ def make_project(n: int = 32768, d_model: int = 3072, n_kv_heads: int = 8,
                  head_dim: int = 128, dtype: str = BF16, seed: int = 0,
                  eps: float = 1e-6, unit_gain: bool = True) -> ProjectCase:
     """M ``[n, d_model]`` ~ N(0,1); W_K, W_V ``[d_model, H_kv*d_h]`` ~
-    N(0, 1/d_model).  Draw order: M, W_K, W_V, then (if not unit_gain) the
+    N(0, 1/d_model).  Streams: 1 M, 2 W_K, 3 W_V, 4 (if not unit_gain) the
     RMSNorm gain ~ 1 + 0.1 N(0,1)."""
-    rng = np.random.default_rng(seed)
-    m = store(_normal(rng, (n, d_model)), dtype)
+    m = store(_normal(seed, 1, (n, d_model)), dtype)
     std = 1.0 / math.sqrt(d_model)
-    w_k = store(_normal(rng, (d_model, n_kv_heads * head_dim), std), dtype)
-    w_v = store(_normal(rng, (d_model, n_kv_heads * head_dim), std), dtype)
+    w_k = store(_normal(seed, 2, (d_model, n_kv_heads * head_dim), std), dtype)
+    w_v = store(_normal(seed, 3, (d_model, n_kv_heads * head_dim), std), dtype)
     if unit_gain:
         gain = np.ones(d_model, dtype=np.float32)
     else:
-        gain = (1.0 + 0.1 * _normal(rng, (d_model,))).astype(np.float32)
+        gain = (1.0 + 0.1 * _normal(seed, 4, (d_model,))).astype(np.float32)
     return ProjectCase(m=m, w_k=w_k, w_v=w_v, gain=gain, n_kv_heads=n_kv_heads,
                        head_dim=head_dim, eps=eps, dtype=dtype)
 

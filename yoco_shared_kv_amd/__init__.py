@@ -1,0 +1,201 @@
+"""MI355X-native shared-KV cross-decoder hot path of YOCO.
+
+Thin Python binding over the C ABI declared in ``include/yoco.h`` (built as
+``libyoco.so`` from ``csrc/``).  Every step of the path runs in the HIP
+kernels; this module only passes pointers, sizes and the current stream.
+PyTorch provides device memory and streams.
+
+The functions mirror the C entry points:
+
+* ``kv_project``      -> ``yoco_kv_project``   (RMSNorm + K^/V^ projection into the cache)
+* ``kv_append``       -> ``yoco_kv_append``    (one new row per sequence)
+* ``q_project``       -> ``yoco_q_project``    (per-layer RMSNorm + Q^ projection)
+* ``cross_attn_prefill`` -> ``yoco_cross_attn_prefill`` (causal block over the cache)
+* ``cross_attn_decode``  -> ``yoco_cross_attn_decode``  (one token per sequence, split-N)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+from ._native import (YOCO_DECODE_COUNTER_BYTES, YOCO_DT_BF16, YOCO_DT_F32, KVCacheStruct,
+                      YocoError, check, lib)
+
+__all__ = [
+    "KVCache", "YocoError", "kv_project", "kv_append", "q_project", "cross_attn_prefill",
+    "cross_attn_decode", "decode_workspace", "decode_workspace_bytes", "kv_cache_bytes", "lib",
+]
+
+_DT = {torch.float32: YOCO_DT_F32, torch.bfloat16: YOCO_DT_BF16}
+
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16") from None
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _on_device(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("inputs must be device tensors")
+
+
+class KVCache:
+    """The one shared K^/V^ cache: k, v ``[n_seq, capacity, H_kv, d_h]`` on the
+    device plus host lengths ``len`` (numpy int64, advanced by project/append)."""
+
+    def __init__(self, n_seq: int, capacity: int, n_kv_heads: int, head_dim: int,
+                 dtype: torch.dtype = torch.bfloat16, device="cuda", zero: bool = False):
+        alloc = torch.zeros if zero else torch.empty
+        shape = (n_seq, capacity, n_kv_heads, head_dim)
+        self.k = alloc(shape, dtype=dtype, device=device)
+        self.v = alloc(shape, dtype=dtype, device=device)
+        self.len = np.zeros(n_seq, dtype=np.int64)
+        self.n_seq, self.capacity = n_seq, capacity
+        self.n_kv_heads, self.head_dim, self.dtype = n_kv_heads, head_dim, dtype
+        self._struct = None
+
+    @classmethod
+    def wrap(cls, k: torch.Tensor, v: torch.Tensor, lens) -> "KVCache":
+        """Use existing k/v tensors ``[n_seq, capacity, H_kv, d_h]``."""
+        obj = cls.__new__(cls)
+        if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 4:
+            raise ValueError("k and v must be matching [n_seq, capacity, H_kv, d_h] tensors")
+        obj.k, obj.v = k, v
+        obj.n_seq, obj.capacity, obj.n_kv_heads, obj.head_dim = k.shape
+        obj.dtype = k.dtype
+        obj.len = np.ascontiguousarray(np.asarray(lens, dtype=np.int64).reshape(obj.n_seq))
+        obj._struct = None
+        return obj
+
+    def struct(self) -> KVCacheStruct:
+        _on_device(self.k, self.v)
+        s = KVCacheStruct()
+        s.k = self.k.data_ptr()
+        s.v = self.v.data_ptr()
+        s.len_host = self.len.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        s.seq_capacity = self.capacity
+        s.n_seq = self.n_seq
+        s.n_kv_heads = self.n_kv_heads
+        s.head_dim = self.head_dim
+        s.dtype = _dt(self.k)
+        self._struct = s  # keep alive with the numpy buffer it points into
+        return s
+
+
+def kv_cache_bytes(n_seq: int, capacity: int, n_kv_heads: int, head_dim: int,
+                   dtype: torch.dtype = torch.bfloat16) -> int:
+    """Bytes of one of k / v (host-only; see ``yoco_kv_cache_bytes``)."""
+    out = ctypes.c_size_t(0)
+    check(lib().yoco_kv_cache_bytes(n_seq, capacity, n_kv_heads, head_dim,
+                                    _DT.get(dtype, -1), ctypes.byref(out)))
+    return int(out.value)
+
+
+def kv_project(cache: KVCache, m: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor,
+               gain: Optional[torch.Tensor] = None, eps: float = 1e-6, seq: int = 0,
+               row_start: int = 0, stream=None) -> None:
+    """RMSNorm(M) W_K and RMSNorm(M) W_V into cache rows [row_start, row_start+n)."""
+    _on_device(m, w_k, w_v, gain)
+    if w_k.dtype != w_v.dtype:
+        raise TypeError("w_k and w_v must share a dtype")
+    n, d = m.shape
+    s = cache.struct()
+    check(lib().yoco_kv_project(_ptr(m), _dt(m), n, d, _ptr(gain), eps, _ptr(w_k), _ptr(w_v),
+                                _dt(w_k), ctypes.byref(s), seq, row_start, _stream(stream)))
+
+
+def kv_append(cache: KVCache, m_new: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor,
+              gain: Optional[torch.Tensor] = None, eps: float = 1e-6, stream=None) -> None:
+    """Project one new row per sequence (m_new ``[n_seq, d_model]``) and append it."""
+    _on_device(m_new, w_k, w_v, gain)
+    if w_k.dtype != w_v.dtype:
+        raise TypeError("w_k and w_v must share a dtype")
+    s = cache.struct()
+    check(lib().yoco_kv_append(_ptr(m_new), _dt(m_new), m_new.shape[1], _ptr(gain), eps,
+                               _ptr(w_k), _ptr(w_v), _dt(w_k), ctypes.byref(s), _stream(stream)))
+
+
+def q_project(x: torch.Tensor, w_q: torch.Tensor, n_q_heads: int, head_dim: int,
+              gain: Optional[torch.Tensor] = None, eps: float = 1e-6,
+              out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """RMSNorm_l(X) W_Q^l -> ``[n, H_q, d_h]``."""
+    _on_device(x, w_q, gain)
+    n, d = x.shape
+    if out is None:
+        out = torch.empty((n, n_q_heads, head_dim), dtype=out_dtype or x.dtype, device=x.device)
+    check(lib().yoco_q_project(_ptr(x), _dt(x), n, d, _ptr(gain), eps, _ptr(w_q), _dt(w_q),
+                               n_q_heads, head_dim, _ptr(out), _dt(out), _stream(stream)))
+    return out
+
+
+def cross_attn_prefill(q: torch.Tensor, cache: KVCache, seq: int = 0, q_start: int = 0,
+                       softmax_scale: Optional[float] = None,
+                       out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None,
+                       want_lse: bool = False, stream=None):
+    """Causal attention of q ``[t, H_q, d_h]`` (row i at position q_start+i)
+    over sequence ``seq`` of the shared cache.  Returns o (and lse)."""
+    _on_device(q)
+    t, hq, dh = q.shape
+    scale = 1.0 / math.sqrt(dh) if softmax_scale is None else softmax_scale
+    if out is None:
+        out = torch.empty((t, hq, dh), dtype=out_dtype, device=q.device)
+    lse = torch.empty((t, hq), dtype=torch.float32, device=q.device) if want_lse else None
+    s = cache.struct()
+    check(lib().yoco_cross_attn_prefill(_ptr(q), _dt(q), q_start, t, hq, ctypes.byref(s), seq,
+                                        scale, _ptr(out), _dt(out), _ptr(lse), _stream(stream)))
+    return (out, lse) if want_lse else out
+
+
+def decode_workspace_bytes(cache: KVCache, n_q_heads: int, rows_per_split: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    s = cache.struct()
+    check(lib().yoco_cross_attn_decode_workspace(ctypes.byref(s), n_q_heads, rows_per_split,
+                                                 ctypes.byref(out)))
+    return int(out.value)
+
+
+def decode_workspace(cache: KVCache, n_q_heads: int, rows_per_split: int = 0) -> torch.Tensor:
+    """A zero-filled workspace large enough for any length up to capacity."""
+    nbytes = decode_workspace_bytes(cache, n_q_heads, rows_per_split)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=cache.k.device)
+
+
+def cross_attn_decode(q: torch.Tensor, cache: KVCache, softmax_scale: Optional[float] = None,
+                      workspace: Optional[torch.Tensor] = None, rows_per_split: int = 0,
+                      out: Optional[torch.Tensor] = None, want_lse: bool = False, stream=None):
+    """One decode step of one cross layer: q ``[n_seq, H_q, d_h]`` at position
+    len-1 of every sequence.  Returns o ``[n_seq, H_q, d_h]`` fp32 (and lse)."""
+    _on_device(q)
+    n_seq, hq, dh = q.shape
+    scale = 1.0 / math.sqrt(dh) if softmax_scale is None else softmax_scale
+    if workspace is None:
+        workspace = decode_workspace(cache, hq, rows_per_split)
+    if out is None:
+        out = torch.empty((n_seq, hq, dh), dtype=torch.float32, device=q.device)
+    lse = torch.empty((n_seq, hq), dtype=torch.float32, device=q.device) if want_lse else None
+    s = cache.struct()
+    check(lib().yoco_cross_attn_decode(_ptr(q), _dt(q), hq, ctypes.byref(s), scale, _ptr(out),
+                                       _ptr(lse), _ptr(workspace), workspace.numel(),
+                                       rows_per_split, _stream(stream)))
+    return (out, lse) if want_lse else out

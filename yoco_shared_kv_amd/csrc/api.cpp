@@ -1,0 +1,371 @@
+// Host side of the C ABI: argument validation, split planning and dispatch.
+// Every check runs before anything is enqueued; on failure nothing is
+// enqueued and no host length changes.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "yoco_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+yoco_status fail(yoco_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+yoco_status ok() {
+  g_err[0] = '\0';
+  return YOCO_OK;
+}
+
+bool dtype_ok(int32_t dt) { return dt == YOCO_DT_F32 || dt == YOCO_DT_BF16; }
+size_t dtype_size(int32_t dt) { return dt == YOCO_DT_F32 ? 4 : 2; }
+bool head_dim_ok(int32_t dh) { return dh == 64 || dh == 128; }
+bool group_ok(int32_t g) { return g == 1 || g == 2 || g == 3 || g == 4 || g == 6 || g == 8; }
+
+// The kernels are built for gfx950 only; refuse any other device loudly.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+yoco_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(YOCO_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(YOCO_ERR_HIP, "device index %d out of range", dev);
+  int st = g_dev_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(YOCO_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_state[dev].store(st, std::memory_order_release);
+    if (st == 2) return fail(YOCO_ERR_HIP, "device %d is %s; this library is built for gfx950", dev, prop.gcnArchName);
+  }
+  if (st != 1) return fail(YOCO_ERR_HIP, "device %d is not gfx950", dev);
+  return YOCO_OK;
+}
+
+yoco_status launched(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(YOCO_ERR_HIP, "%s launch: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+yoco_status check_cache(const yoco_kv_cache *c) {
+  if (c == nullptr) return fail(YOCO_ERR_NULL_POINTER, "cache is NULL");
+  if (c->k == nullptr || c->v == nullptr) return fail(YOCO_ERR_NULL_POINTER, "cache k or v is NULL");
+  if (c->len_host == nullptr) return fail(YOCO_ERR_NULL_POINTER, "cache len_host is NULL");
+  if (c->n_seq < 1 || c->n_seq > YOCO_MAX_SEQ)
+    return fail(YOCO_ERR_BAD_SHAPE, "n_seq %d outside [1, %d]", c->n_seq, YOCO_MAX_SEQ);
+  if (c->n_kv_heads < 1 || c->n_kv_heads > yoco::kMaxKvHeads)
+    return fail(YOCO_ERR_BAD_SHAPE, "n_kv_heads %d outside [1, %d]", c->n_kv_heads, yoco::kMaxKvHeads);
+  if (!head_dim_ok(c->head_dim)) return fail(YOCO_ERR_BAD_SHAPE, "head_dim %d is not 64 or 128", c->head_dim);
+  if (c->seq_capacity < 1 || c->seq_capacity > (int64_t(1) << 31) - 1)
+    return fail(YOCO_ERR_BAD_SHAPE, "seq_capacity %lld outside [1, 2^31)", (long long)c->seq_capacity);
+  if (!dtype_ok(c->dtype)) return fail(YOCO_ERR_BAD_DTYPE, "cache dtype %d unknown", c->dtype);
+  return YOCO_OK;
+}
+
+yoco_status check_eps(float eps) {
+  if (!std::isfinite(eps) || eps < 0.f) return fail(YOCO_ERR_BAD_VALUE, "eps %g must be finite and >= 0", eps);
+  return YOCO_OK;
+}
+
+yoco_status check_heads(int32_t n_q_heads, int32_t n_kv_heads) {
+  if (n_q_heads < 1 || n_q_heads % n_kv_heads != 0)
+    return fail(YOCO_ERR_BAD_SHAPE, "n_q_heads %d is not a positive multiple of n_kv_heads %d", n_q_heads, n_kv_heads);
+  if (!group_ok(n_q_heads / n_kv_heads))
+    return fail(YOCO_ERR_BAD_SHAPE, "group size %d not in {1,2,3,4,6,8}", n_q_heads / n_kv_heads);
+  return YOCO_OK;
+}
+
+yoco_status check_scale(float s) {
+  if (!std::isfinite(s) || s <= 0.f) return fail(YOCO_ERR_BAD_VALUE, "softmax_scale %g must be finite and > 0", s);
+  return YOCO_OK;
+}
+
+// ---- decode split planning -------------------------------------------------
+// Library split size: enough splits for ~kTargetBlocks workgroups over all
+// (sequence, KV head) pairs at the current lengths, rounded to the quantum,
+// at least kMinSplitRows rows so that merge traffic stays ~1% of the stream.
+constexpr int64_t kTargetBlocks = 512;
+constexpr int64_t kMinSplitRows = 1024;
+
+int64_t auto_split_rows(const int64_t *lens, int n_seq, int n_kv_heads) {
+  int64_t total = 0;
+  for (int b = 0; b < n_seq; ++b) total += lens[b];
+  const int64_t want_splits = (kTargetBlocks + n_kv_heads - 1) / n_kv_heads;
+  int64_t rows = (total + want_splits - 1) / want_splits;
+  rows = ((rows + yoco::kDecodeSplitQuantum - 1) / yoco::kDecodeSplitQuantum) * yoco::kDecodeSplitQuantum;
+  if (rows < kMinSplitRows) rows = kMinSplitRows;
+  return rows;
+}
+
+// Upper bound of total splits over every length <= capacity for a split size.
+// With the library's choice the split size grows with the total length, so
+// the bound is want_splits + n_seq; with a fixed size it is n_seq*ceil(cap/rows).
+int64_t max_total_splits(const yoco_kv_cache *c, int64_t rows_per_split) {
+  if (rows_per_split == 0) {
+    const int64_t want_splits = (kTargetBlocks + c->n_kv_heads - 1) / c->n_kv_heads;
+    const int64_t fixed_bound = c->n_seq * ((c->seq_capacity + kMinSplitRows - 1) / kMinSplitRows);
+    const int64_t growing_bound = want_splits + c->n_seq;
+    return fixed_bound < growing_bound ? fixed_bound : growing_bound;
+  }
+  return c->n_seq * ((c->seq_capacity + rows_per_split - 1) / rows_per_split);
+}
+
+size_t decode_workspace_bytes(const yoco_kv_cache *c, int32_t n_q_heads, int64_t total_splits) {
+  const int64_t group = n_q_heads / c->n_kv_heads;
+  const int64_t prow = c->head_dim + 4;
+  return YOCO_DECODE_COUNTER_BYTES +
+         static_cast<size_t>(total_splits) * c->n_kv_heads * group * prow * sizeof(float);
+}
+
+yoco_status check_split_rows(int64_t rows_per_split) {
+  if (rows_per_split < 0 || (rows_per_split % yoco::kDecodeSplitQuantum) != 0 ||
+      rows_per_split > (int64_t(1) << 30))
+    return fail(YOCO_ERR_BAD_VALUE, "rows_per_split %lld must be 0 or a positive multiple of %d",
+                (long long)rows_per_split, yoco::kDecodeSplitQuantum);
+  return YOCO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int yoco_abi_version(void) { return YOCO_ABI_VERSION; }
+
+const char *yoco_last_error(void) { return g_err; }
+
+yoco_status yoco_kv_cache_bytes(int32_t n_seq, int64_t seq_capacity, int32_t n_kv_heads, int32_t head_dim,
+                                int32_t dtype, size_t *bytes) {
+  if (bytes == nullptr) return fail(YOCO_ERR_NULL_POINTER, "bytes is NULL");
+  if (n_seq < 1 || seq_capacity < 1 || n_kv_heads < 1 || head_dim < 1)
+    return fail(YOCO_ERR_BAD_SHAPE, "cache dimensions must be positive");
+  if (!dtype_ok(dtype)) return fail(YOCO_ERR_BAD_DTYPE, "dtype %d unknown", dtype);
+  *bytes = static_cast<size_t>(n_seq) * static_cast<size_t>(seq_capacity) * n_kv_heads * head_dim *
+           dtype_size(dtype);
+  return ok();
+}
+
+yoco_status yoco_kv_project(const void *m, int32_t m_dtype, int64_t n, int32_t d_model, const float *gain,
+                            float eps, const void *w_k, const void *w_v, int32_t w_dtype,
+                            yoco_kv_cache *cache, int32_t seq, int64_t row_start, void *stream) {
+  yoco_status st = check_cache(cache);
+  if (st != YOCO_OK) return st;
+  if (m == nullptr || w_k == nullptr || w_v == nullptr) return fail(YOCO_ERR_NULL_POINTER, "m, w_k or w_v is NULL");
+  if (d_model < 1) return fail(YOCO_ERR_BAD_SHAPE, "d_model %d < 1", d_model);
+  if (seq < 0 || seq >= cache->n_seq) return fail(YOCO_ERR_BAD_SHAPE, "seq %d outside [0, %d)", seq, cache->n_seq);
+  if (!dtype_ok(m_dtype) || !dtype_ok(w_dtype)) return fail(YOCO_ERR_BAD_DTYPE, "m or w dtype unknown");
+  if ((st = check_eps(eps)) != YOCO_OK) return st;
+  if (n < 0 || row_start < 0 || row_start > cache->seq_capacity - n)
+    return fail(YOCO_ERR_OUT_OF_RANGE, "rows [%lld, %lld) outside capacity %lld", (long long)row_start,
+                (long long)(row_start + n), (long long)cache->seq_capacity);
+  if (n == 0) return ok();
+  if ((st = check_device()) != YOCO_OK) return st;
+
+  yoco::ProjArgs a{};
+  a.x = m;
+  a.gain = gain;
+  a.w[0] = w_k;
+  a.w[1] = w_v;
+  a.out[0] = cache->k;
+  a.out[1] = cache->v;
+  a.n = n;
+  a.dst_row_base = static_cast<int64_t>(seq) * cache->seq_capacity + row_start;
+  a.d = d_model;
+  a.ncols = cache->n_kv_heads * cache->head_dim;
+  a.n_out = 2;
+  a.indexed = 0;
+  a.eps = eps;
+  st = launched(yoco::launch_project(a, m_dtype, w_dtype, cache->dtype, static_cast<hipStream_t>(stream)),
+                "kv_project");
+  if (st != YOCO_OK) return st;
+  if (cache->len_host[seq] < row_start + n) cache->len_host[seq] = row_start + n;
+  return ok();
+}
+
+yoco_status yoco_kv_append(const void *m_new, int32_t m_dtype, int32_t d_model, const float *gain, float eps,
+                           const void *w_k, const void *w_v, int32_t w_dtype, yoco_kv_cache *cache,
+                           void *stream) {
+  yoco_status st = check_cache(cache);
+  if (st != YOCO_OK) return st;
+  if (m_new == nullptr || w_k == nullptr || w_v == nullptr)
+    return fail(YOCO_ERR_NULL_POINTER, "m_new, w_k or w_v is NULL");
+  if (d_model < 1) return fail(YOCO_ERR_BAD_SHAPE, "d_model %d < 1", d_model);
+  if (!dtype_ok(m_dtype) || !dtype_ok(w_dtype)) return fail(YOCO_ERR_BAD_DTYPE, "m or w dtype unknown");
+  if ((st = check_eps(eps)) != YOCO_OK) return st;
+  for (int b = 0; b < cache->n_seq; ++b) {
+    const int64_t len = cache->len_host[b];
+    if (len < 0 || len + 1 > cache->seq_capacity)
+      return fail(YOCO_ERR_OUT_OF_RANGE, "sequence %d: length %lld leaves no room under capacity %lld", b,
+                  (long long)len, (long long)cache->seq_capacity);
+  }
+  if ((st = check_device()) != YOCO_OK) return st;
+
+  yoco::ProjArgs a{};
+  a.x = m_new;
+  a.gain = gain;
+  a.w[0] = w_k;
+  a.w[1] = w_v;
+  a.out[0] = cache->k;
+  a.out[1] = cache->v;
+  a.n = cache->n_seq;
+  a.dst_row_base = 0;
+  a.d = d_model;
+  a.ncols = cache->n_kv_heads * cache->head_dim;
+  a.n_out = 2;
+  a.indexed = 1;
+  a.eps = eps;
+  for (int b = 0; b < cache->n_seq; ++b) a.dst_rows[b] = static_cast<int64_t>(b) * cache->seq_capacity + cache->len_host[b];
+  st = launched(yoco::launch_project(a, m_dtype, w_dtype, cache->dtype, static_cast<hipStream_t>(stream)),
+                "kv_append");
+  if (st != YOCO_OK) return st;
+  for (int b = 0; b < cache->n_seq; ++b) cache->len_host[b] += 1;
+  return ok();
+}
+
+yoco_status yoco_q_project(const void *x, int32_t x_dtype, int64_t n, int32_t d_model, const float *gain,
+                           float eps, const void *w_q, int32_t w_dtype, int32_t n_q_heads, int32_t head_dim,
+                           void *q_out, int32_t q_dtype, void *stream) {
+  if (x == nullptr || w_q == nullptr || q_out == nullptr) return fail(YOCO_ERR_NULL_POINTER, "x, w_q or q_out is NULL");
+  if (d_model < 1 || n_q_heads < 1 || n < 0) return fail(YOCO_ERR_BAD_SHAPE, "d_model, n_q_heads and n must be positive");
+  if (!head_dim_ok(head_dim)) return fail(YOCO_ERR_BAD_SHAPE, "head_dim %d is not 64 or 128", head_dim);
+  if (!dtype_ok(x_dtype) || !dtype_ok(w_dtype) || !dtype_ok(q_dtype))
+    return fail(YOCO_ERR_BAD_DTYPE, "x, w or q dtype unknown");
+  yoco_status st = check_eps(eps);
+  if (st != YOCO_OK) return st;
+  if (n == 0) return ok();
+  if ((st = check_device()) != YOCO_OK) return st;
+
+  yoco::ProjArgs a{};
+  a.x = x;
+  a.gain = gain;
+  a.w[0] = w_q;
+  a.w[1] = nullptr;
+  a.out[0] = q_out;
+  a.out[1] = nullptr;
+  a.n = n;
+  a.dst_row_base = 0;
+  a.d = d_model;
+  a.ncols = n_q_heads * head_dim;
+  a.n_out = 1;
+  a.indexed = 0;
+  a.eps = eps;
+  return launched(yoco::launch_project(a, x_dtype, w_dtype, q_dtype, static_cast<hipStream_t>(stream)),
+                  "q_project");
+}
+
+yoco_status yoco_cross_attn_prefill(const void *q, int32_t q_dtype, int64_t q_start, int64_t t, int32_t n_q_heads,
+                                    const yoco_kv_cache *cache, int32_t seq, float softmax_scale, void *o,
+                                    int32_t o_dtype, float *lse, void *stream) {
+  yoco_status st = check_cache(cache);
+  if (st != YOCO_OK) return st;
+  if (q == nullptr || o == nullptr) return fail(YOCO_ERR_NULL_POINTER, "q or o is NULL");
+  if ((st = check_heads(n_q_heads, cache->n_kv_heads)) != YOCO_OK) return st;
+  if (seq < 0 || seq >= cache->n_seq) return fail(YOCO_ERR_BAD_SHAPE, "seq %d outside [0, %d)", seq, cache->n_seq);
+  if (q_dtype != cache->dtype) return fail(YOCO_ERR_BAD_DTYPE, "q dtype %d differs from cache dtype %d", q_dtype, cache->dtype);
+  if (!dtype_ok(o_dtype)) return fail(YOCO_ERR_BAD_DTYPE, "o dtype %d unknown", o_dtype);
+  if ((st = check_scale(softmax_scale)) != YOCO_OK) return st;
+  const int64_t len = cache->len_host[seq];
+  if (q_start < 0 || t < 0 || len > cache->seq_capacity || q_start > len - t)
+    return fail(YOCO_ERR_OUT_OF_RANGE, "query rows at positions [%lld, %lld) exceed cache length %lld",
+                (long long)q_start, (long long)(q_start + t), (long long)len);
+  if (t == 0) return ok();
+  if ((st = check_device()) != YOCO_OK) return st;
+
+  const size_t esz = dtype_size(cache->dtype);
+  const int64_t slab = static_cast<int64_t>(seq) * cache->seq_capacity * cache->n_kv_heads * cache->head_dim;
+  yoco::PrefillArgs a{};
+  a.q = q;
+  a.k = static_cast<const char *>(cache->k) + slab * esz;
+  a.v = static_cast<const char *>(cache->v) + slab * esz;
+  a.o = o;
+  a.lse = lse;
+  a.q_start = q_start;
+  a.t = t;
+  a.kv_len = len;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = cache->n_kv_heads;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.o_bf16 = (o_dtype == YOCO_DT_BF16) ? 1 : 0;
+  return launched(yoco::launch_prefill(a, cache->dtype, cache->head_dim, static_cast<hipStream_t>(stream)),
+                  "cross_attn_prefill");
+}
+
+yoco_status yoco_cross_attn_decode_workspace(const yoco_kv_cache *cache, int32_t n_q_heads, int64_t rows_per_split,
+                                             size_t *bytes) {
+  yoco_status st = check_cache(cache);
+  if (st != YOCO_OK) return st;
+  if (bytes == nullptr) return fail(YOCO_ERR_NULL_POINTER, "bytes is NULL");
+  if ((st = check_heads(n_q_heads, cache->n_kv_heads)) != YOCO_OK) return st;
+  if ((st = check_split_rows(rows_per_split)) != YOCO_OK) return st;
+  *bytes = decode_workspace_bytes(cache, n_q_heads, max_total_splits(cache, rows_per_split));
+  return ok();
+}
+
+yoco_status yoco_cross_attn_decode(const void *q, int32_t q_dtype, int32_t n_q_heads, const yoco_kv_cache *cache,
+                                   float softmax_scale, float *o, float *lse, void *workspace,
+                                   size_t workspace_bytes, int64_t rows_per_split, void *stream) {
+  yoco_status st = check_cache(cache);
+  if (st != YOCO_OK) return st;
+  if (q == nullptr || o == nullptr || workspace == nullptr)
+    return fail(YOCO_ERR_NULL_POINTER, "q, o or workspace is NULL");
+  if ((st = check_heads(n_q_heads, cache->n_kv_heads)) != YOCO_OK) return st;
+  if (q_dtype != cache->dtype) return fail(YOCO_ERR_BAD_DTYPE, "q dtype %d differs from cache dtype %d", q_dtype, cache->dtype);
+  if ((st = check_scale(softmax_scale)) != YOCO_OK) return st;
+  if ((st = check_split_rows(rows_per_split)) != YOCO_OK) return st;
+  for (int b = 0; b < cache->n_seq; ++b) {
+    const int64_t len = cache->len_host[b];
+    if (len < 1 || len > cache->seq_capacity)
+      return fail(YOCO_ERR_OUT_OF_RANGE, "sequence %d: length %lld outside [1, %lld]", b, (long long)len,
+                  (long long)cache->seq_capacity);
+  }
+  const int64_t rows =
+      rows_per_split != 0 ? rows_per_split : auto_split_rows(cache->len_host, cache->n_seq, cache->n_kv_heads);
+  yoco::DecodeArgs a{};
+  int64_t total = 0;
+  for (int b = 0; b < cache->n_seq; ++b) {
+    a.split_begin[b] = static_cast<int32_t>(total);
+    a.len[b] = static_cast<int32_t>(cache->len_host[b]);
+    total += (cache->len_host[b] + rows - 1) / rows;
+  }
+  a.split_begin[cache->n_seq] = static_cast<int32_t>(total);
+  const size_t need = decode_workspace_bytes(cache, n_q_heads, total);
+  if (workspace_bytes < need)
+    return fail(YOCO_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  if (total * cache->n_kv_heads > (int64_t(1) << 31) - 1)
+    return fail(YOCO_ERR_BAD_VALUE, "too many splits (%lld)", (long long)total);
+  if ((st = check_device()) != YOCO_OK) return st;
+
+  const int group = n_q_heads / cache->n_kv_heads;
+  a.k = cache->k;
+  a.v = cache->v;
+  a.q = q;
+  a.o = o;
+  a.lse = lse;
+  a.counters = static_cast<unsigned int *>(workspace);
+  a.part_acc = reinterpret_cast<float *>(static_cast<char *>(workspace) + YOCO_DECODE_COUNTER_BYTES);
+  a.part_ml = nullptr;
+  a.seq_stride = cache->seq_capacity * cache->n_kv_heads * cache->head_dim;
+  a.n_seq = cache->n_seq;
+  a.n_kv_heads = cache->n_kv_heads;
+  a.n_q_heads = n_q_heads;
+  a.split_rows = static_cast<int32_t>(rows);
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.total_splits = static_cast<int32_t>(total);
+  return launched(yoco::launch_decode(a, cache->dtype, cache->head_dim, group, static_cast<hipStream_t>(stream)),
+                  "cross_attn_decode");
+}
+
+}  // extern "C"
