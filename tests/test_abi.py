@@ -174,8 +174,8 @@ def test_decode_workspace_sizes():
     st, auto = _ws_bytes(c, hq=24)
     assert st == 0
     counters = 256 * 64 * 4
-    # library split size: at most 64 splits per KV head plus one per sequence
-    assert auto == counters + (64 + 1) * 8 * 3 * (128 + 4) * 4
+    # library split size: splits <= min(n_seq*ceil(cap/256), ceil(4096/H_kv) + n_seq)
+    assert auto == counters + min(131072 // 256, 4096 // 8 + 1) * 8 * 3 * (128 + 4) * 4
     st, fixed = _ws_bytes(c, hq=24, rows=256)
     assert st == 0 and fixed == counters + 512 * 8 * 3 * 132 * 4
     assert _ws_bytes(c, hq=24, rows=100)[0] == _status("YOCO_ERR_BAD_VALUE")

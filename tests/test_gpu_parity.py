@@ -300,3 +300,39 @@ def test_q_project_bf16_parity():
     assert q.shape == (33, 24, 128) and q.dtype == torch.bfloat16
     abs_terms = np.abs(orc().rmsnorm(x)) @ np.abs(W.as_f32(wq).astype(np.float64))
     assert_projection_bf16(to_stored(q).reshape(33, -1), orc().project(x, wq), abs_terms, 3072, "Q^")
+
+
+@pytest.mark.parametrize("dtype,n,d", [(W.BF16, 1, 3072), (W.BF16, 5, 3072), (W.BF16, 13, 3072),
+                                       (W.BF16, 16, 3072), (W.F32, 1, 256), (W.F32, 8, 256),
+                                       (W.F32, 30, 512), (W.BF16, 3, 8192)])
+def test_small_row_projection_parity(dtype, n, d):
+    """Few-row projections (generation-time append and per-token queries) run
+    on the matrix-vector kernel, in launches of up to 8 rows."""
+    p = W.make_project(n=n, d_model=d, dtype=dtype, unit_gain=False, seed=24)
+    tdt = torch.bfloat16 if dtype == W.BF16 else torch.float32
+    cache = y.KVCache(1, n + 7, 8, 128, tdt)
+    cache.k.fill_(7.0)
+    cache.v.fill_(7.0)
+    y.kv_project(cache, to_dev(p.m), to_dev(p.w_k), to_dev(p.w_v), torch.from_numpy(p.gain).cuda(), p.eps,
+                 row_start=3)
+    k = to_stored(cache.k[0, 3:3 + n]).reshape(n, -1)
+    v = to_stored(cache.v[0, 3:3 + n]).reshape(n, -1)
+    rk = orc().project(p.m, p.w_k, p.gain, p.eps)
+    rv = orc().project(p.m, p.w_v, p.gain, p.eps)
+    if dtype == W.BF16:
+        ynorm = np.abs(orc().rmsnorm(p.m, p.gain, p.eps))
+        assert_projection_bf16(k, rk, ynorm @ np.abs(W.as_f32(p.w_k).astype(np.float64)), d, "K^")
+        assert_projection_bf16(v, rv, ynorm @ np.abs(W.as_f32(p.w_v).astype(np.float64)), d, "V^")
+    else:
+        assert_parity(k, rk, bf16=False, what="K^")
+        assert_parity(v, rv, bf16=False, what="V^")
+    assert torch.all(cache.k[0, :3] == 7.0) and torch.all(cache.k[0, 3 + n:] == 7.0)
+
+
+def test_q_project_single_token():
+    r = rng(25)
+    x = W.store(r.standard_normal((1, 3072)).astype(np.float32), W.BF16)
+    wq = W.store((r.standard_normal((3072, 24 * 128)) / math.sqrt(3072)).astype(np.float32), W.BF16)
+    gain = (1 + 0.1 * r.standard_normal(3072)).astype(np.float32)
+    q = y.q_project(to_dev(x), to_dev(wq), 24, 128, torch.from_numpy(gain).cuda(), out_dtype=torch.float32)
+    assert_parity(to_stored(q).reshape(1, -1), orc().project(x, wq, gain), bf16=False, what="Q^ (fp32 out)")

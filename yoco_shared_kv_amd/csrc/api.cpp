@@ -95,30 +95,54 @@ yoco_status check_scale(float s) {
 }
 
 // ---- decode split planning -------------------------------------------------
-// Library split size: enough splits for ~kTargetBlocks workgroups over all
-// (sequence, KV head) pairs at the current lengths, rounded to the quantum,
-// at least kMinSplitRows rows so that merge traffic stays ~1% of the stream.
-constexpr int64_t kTargetBlocks = 512;
-constexpr int64_t kMinSplitRows = 1024;
+// Library split size: enough splits that the decode grid fills the device in
+// one resident round (CUs x resident workgroups per CU, capped), rounded to
+// kDecodeAutoQuantum rows, at least kDecodeMinSplitRows.  The workspace bound
+// below holds for any device because the target is capped.
+struct DeviceInfo {
+  std::atomic<int> cus{0};
+  std::atomic<int> occ[2][2][9];  // [dtype][head_dim == 128][group]
+};
+DeviceInfo g_dev_info[kMaxDevices];
 
-int64_t auto_split_rows(const int64_t *lens, int n_seq, int n_kv_heads) {
+int decode_target_blocks(int dtype, int head_dim, int group) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  DeviceInfo &info = g_dev_info[dev];
+  int cus = info.cus.load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    info.cus.store(cus, std::memory_order_relaxed);
+  }
+  std::atomic<int> &slot = info.occ[dtype == YOCO_DT_BF16 ? 1 : 0][head_dim == 128 ? 1 : 0][group];
+  int occ = slot.load(std::memory_order_relaxed);
+  if (occ == 0) {
+    occ = yoco::decode_blocks_per_cu(dtype, head_dim, group);
+    if (occ <= 0) occ = 1;
+    slot.store(occ, std::memory_order_relaxed);
+  }
+  const int64_t target = static_cast<int64_t>(cus) * occ;
+  return static_cast<int>(target < yoco::kDecodeMaxTargetBlocks ? target : yoco::kDecodeMaxTargetBlocks);
+}
+
+int64_t auto_split_rows(const int64_t *lens, int n_seq, int n_kv_heads, int64_t target_blocks) {
   int64_t total = 0;
   for (int b = 0; b < n_seq; ++b) total += lens[b];
-  const int64_t want_splits = (kTargetBlocks + n_kv_heads - 1) / n_kv_heads;
-  int64_t rows = (total + want_splits - 1) / want_splits;
-  rows = ((rows + yoco::kDecodeSplitQuantum - 1) / yoco::kDecodeSplitQuantum) * yoco::kDecodeSplitQuantum;
-  if (rows < kMinSplitRows) rows = kMinSplitRows;
+  const int64_t work = total * n_kv_heads;
+  int64_t rows = (work + target_blocks - 1) / target_blocks;
+  rows = ((rows + yoco::kDecodeAutoQuantum - 1) / yoco::kDecodeAutoQuantum) * yoco::kDecodeAutoQuantum;
+  if (rows < yoco::kDecodeMinSplitRows) rows = yoco::kDecodeMinSplitRows;
   return rows;
 }
 
 // Upper bound of total splits over every length <= capacity for a split size.
-// With the library's choice the split size grows with the total length, so
-// the bound is want_splits + n_seq; with a fixed size it is n_seq*ceil(cap/rows).
+// Library choice: rows >= total*H/target, so splits <= target/H + n_seq, and
+// rows >= kDecodeMinSplitRows bounds it by n_seq*ceil(cap/kDecodeMinSplitRows).
 int64_t max_total_splits(const yoco_kv_cache *c, int64_t rows_per_split) {
   if (rows_per_split == 0) {
-    const int64_t want_splits = (kTargetBlocks + c->n_kv_heads - 1) / c->n_kv_heads;
-    const int64_t fixed_bound = c->n_seq * ((c->seq_capacity + kMinSplitRows - 1) / kMinSplitRows);
-    const int64_t growing_bound = want_splits + c->n_seq;
+    const int64_t fixed_bound =
+        c->n_seq * ((c->seq_capacity + yoco::kDecodeMinSplitRows - 1) / yoco::kDecodeMinSplitRows);
+    const int64_t growing_bound = (yoco::kDecodeMaxTargetBlocks + c->n_kv_heads - 1) / c->n_kv_heads + c->n_seq;
     return fixed_bound < growing_bound ? fixed_bound : growing_bound;
   }
   return c->n_seq * ((c->seq_capacity + rows_per_split - 1) / rows_per_split);
@@ -331,8 +355,16 @@ yoco_status yoco_cross_attn_decode(const void *q, int32_t q_dtype, int32_t n_q_h
       return fail(YOCO_ERR_OUT_OF_RANGE, "sequence %d: length %lld outside [1, %lld]", b, (long long)len,
                   (long long)cache->seq_capacity);
   }
-  const int64_t rows =
-      rows_per_split != 0 ? rows_per_split : auto_split_rows(cache->len_host, cache->n_seq, cache->n_kv_heads);
+  const size_t bound = decode_workspace_bytes(cache, n_q_heads, max_total_splits(cache, rows_per_split));
+  if (workspace_bytes < bound)
+    return fail(YOCO_ERR_WORKSPACE, "workspace %zu bytes < %zu (yoco_cross_attn_decode_workspace)",
+                workspace_bytes, bound);
+  const int group = n_q_heads / cache->n_kv_heads;
+  if ((st = check_device()) != YOCO_OK) return st;
+  const int64_t rows = rows_per_split != 0
+                           ? rows_per_split
+                           : auto_split_rows(cache->len_host, cache->n_seq, cache->n_kv_heads,
+                                             decode_target_blocks(cache->dtype, cache->head_dim, group));
   yoco::DecodeArgs a{};
   int64_t total = 0;
   for (int b = 0; b < cache->n_seq; ++b) {
@@ -341,14 +373,11 @@ yoco_status yoco_cross_attn_decode(const void *q, int32_t q_dtype, int32_t n_q_h
     total += (cache->len_host[b] + rows - 1) / rows;
   }
   a.split_begin[cache->n_seq] = static_cast<int32_t>(total);
-  const size_t need = decode_workspace_bytes(cache, n_q_heads, total);
-  if (workspace_bytes < need)
-    return fail(YOCO_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  if (decode_workspace_bytes(cache, n_q_heads, total) > workspace_bytes)
+    return fail(YOCO_ERR_WORKSPACE, "split plan exceeds the workspace (internal bound violated)");
   if (total * cache->n_kv_heads > (int64_t(1) << 31) - 1)
     return fail(YOCO_ERR_BAD_VALUE, "too many splits (%lld)", (long long)total);
-  if ((st = check_device()) != YOCO_OK) return st;
 
-  const int group = n_q_heads / cache->n_kv_heads;
   a.k = cache->k;
   a.v = cache->v;
   a.q = q;

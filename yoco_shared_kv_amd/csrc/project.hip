@@ -8,12 +8,24 @@
 // Dividing after the sum is the same value as normalising first, since the
 // row factor 1/rms_r is common to every term.
 //
-// One workgroup computes a 64-row x 64-column tile of one output (K or V, or
-// Q): it first reduces the 64 row norms (fp32), then streams [64 x 32] slices
-// of x (times gain) and [32 x 64] slices of W through LDS and accumulates a
-// 4x4 block per thread with fp32 FMA.  Destination rows are either
-// contiguous (a cache slab or a Q buffer) or, for the generation-time
-// append, one indexed row per sequence.
+// Two kernels share this arithmetic:
+//  * rows >= 9 (prompt projection): one workgroup computes a 64-row x
+//    64-column tile of one output (K or V, or Q): it first reduces the 64 row
+//    norms (fp32), then streams [64 x 32] slices of x (times gain) and
+//    [32 x 64] slices of W through LDS and accumulates a 4x4 block per thread
+//    with fp32 FMA.
+//  * rows <= 8 (generation-time append, per-token Q): the work is a
+//    matrix-vector product bound by reading W once, so one 1024-thread
+//    workgroup (512 for 8 rows) owns a 64-column strip of one weight for all
+//    d_model rows.
+//    Each 8-lane group reads one 128-byte line of a W row per load (a wave
+//    covers 8 rows, the workgroup 128 rows per pass), multiplies it by the
+//    LDS-resident x*gain of every input row, and the per-lane partial sums
+//    are reduced across lanes (shuffles) and waves (LDS) in a fixed order.
+//    Rows run in launches of up to 8 (fewer when d_model is large, since a
+//    launch stages x*gain in at most 48 KiB of LDS).
+// Destination rows are either contiguous (a cache slab or a Q buffer) or, for
+// the generation-time append, one indexed row per sequence.
 #include "device_common.h"
 #include "yoco_internal.h"
 
@@ -123,10 +135,196 @@ __global__ __launch_bounds__(pj::kThreads) void project_kernel(const ProjArgs a)
   }
 }
 
+
+namespace pg {
+// 16 waves (8 for 8 input rows, whose accumulators need the larger
+// per-lane register budget of a 512-thread workgroup).
+template <int NR>
+struct Shape {
+  static constexpr int kWaves = (NR == 8) ? 8 : 16;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kRowsPerPass = kWaves * 8;
+};
+constexpr int kCols = 64;            // columns per workgroup (8 lanes x 8 bf16 / fp32 pairs)
+constexpr int kMaxRows = 8;
+constexpr int kMaxXBytes = 48 * 1024;  // dynamic LDS for x * gain (within the default 64 KiB)
+constexpr int kMaxChunks = 4;          // launches per call before the tiled kernel takes over
+}  // namespace pg
+
+// W loads of 8 consecutive columns as fp32.
+template <typename TW>
+__device__ __forceinline__ void load_w8(const TW *p, float (&w)[8]);
+template <>
+__device__ __forceinline__ void load_w8<bf16_t>(const bf16_t *p, float (&w)[8]) {
+  const uint4 v = ld16_stream(p);
+  w[0] = bf16_lo(v.x); w[1] = bf16_hi(v.x); w[2] = bf16_lo(v.y); w[3] = bf16_hi(v.y);
+  w[4] = bf16_lo(v.z); w[5] = bf16_hi(v.z); w[6] = bf16_lo(v.w); w[7] = bf16_hi(v.w);
+}
+template <>
+__device__ __forceinline__ void load_w8<float>(const float *p, float (&w)[8]) {
+  const uint4 a = ld16_stream(p), b = ld16_stream(p + 4);
+  w[0] = __uint_as_float(a.x); w[1] = __uint_as_float(a.y); w[2] = __uint_as_float(a.z); w[3] = __uint_as_float(a.w);
+  w[4] = __uint_as_float(b.x); w[5] = __uint_as_float(b.y); w[6] = __uint_as_float(b.z); w[7] = __uint_as_float(b.w);
+}
+
+// Rows [row_base, row_base + nr) of the input, nr <= NR <= 8.
+template <typename TX, typename TW, typename TO, int NR>
+__global__ __launch_bounds__(pg::Shape<NR>::kThreads) void project_small_kernel(const ProjArgs a, int64_t row_base,
+                                                                               int nr) {
+  using namespace pg;
+  constexpr int kWaves = Shape<NR>::kWaves;
+  constexpr int kThreads = Shape<NR>::kThreads;
+  constexpr int kRowsPerPass = Shape<NR>::kRowsPerPass;
+  extern __shared__ float s_dyn[];
+  float *s_x = s_dyn;                          // [NR][d]
+  __shared__ float s_red[kWaves][NR][kCols];
+  __shared__ float s_inv_rms[NR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n_strips = a.ncols / kCols;
+  const int strip = blockIdx.x % n_strips;
+  const int out_id = blockIdx.x / n_strips;
+  const int d = a.d;
+  const TX *x = static_cast<const TX *>(a.x);
+  const TW *w = static_cast<const TW *>(a.w[out_id]);
+
+  // Stage x * gain (fp32) and reduce the row norms: wave r handles row r.
+  for (int idx = tid; idx < NR * d; idx += kThreads) {
+    const int r = idx / d;
+    const int c = idx - r * d;
+    float v = 0.f;
+    if (r < nr) {
+      v = load_elem<TX>(x + (row_base + r) * d + c);
+      if (a.gain != nullptr) v *= a.gain[c];
+    }
+    s_x[idx] = v;
+  }
+  if (wave < NR) {
+    float ss = 0.f;
+    if (wave < nr) {
+      const TX *xr = x + (row_base + wave) * d;
+      for (int c = lane; c < d; c += 64) {
+        const float v = load_elem<TX>(xr + c);
+        ss = fmaf(v, v, ss);
+      }
+    }
+#pragma unroll
+    for (int sft = 32; sft >= 1; sft >>= 1) ss += shfl_xor_f(ss, sft);
+    if (lane == 0) s_inv_rms[wave] = 1.0f / sqrtf(ss / static_cast<float>(d) + a.eps);
+  }
+  __syncthreads();
+
+  const int c8 = lane & 7;        // 8-column chunk of the strip
+  const int rslot = lane >> 3;    // row within the wave's 8 rows
+  float acc[NR][8];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
+
+  // W rows in flight per lane; fewer for more input rows (more accumulators).
+  constexpr int kUnroll = (NR <= 2) ? 8 : 4;
+  const TW *wcol = w + strip * kCols + c8 * 8;
+  for (int k0 = 0; k0 < d; k0 += kRowsPerPass * kUnroll) {
+    float wv[kUnroll][8];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int k = k0 + u * kRowsPerPass + wave * 8 + rslot;
+      if (k < d) {
+        load_w8<TW>(wcol + static_cast<int64_t>(k) * a.ncols, wv[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wv[u][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int k = k0 + u * kRowsPerPass + wave * 8 + rslot;
+      if (k < d) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const float xv = s_x[r * d + k];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(xv, wv[u][e], acc[r][e]);
+        }
+      }
+    }
+  }
+
+  // Reduce over the 8 row slots of the wave (lane bits 3..5), then waves.
+#pragma unroll
+  for (int sft = 8; sft < 64; sft <<= 1) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[r][e] += shfl_xor_f(acc[r][e], sft);
+  }
+  if (rslot == 0) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_red[wave][r][c8 * 8 + e] = acc[r][e];
+  }
+  __syncthreads();
+  TO *out = static_cast<TO *>(a.out[out_id]);
+  for (int idx = tid; idx < NR * kCols; idx += kThreads) {
+    const int r = idx / kCols;
+    const int col = idx - r * kCols;
+    if (r >= nr) continue;
+    float v = 0.f;
+#pragma unroll
+    for (int wv2 = 0; wv2 < kWaves; ++wv2) v += s_red[wv2][r][col];
+    const int64_t row = row_base + r;
+    const int64_t dst = a.indexed ? a.dst_rows[row] : a.dst_row_base + row;
+    store_elem<TO>(out + dst * a.ncols + strip * kCols + col, v * s_inv_rms[r]);
+  }
+}
+
+// Input rows per launch of the small-row kernel: the largest power of two
+// <= 8 whose x*gain fits kMaxXBytes (0 if not even one row fits).
+static int small_chunk_rows(int d) {
+  int nr = pg::kMaxRows;
+  while (nr > 0 && static_cast<int64_t>(nr) * d * 4 > pg::kMaxXBytes) nr >>= 1;
+  return nr;
+}
+
+// Whether the small-row kernel takes this projection.
+static bool use_small(const ProjArgs &a) {
+  const int chunk = small_chunk_rows(a.d);
+  return chunk > 0 && a.n <= static_cast<int64_t>(chunk) * pg::kMaxChunks;
+}
+
+template <typename TX, typename TW, typename TO>
+static hipError_t launch_project_small(const ProjArgs &a, hipStream_t s) {
+  const unsigned int blocks = static_cast<unsigned int>((a.ncols / pg::kCols) * a.n_out);
+  const int chunk = small_chunk_rows(a.d);
+  for (int64_t base = 0; base < a.n; base += chunk) {
+    const int nr = static_cast<int>(a.n - base < chunk ? a.n - base : chunk);
+    const int nr_pow2 = nr <= 1 ? 1 : nr <= 2 ? 2 : nr <= 4 ? 4 : 8;
+    const size_t lds = static_cast<size_t>(nr_pow2) * a.d * sizeof(float);
+    switch (nr_pow2) {
+      case 1: hipLaunchKernelGGL((project_small_kernel<TX, TW, TO, 1>), dim3(blocks), dim3(pg::Shape<1>::kThreads), lds, s, a, base, nr); break;
+      case 2: hipLaunchKernelGGL((project_small_kernel<TX, TW, TO, 2>), dim3(blocks), dim3(pg::Shape<2>::kThreads), lds, s, a, base, nr); break;
+      case 4: hipLaunchKernelGGL((project_small_kernel<TX, TW, TO, 4>), dim3(blocks), dim3(pg::Shape<4>::kThreads), lds, s, a, base, nr); break;
+      default: hipLaunchKernelGGL((project_small_kernel<TX, TW, TO, 8>), dim3(blocks), dim3(pg::Shape<8>::kThreads), lds, s, a, base, nr); break;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <typename TX, typename TW>
 static hipError_t launch_project_o(const ProjArgs &a, int o_dt, hipStream_t s) {
   const int64_t row_tiles = (a.n + pj::BM - 1) / pj::BM;
   const unsigned int blocks = static_cast<unsigned int>(row_tiles * (a.ncols / pj::BN) * a.n_out);
+  if (use_small(a)) {
+    if (o_dt == YOCO_DT_F32) return launch_project_small<TX, TW, float>(a, s);
+    if (o_dt == YOCO_DT_BF16) return launch_project_small<TX, TW, bf16_t>(a, s);
+    return hipErrorInvalidValue;
+  }
   if (o_dt == YOCO_DT_F32) {
     hipLaunchKernelGGL((project_kernel<TX, TW, float>), dim3(blocks), dim3(pj::kThreads), 0, s, a);
   } else if (o_dt == YOCO_DT_BF16) {

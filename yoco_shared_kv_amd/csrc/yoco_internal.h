@@ -11,7 +11,10 @@
 namespace yoco {
 
 constexpr int kMaxKvHeads = 64;        // counters are laid out [YOCO_MAX_SEQ][kMaxKvHeads]
-constexpr int kDecodeSplitQuantum = 256;
+constexpr int kDecodeSplitQuantum = 256;   // caller-chosen split sizes are multiples of this
+constexpr int kDecodeAutoQuantum = 64;     // library-chosen split sizes are multiples of this
+constexpr int kDecodeMinSplitRows = 256;   // library-chosen split sizes are at least this
+constexpr int kDecodeMaxTargetBlocks = 4096;  // cap on the library's workgroup target
 
 // ---------------------------------------------------------------------------
 // Fused RMSNorm + projection (shared K/V, per-layer Q, append).
@@ -60,6 +63,8 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int head_dim, int group, hipStream_t s);
+// Resident workgroups per CU of the decode kernel for this shape (0 on error).
+int decode_blocks_per_cu(int dtype, int head_dim, int group);
 
 // ---------------------------------------------------------------------------
 // Causal prefill over the shared cache.
