@@ -21,6 +21,9 @@ cores for the same decode step (``cpu_baseline``).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--no-prefill]
+       python bench.py --copy-calibration   (a plain 512 MiB device copy, three
+                       times: the known-size reference for scaling the
+                       FETCH_SIZE / WRITE_SIZE hardware counters)
 """
 from __future__ import annotations
 
@@ -49,7 +52,23 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--prefill-reps", type=int, default=5)
+    p.add_argument("--copy-calibration", action="store_true")
     return p.parse_args()
+
+
+COPY_BYTES = 512 * 1024 * 1024
+
+
+def copy_calibration(torch):
+    """Copy 512 MiB device-to-device three times (torch's copy kernel): each
+    dispatch reads and writes exactly COPY_BYTES of algorithmic traffic."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_dispatch": COPY_BYTES, "dispatches": 3}), flush=True)
 
 
 def to_dev(a, torch):
@@ -178,6 +197,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     import workloads as W
     import yoco_shared_kv_amd as y
 

@@ -39,6 +39,8 @@
 //     tiles are shared in that XCD's L2.
 // fp32 path: plain fp32 VALU kernel (one lane per query row, exact online
 // softmax) for fp32 caches.
+#include <type_traits>
+
 #include "device_common.h"
 #include "yoco_internal.h"
 
@@ -75,6 +77,10 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
+__device__ __forceinline__ float dot2_bf16_f32(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 template <int DH>
 struct PrefillShape {
   static constexpr int kChunks = DH / 8;                    // 16-byte chunks per row
@@ -87,43 +93,86 @@ struct PrefillShape {
   static constexpr int DSUB = DH / 32;                      // O^T 32-row tiles over head_dim
 };
 
+// Row-dependent XOR applied to the 16-byte chunk index of a tile row.
+// Mode 0: row % chunks.  Mode 1 (head_dim 128): bits (r1 r0 r2) in the low
+// three bits plus r3, so that 8 consecutive rows hit 8 distinct chunk slots
+// mod 8 (16-byte K reads) and rows 4k..4k+3 with chunks c, c^1 hit 8
+// distinct slots mod 8 (the 8-byte transposed V reads of one 16-lane group).
+// Mode 2 (head_dim 128): (r1 r0) in bits 3..2 and (r3 r2) in bits 1..0.
+template <int DH, int SWZ>
+__device__ __forceinline__ int row_xor(int row) {
+  using S = PrefillShape<DH>;
+  if constexpr (SWZ == 1 && S::kChunks == 16) {
+    return ((row & 3) << 1) | ((row >> 2) & 1) | (row & 8);
+  } else if constexpr (SWZ == 2 && S::kChunks == 16) {
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  } else {
+    return row & (S::kChunks - 1);
+  }
+}
+
 // LDS byte offset of element `dim` (multiple of 4 for 8-byte reads, of 8 for
 // 16-byte reads) of tile row `row`, with the XOR-swizzled chunk layout.
-template <int DH>
+template <int DH, int SWZ>
 __device__ __forceinline__ int swz(int row, int dim) {
   using S = PrefillShape<DH>;
   const int chunk = dim >> 3;
-  const int slot = chunk ^ (row & (S::kChunks - 1));
+  const int slot = chunk ^ row_xor<DH, SWZ>(row);
   return row * S::kRowBytes + slot * 16 + (dim & 7) * 2;
 }
 
-// Issue this wave's share of the direct-to-LDS loads of one K/V tile pair.
-template <int DH>
-__device__ __forceinline__ void stage_tile(char *lds_k, char *lds_v, const bf16_t *kg, const bf16_t *vg,
-                                           int64_t row_stride, int64_t key0, int64_t kv_len, int wave,
-                                           int lane) {
+// Per-lane element offsets (within a tile) of this wave's direct-to-LDS
+// loads: load i of the wave fills 1 KiB block blk = wave * kLoadsPerWave + i,
+// lane L writes LDS bytes blk*1024 + L*16 = (row, slot) and so reads global
+// chunk slot ^ row_xor(row) of that row.
+template <int DH, int SWZ>
+struct StageOffsets {
   using S = PrefillShape<DH>;
+  int row[S::kLoadsPerWave];
+  int goff[S::kLoadsPerWave];  // row * row_stride + chunk * 8 (elements)
+  __device__ __forceinline__ void init(int wave, int lane, int row_stride) {
+#pragma unroll
+    for (int i = 0; i < S::kLoadsPerWave; ++i) {
+      const int blk = wave * S::kLoadsPerWave + i;
+      row[i] = blk * S::kRowsPerLoad + lane / S::kChunks;
+      const int chunk = (lane % S::kChunks) ^ row_xor<DH, SWZ>(row[i]);
+      goff[i] = row[i] * row_stride + chunk * 8;
+    }
+  }
+};
+
+// Issue this wave's share of the direct-to-LDS loads of one K/V tile pair
+// (tile rows key0 .. key0+63; rows at or past kv_len re-read row kv_len-1 and
+// are masked by causality later).
+template <int DH, int SWZ>
+__device__ __forceinline__ void stage_tile(char *lds_k, char *lds_v, const bf16_t *kg, const bf16_t *vg,
+                                           int row_stride, int64_t key0, int64_t kv_len, int wave,
+                                           const StageOffsets<DH, SWZ> &so) {
+  using S = PrefillShape<DH>;
+  const int64_t tile_base = key0 * row_stride;
+  const bf16_t *kt = kg + tile_base;
+  const bf16_t *vt = vg + tile_base;
+  const bool full = key0 + pf::kKeyTile <= kv_len;
 #pragma unroll
   for (int i = 0; i < S::kLoadsPerWave; ++i) {
-    const int blk = wave * S::kLoadsPerWave + i;        // which 1 KiB block of the tile
-    const int row = blk * S::kRowsPerLoad + lane / S::kChunks;
-    const int slot = lane % S::kChunks;
-    const int chunk = slot ^ (row & (S::kChunks - 1));
-    int64_t key = key0 + row;
-    key = key < kv_len ? key : kv_len - 1;              // rows past the data are masked later
-    const int64_t goff = key * row_stride + chunk * 8;
-    __builtin_amdgcn_global_load_lds(static_cast<const void *>(kg + goff),
+    const int blk = wave * S::kLoadsPerWave + i;
+    int off = so.goff[i];
+    if (!full && key0 + so.row[i] >= kv_len) {
+      off += static_cast<int>(kv_len - 1 - key0 - so.row[i]) * row_stride;
+    }
+    __builtin_amdgcn_global_load_lds(static_cast<const void *>(kt + off),
                                      (lds_void_t *)(lds_k + blk * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(static_cast<const void *>(vg + goff),
+    __builtin_amdgcn_global_load_lds(static_cast<const void *>(vt + off),
                                      (lds_void_t *)(lds_v + blk * 1024), 16, 0, 0);
   }
 }
 
-template <int DH>
+template <int DH, int SWZ>
 __global__ __launch_bounds__(pf::kThreads, 2) void prefill_bf16_kernel(const PrefillArgs a) {
   using S = PrefillShape<DH>;
-  __shared__ __attribute__((aligned(1024))) char lds_k[2][S::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_v[2][S::kTileBytes];
+  // [buffer][K, V][tile]: every LDS read below is a per-lane offset plus a
+  // compile-time immediate.
+  __shared__ __attribute__((aligned(1024))) char lds[2][2][S::kTileBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -145,7 +194,7 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_bf16_kernel(const Pre
   const int h = g * group + slot_on_xcd % group;
 
   const int64_t row_stride_q = (int64_t)a.n_q_heads * DH;
-  const int64_t row_stride_kv = (int64_t)a.n_kv_heads * DH;
+  const int row_stride_kv = a.n_kv_heads * DH;
   const bf16_t *qg = static_cast<const bf16_t *>(a.q);
   const bf16_t *kg = static_cast<const bf16_t *>(a.k) + g * DH;
   const bf16_t *vg = static_cast<const bf16_t *>(a.v) + g * DH;
@@ -162,8 +211,10 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_bf16_kernel(const Pre
   const int n_ktiles = static_cast<int>((a.q_start + blk_last_row) / pf::kKeyTile) + 1;
   const bool wave_active = wave_row_first < a.t;
 
+  StageOffsets<DH, SWZ> so;
+  so.init(wave, lane, row_stride_kv);
   // Start loading key tile 0 before touching Q.
-  stage_tile<DH>(lds_k[0], lds_v[0], kg, vg, row_stride_kv, 0, a.kv_len, wave, lane);
+  stage_tile<DH, SWZ>(lds[0][0], lds[0][1], kg, vg, row_stride_kv, 0, a.kv_len, wave, so);
 
   // Q^T as the MFMA B operand: lane holds row `col`, dims ks*16 + half*8 .. +8.
   Frag8 qf[S::KSTEPS];
@@ -173,6 +224,30 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_bf16_kernel(const Pre
     for (int ks = 0; ks < S::KSTEPS; ++ks) qf[ks].u = row_valid ? ld16(qp + ks * 16) : make_uint4(0, 0, 0, 0);
   }
 
+  // LDS read offsets within a tile.  K (A operand of S^T): row sub*32 + col,
+  // dims ks*16 + half*8; the row_xor of the swizzle depends only on row mod
+  // 16, so sub adds the immediate sub*32*rowbytes.
+  int koff[S::KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < S::KSTEPS; ++ks) koff[ks] = swz<DH, SWZ>(col, ks * 16 + half * 8);
+  // V^T (A operand of O^T) via transposed reads: in each 16-lane group,
+  // source lane a + 4j points at key kb + j, dims dbase + 4a .. +3, and lane
+  // i of the group receives keys kb..kb+3 of dim dbase + i.  With
+  // kb = sub*32 + kk*16 + (grp/2)*4 + j and the second read at kb + 8, only
+  // (read r, dim tile d) changes the swizzled offset; sub and kk are
+  // immediates.
+  const int grp = lane >> 4;
+  const int src_a = lane & 3;
+  const int src_j = (lane >> 2) & 3;
+  const int vrow = (grp >> 1) * 4 + src_j;
+  const int dcol = (grp & 1) * 16 + src_a * 4;
+  int voff[2][S::DSUB];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+#pragma unroll
+    for (int d = 0; d < S::DSUB; ++d) voff[r][d] = swz<DH, SWZ>(vrow + 8 * r, d * 32 + dcol);
+  }
+
   floatx16 oacc[S::DSUB];
 #pragma unroll
   for (int d = 0; d < S::DSUB; ++d) {
@@ -180,22 +255,23 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_bf16_kernel(const Pre
     for (int i = 0; i < 16; ++i) oacc[d][i] = 0.f;
   }
   float m_run = -INFINITY;  // reference max (log2 units) of this lane's query row
-  float l_run = 0.f;        // this lane's share of the running sum
+  float l_run = 0.f;        // this lane's share of sum(p), from the bf16 p the MFMA uses
+  const uint32_t kOnesBf16x2 = 0x3F803F80u;  // (1.0, 1.0) in bf16
 
-  for (int kt = 0; kt < n_ktiles; ++kt) {
+  auto tile_step = [&](auto buf_c, int kt) {
+    constexpr int BUF = decltype(buf_c)::value;
     // Tile kt has landed for every wave, and every wave is done with tile kt-1,
     // whose buffer the next loads overwrite.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    const int buf = kt & 1;
     if (kt + 1 < n_ktiles) {
-      stage_tile<DH>(lds_k[buf ^ 1], lds_v[buf ^ 1], kg, vg, row_stride_kv, (int64_t)(kt + 1) * pf::kKeyTile,
-                     a.kv_len, wave, lane);
+      stage_tile<DH, SWZ>(lds[BUF ^ 1][0], lds[BUF ^ 1][1], kg, vg, row_stride_kv,
+                          (int64_t)(kt + 1) * pf::kKeyTile, a.kv_len, wave, so);
     }
     const int64_t key0 = (int64_t)kt * pf::kKeyTile;
-    if (!wave_active || key0 > wave_pos_last) continue;
-    char *tk = lds_k[buf];
-    char *tv = lds_v[buf];
+    if (!wave_active || key0 > wave_pos_last) return;
+    char *tk = lds[BUF][0];
+    char *tv = lds[BUF][1];
 
     // ---- S^T = K Q^T for two 32-key sub-tiles ----
     floatx16 sacc[2];
@@ -203,27 +279,47 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_bf16_kernel(const Pre
     for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[sub][i] = 0.f;
-      const int krow = sub * 32 + col;
 #pragma unroll
       for (int ks = 0; ks < S::KSTEPS; ++ks) {
         Frag8 af;
-        af.u = *reinterpret_cast<const uint4 *>(tk + swz<DH>(krow, ks * 16 + half * 8));
+        af.u = *reinterpret_cast<const uint4 *>(tk + koff[ks] + sub * 32 * S::kRowBytes);
         sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af.v, qf[ks].v, sacc[sub], 0, 0, 0);
       }
     }
-    // ---- causal mask (diagonal tiles only) and tile maximum ----
+    // ---- causal mask (diagonal tiles only) ----
     // Accumulator element i of sub-tile `sub` is key
     //   key0 + sub*32 + (i/4)*8 + half*4 + (i%4)   for query row `col`.
     if (key0 + pf::kKeyTile - 1 > wave_pos_first) {
+      const int64_t rel64 = my_pos - key0;
+      const int rel = rel64 < pf::kKeyTile ? static_cast<int>(rel64) : pf::kKeyTile;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int64_t key = key0 + sub * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-          if (key > my_pos) sacc[sub][i] = -INFINITY;
+          if (sub * 32 + (i >> 2) * 8 + half * 4 + (i & 3) > rel) sacc[sub][i] = -INFINITY;
         }
       }
     }
+    // ---- P^T (bf16) as the B operand of O^T += V^T P^T ----
+    // Probabilities are formed against the current reference first (each
+    // sub-tile as soon as its scores exist, so the exps of sub-tile 0 can
+    // overlap the MFMAs of sub-tile 1); the tile maximum is checked
+    // alongside, and in the rare case that it passes the reference by more
+    // than the slack, O and l are rescaled and P is formed again.
+    Frag8 pfr[2][2];
+    auto make_p = [&](int sub) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p0 = fast_exp2(fmaf(sacc[sub][kk * 8 + 2 * j], a.scale_log2, -m_run));
+          const float p1 = fast_exp2(fmaf(sacc[sub][kk * 8 + 2 * j + 1], a.scale_log2, -m_run));
+          pfr[sub][kk].w[j] = cvt_pk_bf16(p0, p1);
+        }
+      }
+    };
+    make_p(0);
+    make_p(1);
     float tmax = -INFINITY;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -231,7 +327,7 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_bf16_kernel(const Pre
       for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[sub][i]);
     }
     tmax = fmaxf(tmax, shfl_xor_f(tmax, 32)) * a.scale_log2;  // scale > 0 keeps the order
-    // Lazy rescale (both lanes of a row take the same decision).
+    // Both lanes of a row take the same decision.
     const bool need = tmax > m_run + pf::kRescaleSlack;
     if (__any(need)) {
       if (need) {
@@ -244,47 +340,38 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_bf16_kernel(const Pre
         }
         m_run = tmax;
       }
+      make_p(0);
+      make_p(1);
     }
-    // ---- P^T (bf16) as the B operand of O^T += V^T P^T ----
-    Frag8 pfr[2][2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p0 = fast_exp2(fmaf(sacc[sub][kk * 8 + 2 * j], a.scale_log2, -m_run));
-          const float p1 = fast_exp2(fmaf(sacc[sub][kk * 8 + 2 * j + 1], a.scale_log2, -m_run));
-          l_run += p0 + p1;
-          pfr[sub][kk].w[j] = cvt_pk_bf16(p0, p1);
-        }
+        for (int j = 0; j < 4; ++j) l_run = dot2_bf16_f32(pfr[sub][kk].w[j], kOnesBf16x2, l_run);
       }
     }
     // k-slot j of lane half `half` in step (sub, kk) is key
     //   sub*32 + kk*16 + (j/4)*8 + half*4 + (j%4).
-    // A operand V^T via two transposed reads: in each 16-lane group, source
-    // lane a + 4j points at key kb + j, dims dbase + 4a .. +3, and lane i of
-    // the group receives keys kb..kb+3 of dim dbase + i.
-    const int grp = lane >> 4;                 // 16-lane group
-    const int src_a = lane & 3;
-    const int src_j = (lane >> 2) & 3;
-    const int dcol = (grp & 1) * 16 + src_a * 4;
 #pragma unroll
     for (int d = 0; d < S::DSUB; ++d) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const int kb = sub * 32 + kk * 16 + (grp >> 1) * 4 + src_j;
+          const int rows = (sub * 32 + kk * 16) * S::kRowBytes;
           Frag8 af;
-          af.s4[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_shortx4_t *)(tv + swz<DH>(kb, d * 32 + dcol)));
-          af.s4[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_shortx4_t *)(tv + swz<DH>(kb + 8, d * 32 + dcol)));
+          af.s4[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t *)(tv + voff[0][d] + rows));
+          af.s4[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t *)(tv + voff[1][d] + rows));
           oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af.v, pfr[sub][kk].v, oacc[d], 0, 0, 0);
         }
       }
     }
+  };
+
+  for (int kt = 0; kt < n_ktiles; kt += 2) {
+    tile_step(std::integral_constant<int, 0>(), kt);
+    if (kt + 1 < n_ktiles) tile_step(std::integral_constant<int, 1>(), kt + 1);
   }
 
   const float l_tot = l_run + shfl_xor_f(l_run, 32);
@@ -382,6 +469,8 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillArgs a) {
   if (a.lse != nullptr) a.lse[row * a.n_q_heads + h] = (m + log2f(l)) * kLn2;
 }
 
+constexpr int kPrefillSwizzle = 2;  // modes 1 and 2 both remove the 2-way V-read bank conflicts; 2 measured fastest
+
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, int head_dim, hipStream_t s) {
   if (dtype == YOCO_DT_BF16) {
     const int64_t n_qtiles = (a.t + pf::kBlockRows - 1) / pf::kBlockRows;
@@ -390,9 +479,9 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, int head_dim, hipStre
     const unsigned int blocks =
         static_cast<unsigned int>(((n_units + pf::kXcds - 1) / pf::kXcds) * pf::kXcds * group);
     if (head_dim == 128) {
-      hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3(blocks), dim3(pf::kThreads), 0, s, a);
+      hipLaunchKernelGGL((prefill_bf16_kernel<128, kPrefillSwizzle>), dim3(blocks), dim3(pf::kThreads), 0, s, a);
     } else if (head_dim == 64) {
-      hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3(blocks), dim3(pf::kThreads), 0, s, a);
+      hipLaunchKernelGGL((prefill_bf16_kernel<64, kPrefillSwizzle>), dim3(blocks), dim3(pf::kThreads), 0, s, a);
     } else {
       return hipErrorInvalidValue;
     }
