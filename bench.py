@@ -28,9 +28,11 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -57,6 +59,43 @@ def parse_args():
 
 
 COPY_BYTES = 512 * 1024 * 1024
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "decode_128k_counters.md")
+# The decode kernel's own sources: the FETCH/WRITE counters recorded in the
+# summary hold only while these files hash to the digest stored beside them.
+DECODE_SOURCES = (
+    "yoco_shared_kv_amd/csrc/decode_kernel.h",
+    "yoco_shared_kv_amd/csrc/decode.hip",
+    "yoco_shared_kv_amd/csrc/device_common.h",
+    "yoco_shared_kv_amd/csrc/yoco_internal.h",
+)
+
+
+def decode_source_digest():
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def counter_traffic():
+    """HBM bytes per decode launch from the committed counter summary, or
+    (None, reason).  FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each
+    scaled by COPY_BYTES over what the same counter read for the plain copy."""
+    try:
+        text = open(COUNTER_SUMMARY).read()
+    except OSError:
+        return None, "no counter summary"
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if m is None:
+        return None, "counter summary has no json block"
+    rec = json.loads(m.group(1))
+    if rec["decode_source_sha256"] != decode_source_digest():
+        return None, "decode kernel sources changed since the counters were taken"
+    fetch_scale = rec["copy_bytes"] / (rec["copy_fetch_kib"] * 1024)
+    write_scale = rec["copy_bytes"] / (rec["copy_write_kib"] * 1024)
+    return (rec["decode_fetch_kib"] * 1024 * fetch_scale
+            + rec["decode_write_kib"] * 1024 * write_scale), None
 
 
 def copy_calibration(torch):
@@ -206,6 +245,9 @@ def main():
     dec = bench_decode(args, torch, y, W)
     pre = None if args.no_prefill else bench_prefill(args, torch, y, W)
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec, W)
+    traffic, why = counter_traffic()
+    if why:
+        log(f"roofline.traffic is null: {why}")
 
     result = {
         "metric": "cross-attn decode us/token/layer at N=128K (shared bf16 K^/V^, 13 layers)",
@@ -235,7 +277,9 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(dec["achieved_gbps"] / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": None if traffic is None else round(traffic),
+            "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "traffic_over_algorithmic": None if traffic is None else round(traffic / dec["bytes_per_launch"], 4),
             "avg_launch_us": round(dec["kern_avg_us"], 2),
             "p10_launch_us": round(dec["kern_p10_us"], 2),
             "p90_launch_us": round(dec["kern_p90_us"], 2),
