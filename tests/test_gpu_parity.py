@@ -235,6 +235,47 @@ def test_prefill_prefix_invariance_bitwise():
     assert np.array_equal(o_short, o_full[:300])
 
 
+def _overflow_case(n, hot_key, hot_row, hot_head, scale=6.0, seed=16):
+    """Prefill input where query (hot_row, hot_head) meets key hot_key with a
+    logit of about scale*|q|^2/sqrt(128) ~ 68 (98 in log2 units), far above
+    the maximum over its first 32 keys: the kernel's fixed reference must
+    give way to its second pass.  The key row is stored in bf16 like the
+    rest, and the oracle reads the same stored values."""
+    c = W.make_prefill(n=n, n_q_heads=6, n_kv_heads=2, head_dim=128, seed=seed)
+    q = W.as_f32(c.q)
+    k = W.as_f32(c.k)
+    g = hot_head // 3
+    k[hot_key, g] = np.float32(scale) * q[hot_row, hot_head]
+    c.k = W.store(k, W.BF16)
+    return c
+
+
+def test_prefill_overflow_second_pass():
+    c = _overflow_case(n=600, hot_key=300, hot_row=310, hot_head=3)
+    s_hot = float(W.as_f32(c.q)[310, 3] @ W.as_f32(c.k)[300, 1]) * c.softmax_scale
+    assert s_hot / np.log(2.0) > 64 + 16, "the planted logit must exceed the overflow margin"
+    cache = make_cache_from([c.k], [c.v], 600, W.BF16)
+    o, lse = y.cross_attn_prefill(to_dev(c.q), cache, want_lse=True)
+    ro, rl = orc().prefill(c.q, 0, c.k, c.v, c.softmax_scale, want_lse=True)
+    assert_parity(to_stored(o), ro, bf16=True, what="prefill O with an overflowing row")
+    assert_parity(to_stored(lse), rl, bf16=True, what="prefill lse with an overflowing row")
+    # the hot row attends almost only to the hot key
+    assert np.abs(to_stored(o)[310, 3] - W.as_f32(c.v)[300, 1]).max() < 2e-2
+
+
+def test_prefill_overflow_keeps_other_rows_bitwise():
+    # Rows 256..299 share a workgroup with the overflowing row 510 only in
+    # the full run; their results must not change.
+    c = _overflow_case(n=640, hot_key=500, hot_row=510, hot_head=0)
+    full = make_cache_from([c.k], [c.v], 640, W.BF16)
+    o_full = to_stored(y.cross_attn_prefill(to_dev(c.q), full))
+    short = make_cache_from([c.k[:300]], [c.v[:300]], 640, W.BF16)
+    o_short = to_stored(y.cross_attn_prefill(to_dev(c.q[:300]), short))
+    assert np.array_equal(o_short, o_full[:300])
+    ro = orc().prefill(c.q, 0, c.k, c.v, c.softmax_scale, rows=[509, 510, 511])
+    assert_parity(o_full[509:512], ro, bf16=True, what="rows around the overflowing row")
+
+
 def test_decode_matches_last_prefill_row():
     c = W.make_prefill(n=1000, n_q_heads=24, n_kv_heads=8, head_dim=128, seed=15)
     cache = make_cache_from([c.k], [c.v], 1000, W.BF16)

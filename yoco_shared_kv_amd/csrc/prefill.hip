@@ -8,35 +8,44 @@
 //   o = softmax(scale * q K^T) V,  lse = ln sum exp(scale * q K^T).
 //
 // bf16 path (a dense contraction, so it runs on MFMA):
-//   A workgroup is 4 waves = 128 query rows of one query head; each wave owns
-//   32 rows.  Keys are processed in tiles of 64 rows.
+//   A workgroup is 8 waves = 256 query rows of one query head (one workgroup
+//   per CU); each wave owns 32 rows.  Keys are staged in tiles of 64 rows and
+//   computed in halves of 32.
 //   * Staging: each K or V tile (64 rows x head_dim bf16) is copied straight
-//     from global memory into LDS with 16-byte direct-to-LDS loads (no
-//     registers), two buffers deep: the loads of tile kt+1 are in flight
-//     while tile kt is computed.  Rows are stored unpadded with the 16-byte
-//     chunk index XOR-swizzled by the row (slot = chunk ^ (row % chunks)), so
-//     the operand reads below hit distinct LDS banks.
+//     from global memory into LDS with 16-byte buffer loads to LDS (no
+//     registers), two buffers each for K and V in separate arrays (so reads
+//     of one buffer never wait for loads into the other).  The buffer
+//     descriptor ends at the last cache row that holds data; the hardware
+//     range check writes zeros for rows past it.  Rows are stored unpadded
+//     with the 16-byte chunk index XOR-swizzled by the row, so the operand
+//     reads below hit distinct LDS banks.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16 (A = K rows read from LDS, B = Q^T kept in
 //     registers).  In the 32x32 accumulator layout each lane holds ONE query
-//     row (its column) and 16 of the 32 keys; the other 16 keys of the row
-//     sit in lane l ^ 32.  Row maxima need one cross-lane exchange per tile
-//     and the running sum stays lane-local.
+//     row (its column) and 16 of the 32 keys of a half; the other 16 sit in
+//     lane l ^ 32.  Row maxima need one cross-lane exchange per half and the
+//     running sum stays lane-local.
 //   * The output is accumulated transposed too, O^T += V^T P^T.  P^T comes
 //     straight from the score accumulators (rounded to bf16) as the B
 //     operand; the MFMA's k order is free as long as A and B agree, so the
 //     keys each lane already holds define it.  The A operand V^T is read from
 //     the row-major V tile with ds_read_b64_tr_b16, which hands each lane 4
 //     consecutive keys of one head-dim column (two reads per MFMA).
-//   * Softmax: the scale is folded into one FMA per score before exp2, and
-//     the reference maximum moves only when a tile's maximum passes it by
-//     more than 8 (log2 units), so the O^T rescale is rare and every
-//     probability is <= 2^8.
+//   * Software pipeline: the step for half u issues the PV MFMAs of half u-1
+//     and the S MFMAs of half u+1 while the VALU forms P of half u, with the
+//     VALU work split into small pieces placed between the MFMAs, so the
+//     exps run under the matrix work of the same wave.
+//   * Softmax without rescaling: each row's reference maximum comes from its
+//     first 32 keys and never moves, so O is never rescaled inside the loop
+//     (a rescale there would force the accumulators through a branch).
+//     Probabilities above 1 are fine up to 2^64; a row whose later maximum
+//     passes the reference by more than that makes the workgroup run a
+//     second pass, in which that row uses its true maximum.
 //   * Causality: a workgroup visits key tiles 0..(last position it needs)/64;
-//     a wave skips tiles wholly above its rows, and the diagonal tile masks
-//     keys > p.  Workgroups run longest first, and the G query heads of a KV
-//     group for the same query tile are placed on the same XCD so their K/V
-//     tiles are shared in that XCD's L2.
+//     each wave stops after the last half its rows can see and masks keys > p
+//     in halves on its diagonal.  Workgroups run longest first, and the G
+//     query heads of a KV group for the same query tile are placed on the
+//     same XCD so their K/V tiles are shared in that XCD's L2.
 // fp32 path: plain fp32 VALU kernel (one lane per query row, exact online
 // softmax) for fp32 caches.
 #include <type_traits>
@@ -55,13 +64,13 @@ typedef __attribute__((address_space(3))) shortx4_t lds_shortx4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 namespace pf {
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kRowsPerWave = 32;
-constexpr int kBlockRows = kWaves * kRowsPerWave;  // 128 query rows
+constexpr int kBlockRows = kWaves * kRowsPerWave;  // 256 query rows
 constexpr int kKeyTile = 64;
 constexpr int kThreads = kWaves * 64;
 constexpr int kXcds = 8;
-constexpr float kRescaleSlack = 8.0f;
+constexpr float kOverflowLog2 = 64.0f;  // probabilities stay below 2^64 before a recompute
 }  // namespace pf
 
 union Frag8 {
@@ -121,62 +130,65 @@ __device__ __forceinline__ int swz(int row, int dim) {
   return row * S::kRowBytes + slot * 16 + (dim & 7) * 2;
 }
 
-// Per-lane element offsets (within a tile) of this wave's direct-to-LDS
-// loads: load i of the wave fills 1 KiB block blk = wave * kLoadsPerWave + i,
-// lane L writes LDS bytes blk*1024 + L*16 = (row, slot) and so reads global
-// chunk slot ^ row_xor(row) of that row.
+// Per-lane byte offsets (within a tile) of this wave's direct-to-LDS loads:
+// load i of the wave fills 1 KiB block blk = wave * kLoadsPerWave + i, lane
+// L writes LDS bytes blk*1024 + L*16 = (row, slot) and so reads global chunk
+// slot ^ row_xor(row) of that row.
 template <int DH, int SWZ>
 struct StageOffsets {
   using S = PrefillShape<DH>;
-  int row[S::kLoadsPerWave];
-  int goff[S::kLoadsPerWave];  // row * row_stride + chunk * 8 (elements)
+  uint32_t boff[S::kLoadsPerWave];  // (row * row_stride + chunk * 8) * 2
   __device__ __forceinline__ void init(int wave, int lane, int row_stride) {
 #pragma unroll
     for (int i = 0; i < S::kLoadsPerWave; ++i) {
-      const int blk = wave * S::kLoadsPerWave + i;
-      row[i] = blk * S::kRowsPerLoad + lane / S::kChunks;
-      const int chunk = (lane % S::kChunks) ^ row_xor<DH, SWZ>(row[i]);
-      goff[i] = row[i] * row_stride + chunk * 8;
+      const int row = (wave * S::kLoadsPerWave + i) * S::kRowsPerLoad + lane / S::kChunks;
+      const int chunk = (lane % S::kChunks) ^ row_xor<DH, SWZ>(row);
+      boff[i] = static_cast<uint32_t>(row * row_stride + chunk * 8) * 2u;
     }
   }
 };
 
-// Issue this wave's share of the direct-to-LDS loads of one K/V tile pair
-// (tile rows key0 .. key0+63; rows at or past kv_len re-read row kv_len-1 and
-// are masked by causality later).
+// Issue this wave's share of the direct-to-LDS buffer loads of one 64-row K
+// or V tile (rows key0 .. key0+63 of one KV head).  The buffer descriptor
+// covers only the rows that hold data (< kv_len): the hardware range check
+// turns the bytes of rows past it into zeros in LDS, so no lane reads
+// outside the cache.  `wave` is wave-uniform (an SGPR), so the LDS address
+// in M0 is scalar arithmetic.
+constexpr int32_t kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
 template <int DH, int SWZ>
-__device__ __forceinline__ void stage_tile(char *lds_k, char *lds_v, const bf16_t *kg, const bf16_t *vg,
-                                           int row_stride, int64_t key0, int64_t kv_len, int wave,
-                                           const StageOffsets<DH, SWZ> &so) {
+__device__ __forceinline__ void stage_tile(char *lds_dst, const bf16_t *src, int row_stride, int key0, int kv_len,
+                                           int wave, const StageOffsets<DH, SWZ> &so) {
   using S = PrefillShape<DH>;
-  const int64_t tile_base = key0 * row_stride;
-  const bf16_t *kt = kg + tile_base;
-  const bf16_t *vt = vg + tile_base;
-  const bool full = key0 + pf::kKeyTile <= kv_len;
+  // Bytes from the tile start to the end of row kv_len-1 of this head; a
+  // staged tile always starts at or before that row.
+  const int tile_bytes = pf::kKeyTile * row_stride * 2;
+  const int valid = ((kv_len - 1 - key0) * row_stride + DH) * 2;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t *>(src + (int64_t)key0 * row_stride), 0, min(valid, tile_bytes), kBufferFlags);
 #pragma unroll
   for (int i = 0; i < S::kLoadsPerWave; ++i) {
-    const int blk = wave * S::kLoadsPerWave + i;
-    int off = so.goff[i];
-    if (!full && key0 + so.row[i] >= kv_len) {
-      off += static_cast<int>(kv_len - 1 - key0 - so.row[i]) * row_stride;
-    }
-    __builtin_amdgcn_global_load_lds(static_cast<const void *>(kt + off),
-                                     (lds_void_t *)(lds_k + blk * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(static_cast<const void *>(vt + off),
-                                     (lds_void_t *)(lds_v + blk * 1024), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)(lds_dst + (wave * S::kLoadsPerWave + i) * 1024), 16,
+                                             so.boff[i], 0, 0, 0);
   }
 }
 
 template <int DH, int SWZ>
-__global__ __launch_bounds__(pf::kThreads, 2) void prefill_bf16_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const PrefillArgs a) {
   using S = PrefillShape<DH>;
-  // [buffer][K, V][tile]: every LDS read below is a per-lane offset plus a
-  // compile-time immediate.
-  __shared__ __attribute__((aligned(1024))) char lds[2][2][S::kTileBytes];
+  // K and V tiles, two buffers each, as four separate arrays: the compiler
+  // can then tell that reads of one buffer do not alias the direct-to-LDS
+  // loads into another, and need not wait for those loads to land.  Every
+  // LDS read below is a per-lane offset plus a compile-time immediate.
+  __shared__ __attribute__((aligned(1024))) char lds_k0[S::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_k1[S::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v0[S::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v1[S::kTileBytes];
+  auto kbuf = [&](int b) __attribute__((always_inline)) { return b ? lds_k1 : lds_k0; };
+  auto vbuf = [&](int b) __attribute__((always_inline)) { return b ? lds_v1 : lds_v0; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int half = lane >> 5;       // 0 or 1
   const int col = lane & 31;        // the query row this lane owns (within the wave)
 
@@ -199,43 +211,49 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_bf16_kernel(const Pre
   const bf16_t *kg = static_cast<const bf16_t *>(a.k) + g * DH;
   const bf16_t *vg = static_cast<const bf16_t *>(a.v) + g * DH;
 
-  const int64_t blk_row0 = (int64_t)qtile * pf::kBlockRows;
-  const int64_t wave_row_first = blk_row0 + wave * pf::kRowsPerWave;
-  const int64_t my_row = wave_row_first + col;
-  const bool row_valid = my_row < a.t;
-  const int64_t my_pos = a.q_start + (row_valid ? my_row : (a.t - 1));
-  const int64_t wave_last_row = min(wave_row_first + pf::kRowsPerWave, a.t) - 1;
-  const int64_t wave_pos_last = a.q_start + wave_last_row;
-  const int64_t wave_pos_first = a.q_start + wave_row_first;
-  const int64_t blk_last_row = min(blk_row0 + pf::kBlockRows, a.t) - 1;
-  const int n_ktiles = static_cast<int>((a.q_start + blk_last_row) / pf::kKeyTile) + 1;
-  const bool wave_active = wave_row_first < a.t;
+  // Positions fit in int32: the host caps the slab capacity below 2^31.
+  const int t = static_cast<int>(a.t);
+  const int q_start = static_cast<int>(a.q_start);
+  const int kv_len = static_cast<int>(a.kv_len);
+  const int blk_row0 = qtile * pf::kBlockRows;
+  const int wave_row_first = blk_row0 + wave * pf::kRowsPerWave;
+  const int my_row = wave_row_first + col;
+  const bool row_valid = my_row < t;
+  const int my_pos = q_start + (row_valid ? my_row : (t - 1));
+  const bool wave_active = wave_row_first < t;
+  const int wave_last_row = min(wave_row_first + pf::kRowsPerWave, t) - 1;
+  const int wave_pos_last = q_start + wave_last_row;
+  const int wave_pos_first = q_start + wave_row_first;
+  const int blk_last_row = min(blk_row0 + pf::kBlockRows, t) - 1;
+  const int n_ktiles = (q_start + blk_last_row) / pf::kKeyTile + 1;
+  // 32-key halves this wave needs: 0 .. n_half-1 (keys up to its last row).
+  const int n_half = wave_active ? wave_pos_last / 32 + 1 : 0;
 
   StageOffsets<DH, SWZ> so;
   so.init(wave, lane, row_stride_kv);
   // Start loading key tile 0 before touching Q.
-  stage_tile<DH, SWZ>(lds[0][0], lds[0][1], kg, vg, row_stride_kv, 0, a.kv_len, wave, so);
+  stage_tile<DH, SWZ>(lds_k0, kg, row_stride_kv, 0, kv_len, wave, so);
 
   // Q^T as the MFMA B operand: lane holds row `col`, dims ks*16 + half*8 .. +8.
   Frag8 qf[S::KSTEPS];
   {
-    const bf16_t *qp = qg + (row_valid ? my_row : 0) * row_stride_q + (int64_t)h * DH + half * 8;
+    const bf16_t *qp = qg + (int64_t)(row_valid ? my_row : 0) * row_stride_q + (int64_t)h * DH + half * 8;
 #pragma unroll
     for (int ks = 0; ks < S::KSTEPS; ++ks) qf[ks].u = row_valid ? ld16(qp + ks * 16) : make_uint4(0, 0, 0, 0);
   }
 
-  // LDS read offsets within a tile.  K (A operand of S^T): row sub*32 + col,
-  // dims ks*16 + half*8; the row_xor of the swizzle depends only on row mod
-  // 16, so sub adds the immediate sub*32*rowbytes.
+  // LDS read offsets within a tile.  K (A operand of S^T): row col of the
+  // 32-key half, dims ks*16 + half*8; the row_xor of the swizzle depends only
+  // on row mod 16, so the half adds the immediate 32*rowbytes.
   int koff[S::KSTEPS];
 #pragma unroll
   for (int ks = 0; ks < S::KSTEPS; ++ks) koff[ks] = swz<DH, SWZ>(col, ks * 16 + half * 8);
   // V^T (A operand of O^T) via transposed reads: in each 16-lane group,
   // source lane a + 4j points at key kb + j, dims dbase + 4a .. +3, and lane
   // i of the group receives keys kb..kb+3 of dim dbase + i.  With
-  // kb = sub*32 + kk*16 + (grp/2)*4 + j and the second read at kb + 8, only
-  // (read r, dim tile d) changes the swizzled offset; sub and kk are
-  // immediates.
+  // kb = half32*32 + kk*16 + (grp/2)*4 + j and the second read at kb + 8,
+  // only (read r, dim tile d) changes the swizzled offset; the 32-key half
+  // and kk are immediates.
   const int grp = lane >> 4;
   const int src_a = lane & 3;
   const int src_j = (lane >> 2) & 3;
@@ -249,129 +267,230 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_bf16_kernel(const Pre
   }
 
   floatx16 oacc[S::DSUB];
-#pragma unroll
-  for (int d = 0; d < S::DSUB; ++d) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[d][i] = 0.f;
-  }
-  float m_run = -INFINITY;  // reference max (log2 units) of this lane's query row
-  float l_run = 0.f;        // this lane's share of sum(p), from the bf16 p the MFMA uses
+  float l_run;  // this lane's share of sum(p), from the bf16 p the MFMA uses
+  // Reference maximum (log2 units) of this lane's query row.  It is fixed
+  // from the row's first 32 keys, so O never needs rescaling: later
+  // probabilities may exceed 1, and a half whose maximum passes the
+  // reference by more than kOverflowLog2 marks the row as overflowed, which
+  // makes the workgroup run a second pass where that row's reference is its
+  // largest maximum (then every probability of the row is <= 1).
+  float m_ref = -INFINITY;
+  float m_seen = -INFINITY;  // largest half maximum seen by this row
+  bool ovf = false;          // this lane saw a half past m_ref + kOverflowLog2
   const uint32_t kOnesBf16x2 = 0x3F803F80u;  // (1.0, 1.0) in bf16
+  __shared__ int redo_flag;
+  if (tid == 0) redo_flag = 0;  // ordered before any update by the first barrier below
 
-  auto tile_step = [&](auto buf_c, int kt) {
-    constexpr int BUF = decltype(buf_c)::value;
-    // Tile kt has landed for every wave, and every wave is done with tile kt-1,
-    // whose buffer the next loads overwrite.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (kt + 1 < n_ktiles) {
-      stage_tile<DH, SWZ>(lds[BUF ^ 1][0], lds[BUF ^ 1][1], kg, vg, row_stride_kv,
-                          (int64_t)(kt + 1) * pf::kKeyTile, a.kv_len, wave, so);
-    }
-    const int64_t key0 = (int64_t)kt * pf::kKeyTile;
-    if (!wave_active || key0 > wave_pos_last) return;
-    char *tk = lds[BUF][0];
-    char *tv = lds[BUF][1];
+  // Software pipeline over 32-key halves u of the key range.  Step u issues
+  //   PV(u-1): O^T += V^T P^T for half u-1      (MFMA)
+  //   S(u+1):  S^T = K Q^T for half u+1          (MFMA)
+  //   softmax of half u: P(u) from S(u)          (VALU)
+  // so the exps of one half run while the matrix cores work on its
+  // neighbours.  Halves 2p-1 and 2p form period p, which reads K tile p and
+  // V tile p-1 from LDS while K tile p+1 and V tile p are being loaded.
+  floatx16 sa, sb;     // S of the half being normalised / being computed
+  Frag8 pa[2], pb[2];  // P of the half being multiplied / being formed
 
-    // ---- S^T = K Q^T for two 32-key sub-tiles ----
-    floatx16 sacc[2];
+  // Operands of the step's MFMAs.  PV MFMA i (i < 2*DSUB) is dim tile i/2,
+  // key step i%2 of the V half; S MFMA ks reads K rows of the K half.
+  auto read_v = [&](const char *tv, int i) __attribute__((always_inline)) {
+    const int d = i >> 1, kk = i & 1;
+    Frag8 f;
+    f.s4[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t *)(tv + voff[0][d] + kk * 16 * S::kRowBytes));
+    f.s4[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t *)(tv + voff[1][d] + kk * 16 * S::kRowBytes));
+    return f;
+  };
+  auto read_k = [&](const char *tk, int ks) __attribute__((always_inline)) {
+    Frag8 f;
+    f.u = *reinterpret_cast<const uint4 *>(tk + koff[ks]);
+    return f;
+  };
+  // P for accumulator pair j of key step kk: k-slot j of lane half `half`
+  // in step kk is key kk*16 + (j/4)*8 + half*4 + (j%4), which is S^T
+  // accumulator element kk*8 + j.
+  auto make_p_pair = [&](const floatx16 &s, Frag8 (&p)[2], int kk, int j) __attribute__((always_inline)) {
+    const float p0 = fast_exp2(fmaf(s[kk * 8 + 2 * j], a.scale_log2, -m_ref));
+    const float p1 = fast_exp2(fmaf(s[kk * 8 + 2 * j + 1], a.scale_log2, -m_ref));
+    p[kk].w[j] = cvt_pk_bf16(p0, p1);
+  };
+  auto sum_p = [&](const Frag8 &p, float acc) __attribute__((always_inline)) {
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int j = 0; j < 4; ++j) acc = dot2_bf16_f32(p.w[j], kOnesBf16x2, acc);
+    return acc;
+  };
+
+  // One step of the pipeline, scheduled by hand: chunk i issues MFMA i (the
+  // PV MFMAs, then the S MFMAs), the LDS reads of MFMA i+4 and one piece of
+  // the softmax of half u, with a scheduling fence between chunks, so the
+  // VALU work runs under the matrix work and few operands are in flight.
+  // The generic form (first, causal-diagonal and last halves) adds only
+  // selects, never branches, so O and S stay in fixed registers:
+  //  * the causal mask;
+  //  * PV MFMAs without a previous half get a zero V operand (a select:
+  //    LDS that was never written may hold NaN);
+  //  * an S MFMA without a next half produces a value nobody reads;
+  //  * P of a half outside the wave's range is zero, and l, the reference
+  //    and the maxima are updated only for halves in range.
+  auto step = [&](auto generic_c, int u, const char *tk, const char *tv, floatx16 &s_cur, floatx16 &s_next,
+                  Frag8 (&p_prev)[2], Frag8 (&p_cur)[2]) __attribute__((always_inline)) {
+    constexpr bool kGeneric = decltype(generic_c)::value;
+    constexpr int NPV = 2 * S::DSUB;
+    constexpr int NM = NPV + S::KSTEPS;
+    // Softmax pieces: the row maximum (4 pieces of 4 elements), its
+    // cross-lane exchange, the probabilities (8 pieces of one packed pair)
+    // and the running sum of P(u-1) (2 pieces).
+    constexpr int kMax0 = 0, kXchg = 4, kP0 = 5, kL0 = 13, kPieces = 15;
+    const bool do_pv = !kGeneric || (u >= 1 && u - 1 < n_half);
+    const bool do_soft = !kGeneric || (u >= 0 && u < n_half);
+    if constexpr (kGeneric) {
+      // Causal mask: accumulator element i is key 32u + (i/4)*8 + half*4 +
+      // (i%4) of query row `col` (a no-op below the wave's diagonal).
+      const int rel = min(my_pos - u * 32 - half * 4, 32);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[sub][i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < S::KSTEPS; ++ks) {
-        Frag8 af;
-        af.u = *reinterpret_cast<const uint4 *>(tk + koff[ks] + sub * 32 * S::kRowBytes);
-        sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af.v, qf[ks].v, sacc[sub], 0, 0, 0);
-      }
+      for (int i = 0; i < 16; ++i) s_cur[i] = (i >> 2) * 8 + (i & 3) > rel ? -INFINITY : s_cur[i];
     }
-    // ---- causal mask (diagonal tiles only) ----
-    // Accumulator element i of sub-tile `sub` is key
-    //   key0 + sub*32 + (i/4)*8 + half*4 + (i%4)   for query row `col`.
-    if (key0 + pf::kKeyTile - 1 > wave_pos_first) {
-      const int64_t rel64 = my_pos - key0;
-      const int rel = rel64 < pf::kKeyTile ? static_cast<int>(rel64) : pf::kKeyTile;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if (sub * 32 + (i >> 2) * 8 + half * 4 + (i & 3) > rel) sacc[sub][i] = -INFINITY;
-        }
-      }
-    }
-    // ---- P^T (bf16) as the B operand of O^T += V^T P^T ----
-    // Probabilities are formed against the current reference first (each
-    // sub-tile as soon as its scores exist, so the exps of sub-tile 0 can
-    // overlap the MFMAs of sub-tile 1); the tile maximum is checked
-    // alongside, and in the rare case that it passes the reference by more
-    // than the slack, O and l are rescaled and P is formed again.
-    Frag8 pfr[2][2];
-    auto make_p = [&](int sub) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p0 = fast_exp2(fmaf(sacc[sub][kk * 8 + 2 * j], a.scale_log2, -m_run));
-          const float p1 = fast_exp2(fmaf(sacc[sub][kk * 8 + 2 * j + 1], a.scale_log2, -m_run));
-          pfr[sub][kk].w[j] = cvt_pk_bf16(p0, p1);
-        }
+    Frag8 opnd[NM];
+    auto issue_read = [&](int i) __attribute__((always_inline)) {
+      if (i < NPV) {
+        opnd[i] = read_v(tv, i);
+        if (kGeneric && !do_pv) opnd[i].u = make_uint4(0, 0, 0, 0);
+      } else {
+        opnd[i] = read_k(tk, i - NPV);
       }
     };
-    make_p(0);
-    make_p(1);
-    float tmax = -INFINITY;
+    float tmax = s_cur[0];
+    float tmax_other = 0.f;
+    float l_add = 0.f;
+    auto piece = [&](int i) __attribute__((always_inline)) {
+      if (i >= kMax0 && i < kMax0 + 4) {
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[sub][i]);
-    }
-    tmax = fmaxf(tmax, shfl_xor_f(tmax, 32)) * a.scale_log2;  // scale > 0 keeps the order
-    // Both lanes of a row take the same decision.
-    const bool need = tmax > m_run + pf::kRescaleSlack;
-    if (__any(need)) {
-      if (need) {
-        const float alpha = fast_exp2(m_run - tmax);  // m_run = -inf gives 0
-        l_run *= alpha;
-#pragma unroll
-        for (int d = 0; d < S::DSUB; ++d) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+        for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, s_cur[(i - kMax0) * 4 + e]);
+      } else if (i == kXchg) {
+        tmax_other = shfl_xor_f(tmax, 32);
+        if constexpr (kGeneric) {
+          // The row's first half (key 0 is always visible) sets the reference.
+          const float t = fmaxf(tmax, tmax_other) * a.scale_log2;
+          m_ref = (do_soft && m_ref == -INFINITY) ? t : m_ref;
         }
-        m_run = tmax;
+      } else if (i >= kP0 && i < kP0 + 8) {
+        make_p_pair(s_cur, p_cur, (i - kP0) >> 2, (i - kP0) & 3);
+      } else if (i >= kL0 && i < kL0 + 2) {
+        l_add = sum_p(p_prev[i - kL0], l_add);
       }
-      make_p(0);
-      make_p(1);
+    };
+    constexpr int kAhead = 4;  // LDS reads run this many MFMAs ahead
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) issue_read(i);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      if (i + kAhead < NM) issue_read(i + kAhead);
+      if (i < NPV) {
+        oacc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[i].v, p_prev[i & 1].v, oacc[i >> 1], 0, 0, 0);
+      } else {
+        if (i == NPV) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s_next[e] = 0.f;
+        }
+        s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[i].v, qf[i - NPV].v, s_next, 0, 0, 0);
+      }
+      piece(i);
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int i = NM; i < kPieces; ++i) piece(i);  // head_dim 64: fewer MFMAs than pieces
+    const float t = fmaxf(tmax, tmax_other) * a.scale_log2;
+    if constexpr (kGeneric) {
+      l_run += do_pv ? l_add : 0.f;
+      m_seen = do_soft ? fmaxf(m_seen, t) : m_seen;
+      ovf = ovf || (do_soft && t > m_ref + pf::kOverflowLog2);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) l_run = dot2_bf16_f32(pfr[sub][kk].w[j], kOnesBf16x2, l_run);
+        if (!do_soft) p_cur[kk].u = make_uint4(0, 0, 0, 0);
       }
-    }
-    // k-slot j of lane half `half` in step (sub, kk) is key
-    //   sub*32 + kk*16 + (j/4)*8 + half*4 + (j%4).
-#pragma unroll
-    for (int d = 0; d < S::DSUB; ++d) {
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int rows = (sub * 32 + kk * 16) * S::kRowBytes;
-          Frag8 af;
-          af.s4[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t *)(tv + voff[0][d] + rows));
-          af.s4[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t *)(tv + voff[1][d] + rows));
-          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af.v, pfr[sub][kk].v, oacc[d], 0, 0, 0);
-        }
-      }
+    } else {
+      l_run += l_add;
+      m_seen = fmaxf(m_seen, t);
+      ovf = ovf || t > m_ref + pf::kOverflowLog2;
     }
   };
 
-  for (int kt = 0; kt < n_ktiles; kt += 2) {
-    tile_step(std::integral_constant<int, 0>(), kt);
-    if (kt + 1 < n_ktiles) tile_step(std::integral_constant<int, 1>(), kt + 1);
+  // One period: barrier, start the next loads, then halves 2p-1 and 2p.
+  // Step 2p-1 reads K half 2p (tile p, rows 0..31) and V half 2p-2 (tile
+  // p-1, rows 0..31); step 2p the second halves.
+  constexpr int kHalfBytes = 32 * S::kRowBytes;
+  auto period_start = [&](int kb, int p) __attribute__((always_inline)) {
+    // Every wave's loads of K tile p and V tile p-1 have landed, and every
+    // wave is done with K tile p-1 and V tile p-2, whose buffers the next
+    // loads overwrite.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (p + 1 < n_ktiles) stage_tile<DH, SWZ>(kbuf(kb ^ 1), kg, row_stride_kv, (p + 1) * pf::kKeyTile, kv_len, wave, so);
+    if (p < n_ktiles) stage_tile<DH, SWZ>(vbuf(kb), vg, row_stride_kv, p * pf::kKeyTile, kv_len, wave, so);
+  };
+  auto period_fast = [&](auto buf_c, int p) __attribute__((always_inline)) {
+    constexpr int KB = decltype(buf_c)::value;  // K tile p sits in buffer p % 2
+    period_start(KB, p);
+    const char *tk = kbuf(KB);
+    const char *tv = vbuf(KB ^ 1);
+    step(std::false_type(), 2 * p - 1, tk, tv, sa, sb, pa, pb);
+    step(std::false_type(), 2 * p, tk + kHalfBytes, tv + kHalfBytes, sb, sa, pb, pa);
+  };
+  auto period_generic = [&](int p) __attribute__((always_inline)) {
+    const int kb = p & 1;
+    period_start(kb, p);
+    const char *tk = kbuf(kb);
+    const char *tv = vbuf(kb ^ 1);
+    step(std::true_type(), 2 * p - 1, tk, tv, sa, sb, pa, pb);
+    step(std::true_type(), 2 * p, tk + kHalfBytes, tv + kHalfBytes, sb, sa, pb, pa);
+  };
+  // Periods 1 .. p_fast_end-1 take the fast form: both steps have a previous
+  // half, a next half and a half in range, and neither half reaches past
+  // the wave's first row (2p+1 < n_half and 64p+31 <= wave_pos_first).  They
+  // run in pairs (K buffers 1, 0), the rest in the generic form.
+  int p_fast_end = 1;
+  if (wave_active) {
+    const int by_len = n_half / 2;                           // largest p with 2p+1 < n_half, plus one
+    const int by_diag = wave_pos_first >= 31 ? (wave_pos_first - 31) / 64 + 1 : 0;
+    p_fast_end = max(1, min(by_len, by_diag));
+  }
+  const int p_pair_end = 1 + ((p_fast_end - 1) & ~1);
+
+  for (int pass = 0;; ++pass) {
+#pragma unroll
+    for (int d = 0; d < S::DSUB; ++d) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[d][i] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sa[i] = 0.f;
+      sb[i] = 0.f;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      pa[kk].u = make_uint4(0, 0, 0, 0);
+      pb[kk].u = make_uint4(0, 0, 0, 0);
+    }
+    l_run = 0.f;
+    if (pass > 0) stage_tile<DH, SWZ>(lds_k0, kg, row_stride_kv, 0, kv_len, wave, so);
+    period_generic(0);
+    int p = 1;
+    for (; p < p_pair_end; p += 2) {
+      period_fast(std::integral_constant<int, 1>(), p);
+      period_fast(std::integral_constant<int, 0>(), p + 1);
+    }
+    for (; p <= n_ktiles; ++p) period_generic(p);
+    if (pass > 0) break;
+    if (__any(ovf) && lane == 0) redo_flag = 1;
+    __syncthreads();
+    if (redo_flag == 0) break;
+    // Some row of the workgroup overflowed: the workgroup runs again, and
+    // each row that overflowed takes its largest maximum as the reference
+    // (so now every probability is <= 1).  The other rows keep theirs and
+    // repeat the same arithmetic, so a row's result never depends on the
+    // other rows of its workgroup.  The barrier above also retires every
+    // read of the LDS tiles the restart overwrites.
+    m_ref = ovf ? m_seen : m_ref;
   }
 
   const float l_tot = l_run + shfl_xor_f(l_run, 32);
@@ -380,7 +499,7 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_bf16_kernel(const Pre
   // O^T accumulator element i of tile d is dim d*32 + (i/4)*8 + half*4 + (i%4)
   // of query row `col`.
   if (a.o_bf16) {
-    bf16_t *op = static_cast<bf16_t *>(a.o) + my_row * row_stride_q + (int64_t)h * DH;
+    bf16_t *op = static_cast<bf16_t *>(a.o) + (int64_t)my_row * row_stride_q + (int64_t)h * DH;
 #pragma unroll
     for (int d = 0; d < S::DSUB; ++d) {
 #pragma unroll
@@ -393,7 +512,7 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_bf16_kernel(const Pre
       }
     }
   } else {
-    float *op = static_cast<float *>(a.o) + my_row * row_stride_q + (int64_t)h * DH;
+    float *op = static_cast<float *>(a.o) + (int64_t)my_row * row_stride_q + (int64_t)h * DH;
 #pragma unroll
     for (int d = 0; d < S::DSUB; ++d) {
 #pragma unroll
@@ -406,7 +525,7 @@ __global__ __launch_bounds__(pf::kThreads, 2) void prefill_bf16_kernel(const Pre
     }
   }
   if (a.lse != nullptr && half == 0) {
-    a.lse[my_row * a.n_q_heads + h] = (m_run + log2f(l_tot)) * kLn2;
+    a.lse[(int64_t)my_row * a.n_q_heads + h] = (m_ref + log2f(l_tot)) * kLn2;
   }
 }
 
