@@ -66,7 +66,7 @@ DECODE_SOURCES = (
     "yoco_shared_kv_amd/csrc/decode_kernel.h",
     "yoco_shared_kv_amd/csrc/decode.hip",
     "yoco_shared_kv_amd/csrc/device_common.h",
-    "yoco_shared_kv_amd/csrc/yoco_internal.h",
+    "yoco_shared_kv_amd/csrc/decode_args.h",
 )
 
 
@@ -211,6 +211,36 @@ def bench_prefill(args, torch, y, W):
                 frac=tflops / BF16_DENSE_PEAK_TFLOPS)
 
 
+def bench_project(args, torch, y, W):
+    """K^/V^ projection of a 32768-row prompt at 3B-like widths (3072 -> 2 x
+    1024, bf16, matrix cores), with unit gain and with an fp32 gain."""
+    cfg = W.PROJECT_3B
+    log(f"generating projection workload N={cfg['n']}")
+    pc = W.make_project(**cfg, unit_gain=False)
+    n, d = pc.m.shape
+    m, w_k, w_v = to_dev(pc.m, torch), to_dev(pc.w_k, torch), to_dev(pc.w_v, torch)
+    gain = torch.from_numpy(pc.gain).cuda()
+    cache = y.KVCache(1, n, pc.n_kv_heads, pc.head_dim, torch.bfloat16)
+    stream = torch.cuda.current_stream()
+    flops = 2.0 * n * d * 2 * pc.n_kv_heads * pc.head_dim
+    res = {}
+    for name, g in (("unit_gain", None), ("fp32_gain", gain)):
+        y.kv_project(cache, m, w_k, w_v, g, pc.eps, stream=stream)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.prefill_reps)]
+        for s_ev, e_ev in evs:
+            s_ev.record(stream)
+            y.kv_project(cache, m, w_k, w_v, g, pc.eps, stream=stream)
+            e_ev.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        res[name] = dict(ms=ms, tflops=flops / (ms * 1e-3) / 1e12)
+        log(f"kv_project ({name}) {ms:.3f} ms -> {res[name]['tflops']:.1f} TFLOP/s")
+    res["flops"] = flops
+    return res
+
+
 def cpu_baseline(dec, W):
     import oracle
     case = dec["case"]
@@ -244,6 +274,7 @@ def main():
 
     dec = bench_decode(args, torch, y, W)
     pre = None if args.no_prefill else bench_prefill(args, torch, y, W)
+    proj = None if args.no_prefill else bench_project(args, torch, y, W)
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec, W)
     traffic, why = counter_traffic()
     if why:
@@ -294,6 +325,17 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(pre["tflops"], 1),
                          "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(pre["frac"], 4), "flops_per_launch": pre["flops"]},
+        }
+    if proj is not None:
+        u = proj["unit_gain"]
+        result["kv_project"] = {
+            "workload": "K^/V^ projection of 32768 rows, 3072 -> 2 x 1024 (8 KV heads x 128), bf16 MFMA, "
+                        "RMSNorm fused, written into the cache",
+            "ms": round(u["ms"], 4), "tflops": round(u["tflops"], 1),
+            "ms_fp32_gain": round(proj["fp32_gain"]["ms"], 4),
+            "roofline": {"bound": "mfma", "achieved": round(u["tflops"], 1), "peak": BF16_DENSE_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(u["tflops"] / BF16_DENSE_PEAK_TFLOPS, 4),
+                         "flops_per_launch": proj["flops"]},
         }
     print(json.dumps(result), flush=True)
 

@@ -314,6 +314,41 @@ def test_kv_project_parity(dtype, n, d):
     assert torch.all(cache.v[1, 20 + n:] == 7.0)
 
 
+@pytest.mark.parametrize("n,d,hkv,dh,unit_gain", [
+    (600, 256, 2, 128, True),     # 3 row tiles with a ragged tail, unit gain (NULL)
+    (600, 256, 2, 128, False),    # same rows, fp32 gain (hi/lo split)
+    (257, 1024, 4, 64, False),    # one full row tile plus one row
+    (96, 192, 2, 128, False),     # d_model % 128 != 0: the fp32-FMA tiled kernel
+])
+def test_prompt_projection_paths(n, d, hkv, dh, unit_gain):
+    """Prompt-sized bf16 projections run on the matrix cores when d_model is a
+    multiple of 128 and the columns a multiple of 256, else on the fp32-FMA
+    tiled kernel; both meet the same bound."""
+    p = W.make_project(n=n, d_model=d, n_kv_heads=hkv, head_dim=dh, unit_gain=unit_gain, seed=25)
+    cache = y.KVCache(2, n + 9, hkv, dh, torch.bfloat16)
+    cache.k.fill_(7.0)
+    cache.v.fill_(7.0)
+    gain = None if unit_gain else torch.from_numpy(p.gain).cuda()
+    y.kv_project(cache, to_dev(p.m), to_dev(p.w_k), to_dev(p.w_v), gain, p.eps, seq=1, row_start=5)
+    g = None if unit_gain else p.gain
+    ynorm = np.abs(orc().rmsnorm(p.m, g, p.eps))
+    for got, w, name in ((cache.k, p.w_k, "K^"), (cache.v, p.w_v, "V^")):
+        stored = to_stored(got[1, 5:5 + n]).reshape(n, -1)
+        ref = orc().project(p.m, w, g, p.eps)
+        assert_projection_bf16(stored, ref, ynorm @ np.abs(W.as_f32(w).astype(np.float64)), d, name)
+        assert torch.all(got[0] == 7.0) and torch.all(got[1, :5] == 7.0) and torch.all(got[1, 5 + n:] == 7.0)
+
+
+def test_q_project_prompt_mfma():
+    r = rng(26)
+    x = W.store(r.standard_normal((300, 512)).astype(np.float32), W.BF16)
+    wq = W.store((r.standard_normal((512, 8 * 64)) / math.sqrt(512)).astype(np.float32), W.BF16)
+    gain = (0.5 + r.random(512)).astype(np.float32)
+    q = y.q_project(to_dev(x), to_dev(wq), 8, 64, gain=torch.from_numpy(gain).cuda(), eps=1e-5)
+    abs_terms = np.abs(orc().rmsnorm(x, gain, 1e-5)) @ np.abs(W.as_f32(wq).astype(np.float64))
+    assert_projection_bf16(to_stored(q).reshape(300, -1), orc().project(x, wq, gain, 1e-5), abs_terms, 512, "Q^")
+
+
 def test_append_matches_project_and_advances_lengths():
     p = W.make_project(n=3, d_model=3072, seed=22)
     cache = y.KVCache(3, 50, 8, 128, torch.bfloat16)

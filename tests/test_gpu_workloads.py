@@ -9,7 +9,10 @@ benchmark times (library-chosen split size, fp32 outputs):
 * ragged decode, 16 sequences of 8192..131072 rows: layers 0 and 12 against
   the oracle (all sequences, all heads);
 * decode over 2^20 rows with a planted needle per KV head: the needle check
-  for all 13 layers and oracle parity for layers 0 and 7.
+  for all 13 layers and oracle parity for layers 0 and 7;
+* K^/V^ projection of 32768 rows at 3B-like widths (3072 -> 2 x 1024, matrix
+  cores): a seeded sample of rows against the fp64 projection, every value
+  finite, and the cache rows outside the range untouched.
 """
 import math
 import sys
@@ -20,7 +23,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_helpers import assert_parity, metrics, to_dev, to_stored
+from tests.gpu_helpers import assert_parity, assert_projection_bf16, metrics, to_dev, to_stored
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -125,3 +128,23 @@ def test_needle_1m():
         ref = oracle.decode(case.q[l:l + 1, 0], n, case.k[0], v_all, case.softmax_scale)
         assert_parity(outs[l], ref[0], bf16=True, what=f"needle layer {l}")
     say(f"needle 1M: worst cos(o, V_needle) {worst_cos:.5f}")
+
+
+def test_kv_project_3b_sampled_rows():
+    p = W.make_project(**W.PROJECT_3B)
+    n, d = p.m.shape
+    cache = y.KVCache(1, n + 8, p.n_kv_heads, p.head_dim, torch.bfloat16)
+    cache.k.fill_(7.0)
+    cache.v.fill_(7.0)
+    y.kv_project(cache, to_dev(p.m), to_dev(p.w_k), to_dev(p.w_v), None, p.eps, row_start=4)
+    assert cache.len.tolist() == [n + 4]
+    assert torch.all(cache.k[0, :4] == 7.0) and torch.all(cache.v[0, n + 4:] == 7.0)
+    assert torch.isfinite(cache.k[0, 4:n + 4].float()).all() and torch.isfinite(cache.v[0, 4:n + 4].float()).all()
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, n - 1], np.random.default_rng(7).integers(0, n, 59)]))
+    m_s = p.m[rows]
+    ynorm = np.abs(oracle.rmsnorm(m_s, None, p.eps))
+    for got, w, name in ((cache.k, p.w_k, "K^"), (cache.v, p.w_v, "V^")):
+        stored = to_stored(got[0, torch.from_numpy(4 + rows).cuda()]).reshape(len(rows), -1)
+        ref = oracle.project(m_s, w, None, p.eps)
+        assert_projection_bf16(stored, ref, ynorm @ np.abs(W.as_f32(w).astype(np.float64)), d, name)
+    say(f"kv_project 3B: {len(rows)} sampled rows of {n} within one ulp + fp32 bound")

@@ -371,3 +371,4 @@ PREFILL_32K = dict(n=32768, n_q_heads=24, n_kv_heads=8, head_dim=128)
 RAGGED_16 = dict(n_seq=16, lo=RAGGED_LO, hi=RAGGED_HI, n_q_heads=24, n_kv_heads=8,
                  head_dim=128, layers=13)
 NEEDLE_1M = dict(n_rows=1 << 20, n_q_heads=24, n_kv_heads=8, head_dim=128, layers=13)
+PROJECT_3B = dict(n=32768, d_model=3072, n_kv_heads=8, head_dim=128)

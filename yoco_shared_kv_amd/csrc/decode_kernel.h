@@ -42,7 +42,7 @@
 #pragma once
 
 #include "device_common.h"
-#include "yoco_internal.h"
+#include "decode_args.h"
 
 namespace yoco {
 

@@ -9,6 +9,8 @@
 // row factor 1/rms_r is common to every term.
 //
 // Two kernels share this arithmetic:
+//  * prompt projections in bf16 with d_model % 64 == 0 and a multiple of 256
+//    columns run on the matrix cores (project_mfma.hip); the others here:
 //  * rows >= 9 (prompt projection): one workgroup computes a 64-row x
 //    64-column tile of one output (K or V, or Q): it first reduces the 64 row
 //    norms (fp32), then streams [64 x 32] slices of x (times gain) and
@@ -343,6 +345,7 @@ static hipError_t launch_project_w(const ProjArgs &a, int w_dt, int o_dt, hipStr
 }
 
 hipError_t launch_project(const ProjArgs &a, int x_dt, int w_dt, int o_dt, hipStream_t s) {
+  if (!use_small(a) && project_mfma_applies(a, x_dt, w_dt, o_dt)) return launch_project_mfma(a, s);
   if (x_dt == YOCO_DT_F32) return launch_project_w<float>(a, w_dt, o_dt, s);
   if (x_dt == YOCO_DT_BF16) return launch_project_w<bf16_t>(a, w_dt, o_dt, s);
   return hipErrorInvalidValue;

@@ -1,0 +1,313 @@
+// Prompt-sized fused RMSNorm + projection on the matrix cores (bf16 in, bf16
+// out), written straight to its destination rows.
+//
+// What it computes ([Notes] "YOCO：You Only Cache Once 中文精读笔记" s.2.1
+// Eq. 2: K^ = LN(M) W_K, V^ = LN(M) W_V with LN = RMSNorm, projected once at
+// the self/cross boundary; Eq. 3: Q^l = LN(X^l) W_Q^l):
+//   out_p[row][j] = (sum_c x[row][c] * gain[c] * W_p[c][j]) / rms_row,
+//   rms_row = sqrt(mean_c x[row][c]^2 + eps).
+// The row factor 1/rms is applied after the sum (the same value).
+//
+// Layout of the work: the product is computed transposed, out^T = W^T x^T,
+// with v_mfma_f32_32x32x16_bf16:
+//   * A = W^T: lane l holds output column l%32 and 8 consecutive k; read
+//     from the row-major W tile in LDS with ds_read_b64_tr_b16 (4 k rows of
+//     one column per read, two reads per fragment);
+//   * B = x^T: lane l holds input row l%32 and 8 consecutive k, one 16-byte
+//     LDS read from the row-major x tile;
+//   * C: each lane owns ONE input row and 16 output columns, so the 1/rms
+//     factor is lane-local and the bf16 stores are 8 bytes wide.
+// The sum of squares of each row comes from the same x fragments (bf16 dot2
+// of a fragment with itself, exact products, fp32 sums).  With a gain, x*g is
+// formed in fp32 and split into bf16 hi + lo (hi = RNE(x*g), lo = RNE(x*g -
+// hi)), two MFMAs per fragment: the split leaves about 2^-17 of the term,
+// far below the fp32 accumulation error; without a gain x enters as stored.
+//
+// A workgroup is 8 waves and computes 256 input rows x 256 output columns of
+// one weight; wave (wr, wc) owns rows wr*64.. and columns wc*128... The
+// reduction runs in slices of 64, staged global -> LDS with 16-byte buffer
+// loads to LDS, two stages deep: x slice [256][64] (128-byte rows, chunk
+// index XOR row%8), W slice [64][256] as two [64][128] halves (256-byte rows,
+// chunk index XOR a 4-bit function of the row).  The x descriptor ends at the
+// last input row, so rows past it load as zeros and are not stored.
+#include "device_common.h"
+#include "yoco_internal.h"
+
+namespace yoco {
+namespace pm {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx2_t __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef short shortx4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4_t lds_shortx4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kRows = 256;                      // input rows per workgroup
+constexpr int kCols = 256;                      // output columns per workgroup
+constexpr int kK = 64;                          // reduction slice per stage
+constexpr int kXRowBytes = kK * 2;              // 128
+constexpr int kXTileBytes = kRows * kXRowBytes;  // 32 KiB
+constexpr int kWRowBytes = 128 * 2;             // one half: 128 columns
+constexpr int kWHalfBytes = kK * kWRowBytes;    // 16 KiB
+constexpr int kXLoads = kXTileBytes / 1024 / kWaves;     // 1 KiB loads per wave per stage
+constexpr int kWLoads = 2 * kWHalfBytes / 1024 / kWaves;
+constexpr int kXcds = 8;
+constexpr int32_t kBufferFlags = 0x00020000;    // raw buffer, 32-bit data format
+
+union Frag8 {
+  bf16x8_t v;
+  uint4 u;
+  uint32_t w[4];
+  shortx4_t s4[2];
+};
+
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const floatx2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Chunk-index XOR of a W half-tile row (16 chunks of 16 bytes).
+__device__ __forceinline__ int w_xor(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
+
+// LDS byte offset of column `col` (multiple of 4) in row k of a W half tile.
+__device__ __forceinline__ int w_off(int k, int col) {
+  return k * kWRowBytes + (((col >> 3) ^ w_xor(k)) << 4) + (col & 7) * 2;
+}
+
+}  // namespace pm
+
+template <bool kGain>
+__global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const ProjArgs a) {
+  using namespace pm;
+  __shared__ __attribute__((aligned(1024))) char lds_x0[kXTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_x1[kXTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_w0[2 * kWHalfBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_w1[2 * kWHalfBytes];
+  __shared__ __attribute__((aligned(1024))) float lds_g0[256];
+  __shared__ __attribute__((aligned(1024))) float lds_g1[256];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  // Block -> (row tile, column tile): the column tiles of one row tile run
+  // on consecutive slots of one XCD, so their x rows are shared in its L2.
+  const int col_tiles_per_out = a.ncols / kCols;
+  const int col_tiles = col_tiles_per_out * a.n_out;
+  const int row_tiles = static_cast<int>((a.n + kRows - 1) / kRows);
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int row_tile = (slot / col_tiles) * kXcds + xcd;
+  if (row_tile >= row_tiles) return;
+  const int ct = slot % col_tiles;
+  const int p = ct / col_tiles_per_out;
+  const int col0 = (ct % col_tiles_per_out) * kCols;
+  const int64_t row0 = static_cast<int64_t>(row_tile) * kRows;
+  const int rows_here = a.n - row0 < kRows ? static_cast<int>(a.n - row0) : kRows;
+  const int d = a.d;
+  const int n_stages = d / kK;
+
+  const bf16_t *xg = static_cast<const bf16_t *>(a.x) + row0 * d;
+  const bf16_t *wg = static_cast<const bf16_t *>(a.w[p]);
+  const __amdgpu_buffer_rsrc_t x_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(xg), 0, rows_here * d * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t w_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(wg), 0, d * a.ncols * 2, kBufferFlags);
+  __amdgpu_buffer_rsrc_t g_rsrc;
+  if constexpr (kGain) g_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.gain), 0, d * 4, kBufferFlags);
+
+  // Per-lane byte offsets of this wave's staging loads.  x block b (8 rows):
+  // lane L -> row b*8 + L/8, LDS slot L%8 holding global chunk slot^(row%8).
+  // W block b (4 rows of half b/16): lane L -> row (b%16)*4 + L/16, slot
+  // L%16 holding global chunk slot^w_xor(row).
+  uint32_t xsoff[kXLoads], wsoff[kWLoads];
+#pragma unroll
+  for (int i = 0; i < kXLoads; ++i) {
+    const int row = (wave * kXLoads + i) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ (row & 7);
+    xsoff[i] = static_cast<uint32_t>(row * d * 2 + chunk * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < kWLoads; ++i) {
+    const int blk = wave * kWLoads + i;
+    const int k = (blk & 15) * 4 + (lane >> 4);
+    const int chunk = (lane & 15) ^ w_xor(k);
+    wsoff[i] = static_cast<uint32_t>((k * a.ncols + (blk >> 4) * 128) * 2 + chunk * 16);
+  }
+  auto stage = [&](char *xdst, char *wdst, float *gdst, int s) __attribute__((always_inline)) {
+    const uint32_t k0 = static_cast<uint32_t>(s * kK);
+#pragma unroll
+    for (int i = 0; i < kXLoads; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, (lds_void_t *)(xdst + (wave * kXLoads + i) * 1024), 16, xsoff[i],
+                                               k0 * 2, 0, 0);
+    }
+    const uint32_t wbase = (k0 * a.ncols + col0) * 2;
+#pragma unroll
+    for (int i = 0; i < kWLoads; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_t *)(wdst + (wave * kWLoads + i) * 1024), 16, wsoff[i],
+                                               wbase, 0, 0);
+    }
+    if constexpr (kGain) {
+      // 64 gains of this slice (lanes 16..63 fetch the next ones, unused).
+      if (wave == 0) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(g_rsrc, (lds_void_t *)gdst, 16, lane * 16u, k0 * 4, 0, 0);
+      }
+    }
+  };
+
+  // Wave tile: rows wr*64 + s*32 (s = 0, 1), columns wc*128 + t*32 (t = 0..3).
+  const int wr = wave & 3;
+  const int wc = wave >> 2;
+  // B (x^T) read: row wr*64 + s*32 + col, chunk 2*ks + half; row % 8 = col % 8.
+  int xoff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) xoff[ks] = (wr * 64 + col) * kXRowBytes + (((2 * ks + half) ^ (col & 7)) << 4);
+  // A (W^T) reads: in each 16-lane group, source lane a + 4j points at k row
+  // kb + j, columns cb + 4a .. +3, and lane i of the group receives k rows
+  // kb..kb+3 of column cb + i.  Lanes 0..31 take k rows 0..7 of the step (two
+  // reads: kb = 0 and 4), lanes 32..63 rows 8..15, matching the B operand.
+  const int grp = lane >> 4;
+  const int src_a = lane & 3;
+  const int src_j = (lane >> 2) & 3;
+  const int krow = (grp >> 1) * 8 + src_j;
+  const int ccol = (grp & 1) * 16 + src_a * 4;
+  int woff[2][4];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) woff[r][t] = wc * kWHalfBytes + w_off(krow + 4 * r, t * 32 + ccol);
+  }
+
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[t][s2][i] = 0.f;
+    }
+  }
+  float sumsq[2] = {0.f, 0.f};
+
+  auto compute = [&](const char *xt, const char *wt, const float *gt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      Frag8 b[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) b[s2].u = *reinterpret_cast<const uint4 *>(xt + xoff[ks] + s2 * 32 * kXRowBytes);
+      Frag8 af[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        af[t].s4[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t *)(wt + woff[0][t] + ks * 16 * kWRowBytes));
+        af[t].s4[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t *)(wt + woff[1][t] + ks * 16 * kWRowBytes));
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sumsq[s2] = dot2_bf16(b[s2].w[j], b[s2].w[j], sumsq[s2]);
+      }
+      if constexpr (kGain) {
+        const float4 g0 = *reinterpret_cast<const float4 *>(gt + ks * 16 + half * 8);
+        const float4 g1 = *reinterpret_cast<const float4 *>(gt + ks * 16 + half * 8 + 4);
+        const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          Frag8 hi, lo;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float x0 = __uint_as_float(b[s2].w[j] << 16) * g[2 * j];
+            const float x1 = __uint_as_float(b[s2].w[j] & 0xffff0000u) * g[2 * j + 1];
+            hi.w[j] = cvt_pk_bf16(x0, x1);
+            lo.w[j] = cvt_pk_bf16(x0 - __uint_as_float(hi.w[j] << 16), x1 - __uint_as_float(hi.w[j] & 0xffff0000u));
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            acc[t][s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t].v, hi.v, acc[t][s2], 0, 0, 0);
+            acc[t][s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t].v, lo.v, acc[t][s2], 0, 0, 0);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            acc[t][s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t].v, b[s2].v, acc[t][s2], 0, 0, 0);
+          }
+        }
+      }
+      // One k-step's operands in flight at a time (the accumulators take
+      // half the registers).
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // n_stages is even (d_model % 128 == 0), so the loop runs whole pairs and
+  // the accumulators never leave it from two places.
+  stage(lds_x0, lds_w0, lds_g0, 0);
+  for (int s = 0; s < n_stages; s += 2) {
+    // Stage s has landed for every wave and every wave is done with stage
+    // s-1, whose buffers the next loads overwrite.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    stage(lds_x1, lds_w1, lds_g1, s + 1);
+    compute(lds_x0, lds_w0, lds_g0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (s + 2 < n_stages) stage(lds_x0, lds_w0, lds_g0, s + 2);
+    compute(lds_x1, lds_w1, lds_g1);
+  }
+
+  // Epilogue: acc[t][s2] element i is output column
+  //   col0 + wc*128 + t*32 + (i/4)*8 + half*4 + (i%4)
+  // of input row row0 + wr*64 + s2*32 + col.
+  bf16_t *out = static_cast<bf16_t *>(a.out[p]);
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    const float ss = sumsq[s2] + shfl_xor_f(sumsq[s2], 32);
+    const int r = wr * 64 + s2 * 32 + col;
+    if (r >= rows_here) continue;
+    const float inv = 1.0f / sqrtf(ss / static_cast<float>(d) + a.eps);
+    bf16_t *orow = out + (a.dst_row_base + row0 + r) * a.ncols + col0 + wc * 128;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        uint2 v;
+        v.x = cvt_pk_bf16(acc[t][s2][i4 * 4 + 0] * inv, acc[t][s2][i4 * 4 + 1] * inv);
+        v.y = cvt_pk_bf16(acc[t][s2][i4 * 4 + 2] * inv, acc[t][s2][i4 * 4 + 3] * inv);
+        *reinterpret_cast<uint2 *>(orow + t * 32 + i4 * 8 + half * 4) = v;
+      }
+    }
+  }
+}
+
+bool project_mfma_applies(const ProjArgs &a, int x_dt, int w_dt, int o_dt) {
+  return x_dt == YOCO_DT_BF16 && w_dt == YOCO_DT_BF16 && o_dt == YOCO_DT_BF16 && !a.indexed && a.n > 0 &&
+         a.d % (2 * pm::kK) == 0 && a.ncols % pm::kCols == 0 &&
+         static_cast<int64_t>(a.d) * a.ncols * 2 < (int64_t(1) << 31) &&
+         static_cast<int64_t>(pm::kRows) * a.d * 2 < (int64_t(1) << 31);
+}
+
+hipError_t launch_project_mfma(const ProjArgs &a, hipStream_t s) {
+  const int64_t row_tiles = (a.n + pm::kRows - 1) / pm::kRows;
+  const int64_t col_tiles = static_cast<int64_t>(a.ncols / pm::kCols) * a.n_out;
+  const int64_t blocks = (row_tiles + pm::kXcds - 1) / pm::kXcds * pm::kXcds * col_tiles;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (a.gain != nullptr) {
+    hipLaunchKernelGGL(project_mfma_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(pm::kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(project_mfma_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(pm::kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace yoco
