@@ -20,10 +20,17 @@ MFMA) and reports its TFLOP/s, and times the fp64 CPU oracle on the host
 cores for the same decode step (``cpu_baseline``).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-prefill]
+                       [--no-prefill] [--prefill-reps R] [--cold-steps C]
+                       [--workload decode128k|ragged16|decode1m]
        python bench.py --copy-calibration   (a plain 512 MiB device copy, three
                        times: the known-size reference for scaling the
                        FETCH_SIZE / WRITE_SIZE hardware counters)
+
+The default workload is the 128K decode; ragged16 (16 sequences of 8192..131072
+rows) and decode1m (2^20 rows) run the same step and report the same fields.
+The cold figure repeats C steps with a 512 MiB copy before every decode launch,
+so no cache level holds any of the shared K^/V^; it is reported apart from
+``value``.
 """
 from __future__ import annotations
 
@@ -49,11 +56,14 @@ BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, AMD published
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", choices=sorted(WORKLOADS), default="decode128k")
+    p.add_argument("--cold-steps", type=int, default=3,
+                   help="extra steps with a 512 MiB copy before every decode launch (reported apart)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
-    p.add_argument("--prefill-reps", type=int, default=5)
+    p.add_argument("--prefill-reps", type=int, default=20)
     p.add_argument("--copy-calibration", action="store_true")
     return p.parse_args()
 
@@ -120,39 +130,81 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def bench_decode(args, torch, y, W):
-    cfg = W.DECODE_128K
-    n, hq, hkv, dh, layers = cfg["n_rows"], cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"], cfg["layers"]
-    d_model = 3072
-    log(f"generating decode workload N={n}")
-    case = W.make_decode(**cfg)
-    proj = W.make_project(n=args.warmup + args.steps, d_model=d_model, n_kv_heads=hkv, head_dim=dh, seed=1)
+WORKLOADS = {
+    # name: (generator, size dict, description)
+    "decode128k": ("make_decode", "DECODE_128K",
+                   "decode, shared cache N=131072, H_q=24, H_kv=8, d_h=128, bf16, batch 1, 13 cross layers, "
+                   "plus one appended row (d_model=3072)"),
+    "ragged16": ("make_ragged_decode", "RAGGED_16",
+                 "ragged decode, 16 sequences of 8192..131072 rows (sum 1,122,749), H_q=24, H_kv=8, "
+                 "d_h=128, bf16, 13 cross layers, plus one appended row per sequence (d_model=3072)"),
+    "decode1m": ("make_needle_decode", "NEEDLE_1M",
+                 "decode, shared cache N=1048576 with a planted needle per KV head, H_q=24, H_kv=8, "
+                 "d_h=128, bf16, batch 1, 13 cross layers, plus one appended row (d_model=3072)"),
+}
 
-    cache = y.KVCache(1, n, hkv, dh, torch.bfloat16)
-    cache.k[0] = to_dev(case.k[0], torch)
-    cache.v[0] = to_dev(case.v[0], torch)
-    q_layers = [to_dev(case.q[l], torch) for l in range(layers)]          # each [1, 24, 128]
-    m_rows = to_dev(proj.m, torch)                                        # [steps, 3072]
+
+def pct(xs, q):
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
+
+
+def bench_decode(args, torch, y, W):
+    gen, size_name, _ = WORKLOADS[args.workload]
+    cfg = getattr(W, size_name)
+    log(f"generating {args.workload} workload")
+    case = getattr(W, gen)(**cfg)
+    n_seq = len(case.lens)
+    lens = np.asarray(case.lens, dtype=np.int64)
+    hq, hkv, dh, layers = case.n_q_heads, case.n_kv_heads, case.head_dim, case.layers
+    cap = int(lens.max())
+    d_model = 3072
+    proj = W.make_project(n=(args.warmup + args.steps + args.cold_steps) * n_seq, d_model=d_model,
+                          n_kv_heads=hkv, head_dim=dh, seed=1)
+
+    cache = y.KVCache(n_seq, cap, hkv, dh, torch.bfloat16)
+    for b in range(n_seq):
+        cache.k[b, :lens[b]] = to_dev(case.k[b], torch)
+        cache.v[b, :lens[b]] = to_dev(case.v[b], torch)
+    q_layers = [to_dev(case.q[l], torch) for l in range(layers)]          # each [n_seq, 24, 128]
+    m_rows = to_dev(proj.m, torch)                                        # [steps * n_seq, 3072]
     w_k, w_v = to_dev(proj.w_k, torch), to_dev(proj.w_v, torch)
     gain = torch.ones(d_model, dtype=torch.float32, device="cuda")
     ws = y.decode_workspace(cache, hq)
-    outs = [torch.empty((1, hq, dh), dtype=torch.float32, device="cuda") for _ in range(layers)]
+    outs = [torch.empty((n_seq, hq, dh), dtype=torch.float32, device="cuda") for _ in range(layers)]
     stream = torch.cuda.current_stream()
+    # Cold variant: a 512 MiB copy between layer calls evicts every cache level
+    # (the MALL is 256 MB) before each decode launch.
+    flush_src = flush_dst = None
+    if args.cold_steps > 0:
+        flush_src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        flush_dst = torch.empty_like(flush_src)
     torch.cuda.synchronize()
 
     n_ev = layers * args.steps
     ev_start = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     ev_end = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    cold_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(layers * args.cold_steps)]
 
-    def step(i, record):
-        cache.len[0] = n - 1
-        y.kv_append(cache, m_rows[i:i + 1], w_k, w_v, gain, 1e-6, stream=stream)
+    def step(i, record, cold=None):
+        cache.len[:] = lens - 1
+        if record is not None:
+            step_ev[record][0].record(stream)
+        y.kv_append(cache, m_rows[i * n_seq:(i + 1) * n_seq], w_k, w_v, gain, 1e-6, stream=stream)
         for l in range(layers):
+            if cold is not None:
+                flush_dst.copy_(flush_src)
+                cold_ev[cold * layers + l][0].record(stream)
             if record is not None:
                 ev_start[record * layers + l].record(stream)
             y.cross_attn_decode(q_layers[l], cache, workspace=ws, out=outs[l], stream=stream)
             if record is not None:
                 ev_end[record * layers + l].record(stream)
+            if cold is not None:
+                cold_ev[cold * layers + l][1].record(stream)
+        if record is not None:
+            step_ev[record][1].record(stream)
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
@@ -165,20 +217,32 @@ def bench_decode(args, torch, y, W):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    kern_ms = [s.elapsed_time(e) for s, e in zip(ev_start, ev_end)]
+    kern_ms = [s_.elapsed_time(e_) for s_, e_ in zip(ev_start, ev_end)]
+    step_ms = [s_.elapsed_time(e_) for s_, e_ in step_ev]
     kern_avg_ms = float(np.mean(kern_ms))
-    bytes_per_launch = 2 * n * hkv * dh * 2            # K^ + V^ read once per layer call
+    bytes_per_launch = int(2 * lens.sum() * hkv * dh * 2)   # K^ + V^ read once per layer call
     achieved_gbps = bytes_per_launch / (kern_avg_ms * 1e-3) / 1e9
     us_per_token_layer = ms_per_step * 1e3 / layers
-    step_bytes = layers * bytes_per_launch + 2 * d_model * hkv * dh * 2
+    step_bytes = layers * bytes_per_launch + n_seq * 2 * d_model * hkv * dh * 2
     log(f"decode step {ms_per_step:.3f} ms; {us_per_token_layer:.2f} us/token/layer; "
         f"decode kernel avg {kern_avg_ms * 1e3:.2f} us -> {achieved_gbps:.0f} GB/s")
+    cold = None
+    if args.cold_steps > 0:
+        for i in range(args.cold_steps):
+            step(args.warmup + args.steps + i, None, cold=i)
+        torch.cuda.synchronize()
+        cold_ms = [s_.elapsed_time(e_) for s_, e_ in cold_ev]
+        cold = dict(avg_launch_us=float(np.mean(cold_ms)) * 1e3, p50_launch_us=pct(cold_ms, 50) * 1e3,
+                    GBps=bytes_per_launch / (float(np.mean(cold_ms)) * 1e-3) / 1e9, launches=len(cold_ms))
+        log(f"cold decode (512 MiB flush before each launch): avg {cold['avg_launch_us']:.2f} us "
+            f"-> {cold['GBps']:.0f} GB/s")
     return dict(case=case, cache=cache, q_layers=q_layers, outs=outs, ms_per_step=ms_per_step,
                 us_per_token_layer=us_per_token_layer, kern_avg_us=kern_avg_ms * 1e3,
-                kern_p10_us=float(np.percentile(kern_ms, 10)) * 1e3,
-                kern_p90_us=float(np.percentile(kern_ms, 90)) * 1e3,
+                kern_p10_us=pct(kern_ms, 10) * 1e3, kern_p50_us=pct(kern_ms, 50) * 1e3,
+                kern_p90_us=pct(kern_ms, 90) * 1e3,
+                step_p10_ms=pct(step_ms, 10), step_p50_ms=pct(step_ms, 50), step_p90_ms=pct(step_ms, 90),
                 achieved_gbps=achieved_gbps, bytes_per_launch=bytes_per_launch,
-                step_gbps=step_bytes / (ms_per_step * 1e-3) / 1e9)
+                step_gbps=step_bytes / (ms_per_step * 1e-3) / 1e9, cold=cold, n_seq=n_seq, lens=lens)
 
 
 def bench_prefill(args, torch, y, W):
@@ -206,8 +270,8 @@ def bench_prefill(args, torch, y, W):
     flops = 2.0 * dh * hq * n * (n + 1)                # causal QK^T and PV, diagonal included
     avg = float(np.mean(ms))
     tflops = flops / (avg * 1e-3) / 1e12
-    log(f"prefill {avg:.3f} ms -> {tflops:.1f} TFLOP/s")
-    return dict(ms=avg, ms_min=float(np.min(ms)), tflops=tflops, flops=flops,
+    log(f"prefill {avg:.3f} ms (p50 {pct(ms, 50):.3f}) -> {tflops:.1f} TFLOP/s")
+    return dict(ms=avg, ms_p10=pct(ms, 10), ms_p50=pct(ms, 50), ms_p90=pct(ms, 90), tflops=tflops, flops=flops,
                 frac=tflops / BF16_DENSE_PEAK_TFLOPS)
 
 
@@ -244,16 +308,17 @@ def bench_project(args, torch, y, W):
 def cpu_baseline(dec, W):
     import oracle
     case = dec["case"]
-    n = int(case.lens[0])
     threads = oracle.num_threads()
-    log(f"cpu baseline: fp64 oracle decode, 13 layers x 24 heads over {n} rows, {threads} threads")
+    rows = int(np.sum(case.lens))
+    log(f"cpu baseline: fp64 oracle decode, 13 layers x 24 heads over {rows} rows, {threads} threads")
     t0 = time.perf_counter()
-    oracle.decode(case.q[:, 0], n, case.k[0], case.v[0], case.softmax_scale)
+    for b, n in enumerate(case.lens):
+        oracle.decode(case.q[:, b], int(n), case.k[b], case.v[b], case.softmax_scale)
     dt = time.perf_counter() - t0
     return {"value": dt * 1e6 / case.layers, "unit": "us/token/layer", "cores": threads,
             "kind": "oracle",
-            "sample": f"one full decode step: 13 layers x 24 query heads over all {n} cache rows "
-                      f"(fp64, {dt:.2f} s wall)"}
+            "sample": f"one full decode step: 13 layers x 24 query heads over all {rows} cache rows of "
+                      f"{len(case.lens)} sequence(s) (fp64, {dt:.2f} s wall)"}
 
 
 def main():
@@ -276,12 +341,16 @@ def main():
     pre = None if args.no_prefill else bench_prefill(args, torch, y, W)
     proj = None if args.no_prefill else bench_project(args, torch, y, W)
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec, W)
-    traffic, why = counter_traffic()
+    # The committed counters were taken on the 128K workload.
+    traffic, why = counter_traffic() if args.workload == "decode128k" else (None, "counters cover decode128k only")
     if why:
         log(f"roofline.traffic is null: {why}")
+    metric = "cross-attn decode us/token/layer at N=128K (shared bf16 K^/V^, 13 layers)"
+    if args.workload != "decode128k":
+        metric = f"cross-attn decode us/token/layer, {args.workload} (shared bf16 K^/V^, 13 layers)"
 
     result = {
-        "metric": "cross-attn decode us/token/layer at N=128K (shared bf16 K^/V^, 13 layers)",
+        "metric": metric,
         "value": round(dec["us_per_token_layer"], 3),
         "unit": "us/token/layer",
         "n_gpus": 1,
@@ -294,11 +363,12 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1), no weights)",
         "config": {
-            "workload": "decode, shared cache N=131072, H_q=24, H_kv=8, d_h=128, bf16, batch 1, "
-                        "13 cross layers, plus one appended row (d_model=3072)",
-            "n_rows": 131072, "layers": 13, "n_q_heads": 24, "n_kv_heads": 8, "head_dim": 128,
-            "d_model": 3072, "batch": 1,
+            "workload": WORKLOADS[args.workload][2],
+            "n_rows": int(dec["lens"].sum()), "layers": 13, "n_q_heads": 24, "n_kv_heads": 8, "head_dim": 128,
+            "d_model": 3072, "batch": dec["n_seq"],
         },
+        "step_ms_p10_p50_p90": [round(dec["step_p10_ms"], 4), round(dec["step_p50_ms"], 4),
+                                round(dec["step_p90_ms"], 4)],
         "decode_hbm_GBps": round(dec["achieved_gbps"], 1),
         "step_GBps": round(dec["step_gbps"], 1),
         "roofline": {
@@ -313,15 +383,22 @@ def main():
             "traffic_over_algorithmic": None if traffic is None else round(traffic / dec["bytes_per_launch"], 4),
             "avg_launch_us": round(dec["kern_avg_us"], 2),
             "p10_launch_us": round(dec["kern_p10_us"], 2),
+            "p50_launch_us": round(dec["kern_p50_us"], 2),
             "p90_launch_us": round(dec["kern_p90_us"], 2),
             "bytes_per_launch": dec["bytes_per_launch"],
         },
+        "decode_cold": None if dec["cold"] is None else {
+            "what": "a 512 MiB device copy before every decode launch (evicts L2 and the 256 MB MALL)",
+            "avg_launch_us": round(dec["cold"]["avg_launch_us"], 2),
+            "p50_launch_us": round(dec["cold"]["p50_launch_us"], 2),
+            "GBps": round(dec["cold"]["GBps"], 1), "launches": dec["cold"]["launches"]},
         "cpu_baseline": cpu,
     }
     if pre is not None:
         result["prefill"] = {
             "workload": "causal prefill N=32768, H_q=24, H_kv=8, d_h=128, bf16 MFMA, fp32 out",
             "ms": round(pre["ms"], 3), "tflops": round(pre["tflops"], 1),
+            "ms_p10_p50_p90": [round(pre["ms_p10"], 3), round(pre["ms_p50"], 3), round(pre["ms_p90"], 3)],
             "roofline": {"bound": "mfma", "achieved": round(pre["tflops"], 1),
                          "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(pre["frac"], 4), "flops_per_launch": pre["flops"]},
