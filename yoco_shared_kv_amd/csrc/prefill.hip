@@ -70,7 +70,7 @@ constexpr int kBlockRows = kWaves * kRowsPerWave;  // 256 query rows
 constexpr int kKeyTile = 64;
 constexpr int kThreads = kWaves * 64;
 constexpr int kXcds = 8;
-constexpr float kOverflowLog2 = 64.0f;  // probabilities stay below 2^64 before a recompute
+constexpr float kSumLimit = 1.152921504606846976e18f;  // 2^60: a row sum at or above it is recomputed
 }  // namespace pf
 
 union Frag8 {
@@ -270,13 +270,14 @@ __global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const Pre
   float l_run;  // this lane's share of sum(p), from the bf16 p the MFMA uses
   // Reference maximum (log2 units) of this lane's query row.  It is fixed
   // from the row's first 32 keys, so O never needs rescaling: later
-  // probabilities may exceed 1, and a half whose maximum passes the
-  // reference by more than kOverflowLog2 marks the row as overflowed, which
-  // makes the workgroup run a second pass where that row's reference is its
-  // largest maximum (then every probability of the row is <= 1).
+  // probabilities may exceed 1.  A row whose probabilities sum to 2^60 or
+  // more (or to inf/NaN) may have lost range, which makes the workgroup run
+  // a pass that finds each row's largest maximum and then a final pass in
+  // which that row's reference is its largest maximum (every probability of
+  // the row is then <= 1); the other rows repeat their arithmetic.
   float m_ref = -INFINITY;
-  float m_seen = -INFINITY;  // largest half maximum seen by this row
-  bool ovf = false;          // this lane saw a half past m_ref + kOverflowLog2
+  float m_seen = -INFINITY;  // largest half maximum of this row (generic steps)
+  bool row_ovf = false;      // this row's sum reached the limit in the first pass
   const uint32_t kOnesBf16x2 = 0x3F803F80u;  // (1.0, 1.0) in bf16
   __shared__ int redo_flag;
   if (tid == 0) redo_flag = 0;  // ordered before any update by the first barrier below
@@ -336,10 +337,13 @@ __global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const Pre
     constexpr bool kGeneric = decltype(generic_c)::value;
     constexpr int NPV = 2 * S::DSUB;
     constexpr int NM = NPV + S::KSTEPS;
-    // Softmax pieces: the row maximum (4 pieces of 4 elements), its
-    // cross-lane exchange, the probabilities (8 pieces of one packed pair)
-    // and the running sum of P(u-1) (2 pieces).
-    constexpr int kMax0 = 0, kXchg = 4, kP0 = 5, kL0 = 13, kPieces = 15;
+    // Softmax pieces: (generic only) the row maximum (4 pieces of 4
+    // elements) and its cross-lane exchange, then the probabilities (8
+    // pieces of one packed pair) and the running sum of P(u-1) (2 pieces).
+    // The fast form needs no maximum: the reference is fixed, and range is
+    // checked once, from the row sum, at the end of the pass.
+    constexpr int kMax0 = 0, kXchg = kGeneric ? 4 : -1;
+    constexpr int kP0 = kGeneric ? 5 : 0, kL0 = kP0 + 8, kPieces = kL0 + 2;
     const bool do_pv = !kGeneric || (u >= 1 && u - 1 < n_half);
     const bool do_soft = !kGeneric || (u >= 0 && u < n_half);
     if constexpr (kGeneric) {
@@ -362,16 +366,14 @@ __global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const Pre
     float tmax_other = 0.f;
     float l_add = 0.f;
     auto piece = [&](int i) __attribute__((always_inline)) {
-      if (i >= kMax0 && i < kMax0 + 4) {
+      if (kGeneric && i >= kMax0 && i < kMax0 + 4) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, s_cur[(i - kMax0) * 4 + e]);
-      } else if (i == kXchg) {
+      } else if (kGeneric && i == kXchg) {
         tmax_other = shfl_xor_f(tmax, 32);
-        if constexpr (kGeneric) {
-          // The row's first half (key 0 is always visible) sets the reference.
-          const float t = fmaxf(tmax, tmax_other) * a.scale_log2;
-          m_ref = (do_soft && m_ref == -INFINITY) ? t : m_ref;
-        }
+        // The row's first half (key 0 is always visible) sets the reference.
+        const float t = fmaxf(tmax, tmax_other) * a.scale_log2;
+        m_ref = (do_soft && m_ref == -INFINITY) ? t : m_ref;
       } else if (i >= kP0 && i < kP0 + 8) {
         make_p_pair(s_cur, p_cur, (i - kP0) >> 2, (i - kP0) & 3);
       } else if (i >= kL0 && i < kL0 + 2) {
@@ -398,19 +400,16 @@ __global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const Pre
     }
 #pragma unroll
     for (int i = NM; i < kPieces; ++i) piece(i);  // head_dim 64: fewer MFMAs than pieces
-    const float t = fmaxf(tmax, tmax_other) * a.scale_log2;
     if constexpr (kGeneric) {
+      const float t = fmaxf(tmax, tmax_other) * a.scale_log2;
       l_run += do_pv ? l_add : 0.f;
       m_seen = do_soft ? fmaxf(m_seen, t) : m_seen;
-      ovf = ovf || (do_soft && t > m_ref + pf::kOverflowLog2);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         if (!do_soft) p_cur[kk].u = make_uint4(0, 0, 0, 0);
       }
     } else {
       l_run += l_add;
-      m_seen = fmaxf(m_seen, t);
-      ovf = ovf || t > m_ref + pf::kOverflowLog2;
     }
   };
 
@@ -475,22 +474,32 @@ __global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const Pre
     if (pass > 0) stage_tile<DH, SWZ>(lds_k0, kg, row_stride_kv, 0, kv_len, wave, so);
     period_generic(0);
     int p = 1;
-    for (; p < p_pair_end; p += 2) {
+    // The maximum-finding pass runs every period in the generic form.
+    const int p_fast = pass == 1 ? 1 : p_pair_end;
+    for (; p < p_fast; p += 2) {
       period_fast(std::integral_constant<int, 1>(), p);
       period_fast(std::integral_constant<int, 0>(), p + 1);
     }
     for (; p <= n_ktiles; ++p) period_generic(p);
-    if (pass > 0) break;
-    if (__any(ovf) && lane == 0) redo_flag = 1;
-    __syncthreads();
-    if (redo_flag == 0) break;
-    // Some row of the workgroup overflowed: the workgroup runs again, and
-    // each row that overflowed takes its largest maximum as the reference
-    // (so now every probability is <= 1).  The other rows keep theirs and
-    // repeat the same arithmetic, so a row's result never depends on the
-    // other rows of its workgroup.  The barrier above also retires every
-    // read of the LDS tiles the restart overwrites.
-    m_ref = ovf ? m_seen : m_ref;
+    if (pass == 2) break;
+    if (pass == 0) {
+      // Range check: every probability of a row is below its sum.
+      const float l_sum = l_run + shfl_xor_f(l_run, 32);
+      row_ovf = !(l_sum < pf::kSumLimit);
+      if (__any(row_ovf) && lane == 0) redo_flag = 1;
+      __syncthreads();
+      if (redo_flag == 0) break;
+      m_seen = -INFINITY;
+    } else {
+      // Each row that overflowed takes its largest maximum as the reference
+      // for the final pass; the other rows keep theirs and repeat the same
+      // arithmetic, so a row's result never depends on the other rows of its
+      // workgroup.
+      m_ref = row_ovf ? m_seen : m_ref;
+      __syncthreads();
+    }
+    // The barrier above also retires every read of the LDS tiles the next
+    // pass overwrites.
   }
 
   const float l_tot = l_run + shfl_xor_f(l_run, 32);
