@@ -14,6 +14,8 @@ query rows and heads).  This module only marshals numpy arrays to it:
 * ``attention``   -- causal GQA softmax attention of one query block over one
                      shared K/V slab (Eq. 3; the blog's section 2 formula).
 * ``prefill`` / ``decode`` -- position bookkeeping around ``attention``.
+* ``rope``        -- rotary position embedding of K^ / Q^ heads (the blog's
+                     section 7: K^ and each layer's Q are rotated, V is not).
 
 Inputs are the stored values: float32 arrays, or bf16 kept as ``uint16`` bits.
 """
@@ -60,6 +62,14 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
+def _as_f64(a: np.ndarray) -> np.ndarray:
+    """Stored values (float32, or bf16 bits as uint16) widened exactly."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
 class Oracle:
     """Marshalling around one compiled copy of ``oracle.c``."""
 
@@ -75,6 +85,7 @@ class Oracle:
         lib.oracle_attention.argtypes = [vp, i32, i64, vp, i32, vp, vp, i32, i64, i32, i32,
                                          dbl, vp, vp]
         lib.oracle_attention.restype = i32
+        lib.oracle_rope.argtypes = [vp, i64, i32, i32, vp, dbl, i32]
         self.lib = lib
         self.path = path
 
@@ -119,6 +130,21 @@ class Oracle:
         if rc != 0:
             raise MemoryError("oracle_project could not allocate scratch")
         return out
+
+    def rope(self, x: np.ndarray, pos, theta: float, head_dim: int, interleaved: bool = True) -> np.ndarray:
+        """Rotary position embedding of every head: x [n, H*d_h] or
+        [n, H, d_h] (fp64 or stored values), row r at absolute position
+        pos[r].  Returns an fp64 copy of the same shape."""
+        shape = np.shape(x)
+        n = shape[0]
+        xd = np.array(x if np.asarray(x).dtype == np.float64 else _as_f64(x), dtype=np.float64).reshape(n, -1)
+        if xd.shape[1] % head_dim or head_dim % 2:
+            raise ValueError("row width must be a multiple of an even head_dim")
+        heads = xd.shape[1] // head_dim
+        pos = np.ascontiguousarray(np.broadcast_to(np.asarray(pos, dtype=np.int64), (n,)))
+        xd = np.ascontiguousarray(xd)
+        self.lib.oracle_rope(_ptr(xd), n, heads, head_dim, _ptr(pos), float(theta), 1 if interleaved else 0)
+        return xd.reshape(shape)
 
     def attention(self, q: np.ndarray, pos, k: np.ndarray, v: np.ndarray, scale: float,
                   want_lse: bool = False):
@@ -196,6 +222,10 @@ def matmul(y, w):
 
 def project(x, w, gain=None, eps: float = 1e-6):
     return default().project(x, w, gain, eps)
+
+
+def rope(x, pos, theta, head_dim, interleaved=True):
+    return default().rope(x, pos, theta, head_dim, interleaved)
 
 
 def attention(q, pos, k, v, scale, want_lse: bool = False):

@@ -129,6 +129,44 @@ int oracle_project(const void *x, int x_dtype, int64_t n, int64_t d,
   return 0;
 }
 
+/* Rotary position embedding (RoPE) of every head of every row, in place.
+ *
+ * [Blog] s.7: the shared projection rotates K^ by position and each cross
+ * layer rotates its own Q likewise; V is not rotated.  [Notes] s.4.3,
+ * Table 7: the base theta of each training stage (640K for 64K tokens, 5M
+ * for 256K, 80M for 1M).
+ *
+ * Readings where the pages are silent: pair i (0 <= i < dh/2) of a head
+ * turns by the angle pos * theta^(-2i/dh).  interleaved = 1: the pair is
+ * elements (2i, 2i+1), read as the complex number x_2i + j*x_2i+1 times
+ * exp(j*angle) -- the complex notation Theta_n = exp(i*n*theta) the pages use
+ * for the retention of the self-decoder; interleaved = 0: the pair is
+ * (i, i + dh/2).
+ *
+ * x: [n][heads][dh] double, rotated in place; pos: [n] absolute positions.
+ */
+void oracle_rope(double *x, int64_t n, int heads, int dh, const int64_t *pos,
+                 double theta, int interleaved) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r) {
+    for (int h = 0; h < heads; ++h) {
+      double *xh = x + (r * heads + h) * dh;
+      for (int i = 0; i < dh / 2; ++i) {
+        const double freq = pow(theta, -2.0 * (double)i / (double)dh);
+        const double angle = (double)pos[r] * freq;
+        const double c = cos(angle);
+        const double s = sin(angle);
+        const int j0 = interleaved ? 2 * i : i;
+        const int j1 = interleaved ? 2 * i + 1 : i + dh / 2;
+        const double a = xh[j0];
+        const double b = xh[j1];
+        xh[j0] = a * c - b * s;
+        xh[j1] = a * s + b * c;
+      }
+    }
+  }
+}
+
 /* Causal GQA softmax attention over one shared K/V slab.
  *
  * [Notes] s.2.1, Eq. 3: Attention(Q^l, K^, V^) with a causal mask -- the

@@ -334,6 +334,98 @@ def pin_decode_is_last_prefill_row(orc):
         raise AssertionError("decode must equal the last prefill row")
 
 
+# ---------------------------------------------------------------------------
+# Rotary position embedding (the blog's section 7: K^ and each layer's Q are
+# rotated by position, V is not; base theta per stage from the notes' Table 7)
+# ---------------------------------------------------------------------------
+def pin_rope_position_zero_is_identity(orc):
+    """At position 0 every angle is 0: the rotation leaves x unchanged."""
+    x = _rng(20).standard_normal((2, 3, 16))
+    for inter in (True, False):
+        if not np.array_equal(orc.rope(x, [0, 0], 1e4, 16, inter), x):
+            raise AssertionError("RoPE at position 0 must be the identity")
+
+
+def pin_rope_single_pair_closed_form(orc):
+    """One pair (d_h = 2, frequency theta^0 = 1): (1, 0) at position p turns
+    to (cos p, sin p) and (0, 1) to (-sin p, cos p)."""
+    pos = np.array([1, 2, 7, 100], dtype=np.int64)
+    e0 = np.tile(np.array([[1.0, 0.0]]), (4, 1))
+    e1 = np.tile(np.array([[0.0, 1.0]]), (4, 1))
+    r0 = orc.rope(e0, pos, 640e3, 2)
+    r1 = orc.rope(e1, pos, 640e3, 2)
+    _close(r0, np.stack([np.cos(pos), np.sin(pos)], 1), 0, 1e-15, "RoPE of (1, 0)")
+    _close(r1, np.stack([-np.sin(pos), np.cos(pos)], 1), 0, 1e-15, "RoPE of (0, 1)")
+
+
+def _torch_rope_interleaved(x, pos, theta, dh):
+    """Complex multiplication in torch: consecutive pairs as complex numbers
+    times exp(j * pos * theta^(-2i/d_h))."""
+    xt = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))
+    n, h, _ = xt.shape
+    z = torch.view_as_complex(xt.reshape(n, h, dh // 2, 2))
+    freq = torch.tensor(theta, dtype=torch.float64) ** (-torch.arange(0, dh, 2, dtype=torch.float64) / dh)
+    ang = torch.from_numpy(np.asarray(pos, dtype=np.float64))[:, None] * freq[None, :]
+    rot = torch.polar(torch.ones_like(ang), ang)[:, None, :]
+    return torch.view_as_real(z * rot).reshape(n, h, dh).numpy()
+
+
+def pin_rope_library_complex(orc):
+    """Against torch complex arithmetic, including positions near 2^20 with
+    the 1M-stage base (80M), where a single-precision angle would be off."""
+    rng = _rng(21)
+    for theta, pos in ((640e3, [0, 1, 5, 4096]), (80e6, [1 << 20, (1 << 20) - 1, 999_983, 3])):
+        x = rng.standard_normal((4, 3, 64))
+        _close(orc.rope(x, pos, theta, 64), _torch_rope_interleaved(x, pos, theta, 64), 1e-12, 1e-12,
+               f"RoPE vs torch complex (theta {theta:g})")
+
+
+def pin_rope_preserves_norms(orc):
+    """A rotation keeps the length of every pair (so of every head)."""
+    x = _rng(22).standard_normal((5, 2, 32))
+    pos = [3, 17, 4095, 65536, 131071]
+    for inter in (True, False):
+        y = orc.rope(x, pos, 5e6, 32, inter)
+        _close(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), 1e-14, 0, "RoPE norm")
+
+
+def pin_rope_composition(orc):
+    """Turning by a then by b is turning by a + b."""
+    x = _rng(23).standard_normal((3, 2, 16))
+    a = np.array([5, 1000, 77], dtype=np.int64)
+    b = np.array([9, 31, 65536], dtype=np.int64)
+    for inter in (True, False):
+        two = orc.rope(orc.rope(x, a, 640e3, 16, inter), b, 640e3, 16, inter)
+        _close(two, orc.rope(x, a + b, 640e3, 16, inter), 1e-11, 1e-11, "RoPE composition")
+
+
+def pin_rope_scores_depend_on_offset(orc):
+    """<R(m) q, R(n) k> depends only on m - n: shifting both positions leaves
+    the score unchanged (what lets attention read relative position)."""
+    rng = _rng(24)
+    q = rng.standard_normal((1, 1, 64))
+    k = rng.standard_normal((1, 1, 64))
+    base = np.sum(orc.rope(q, [100], 5e6, 64) * orc.rope(k, [37], 5e6, 64))
+    for shift in (1, 1000, 500_000):
+        s = np.sum(orc.rope(q, [100 + shift], 5e6, 64) * orc.rope(k, [37 + shift], 5e6, 64))
+        _close(s, base, 1e-9, 1e-9, f"RoPE score after shift {shift}")
+    moved = np.sum(orc.rope(q, [101], 5e6, 64) * orc.rope(k, [37], 5e6, 64))
+    if abs(moved - base) < 1e-6:
+        raise AssertionError("the score must change with the offset")
+
+
+def pin_rope_half_is_permuted_interleaved(orc):
+    """Pairs (i, i + d_h/2) are pairs (2i, 2i+1) after the permutation that
+    interleaves the two halves of a head."""
+    x = _rng(25).standard_normal((2, 2, 16))
+    perm = np.empty(16, dtype=np.int64)
+    perm[0::2] = np.arange(8)
+    perm[1::2] = np.arange(8) + 8          # interleaved slot 2i <- i, 2i+1 <- i+8
+    half = orc.rope(x, [11, 5000], 1e4, 16, interleaved=False)
+    inter = orc.rope(x[..., perm], [11, 5000], 1e4, 16, interleaved=True)
+    _close(half[..., perm], inter, 1e-14, 1e-14, "rotate-half vs interleaved")
+
+
 ALL_PINS = [
     pin_rmsnorm_constant_row,
     pin_rmsnorm_one_hot,
@@ -353,4 +445,11 @@ ALL_PINS = [
     pin_attn_row_permutation,
     pin_attn_library,
     pin_decode_is_last_prefill_row,
+    pin_rope_position_zero_is_identity,
+    pin_rope_single_pair_closed_form,
+    pin_rope_library_complex,
+    pin_rope_preserves_norms,
+    pin_rope_composition,
+    pin_rope_scores_depend_on_offset,
+    pin_rope_half_is_permuted_interleaved,
 ]

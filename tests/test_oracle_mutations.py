@@ -31,6 +31,10 @@ MUTATIONS = {
                   "acc[e] += logits[j] * read_elem(k, kv_dtype, v_base + e);"),
     "dot_skips_last_element": ("for (int e = 0; e < dh; ++e) {\n          dot +=",
                                "for (int e = 0; e < dh - 1; ++e) {\n          dot +="),
+    "rope_sin_sign": ("xh[j0] = a * c - b * s;", "xh[j0] = a * c + b * s;"),
+    "rope_frequency_exponent": ("pow(theta, -2.0 * (double)i / (double)dh)", "pow(theta, -1.0 * (double)i / (double)dh)"),
+    "rope_position_off_by_one": ("(double)pos[r] * freq", "(double)(pos[r] + 1) * freq"),
+    "rope_pairing_swapped": ("const int j0 = interleaved ? 2 * i : i;", "const int j0 = interleaved ? i : 2 * i;"),
 }
 
 
