@@ -277,7 +277,8 @@ def bench_prefill(args, torch, y, W):
 
 def bench_project(args, torch, y, W):
     """K^/V^ projection of a 32768-row prompt at 3B-like widths (3072 -> 2 x
-    1024, bf16, matrix cores), with unit gain and with an fp32 gain."""
+    1024, bf16, matrix cores), with unit gain, with an fp32 gain, and with an
+    fp32 gain plus RoPE on K^."""
     cfg = W.PROJECT_3B
     log(f"generating projection workload N={cfg['n']}")
     pc = W.make_project(**cfg, unit_gain=False)
@@ -288,14 +289,15 @@ def bench_project(args, torch, y, W):
     stream = torch.cuda.current_stream()
     flops = 2.0 * n * d * 2 * pc.n_kv_heads * pc.head_dim
     res = {}
-    for name, g in (("unit_gain", None), ("fp32_gain", gain)):
-        y.kv_project(cache, m, w_k, w_v, g, pc.eps, stream=stream)
+    # rope: K^ rotated at its row positions in the epilogue (base 640K)
+    for name, g, theta in (("unit_gain", None, None), ("fp32_gain", gain, None), ("fp32_gain_rope", gain, 640e3)):
+        y.kv_project(cache, m, w_k, w_v, g, pc.eps, stream=stream, rope_theta=theta)
         torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.prefill_reps)]
         for s_ev, e_ev in evs:
             s_ev.record(stream)
-            y.kv_project(cache, m, w_k, w_v, g, pc.eps, stream=stream)
+            y.kv_project(cache, m, w_k, w_v, g, pc.eps, stream=stream, rope_theta=theta)
             e_ev.record(stream)
         torch.cuda.synchronize()
         ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
@@ -447,6 +449,7 @@ def main():
                         "RMSNorm fused, written into the cache",
             "ms": round(u["ms"], 4), "tflops": round(u["tflops"], 1),
             "ms_fp32_gain": round(proj["fp32_gain"]["ms"], 4),
+            "ms_fp32_gain_rope": round(proj["fp32_gain_rope"]["ms"], 4),
             "roofline": {"bound": "mfma", "achieved": round(u["tflops"], 1), "peak": BF16_DENSE_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(u["tflops"] / BF16_DENSE_PEAK_TFLOPS, 4),
                          "flops_per_launch": proj["flops"]},

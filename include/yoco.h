@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define YOCO_ABI_VERSION 1
+#define YOCO_ABI_VERSION 2
 #define YOCO_MAX_SEQ 256
 
 /* Storage types. */
@@ -151,6 +151,48 @@ yoco_status yoco_q_project(const void *x, int32_t x_dtype, int64_t n, int32_t d_
                            const float *gain, float eps, const void *w_q, int32_t w_dtype,
                            int32_t n_q_heads, int32_t head_dim, void *q_out, int32_t q_dtype,
                            void *stream);
+
+/* Rotary position embedding on the projections ([Blog] "NeurIPS'24 | YOCO:
+ * 长上下文 LLM 为什么不必每层都存一份 KV Cache?" section 7: the shared projection
+ * rotates K^ by position and each cross layer rotates its own Q; V is not
+ * rotated.  [Notes] section 4.3, Table 7: the base theta of each training
+ * stage -- 640K for 64K tokens, 5M for 256K, 80M for 1M).
+ *
+ * Pair i (0 <= i < head_dim/2) of every head, elements (2i, 2i+1), turns by
+ * pos * rope_theta^(-2i/head_dim) radians:
+ *   x'_2i = x_2i cos - x_2i+1 sin,   x'_2i+1 = x_2i sin + x_2i+1 cos.
+ * (The pages do not fix which elements pair up; a model trained with the
+ * pairs (i, i + head_dim/2) uses these calls after the same permutation of
+ * the columns of its W_K and W_Q, which leaves every score unchanged.)
+ * The angle is formed in double precision and reduced mod 2*pi there, sine
+ * and cosine are taken in single precision, and the rotation is applied to
+ * the fp32 projection before its one rounding to the output type.
+ * rope_theta must be finite and > 1, else BAD_VALUE; everything else is as
+ * in the call without _rope. */
+
+/* yoco_kv_project with K^ row row_start + r rotated at position
+ * row_start + r (its cache row); V^ is not rotated. */
+yoco_status yoco_kv_project_rope(const void *m, int32_t m_dtype, int64_t n, int32_t d_model,
+                                 const float *gain, float eps, const void *w_k, const void *w_v,
+                                 int32_t w_dtype, yoco_kv_cache *cache, int32_t seq,
+                                 int64_t row_start, double rope_theta, void *stream);
+
+/* yoco_kv_append with the new K^ row of sequence b rotated at position
+ * len_host[b] (its cache row). */
+yoco_status yoco_kv_append_rope(const void *m_new, int32_t m_dtype, int32_t d_model,
+                                const float *gain, float eps, const void *w_k, const void *w_v,
+                                int32_t w_dtype, yoco_kv_cache *cache, double rope_theta,
+                                void *stream);
+
+/* yoco_q_project with query row r rotated at position pos_host[r] (a HOST
+ * array of n >= 0 positions, n <= YOCO_MAX_SEQ, else BAD_SHAPE; decode: the
+ * query of sequence b sits at len_host[b] - 1) or, when pos_host is NULL, at
+ * pos0 + r (prefill: pos0 = q_start).  A negative position is OUT_OF_RANGE. */
+yoco_status yoco_q_project_rope(const void *x, int32_t x_dtype, int64_t n, int32_t d_model,
+                                const float *gain, float eps, const void *w_q, int32_t w_dtype,
+                                int32_t n_q_heads, int32_t head_dim, void *q_out,
+                                int32_t q_dtype, const int64_t *pos_host, int64_t pos0,
+                                double rope_theta, void *stream);
 
 /* Causal cross-attention over the shared cache for a block of query rows
  * (prefill / training forward: [Notes] Eq. 3 with the causal mask; [Blog]

@@ -27,7 +27,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = _lib()
     names = _declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 12, names
     for name in names:
         assert hasattr(lib, name), f"{name} declared in yoco.h but not exported"
 
@@ -222,3 +222,23 @@ def test_python_binding_refuses_host_tensors():
     import yoco_shared_kv_amd as y
     with pytest.raises(ValueError):
         y.q_project(torch.zeros(2, 32), torch.zeros(32, 256), 4, 64)
+
+
+def test_rope_entry_points_reject_bad_theta_and_positions():
+    L = _lib()
+    c, lens = _cache()
+    for theta in (0.0, 1.0, 0.5, float("inf"), float("nan")):
+        st = L.yoco_kv_project_rope(FAKE, 1, 4, 32, None, 1e-6, FAKE, FAKE, 1, ctypes.byref(c), 0, 0, theta, None)
+        assert st == _status("YOCO_ERR_BAD_VALUE"), theta
+        st = L.yoco_kv_append_rope(FAKE, 1, 32, None, 1e-6, FAKE, FAKE, 1, ctypes.byref(c), theta, None)
+        assert st == _status("YOCO_ERR_BAD_VALUE"), theta
+    assert lens.tolist() == [10, 20]
+    pos = (ctypes.c_int64 * 3)(5, -1, 7)
+    assert L.yoco_q_project_rope(FAKE, 1, 3, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 1, pos, 0, 1e4, None) == \
+        _status("YOCO_ERR_OUT_OF_RANGE")
+    assert L.yoco_q_project_rope(FAKE, 1, 3, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 1, None, -2, 1e4, None) == \
+        _status("YOCO_ERR_OUT_OF_RANGE")
+    big = (ctypes.c_int64 * 257)()
+    assert L.yoco_q_project_rope(FAKE, 1, 257, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 1, big, 0, 1e4, None) == \
+        _status("YOCO_ERR_BAD_SHAPE")
+    assert L.yoco_q_project_rope(FAKE, 1, 0, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 1, None, 0, 1e4, None) == 0

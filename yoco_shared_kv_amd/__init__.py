@@ -113,39 +113,60 @@ def kv_cache_bytes(n_seq: int, capacity: int, n_kv_heads: int, head_dim: int,
 
 def kv_project(cache: KVCache, m: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor,
                gain: Optional[torch.Tensor] = None, eps: float = 1e-6, seq: int = 0,
-               row_start: int = 0, stream=None) -> None:
-    """RMSNorm(M) W_K and RMSNorm(M) W_V into cache rows [row_start, row_start+n)."""
+               row_start: int = 0, stream=None, rope_theta: Optional[float] = None) -> None:
+    """RMSNorm(M) W_K and RMSNorm(M) W_V into cache rows [row_start, row_start+n);
+    with ``rope_theta``, K^ row r is rotated at position row_start + r."""
     _on_device(m, w_k, w_v, gain)
     if w_k.dtype != w_v.dtype:
         raise TypeError("w_k and w_v must share a dtype")
     n, d = m.shape
     s = cache.struct()
-    check(lib().yoco_kv_project(_ptr(m), _dt(m), n, d, _ptr(gain), eps, _ptr(w_k), _ptr(w_v),
-                                _dt(w_k), ctypes.byref(s), seq, row_start, _stream(stream)))
+    args = (_ptr(m), _dt(m), n, d, _ptr(gain), eps, _ptr(w_k), _ptr(w_v), _dt(w_k), ctypes.byref(s), seq, row_start)
+    if rope_theta is None:
+        check(lib().yoco_kv_project(*args, _stream(stream)))
+    else:
+        check(lib().yoco_kv_project_rope(*args, float(rope_theta), _stream(stream)))
 
 
 def kv_append(cache: KVCache, m_new: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor,
-              gain: Optional[torch.Tensor] = None, eps: float = 1e-6, stream=None) -> None:
-    """Project one new row per sequence (m_new ``[n_seq, d_model]``) and append it."""
+              gain: Optional[torch.Tensor] = None, eps: float = 1e-6, stream=None,
+              rope_theta: Optional[float] = None) -> None:
+    """Project one new row per sequence (m_new ``[n_seq, d_model]``) and append it;
+    with ``rope_theta``, the new K^ row of sequence b is rotated at position len[b]."""
     _on_device(m_new, w_k, w_v, gain)
     if w_k.dtype != w_v.dtype:
         raise TypeError("w_k and w_v must share a dtype")
     s = cache.struct()
-    check(lib().yoco_kv_append(_ptr(m_new), _dt(m_new), m_new.shape[1], _ptr(gain), eps,
-                               _ptr(w_k), _ptr(w_v), _dt(w_k), ctypes.byref(s), _stream(stream)))
+    args = (_ptr(m_new), _dt(m_new), m_new.shape[1], _ptr(gain), eps, _ptr(w_k), _ptr(w_v), _dt(w_k),
+            ctypes.byref(s))
+    if rope_theta is None:
+        check(lib().yoco_kv_append(*args, _stream(stream)))
+    else:
+        check(lib().yoco_kv_append_rope(*args, float(rope_theta), _stream(stream)))
 
 
 def q_project(x: torch.Tensor, w_q: torch.Tensor, n_q_heads: int, head_dim: int,
               gain: Optional[torch.Tensor] = None, eps: float = 1e-6,
               out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
-              stream=None) -> torch.Tensor:
-    """RMSNorm_l(X) W_Q^l -> ``[n, H_q, d_h]``."""
+              stream=None, rope_theta: Optional[float] = None, positions=None,
+              pos0: int = 0) -> torch.Tensor:
+    """RMSNorm_l(X) W_Q^l -> ``[n, H_q, d_h]``; with ``rope_theta``, row r is
+    rotated at position ``positions[r]`` (host sequence) or pos0 + r."""
     _on_device(x, w_q, gain)
     n, d = x.shape
     if out is None:
         out = torch.empty((n, n_q_heads, head_dim), dtype=out_dtype or x.dtype, device=x.device)
-    check(lib().yoco_q_project(_ptr(x), _dt(x), n, d, _ptr(gain), eps, _ptr(w_q), _dt(w_q),
-                               n_q_heads, head_dim, _ptr(out), _dt(out), _stream(stream)))
+    args = (_ptr(x), _dt(x), n, d, _ptr(gain), eps, _ptr(w_q), _dt(w_q), n_q_heads, head_dim, _ptr(out), _dt(out))
+    if rope_theta is None:
+        check(lib().yoco_q_project(*args, _stream(stream)))
+    else:
+        pos = None
+        if positions is not None:
+            pos = np.ascontiguousarray(positions, dtype=np.int64)
+            if pos.shape != (n,):
+                raise ValueError(f"positions must hold {n} entries")
+        pos_ptr = None if pos is None else pos.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        check(lib().yoco_q_project_rope(*args, pos_ptr, int(pos0), float(rope_theta), _stream(stream)))
     return out
 
 

@@ -63,6 +63,13 @@ def _declare(lib):
     lib.yoco_kv_append.argtypes = [vp, i32, i32, vp, f32, vp, vp, i32, cp, vp]
     lib.yoco_q_project.restype = st
     lib.yoco_q_project.argtypes = [vp, i32, i64, i32, vp, f32, vp, i32, i32, i32, vp, i32, vp]
+    f64 = ctypes.c_double
+    lib.yoco_kv_project_rope.restype = st
+    lib.yoco_kv_project_rope.argtypes = [vp, i32, i64, i32, vp, f32, vp, vp, i32, cp, i32, i64, f64, vp]
+    lib.yoco_kv_append_rope.restype = st
+    lib.yoco_kv_append_rope.argtypes = [vp, i32, i32, vp, f32, vp, vp, i32, cp, f64, vp]
+    lib.yoco_q_project_rope.restype = st
+    lib.yoco_q_project_rope.argtypes = [vp, i32, i64, i32, vp, f32, vp, i32, i32, i32, vp, i32, vp, i64, f64, vp]
     lib.yoco_cross_attn_prefill.restype = st
     lib.yoco_cross_attn_prefill.argtypes = [vp, i32, i64, i64, i32, cp, i32, f32, vp, i32, vp, vp]
     lib.yoco_cross_attn_decode_workspace.restype = st

@@ -182,9 +182,35 @@ yoco_status yoco_kv_cache_bytes(int32_t n_seq, int64_t seq_capacity, int32_t n_k
   return ok();
 }
 
-yoco_status yoco_kv_project(const void *m, int32_t m_dtype, int64_t n, int32_t d_model, const float *gain,
+}  // extern "C"
+
+namespace {
+
+// Rotary position embedding requested by a *_rope entry point (theta 0: none).
+struct RopeSpec {
+  double theta = 0.0;
+  const int64_t *pos_host = nullptr;  // q_project: per-row positions, or NULL
+  int64_t pos0 = 0;                   // q_project: position of row 0 when pos_host is NULL
+};
+
+yoco_status check_rope(const RopeSpec &r) {
+  if (r.theta == 0.0) return YOCO_OK;
+  if (!std::isfinite(r.theta) || r.theta <= 1.0)
+    return fail(YOCO_ERR_BAD_VALUE, "rope_theta %g must be finite and > 1", r.theta);
+  return YOCO_OK;
+}
+
+void set_rope(yoco::ProjArgs &a, const RopeSpec &r, int head_dim) {
+  if (r.theta == 0.0) return;
+  a.rope_out = 0;
+  a.head_dim = head_dim;
+  a.rope_log2_theta = std::log2(r.theta);
+}
+
+yoco_status kv_project_impl(const void *m, int32_t m_dtype, int64_t n, int32_t d_model, const float *gain,
                             float eps, const void *w_k, const void *w_v, int32_t w_dtype,
-                            yoco_kv_cache *cache, int32_t seq, int64_t row_start, void *stream) {
+                            yoco_kv_cache *cache, int32_t seq, int64_t row_start, const RopeSpec &rope,
+                            void *stream) {
   yoco_status st = check_cache(cache);
   if (st != YOCO_OK) return st;
   if (m == nullptr || w_k == nullptr || w_v == nullptr) return fail(YOCO_ERR_NULL_POINTER, "m, w_k or w_v is NULL");
@@ -192,6 +218,7 @@ yoco_status yoco_kv_project(const void *m, int32_t m_dtype, int64_t n, int32_t d
   if (seq < 0 || seq >= cache->n_seq) return fail(YOCO_ERR_BAD_SHAPE, "seq %d outside [0, %d)", seq, cache->n_seq);
   if (!dtype_ok(m_dtype) || !dtype_ok(w_dtype)) return fail(YOCO_ERR_BAD_DTYPE, "m or w dtype unknown");
   if ((st = check_eps(eps)) != YOCO_OK) return st;
+  if ((st = check_rope(rope)) != YOCO_OK) return st;
   if (n < 0 || row_start < 0 || row_start > cache->seq_capacity - n)
     return fail(YOCO_ERR_OUT_OF_RANGE, "rows [%lld, %lld) outside capacity %lld", (long long)row_start,
                 (long long)(row_start + n), (long long)cache->seq_capacity);
@@ -212,6 +239,8 @@ yoco_status yoco_kv_project(const void *m, int32_t m_dtype, int64_t n, int32_t d
   a.n_out = 2;
   a.indexed = 0;
   a.eps = eps;
+  set_rope(a, rope, cache->head_dim);  // K^ only; row r at position row_start + r
+  a.pos_base = row_start;
   st = launched(yoco::launch_project(a, m_dtype, w_dtype, cache->dtype, static_cast<hipStream_t>(stream)),
                 "kv_project");
   if (st != YOCO_OK) return st;
@@ -219,9 +248,9 @@ yoco_status yoco_kv_project(const void *m, int32_t m_dtype, int64_t n, int32_t d
   return ok();
 }
 
-yoco_status yoco_kv_append(const void *m_new, int32_t m_dtype, int32_t d_model, const float *gain, float eps,
+yoco_status kv_append_impl(const void *m_new, int32_t m_dtype, int32_t d_model, const float *gain, float eps,
                            const void *w_k, const void *w_v, int32_t w_dtype, yoco_kv_cache *cache,
-                           void *stream) {
+                           const RopeSpec &rope, void *stream) {
   yoco_status st = check_cache(cache);
   if (st != YOCO_OK) return st;
   if (m_new == nullptr || w_k == nullptr || w_v == nullptr)
@@ -229,6 +258,7 @@ yoco_status yoco_kv_append(const void *m_new, int32_t m_dtype, int32_t d_model, 
   if (d_model < 1) return fail(YOCO_ERR_BAD_SHAPE, "d_model %d < 1", d_model);
   if (!dtype_ok(m_dtype) || !dtype_ok(w_dtype)) return fail(YOCO_ERR_BAD_DTYPE, "m or w dtype unknown");
   if ((st = check_eps(eps)) != YOCO_OK) return st;
+  if ((st = check_rope(rope)) != YOCO_OK) return st;
   for (int b = 0; b < cache->n_seq; ++b) {
     const int64_t len = cache->len_host[b];
     if (len < 0 || len + 1 > cache->seq_capacity)
@@ -252,6 +282,9 @@ yoco_status yoco_kv_append(const void *m_new, int32_t m_dtype, int32_t d_model, 
   a.indexed = 1;
   a.eps = eps;
   for (int b = 0; b < cache->n_seq; ++b) a.dst_rows[b] = static_cast<int64_t>(b) * cache->seq_capacity + cache->len_host[b];
+  set_rope(a, rope, cache->head_dim);  // the new row of sequence b sits at position len_b
+  a.pos_indexed = 1;
+  a.pos_stride = cache->seq_capacity;
   st = launched(yoco::launch_project(a, m_dtype, w_dtype, cache->dtype, static_cast<hipStream_t>(stream)),
                 "kv_append");
   if (st != YOCO_OK) return st;
@@ -259,9 +292,9 @@ yoco_status yoco_kv_append(const void *m_new, int32_t m_dtype, int32_t d_model, 
   return ok();
 }
 
-yoco_status yoco_q_project(const void *x, int32_t x_dtype, int64_t n, int32_t d_model, const float *gain,
+yoco_status q_project_impl(const void *x, int32_t x_dtype, int64_t n, int32_t d_model, const float *gain,
                            float eps, const void *w_q, int32_t w_dtype, int32_t n_q_heads, int32_t head_dim,
-                           void *q_out, int32_t q_dtype, void *stream) {
+                           void *q_out, int32_t q_dtype, const RopeSpec &rope, void *stream) {
   if (x == nullptr || w_q == nullptr || q_out == nullptr) return fail(YOCO_ERR_NULL_POINTER, "x, w_q or q_out is NULL");
   if (d_model < 1 || n_q_heads < 1 || n < 0) return fail(YOCO_ERR_BAD_SHAPE, "d_model, n_q_heads and n must be positive");
   if (!head_dim_ok(head_dim)) return fail(YOCO_ERR_BAD_SHAPE, "head_dim %d is not 64 or 128", head_dim);
@@ -269,6 +302,19 @@ yoco_status yoco_q_project(const void *x, int32_t x_dtype, int64_t n, int32_t d_
     return fail(YOCO_ERR_BAD_DTYPE, "x, w or q dtype unknown");
   yoco_status st = check_eps(eps);
   if (st != YOCO_OK) return st;
+  if ((st = check_rope(rope)) != YOCO_OK) return st;
+  if (rope.theta != 0.0) {
+    if (rope.pos_host != nullptr) {
+      if (n > YOCO_MAX_SEQ) return fail(YOCO_ERR_BAD_SHAPE, "a position table covers at most %d rows, got %lld",
+                                        YOCO_MAX_SEQ, (long long)n);
+      for (int64_t r = 0; r < n; ++r) {
+        if (rope.pos_host[r] < 0) return fail(YOCO_ERR_OUT_OF_RANGE, "position %lld of row %lld is negative",
+                                              (long long)rope.pos_host[r], (long long)r);
+      }
+    } else if (rope.pos0 < 0) {
+      return fail(YOCO_ERR_OUT_OF_RANGE, "pos0 %lld is negative", (long long)rope.pos0);
+    }
+  }
   if (n == 0) return ok();
   if ((st = check_device()) != YOCO_OK) return st;
 
@@ -286,8 +332,73 @@ yoco_status yoco_q_project(const void *x, int32_t x_dtype, int64_t n, int32_t d_
   a.n_out = 1;
   a.indexed = 0;
   a.eps = eps;
+  set_rope(a, rope, head_dim);
+  if (rope.pos_host != nullptr) {
+    // The destination rows are contiguous, so dst_rows holds the positions.
+    a.pos_indexed = 1;
+    a.pos_stride = 0;
+    for (int64_t r = 0; r < n; ++r) a.dst_rows[r] = rope.pos_host[r];
+  } else {
+    a.pos_base = rope.pos0;
+  }
   return launched(yoco::launch_project(a, x_dtype, w_dtype, q_dtype, static_cast<hipStream_t>(stream)),
                   "q_project");
+}
+
+}  // namespace
+
+extern "C" {
+
+yoco_status yoco_kv_project(const void *m, int32_t m_dtype, int64_t n, int32_t d_model, const float *gain,
+                            float eps, const void *w_k, const void *w_v, int32_t w_dtype,
+                            yoco_kv_cache *cache, int32_t seq, int64_t row_start, void *stream) {
+  return kv_project_impl(m, m_dtype, n, d_model, gain, eps, w_k, w_v, w_dtype, cache, seq, row_start, RopeSpec{},
+                         stream);
+}
+
+yoco_status yoco_kv_project_rope(const void *m, int32_t m_dtype, int64_t n, int32_t d_model, const float *gain,
+                                 float eps, const void *w_k, const void *w_v, int32_t w_dtype,
+                                 yoco_kv_cache *cache, int32_t seq, int64_t row_start, double rope_theta,
+                                 void *stream) {
+  RopeSpec r;
+  r.theta = rope_theta;
+  if (rope_theta == 0.0) return fail(YOCO_ERR_BAD_VALUE, "rope_theta must be finite and > 1");
+  return kv_project_impl(m, m_dtype, n, d_model, gain, eps, w_k, w_v, w_dtype, cache, seq, row_start, r, stream);
+}
+
+yoco_status yoco_kv_append(const void *m_new, int32_t m_dtype, int32_t d_model, const float *gain, float eps,
+                           const void *w_k, const void *w_v, int32_t w_dtype, yoco_kv_cache *cache,
+                           void *stream) {
+  return kv_append_impl(m_new, m_dtype, d_model, gain, eps, w_k, w_v, w_dtype, cache, RopeSpec{}, stream);
+}
+
+yoco_status yoco_kv_append_rope(const void *m_new, int32_t m_dtype, int32_t d_model, const float *gain, float eps,
+                                const void *w_k, const void *w_v, int32_t w_dtype, yoco_kv_cache *cache,
+                                double rope_theta, void *stream) {
+  RopeSpec r;
+  r.theta = rope_theta;
+  if (rope_theta == 0.0) return fail(YOCO_ERR_BAD_VALUE, "rope_theta must be finite and > 1");
+  return kv_append_impl(m_new, m_dtype, d_model, gain, eps, w_k, w_v, w_dtype, cache, r, stream);
+}
+
+yoco_status yoco_q_project(const void *x, int32_t x_dtype, int64_t n, int32_t d_model, const float *gain,
+                           float eps, const void *w_q, int32_t w_dtype, int32_t n_q_heads, int32_t head_dim,
+                           void *q_out, int32_t q_dtype, void *stream) {
+  return q_project_impl(x, x_dtype, n, d_model, gain, eps, w_q, w_dtype, n_q_heads, head_dim, q_out, q_dtype,
+                        RopeSpec{}, stream);
+}
+
+yoco_status yoco_q_project_rope(const void *x, int32_t x_dtype, int64_t n, int32_t d_model, const float *gain,
+                                float eps, const void *w_q, int32_t w_dtype, int32_t n_q_heads, int32_t head_dim,
+                                void *q_out, int32_t q_dtype, const int64_t *pos_host, int64_t pos0,
+                                double rope_theta, void *stream) {
+  RopeSpec r;
+  r.theta = rope_theta;
+  r.pos_host = pos_host;
+  r.pos0 = pos0;
+  if (rope_theta == 0.0) return fail(YOCO_ERR_BAD_VALUE, "rope_theta must be finite and > 1");
+  return q_project_impl(x, x_dtype, n, d_model, gain, eps, w_q, w_dtype, n_q_heads, head_dim, q_out, q_dtype, r,
+                        stream);
 }
 
 yoco_status yoco_cross_attn_prefill(const void *q, int32_t q_dtype, int64_t q_start, int64_t t, int32_t n_q_heads,

@@ -29,6 +29,7 @@
 // Destination rows are either contiguous (a cache slab or a Q buffer) or, for
 // the generation-time append, one indexed row per sequence.
 #include "device_common.h"
+#include "rope.h"
 #include "yoco_internal.h"
 
 namespace yoco {
@@ -132,8 +133,18 @@ __global__ __launch_bounds__(pj::kThreads) void project_kernel(const ProjArgs a)
     const int64_t dst = a.indexed ? a.dst_rows[row] : a.dst_row_base + row;
     const float inv = s_inv_rms[rr];
     TO *orow = out + dst * a.ncols + col_tile * BN + tx * 4;
+    float v[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) store_elem<TO>(orow + j, acc[i][j] * inv);
+    for (int j = 0; j < 4; ++j) v[j] = acc[i][j] * inv;
+    if (a.rope_out == out_id) {
+      // columns tx*4 .. +3 are pairs (2i, 2i+1) and (2i+2, 2i+3) of a head
+      const int pair = ((col_tile * BN + tx * 4) % a.head_dim) >> 1;
+      const int64_t pos = proj_row_pos(a, row);
+      rope_turn(v[0], v[1], pos, rope_rev(pair, a.head_dim, a.rope_log2_theta));
+      rope_turn(v[2], v[3], pos, rope_rev(pair + 1, a.head_dim, a.rope_log2_theta));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) store_elem<TO>(orow + j, v[j]);
   }
 }
 
@@ -270,17 +281,29 @@ __global__ __launch_bounds__(pg::Shape<NR>::kThreads) void project_small_kernel(
       for (int e = 0; e < 8; ++e) s_red[wave][r][c8 * 8 + e] = acc[r][e];
   }
   __syncthreads();
+  // One thread per column pair (2c, 2c+1), so the RoPE rotation has both.
   TO *out = static_cast<TO *>(a.out[out_id]);
-  for (int idx = tid; idx < NR * kCols; idx += kThreads) {
-    const int r = idx / kCols;
-    const int col = idx - r * kCols;
+  const bool rope = a.rope_out == out_id;
+  for (int idx = tid; idx < NR * (kCols / 2); idx += kThreads) {
+    const int r = idx / (kCols / 2);
+    const int col = 2 * (idx - r * (kCols / 2));
     if (r >= nr) continue;
-    float v = 0.f;
+    float v0 = 0.f, v1 = 0.f;
 #pragma unroll
-    for (int wv2 = 0; wv2 < kWaves; ++wv2) v += s_red[wv2][r][col];
+    for (int wv2 = 0; wv2 < kWaves; ++wv2) {
+      v0 += s_red[wv2][r][col];
+      v1 += s_red[wv2][r][col + 1];
+    }
+    v0 *= s_inv_rms[r];
+    v1 *= s_inv_rms[r];
     const int64_t row = row_base + r;
+    if (rope) {
+      const int pair = ((strip * kCols + col) % a.head_dim) >> 1;
+      rope_turn(v0, v1, proj_row_pos(a, row), rope_rev(pair, a.head_dim, a.rope_log2_theta));
+    }
     const int64_t dst = a.indexed ? a.dst_rows[row] : a.dst_row_base + row;
-    store_elem<TO>(out + dst * a.ncols + strip * kCols + col, v * s_inv_rms[r]);
+    store_elem<TO>(out + dst * a.ncols + strip * kCols + col, v0);
+    store_elem<TO>(out + dst * a.ncols + strip * kCols + col + 1, v1);
   }
 }
 

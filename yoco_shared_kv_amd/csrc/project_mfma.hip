@@ -31,6 +31,7 @@
 // chunk index XOR a 4-bit function of the row).  The x descriptor ends at the
 // last input row, so rows past it load as zeros and are not stored.
 #include "device_common.h"
+#include "rope.h"
 #include "yoco_internal.h"
 
 namespace yoco {
@@ -93,6 +94,7 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
   __shared__ __attribute__((aligned(1024))) char lds_w1[2 * kWHalfBytes];
   __shared__ __attribute__((aligned(1024))) float lds_g0[256];
   __shared__ __attribute__((aligned(1024))) float lds_g1[256];
+  __shared__ double lds_rev[64];  // RoPE turns per position, per pair of a head
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -268,7 +270,13 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
 
   // Epilogue: acc[t][s2] element i is output column
   //   col0 + wc*128 + t*32 + (i/4)*8 + half*4 + (i%4)
-  // of input row row0 + wr*64 + s2*32 + col.
+  // of input row row0 + wr*64 + s2*32 + col.  With RoPE, columns (2i, 2i+1)
+  // of a head sit in elements (i4*4 + 2j, i4*4 + 2j + 1) of the same lane.
+  const bool rope = a.rope_out == p;  // block-uniform
+  if (rope) {
+    if (threadIdx.x < a.head_dim / 2) lds_rev[threadIdx.x] = rope_rev(threadIdx.x, a.head_dim, a.rope_log2_theta);
+    __syncthreads();
+  }
   bf16_t *out = static_cast<bf16_t *>(a.out[p]);
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2) {
@@ -277,13 +285,21 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
     if (r >= rows_here) continue;
     const float inv = 1.0f / sqrtf(ss / static_cast<float>(d) + a.eps);
     bf16_t *orow = out + (a.dst_row_base + row0 + r) * a.ncols + col0 + wc * 128;
+    const int64_t pos = rope ? proj_row_pos(a, row0 + r) : 0;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
+        float v0 = acc[t][s2][i4 * 4 + 0] * inv, v1 = acc[t][s2][i4 * 4 + 1] * inv;
+        float v2 = acc[t][s2][i4 * 4 + 2] * inv, v3 = acc[t][s2][i4 * 4 + 3] * inv;
+        if (rope) {
+          const int pair = ((col0 + wc * 128 + t * 32 + i4 * 8 + half * 4) % a.head_dim) >> 1;
+          rope_turn(v0, v1, pos, lds_rev[pair]);
+          rope_turn(v2, v3, pos, lds_rev[pair + 1]);
+        }
         uint2 v;
-        v.x = cvt_pk_bf16(acc[t][s2][i4 * 4 + 0] * inv, acc[t][s2][i4 * 4 + 1] * inv);
-        v.y = cvt_pk_bf16(acc[t][s2][i4 * 4 + 2] * inv, acc[t][s2][i4 * 4 + 3] * inv);
+        v.x = cvt_pk_bf16(v0, v1);
+        v.y = cvt_pk_bf16(v2, v3);
         *reinterpret_cast<uint2 *>(orow + t * 32 + i4 * 8 + half * 4) = v;
       }
     }

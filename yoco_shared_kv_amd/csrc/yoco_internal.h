@@ -30,8 +30,21 @@ struct ProjArgs {
   int32_t n_out;             // 1 (Q) or 2 (K and V)
   int32_t indexed;           // 1: use dst_rows
   float eps;
+  // Rotary position embedding of output rope_out (-1: none), pairs
+  // (2i, 2i+1) of each head_dim-wide head.  Input row r sits at position
+  //   pos_indexed ? dst_rows[r] - r * pos_stride : pos_base + r.
+  double rope_log2_theta = 0.0;
+  int32_t rope_out = -1;
+  int32_t head_dim = 0;
+  int32_t pos_indexed;
+  int64_t pos_base;
+  int64_t pos_stride;
   int64_t dst_rows[YOCO_MAX_SEQ];
 };
+
+__device__ __forceinline__ int64_t proj_row_pos(const ProjArgs &a, int64_t r) {
+  return a.pos_indexed ? a.dst_rows[r] - r * a.pos_stride : a.pos_base + r;
+}
 
 hipError_t launch_project(const ProjArgs &a, int x_dt, int w_dt, int o_dt, hipStream_t s);
 // Matrix-core path for prompt-sized bf16 projections (d_model % 64 == 0,
