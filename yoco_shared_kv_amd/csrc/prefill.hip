@@ -314,11 +314,6 @@ __global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const Pre
     const float p1 = fast_exp2(fmaf(s[kk * 8 + 2 * j + 1], a.scale_log2, -m_ref));
     p[kk].w[j] = cvt_pk_bf16(p0, p1);
   };
-  auto sum_p = [&](const Frag8 &p, float acc) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc = dot2_bf16_f32(p.w[j], kOnesBf16x2, acc);
-    return acc;
-  };
 
   // One step of the pipeline, scheduled by hand: chunk i issues MFMA i (the
   // PV MFMAs, then the S MFMAs), the LDS reads of MFMA i+4 and one piece of
@@ -332,9 +327,17 @@ __global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const Pre
   //  * an S MFMA without a next half produces a value nobody reads;
   //  * P of a half outside the wave's range is zero, and l, the reference
   //    and the maxima are updated only for halves in range.
-  auto step = [&](auto generic_c, int u, const char *tk, const char *tv, floatx16 &s_cur, floatx16 &s_next,
-                  Frag8 (&p_prev)[2], Frag8 (&p_cur)[2]) __attribute__((always_inline)) {
+  // Fast steps of one period are linked: the first reads the V operands of
+  // the second's first kAhead MFMAs in its last chunks (into `carry`), so
+  // the second starts without waiting for LDS.  link_c: 0 none, 1 fill
+  // carry from tv + one half, 2 start from carry.
+  constexpr int kAhead = 4;  // LDS reads run this many MFMAs ahead
+  constexpr int kHalfBytes = 32 * S::kRowBytes;
+  Frag8 carry[kAhead];
+  auto step = [&](auto generic_c, auto link_c, int u, const char *tk, const char *tv, floatx16 &s_cur,
+                  floatx16 &s_next, Frag8 (&p_prev)[2], Frag8 (&p_cur)[2]) __attribute__((always_inline)) {
     constexpr bool kGeneric = decltype(generic_c)::value;
+    constexpr int kLink = decltype(link_c)::value;
     constexpr int NPV = 2 * S::DSUB;
     constexpr int NM = NPV + S::KSTEPS;
     // Softmax pieces: (generic only) the row maximum (4 pieces of 4
@@ -377,15 +380,25 @@ __global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const Pre
       } else if (i >= kP0 && i < kP0 + 8) {
         make_p_pair(s_cur, p_cur, (i - kP0) >> 2, (i - kP0) & 3);
       } else if (i >= kL0 && i < kL0 + 2) {
-        l_add = sum_p(p_prev[i - kL0], l_add);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) l_add = dot2_bf16_f32(p_prev[i - kL0].w[j], kOnesBf16x2, l_add);
       }
     };
-    constexpr int kAhead = 4;  // LDS reads run this many MFMAs ahead
 #pragma unroll
-    for (int i = 0; i < kAhead; ++i) issue_read(i);
+    for (int i = 0; i < kAhead; ++i) {
+      if constexpr (kLink == 2) {
+        opnd[i] = carry[i];
+      } else {
+        issue_read(i);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
-      if (i + kAhead < NM) issue_read(i + kAhead);
+      if (i + kAhead < NM) {
+        issue_read(i + kAhead);
+      } else if constexpr (kLink == 1) {
+        carry[i + kAhead - NM] = read_v(tv + kHalfBytes, i + kAhead - NM);
+      }
       if (i < NPV) {
         oacc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[i].v, p_prev[i & 1].v, oacc[i >> 1], 0, 0, 0);
       } else {
@@ -416,41 +429,47 @@ __global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const Pre
   // One period: barrier, start the next loads, then halves 2p-1 and 2p.
   // Step 2p-1 reads K half 2p (tile p, rows 0..31) and V half 2p-2 (tile
   // p-1, rows 0..31); step 2p the second halves.
-  constexpr int kHalfBytes = 32 * S::kRowBytes;
-  auto period_start = [&](int kb, int p) __attribute__((always_inline)) {
+  // `inner_c` (fast periods: p + 1 < n_ktiles) stages without a branch, so
+  // the steps of consecutive periods share one basic block and the compiler
+  // cannot move a step's softmax past the barrier, away from the MFMAs it
+  // is scheduled against.
+  auto period_start = [&](auto inner_c, int kb, int p) __attribute__((always_inline)) {
     // Every wave's loads of K tile p and V tile p-1 have landed, and every
     // wave is done with K tile p-1 and V tile p-2, whose buffers the next
     // loads overwrite.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (p + 1 < n_ktiles) stage_tile<DH, SWZ>(kbuf(kb ^ 1), kg, row_stride_kv, (p + 1) * pf::kKeyTile, kv_len, wave, so);
-    if (p < n_ktiles) stage_tile<DH, SWZ>(vbuf(kb), vg, row_stride_kv, p * pf::kKeyTile, kv_len, wave, so);
+    if (decltype(inner_c)::value || p + 1 < n_ktiles)
+      stage_tile<DH, SWZ>(kbuf(kb ^ 1), kg, row_stride_kv, (p + 1) * pf::kKeyTile, kv_len, wave, so);
+    if (decltype(inner_c)::value || p < n_ktiles)
+      stage_tile<DH, SWZ>(vbuf(kb), vg, row_stride_kv, p * pf::kKeyTile, kv_len, wave, so);
   };
   auto period_fast = [&](auto buf_c, int p) __attribute__((always_inline)) {
     constexpr int KB = decltype(buf_c)::value;  // K tile p sits in buffer p % 2
-    period_start(KB, p);
+    period_start(std::true_type(), KB, p);
     const char *tk = kbuf(KB);
     const char *tv = vbuf(KB ^ 1);
-    step(std::false_type(), 2 * p - 1, tk, tv, sa, sb, pa, pb);
-    step(std::false_type(), 2 * p, tk + kHalfBytes, tv + kHalfBytes, sb, sa, pb, pa);
+    step(std::false_type(), std::integral_constant<int, 1>(), 2 * p - 1, tk, tv, sa, sb, pa, pb);
+    step(std::false_type(), std::integral_constant<int, 2>(), 2 * p, tk + kHalfBytes, tv + kHalfBytes, sb, sa, pb, pa);
   };
   auto period_generic = [&](int p) __attribute__((always_inline)) {
     const int kb = p & 1;
-    period_start(kb, p);
+    period_start(std::false_type(), kb, p);
     const char *tk = kbuf(kb);
     const char *tv = vbuf(kb ^ 1);
-    step(std::true_type(), 2 * p - 1, tk, tv, sa, sb, pa, pb);
-    step(std::true_type(), 2 * p, tk + kHalfBytes, tv + kHalfBytes, sb, sa, pb, pa);
+    step(std::true_type(), std::integral_constant<int, 0>(), 2 * p - 1, tk, tv, sa, sb, pa, pb);
+    step(std::true_type(), std::integral_constant<int, 0>(), 2 * p, tk + kHalfBytes, tv + kHalfBytes, sb, sa, pb, pa);
   };
   // Periods 1 .. p_fast_end-1 take the fast form: both steps have a previous
-  // half, a next half and a half in range, and neither half reaches past
-  // the wave's first row (2p+1 < n_half and 64p+31 <= wave_pos_first).  They
-  // run in pairs (K buffers 1, 0), the rest in the generic form.
+  // half, a next half and a half in range, neither half reaches past the
+  // wave's first row (2p+1 < n_half and 64p+31 <= wave_pos_first), and the
+  // workgroup stages K tile p+1 (p+1 < n_ktiles).  They run in pairs (K
+  // buffers 1, 0), the rest in the generic form.
   int p_fast_end = 1;
   if (wave_active) {
     const int by_len = n_half / 2;                           // largest p with 2p+1 < n_half, plus one
     const int by_diag = wave_pos_first >= 31 ? (wave_pos_first - 31) / 64 + 1 : 0;
-    p_fast_end = max(1, min(by_len, by_diag));
+    p_fast_end = max(1, min(min(by_len, by_diag), n_ktiles - 1));
   }
   const int p_pair_end = 1 + ((p_fast_end - 1) & ~1);
 
