@@ -16,8 +16,13 @@ query rows and heads).  This module only marshals numpy arrays to it:
 * ``prefill`` / ``decode`` -- position bookkeeping around ``attention``.
 * ``rope``        -- rotary position embedding of K^ / Q^ heads (the blog's
                      section 7: K^ and each layer's Q are rotated, V is not).
+* ``attention_bwd`` -- gradients of ``attention`` with respect to the query,
+                     K^ and V^ (K^/V^ gradients added, so layers sum).
+* ``project_bwd`` -- gradients of the shared projection with respect to M,
+                     the norm gain, W_K and W_V.
 
-Inputs are the stored values: float32 arrays, or bf16 kept as ``uint16`` bits.
+Inputs are the stored values: float32 arrays, bf16 kept as ``uint16`` bits,
+or float64 (for finite-difference checks).
 """
 from __future__ import annotations
 
@@ -34,7 +39,7 @@ _LIB = os.path.join(_DIR, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 
 
 def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
@@ -55,7 +60,9 @@ def _code(a: np.ndarray) -> int:
         return F32
     if a.dtype == np.uint16:
         return BF16
-    raise TypeError(f"oracle inputs are float32 or bf16 bits (uint16), got {a.dtype}")
+    if a.dtype == np.float64:
+        return F64
+    raise TypeError(f"oracle inputs are float32, float64 or bf16 bits (uint16), got {a.dtype}")
 
 
 def _ptr(a: np.ndarray):
@@ -86,6 +93,12 @@ class Oracle:
                                          dbl, vp, vp]
         lib.oracle_attention.restype = i32
         lib.oracle_rope.argtypes = [vp, i64, i32, i32, vp, dbl, i32]
+        lib.oracle_attention_bwd.argtypes = [vp, i32, i64, vp, i32, vp, vp, i32, i64, i32, i32,
+                                             vp, i32, dbl, vp, vp, vp]
+        lib.oracle_attention_bwd.restype = i32
+        lib.oracle_project_bwd.argtypes = [vp, i32, i64, i64, vp, dbl, vp, vp, i32, i64, vp, vp, i32,
+                                           vp, vp, vp, vp]
+        lib.oracle_project_bwd.restype = i32
         self.lib = lib
         self.path = path
 
@@ -177,6 +190,69 @@ class Oracle:
             raise MemoryError("oracle_attention could not allocate scratch")
         return (o, lse) if want_lse else o
 
+    def attention_bwd(self, q: np.ndarray, pos, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
+                      scale: float, dk=None, dv=None):
+        """Gradients of ``attention(q, pos, k, v, scale)`` for the upstream
+        gradient ``dout`` ([n_q, H_q, d_h]).  Returns (dq, dk, dv) in fp64;
+        dk, dv ([rows, H_kv, d_h]) are added to the given fp64 arrays (zeros
+        if None), so that several layers, or disjoint query rows, sum."""
+        q = np.ascontiguousarray(q)
+        k = np.ascontiguousarray(k)
+        v = np.ascontiguousarray(v)
+        dout = np.ascontiguousarray(dout)
+        if k.dtype != v.dtype:
+            raise TypeError("k and v must share a storage type")
+        n_q, hq, dh = q.shape
+        rows, hkv, dhk = k.shape
+        if v.shape != k.shape or dhk != dh or dout.shape != q.shape:
+            raise ValueError("shape mismatch between q, dout, k and v")
+        pos = np.ascontiguousarray(pos, dtype=np.int64).reshape(-1)
+        if pos.shape[0] != n_q:
+            raise ValueError("one position per query row")
+        dq = np.empty((n_q, hq, dh), dtype=np.float64)
+        dk = np.zeros(k.shape, dtype=np.float64) if dk is None else dk
+        dv = np.zeros(v.shape, dtype=np.float64) if dv is None else dv
+        for a in (dk, dv):
+            if a.dtype != np.float64 or a.shape != k.shape or not a.flags.c_contiguous:
+                raise ValueError("dk, dv must be C-contiguous float64 [rows, H_kv, d_h]")
+        rc = self.lib.oracle_attention_bwd(_ptr(q), _code(q), n_q, _ptr(pos), hq, _ptr(k), _ptr(v),
+                                           _code(k), rows, hkv, dh, _ptr(dout), _code(dout),
+                                           float(scale), _ptr(dq), _ptr(dk), _ptr(dv))
+        if rc == -1:
+            raise ValueError("bad attention arguments (H_q % H_kv, or a position outside the slab)")
+        if rc != 0:
+            raise MemoryError("oracle_attention_bwd could not allocate scratch")
+        return dq, dk, dv
+
+    def project_bwd(self, x: np.ndarray, w_k: np.ndarray, w_v: np.ndarray, dz_k: np.ndarray,
+                    dz_v: np.ndarray, gain=None, eps: float = 1e-6):
+        """Gradients of ``K^ = RMSNorm(x) W_K, V^ = RMSNorm(x) W_V`` for the
+        upstream gradients dz_k, dz_v ([n, ncols], one storage type).
+        Returns (dx [n, d], dw_k, dw_v [d, ncols], dgain [d] or None), fp64."""
+        x = np.ascontiguousarray(x)
+        w_k = np.ascontiguousarray(w_k)
+        w_v = np.ascontiguousarray(w_v)
+        dz_k = np.ascontiguousarray(dz_k)
+        dz_v = np.ascontiguousarray(dz_v)
+        n, d = x.shape
+        if w_k.shape != w_v.shape or w_k.dtype != w_v.dtype or w_k.shape[0] != d:
+            raise ValueError("w_k, w_v must be matching [d_model, ncols] arrays")
+        ncols = w_k.shape[1]
+        if dz_k.shape != (n, ncols) or dz_v.shape != (n, ncols) or dz_k.dtype != dz_v.dtype:
+            raise ValueError("dz_k, dz_v must be matching [n, ncols] arrays")
+        g = None if gain is None else np.ascontiguousarray(gain, dtype=np.float32)
+        dx = np.empty((n, d), dtype=np.float64)
+        dw_k = np.empty((d, ncols), dtype=np.float64)
+        dw_v = np.empty((d, ncols), dtype=np.float64)
+        dgain = None if g is None else np.empty(d, dtype=np.float64)
+        rc = self.lib.oracle_project_bwd(_ptr(x), _code(x), n, d, None if g is None else _ptr(g), eps,
+                                         _ptr(w_k), _ptr(w_v), _code(w_k), ncols, _ptr(dz_k), _ptr(dz_v),
+                                         _code(dz_k), _ptr(dx), _ptr(dw_k), _ptr(dw_v),
+                                         None if dgain is None else _ptr(dgain))
+        if rc != 0:
+            raise MemoryError("oracle_project_bwd could not allocate scratch")
+        return dx, dw_k, dw_v, dgain
+
     def prefill(self, q: np.ndarray, q_start: int, k: np.ndarray, v: np.ndarray,
                 scale: float, rows=None, want_lse: bool = False):
         """Causal prefill: query row i sits at position q_start + i.  ``rows``
@@ -238,3 +314,11 @@ def prefill(q, q_start, k, v, scale, rows=None, want_lse: bool = False):
 
 def decode(q, length, k, v, scale, want_lse: bool = False):
     return default().decode(q, length, k, v, scale, want_lse)
+
+
+def attention_bwd(q, pos, k, v, dout, scale, dk=None, dv=None):
+    return default().attention_bwd(q, pos, k, v, dout, scale, dk, dv)
+
+
+def project_bwd(x, w_k, w_v, dz_k, dz_v, gain=None, eps: float = 1e-6):
+    return default().project_bwd(x, w_k, w_v, dz_k, dz_v, gain, eps)

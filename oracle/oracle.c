@@ -39,7 +39,7 @@
  * (query row, head) tasks; it changes no arithmetic.
  *
  * Input storage codes: 0 = float32, 1 = bf16 (raw uint16 bits, widened
- * exactly).  Every element is converted to double when read.
+ * exactly), 2 = float64.  Every element is converted to double when read.
  */
 #include <math.h>
 #include <stdint.h>
@@ -51,10 +51,14 @@
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+#define ORACLE_F64 2
 
 static double read_elem(const void *p, int dtype, int64_t i) {
   if (dtype == ORACLE_F32) {
     return (double)((const float *)p)[i];
+  }
+  if (dtype == ORACLE_F64) {
+    return ((const double *)p)[i];
   }
   uint32_t bits = ((uint32_t)((const uint16_t *)p)[i]) << 16;
   float f;
@@ -255,4 +259,231 @@ int oracle_attention(const void *q, int q_dtype, int64_t n_q, const int64_t *pos
     free(acc);
   }
   return failed ? -2 : 0;
+}
+
+/* Backward of causal GQA attention (the gradient of [Notes] Eq. 3 with
+ * respect to the query, K^ and V^; [Deep] s.2.2: every cross layer reads the
+ * same K^/V^, so by the chain rule their gradients are the sums of each
+ * layer's contribution).
+ *
+ * For query row i at position pos[i], head h (KV head g = h / (hq / hkv)),
+ * logits x_j = scale * <q, k_j> over the visible rows j = 0..pos[i], and
+ * upstream gradient dO of the output o = sum_j p_j v_j:
+ *   p_j  = softmax(x)_j                      (max, exp, sum, divide)
+ *   dp_j = <dO, v_j>                          (gradient of o wrt p_j)
+ *   D    = sum_j p_j dp_j                     (softmax Jacobian term)
+ *   ds_j = p_j (dp_j - D)                     (gradient wrt x_j)
+ *   dq   = scale * sum_j ds_j k_j
+ *   dk_j += scale * ds_j q,   dv_j += p_j dO.
+ *
+ * q, dout: [n_q][hq][dh]; k, v: [kv_rows][hkv][dh]; dq: [n_q][hq][dh]
+ * (written); dk, dv: [kv_rows][hkv][dh] (ADDED to, so that calls for several
+ * layers, or for disjoint sets of query rows, sum).  Only rows j <= pos[i]
+ * of the given query rows contribute to dk, dv.
+ *
+ * The work is split in two passes that do not change the arithmetic of a
+ * term: pass 1 (independent (row, head) tasks) forms the softmax statistics
+ * m, l, D and dq; pass 2 (independent (KV head, block of 64 cache rows)
+ * tasks) adds every (row, head) contribution to its cache rows, in order of
+ * ascending query row, then query head.
+ *
+ * Returns 0; -1 on bad arguments; -2 if scratch memory cannot be obtained.
+ */
+int oracle_attention_bwd(const void *q, int q_dtype, int64_t n_q, const int64_t *pos, int hq,
+                         const void *k, const void *v, int kv_dtype, int64_t kv_rows, int hkv,
+                         int dh, const void *dout, int do_dtype, double scale, double *dq,
+                         double *dk, double *dv) {
+  if (hq <= 0 || hkv <= 0 || dh <= 0 || hq % hkv != 0) return -1;
+  for (int64_t i = 0; i < n_q; ++i) {
+    if (pos[i] < 0 || pos[i] >= kv_rows) return -1;
+  }
+  const int group = hq / hkv;
+  const int64_t n_tasks = n_q * (int64_t)hq;
+  double *stat_m = (double *)malloc((size_t)(n_tasks > 0 ? n_tasks : 1) * sizeof(double));
+  double *stat_l = (double *)malloc((size_t)(n_tasks > 0 ? n_tasks : 1) * sizeof(double));
+  double *stat_d = (double *)malloc((size_t)(n_tasks > 0 ? n_tasks : 1) * sizeof(double));
+  if (!stat_m || !stat_l || !stat_d) {
+    free(stat_m);
+    free(stat_l);
+    free(stat_d);
+    return -2;
+  }
+  int failed = 0;
+
+  /* Pass 1: per (row, head), the logits, softmax, D and dq. */
+#pragma omp parallel
+  {
+    int64_t cap = 0;
+    double *x = NULL, *dp = NULL;
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t task = 0; task < n_tasks; ++task) {
+      const int64_t i = task / hq;
+      const int h = (int)(task % hq);
+      const int g = h / group;
+      const int64_t n_keys = pos[i] + 1;
+      if (n_keys > cap) {
+        free(x);
+        free(dp);
+        cap = n_keys;
+        x = (double *)malloc((size_t)cap * sizeof(double));
+        dp = (double *)malloc((size_t)cap * sizeof(double));
+      }
+      if (!x || !dp) {
+        cap = 0;
+#pragma omp atomic write
+        failed = 1;
+        continue;
+      }
+      const int64_t q_base = (i * hq + h) * (int64_t)dh;
+      for (int64_t j = 0; j < n_keys; ++j) {
+        const int64_t kv_base = (j * hkv + g) * (int64_t)dh;
+        double dot = 0.0, dpj = 0.0;
+        for (int e = 0; e < dh; ++e) {
+          dot += read_elem(q, q_dtype, q_base + e) * read_elem(k, kv_dtype, kv_base + e);
+          dpj += read_elem(dout, do_dtype, q_base + e) * read_elem(v, kv_dtype, kv_base + e);
+        }
+        x[j] = scale * dot;
+        dp[j] = dpj;
+      }
+      double m = x[0];
+      for (int64_t j = 1; j < n_keys; ++j) {
+        if (x[j] > m) m = x[j];
+      }
+      double l = 0.0;
+      for (int64_t j = 0; j < n_keys; ++j) l += exp(x[j] - m);
+      double d_term = 0.0;
+      for (int64_t j = 0; j < n_keys; ++j) d_term += (exp(x[j] - m) / l) * dp[j];
+      for (int e = 0; e < dh; ++e) dq[q_base + e] = 0.0;
+      for (int64_t j = 0; j < n_keys; ++j) {
+        const double ds = (exp(x[j] - m) / l) * (dp[j] - d_term);
+        const int64_t kv_base = (j * hkv + g) * (int64_t)dh;
+        for (int e = 0; e < dh; ++e) dq[q_base + e] += ds * read_elem(k, kv_dtype, kv_base + e);
+      }
+      for (int e = 0; e < dh; ++e) dq[q_base + e] *= scale;
+      stat_m[task] = m;
+      stat_l[task] = l;
+      stat_d[task] = d_term;
+    }
+    free(x);
+    free(dp);
+  }
+
+  /* Pass 2: per (KV head, block of cache rows), every contribution to dk, dv. */
+  const int64_t kBlock = 64;
+  const int64_t n_blocks = (kv_rows + kBlock - 1) / kBlock;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t task = 0; task < n_blocks * hkv; ++task) {
+    const int g = (int)(task % hkv);
+    const int64_t j0 = (task / hkv) * kBlock;
+    const int64_t j1 = j0 + kBlock < kv_rows ? j0 + kBlock : kv_rows;
+    for (int64_t i = 0; i < n_q; ++i) {
+      if (pos[i] < j0) continue;
+      const int64_t j_end = pos[i] + 1 < j1 ? pos[i] + 1 : j1;
+      for (int h = g * group; h < (g + 1) * group; ++h) {
+        const int64_t t = i * hq + h;
+        const int64_t q_base = t * (int64_t)dh;
+        for (int64_t j = j0; j < j_end; ++j) {
+          const int64_t kv_base = (j * hkv + g) * (int64_t)dh;
+          double dot = 0.0, dpj = 0.0;
+          for (int e = 0; e < dh; ++e) {
+            dot += read_elem(q, q_dtype, q_base + e) * read_elem(k, kv_dtype, kv_base + e);
+            dpj += read_elem(dout, do_dtype, q_base + e) * read_elem(v, kv_dtype, kv_base + e);
+          }
+          const double p = exp(scale * dot - stat_m[t]) / stat_l[t];
+          const double ds = p * (dpj - stat_d[t]);
+          for (int e = 0; e < dh; ++e) {
+            dv[kv_base + e] += p * read_elem(dout, do_dtype, q_base + e);
+            dk[kv_base + e] += scale * ds * read_elem(q, q_dtype, q_base + e);
+          }
+        }
+      }
+    }
+  }
+  free(stat_m);
+  free(stat_l);
+  free(stat_d);
+  return failed ? -2 : 0;
+}
+
+/* Backward of the shared projection K^ = RMSNorm(x) W_K, V^ = RMSNorm(x) W_V
+ * ([Notes] Eq. 2; the norm's formula is the reading stated at the top).
+ *
+ * With y = RMSNorm(x; g, eps), r = sqrt(mean_c x_c^2 + eps) per row, and the
+ * upstream gradients dz_k, dz_v of the two outputs:
+ *   dW_t[c][j] = sum_rows y[c] dz_t[j]                  (t = K, V)
+ *   dy[c]      = sum_j dz_k[j] W_K[c][j] + sum_j dz_v[j] W_V[c][j]
+ *   dgain[c]   = sum_rows dy[c] x[c] / r
+ *   dx[c]      = g[c] dy[c] / r - x[c] / (d r^3) * sum_c' g[c'] dy[c'] x[c']
+ * (the last from dr/dx_c = x_c / (d r)).
+ *
+ * x: [n][d] stored; gain: [d] float32 or NULL (all ones); w_k, w_v:
+ * [d][ncols] stored; dz_k, dz_v: [n][ncols] stored; outputs double: dx
+ * [n][d], dw_k, dw_v [d][ncols], dgain [d] (skipped when NULL).
+ * Returns 0, or -2 if scratch memory cannot be obtained.
+ */
+int oracle_project_bwd(const void *x, int x_dtype, int64_t n, int64_t d, const float *gain,
+                       double eps, const void *w_k, const void *w_v, int w_dtype, int64_t ncols,
+                       const void *dz_k, const void *dz_v, int dz_dtype, double *dx,
+                       double *dw_k, double *dw_v, double *dgain) {
+  double *y = (double *)malloc((size_t)(n * d > 0 ? n * d : 1) * sizeof(double));
+  double *dy = (double *)malloc((size_t)(n * d > 0 ? n * d : 1) * sizeof(double));
+  double *rr = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+  if (!y || !dy || !rr) {
+    free(y);
+    free(dy);
+    free(rr);
+    return -2;
+  }
+  oracle_rmsnorm(x, x_dtype, n, d, gain, eps, y);
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r) {
+    double sum_sq = 0.0;
+    for (int64_t c = 0; c < d; ++c) {
+      const double xv = read_elem(x, x_dtype, r * d + c);
+      sum_sq += xv * xv;
+    }
+    rr[r] = sqrt(sum_sq / (double)d + eps);
+    for (int64_t c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int64_t j = 0; j < ncols; ++j) {
+        acc += read_elem(dz_k, dz_dtype, r * ncols + j) * read_elem(w_k, w_dtype, c * ncols + j);
+      }
+      for (int64_t j = 0; j < ncols; ++j) {
+        acc += read_elem(dz_v, dz_dtype, r * ncols + j) * read_elem(w_v, w_dtype, c * ncols + j);
+      }
+      dy[r * d + c] = acc;
+    }
+    double proj = 0.0;
+    for (int64_t c = 0; c < d; ++c) {
+      const double g = gain ? (double)gain[c] : 1.0;
+      proj += g * dy[r * d + c] * read_elem(x, x_dtype, r * d + c);
+    }
+    const double r3 = rr[r] * rr[r] * rr[r];
+    for (int64_t c = 0; c < d; ++c) {
+      const double g = gain ? (double)gain[c] : 1.0;
+      const double xv = read_elem(x, x_dtype, r * d + c);
+      dx[r * d + c] = g * dy[r * d + c] / rr[r] - xv / ((double)d * r3) * proj;
+    }
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t c = 0; c < d; ++c) {
+    for (int64_t j = 0; j < ncols; ++j) {
+      double ak = 0.0, av = 0.0;
+      for (int64_t r = 0; r < n; ++r) {
+        ak += y[r * d + c] * read_elem(dz_k, dz_dtype, r * ncols + j);
+        av += y[r * d + c] * read_elem(dz_v, dz_dtype, r * ncols + j);
+      }
+      dw_k[c * ncols + j] = ak;
+      dw_v[c * ncols + j] = av;
+    }
+    if (dgain) {
+      double ag = 0.0;
+      for (int64_t r = 0; r < n; ++r) ag += dy[r * d + c] * read_elem(x, x_dtype, r * d + c) / rr[r];
+      dgain[c] = ag;
+    }
+  }
+  free(y);
+  free(dy);
+  free(rr);
+  return 0;
 }

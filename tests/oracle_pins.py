@@ -426,6 +426,184 @@ def pin_rope_half_is_permuted_interleaved(orc):
     _close(half[..., perm], inter, 1e-14, 1e-14, "rotate-half vs interleaved")
 
 
+
+# ---------------------------------------------------------------------------
+# Backward (gradients of the attention and of the shared projection)
+# ---------------------------------------------------------------------------
+def _fd_grad(f, x, h):
+    """Central differences of the scalar f at x (fp64, every element)."""
+    g = np.empty_like(x)
+    flat, gf = x.reshape(-1), g.reshape(-1)
+    for i in range(flat.size):
+        old = flat[i]
+        flat[i] = old + h
+        fp = f()
+        flat[i] = old - h
+        fm = f()
+        flat[i] = old
+        gf[i] = (fp - fm) / (2 * h)
+    return g
+
+
+def pin_attn_bwd_finite_differences(orc):
+    """dq, dk, dv are the derivatives of L = sum(dO * O) (O from the pinned
+    forward): central differences on fp64 inputs, query rows at repeated and
+    out-of-order positions."""
+    rng = _rng(30)
+    pos = np.array([2, 4, 4, 0, 3])
+    q = rng.standard_normal((5, 4, 6))
+    k = rng.standard_normal((5, 2, 6))
+    v = rng.standard_normal((5, 2, 6))
+    dout = rng.standard_normal((5, 4, 6))
+    scale = 0.45
+    loss = lambda: float(np.sum(dout * orc.attention(q, pos, k, v, scale)))
+    dq, dk, dv = orc.attention_bwd(q, pos, k, v, dout, scale)
+    for name, got, arr in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _close(got, _fd_grad(loss, arr, 1e-6), 1e-6, 1e-8, f"attention {name} vs finite differences")
+
+
+def _torch_attn_grads(q, pos, k, v, dout, scale):
+    """fp64 autograd of masked softmax attention with repeat-interleaved K/V."""
+    qt = torch.tensor(as_f32(q).astype(np.float64), requires_grad=True)
+    kt = torch.tensor(as_f32(k).astype(np.float64), requires_grad=True)
+    vt = torch.tensor(as_f32(v).astype(np.float64), requires_grad=True)
+    hq, hkv = q.shape[1], k.shape[1]
+    kr = kt.repeat_interleave(hq // hkv, dim=1).permute(1, 0, 2)
+    vr = vt.repeat_interleave(hq // hkv, dim=1).permute(1, 0, 2)
+    qh = qt.permute(1, 0, 2)
+    mask = torch.arange(k.shape[0])[None, :] <= torch.as_tensor(np.asarray(pos))[:, None]
+    logits = torch.matmul(qh, kr.transpose(1, 2).contiguous()) * scale
+    o = torch.matmul(torch.softmax(logits.masked_fill(~mask, float("-inf")), dim=-1), vr).permute(1, 0, 2)
+    (o * torch.from_numpy(as_f32(dout).astype(np.float64))).sum().backward()
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+def pin_attn_bwd_library(orc):
+    """Against torch autograd (fp64) for a prefill block at q_start = 10 over
+    40 cache rows, GQA 6/2, bf16 and fp32 storage."""
+    rng = _rng(31)
+    for dtype in (F32, BF16):
+        q = store(rng.standard_normal((30, 6, 16)).astype(np.float32), dtype)
+        k = store(rng.standard_normal((40, 2, 16)).astype(np.float32), dtype)
+        v = store(rng.standard_normal((40, 2, 16)).astype(np.float32), dtype)
+        dout = store(rng.standard_normal((30, 6, 16)).astype(np.float32), dtype)
+        pos = 10 + np.arange(30)
+        got = orc.attention_bwd(q, pos, k, v, dout, 0.25)
+        want = _torch_attn_grads(q, pos, k, v, dout, 0.25)
+        for name, a, b in zip(("dq", "dk", "dv"), got, want):
+            _close(a, b, 1e-10, 1e-12, f"attention {name} vs torch autograd ({dtype})")
+
+
+def pin_attn_bwd_sums(orc):
+    """Softmax weights sum to one and their gradients sum to zero: over all
+    cache rows, sum_j dk_j = 0 and sum_j dv_j = sum of dO over the query rows
+    and the query heads of each KV head."""
+    rng = _rng(32)
+    q = rng.standard_normal((24, 6, 8))
+    k = rng.standard_normal((24, 3, 8))
+    v = rng.standard_normal((24, 3, 8))
+    dout = rng.standard_normal((24, 6, 8))
+    _, dk, dv = orc.attention_bwd(q, np.arange(24), k, v, dout, 0.5)
+    _close(dk.sum(axis=0), np.zeros((3, 8)), 0, 1e-12, "sum of dk over cache rows")
+    _close(dv.sum(axis=0), dout.reshape(24, 3, 2, 8).sum(axis=(0, 2)), 1e-12, 1e-12, "sum of dv over cache rows")
+
+
+def pin_attn_bwd_single_key(orc):
+    """A query at position 0 sees only row 0 (p = 1): dq = 0, its dv_0 is dO
+    and its dk_0 is 0, exactly."""
+    rng = _rng(33)
+    q = rng.standard_normal((1, 2, 8))
+    k = rng.standard_normal((3, 1, 8))
+    v = rng.standard_normal((3, 1, 8))
+    dout = rng.standard_normal((1, 2, 8))
+    dq, dk, dv = orc.attention_bwd(q, [0], k, v, dout, 0.7)
+    if np.any(dq != 0) or np.any(dk != 0) or np.any(dv[1:] != 0):
+        raise AssertionError("one visible key: dq, dk and the other rows' dv must be zero")
+    if not np.array_equal(dv[0, 0], dout[0, 0] + dout[0, 1]):
+        raise AssertionError("one visible key: dv_0 must be the sum of dO over the group")
+
+
+def pin_attn_bwd_accumulates(orc):
+    """dk, dv add up: two calls over disjoint query rows (or two layers)
+    equal one call over all of them."""
+    rng = _rng(34)
+    q = rng.standard_normal((12, 4, 8))
+    k = rng.standard_normal((12, 2, 8))
+    v = rng.standard_normal((12, 2, 8))
+    dout = rng.standard_normal((12, 4, 8))
+    pos = np.arange(12)
+    _, dk1, dv1 = orc.attention_bwd(q, pos, k, v, dout, 0.3)
+    _, dk2, dv2 = orc.attention_bwd(q[:5], pos[:5], k, v, dout[:5], 0.3)
+    orc.attention_bwd(q[5:], pos[5:], k, v, dout[5:], 0.3, dk2, dv2)
+    _close(dk2, dk1, 1e-12, 1e-13, "dk over two calls")
+    _close(dv2, dv1, 1e-12, 1e-13, "dv over two calls")
+
+
+def pin_project_bwd_finite_differences(orc):
+    """dx, dgain, dw_k, dw_v are the derivatives of L = sum(dz_k * K^) +
+    sum(dz_v * V^) (K^, V^ from the pinned forward projection); L is linear
+    in the gain and the weights, so a grid step gives exact differences
+    there."""
+    rng = _rng(35)
+    x = rng.standard_normal((3, 8))
+    w_k = rng.standard_normal((8, 4))
+    w_v = rng.standard_normal((8, 4))
+    gain = (1.0 + np.round(rng.uniform(-0.5, 0.5, 8) * 64) / 64).astype(np.float32)
+    dz_k = rng.standard_normal((3, 4))
+    dz_v = rng.standard_normal((3, 4))
+    eps = 1e-2
+    loss = lambda: float(np.sum(dz_k * orc.project(x, w_k, gain, eps)) + np.sum(dz_v * orc.project(x, w_v, gain, eps)))
+    dx, dw_k, dw_v, dgain = orc.project_bwd(x, w_k, w_v, dz_k, dz_v, gain, eps)
+    _close(dx, _fd_grad(loss, x, 1e-6), 1e-6, 1e-8, "project dx vs finite differences")
+    _close(dw_k, _fd_grad(loss, w_k, 1e-3), 1e-9, 1e-10, "project dw_k vs finite differences")
+    _close(dw_v, _fd_grad(loss, w_v, 1e-3), 1e-9, 1e-10, "project dw_v vs finite differences")
+    g = gain
+    fd = np.empty(8)
+    for c in range(8):
+        old = g[c]
+        g[c] = old + np.float32(2.0 ** -6)
+        lp = loss()
+        g[c] = old - np.float32(2.0 ** -6)
+        lm = loss()
+        g[c] = old
+        fd[c] = (lp - lm) / 2.0 ** -5
+    _close(dgain, fd, 1e-9, 1e-10, "project dgain vs finite differences")
+
+
+def pin_project_bwd_scale_invariance(orc):
+    """With eps = 0, RMSNorm(a x) = RMSNorm(x) for a > 0, so the gradient
+    with respect to a row is orthogonal to the row."""
+    rng = _rng(36)
+    x = rng.standard_normal((4, 16))
+    w = rng.standard_normal((16, 8))
+    gain = (1.0 + 0.25 * rng.standard_normal(16)).astype(np.float32)
+    dx, _, _, _ = orc.project_bwd(x, w, w, rng.standard_normal((4, 8)), rng.standard_normal((4, 8)), gain, 0.0)
+    _close(np.sum(dx * x, axis=1), np.zeros(4), 0, 1e-12, "x . dx with eps = 0")
+
+
+def pin_project_bwd_library(orc):
+    """Against torch autograd (fp64) of rms_norm followed by two matmuls, with
+    bf16 storage of x and the weights."""
+    rng = _rng(37)
+    n, d, nc = 10, 32, 12
+    x = store(rng.standard_normal((n, d)).astype(np.float32), BF16)
+    w_k = store((rng.standard_normal((d, nc)) / 4).astype(np.float32), BF16)
+    w_v = store((rng.standard_normal((d, nc)) / 4).astype(np.float32), BF16)
+    gain = (1.0 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    dz_k = rng.standard_normal((n, nc)).astype(np.float32)
+    dz_v = rng.standard_normal((n, nc)).astype(np.float32)
+    got = orc.project_bwd(x, w_k, w_v, dz_k, dz_v, gain, 1e-6)
+    xt = torch.tensor(as_f32(x).astype(np.float64), requires_grad=True)
+    gt = torch.tensor(gain.astype(np.float64), requires_grad=True)
+    wk = torch.tensor(as_f32(w_k).astype(np.float64), requires_grad=True)
+    wv = torch.tensor(as_f32(w_v).astype(np.float64), requires_grad=True)
+    y = torch.nn.functional.rms_norm(xt, (d,), gt, 1e-6)
+    loss = (torch.matmul(y, wk) * torch.from_numpy(dz_k.astype(np.float64))).sum() + \
+        (torch.matmul(y, wv) * torch.from_numpy(dz_v.astype(np.float64))).sum()
+    loss.backward()
+    for name, a, b in zip(("dx", "dw_k", "dw_v", "dgain"), got, (xt.grad, wk.grad, wv.grad, gt.grad)):
+        _close(a, b.numpy(), 1e-10, 1e-12, f"project {name} vs torch autograd")
+
 ALL_PINS = [
     pin_rmsnorm_constant_row,
     pin_rmsnorm_one_hot,
@@ -452,4 +630,12 @@ ALL_PINS = [
     pin_rope_composition,
     pin_rope_scores_depend_on_offset,
     pin_rope_half_is_permuted_interleaved,
+    pin_attn_bwd_finite_differences,
+    pin_attn_bwd_library,
+    pin_attn_bwd_sums,
+    pin_attn_bwd_single_key,
+    pin_attn_bwd_accumulates,
+    pin_project_bwd_finite_differences,
+    pin_project_bwd_scale_invariance,
+    pin_project_bwd_library,
 ]

@@ -35,6 +35,26 @@ MUTATIONS = {
     "rope_frequency_exponent": ("pow(theta, -2.0 * (double)i / (double)dh)", "pow(theta, -1.0 * (double)i / (double)dh)"),
     "rope_position_off_by_one": ("(double)pos[r] * freq", "(double)(pos[r] + 1) * freq"),
     "rope_pairing_swapped": ("const int j0 = interleaved ? 2 * i : i;", "const int j0 = interleaved ? i : 2 * i;"),
+    "bwd_softmax_jacobian_term_dropped": ("const double ds = (exp(x[j] - m) / l) * (dp[j] - d_term);",
+                                          "const double ds = (exp(x[j] - m) / l) * dp[j];"),
+    "bwd_dk_missing_scale": ("dk[kv_base + e] += scale * ds * read_elem(q, q_dtype, q_base + e);",
+                             "dk[kv_base + e] += ds * read_elem(q, q_dtype, q_base + e);"),
+    "bwd_dv_unnormalised": ("const double p = exp(scale * dot - stat_m[t]) / stat_l[t];",
+                            "const double p = exp(scale * dot - stat_m[t]);"),
+    "bwd_causal_boundary_exclusive": ("const int64_t j_end = pos[i] + 1 < j1 ? pos[i] + 1 : j1;",
+                                      "const int64_t j_end = pos[i] < j1 ? pos[i] : j1;"),
+    "bwd_gqa_modulo_mapping": ("for (int h = g * group; h < (g + 1) * group; ++h) {",
+                               "for (int h = g; h < hq; h += hkv) {"),
+    "bwd_dq_reads_v": ("dq[q_base + e] += ds * read_elem(k, kv_dtype, kv_base + e);",
+                       "dq[q_base + e] += ds * read_elem(v, kv_dtype, kv_base + e);"),
+    "bwd_rms_projection_term_dropped": ("dx[r * d + c] = g * dy[r * d + c] / rr[r] - xv / ((double)d * r3) * proj;",
+                                        "dx[r * d + c] = g * dy[r * d + c] / rr[r];"),
+    "bwd_rms_cubed_as_squared": ("const double r3 = rr[r] * rr[r] * rr[r];", "const double r3 = rr[r] * rr[r];"),
+    "bwd_dgain_missing_rms": ("ag += dy[r * d + c] * read_elem(x, x_dtype, r * d + c) / rr[r];",
+                              "ag += dy[r * d + c] * read_elem(x, x_dtype, r * d + c);"),
+    "bwd_dw_uses_unnormalised_x": ("ak += y[r * d + c] * read_elem(dz_k, dz_dtype, r * ncols + j);",
+                                   "ak += read_elem(x, x_dtype, r * d + c) * read_elem(dz_k, dz_dtype, r * ncols + j);"),
+    "bwd_dy_weight_transposed": ("read_elem(w_k, w_dtype, c * ncols + j);", "read_elem(w_k, w_dtype, j * d + c);"),
 }
 
 
