@@ -319,12 +319,12 @@ int oracle_attention_bwd(const void *q, int q_dtype, int64_t n_q, const int64_t 
     for (int64_t task = 0; task < n_tasks; ++task) {
       const int64_t i = task / hq;
       const int h = (int)(task % hq);
-      const int g = h / group;
-      const int64_t n_keys = pos[i] + 1;
-      if (n_keys > cap) {
+      const int kvh = h / group;
+      const int64_t n_vis = pos[i] + 1;
+      if (n_vis > cap) {
         free(x);
         free(dp);
-        cap = n_keys;
+        cap = n_vis;
         x = (double *)malloc((size_t)cap * sizeof(double));
         dp = (double *)malloc((size_t)cap * sizeof(double));
       }
@@ -335,28 +335,28 @@ int oracle_attention_bwd(const void *q, int q_dtype, int64_t n_q, const int64_t 
         continue;
       }
       const int64_t q_base = (i * hq + h) * (int64_t)dh;
-      for (int64_t j = 0; j < n_keys; ++j) {
-        const int64_t kv_base = (j * hkv + g) * (int64_t)dh;
-        double dot = 0.0, dpj = 0.0;
+      for (int64_t j = 0; j < n_vis; ++j) {
+        const int64_t kv_base = (j * hkv + kvh) * (int64_t)dh;
+        double qk = 0.0, dpj = 0.0;
         for (int e = 0; e < dh; ++e) {
-          dot += read_elem(q, q_dtype, q_base + e) * read_elem(k, kv_dtype, kv_base + e);
+          qk += read_elem(q, q_dtype, q_base + e) * read_elem(k, kv_dtype, kv_base + e);
           dpj += read_elem(dout, do_dtype, q_base + e) * read_elem(v, kv_dtype, kv_base + e);
         }
-        x[j] = scale * dot;
+        x[j] = scale * qk;
         dp[j] = dpj;
       }
       double m = x[0];
-      for (int64_t j = 1; j < n_keys; ++j) {
+      for (int64_t j = 1; j < n_vis; ++j) {
         if (x[j] > m) m = x[j];
       }
       double l = 0.0;
-      for (int64_t j = 0; j < n_keys; ++j) l += exp(x[j] - m);
+      for (int64_t j = 0; j < n_vis; ++j) l += exp(x[j] - m);
       double d_term = 0.0;
-      for (int64_t j = 0; j < n_keys; ++j) d_term += (exp(x[j] - m) / l) * dp[j];
+      for (int64_t j = 0; j < n_vis; ++j) d_term += (exp(x[j] - m) / l) * dp[j];
       for (int e = 0; e < dh; ++e) dq[q_base + e] = 0.0;
-      for (int64_t j = 0; j < n_keys; ++j) {
+      for (int64_t j = 0; j < n_vis; ++j) {
         const double ds = (exp(x[j] - m) / l) * (dp[j] - d_term);
-        const int64_t kv_base = (j * hkv + g) * (int64_t)dh;
+        const int64_t kv_base = (j * hkv + kvh) * (int64_t)dh;
         for (int e = 0; e < dh; ++e) dq[q_base + e] += ds * read_elem(k, kv_dtype, kv_base + e);
       }
       for (int e = 0; e < dh; ++e) dq[q_base + e] *= scale;
@@ -384,12 +384,12 @@ int oracle_attention_bwd(const void *q, int q_dtype, int64_t n_q, const int64_t 
         const int64_t q_base = t * (int64_t)dh;
         for (int64_t j = j0; j < j_end; ++j) {
           const int64_t kv_base = (j * hkv + g) * (int64_t)dh;
-          double dot = 0.0, dpj = 0.0;
+          double qk = 0.0, dpj = 0.0;
           for (int e = 0; e < dh; ++e) {
-            dot += read_elem(q, q_dtype, q_base + e) * read_elem(k, kv_dtype, kv_base + e);
+            qk += read_elem(q, q_dtype, q_base + e) * read_elem(k, kv_dtype, kv_base + e);
             dpj += read_elem(dout, do_dtype, q_base + e) * read_elem(v, kv_dtype, kv_base + e);
           }
-          const double p = exp(scale * dot - stat_m[t]) / stat_l[t];
+          const double p = exp(scale * qk - stat_m[t]) / stat_l[t];
           const double ds = p * (dpj - stat_d[t]);
           for (int e = 0; e < dh; ++e) {
             dv[kv_base + e] += p * read_elem(dout, do_dtype, q_base + e);
@@ -437,12 +437,12 @@ int oracle_project_bwd(const void *x, int x_dtype, int64_t n, int64_t d, const f
   oracle_rmsnorm(x, x_dtype, n, d, gain, eps, y);
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < n; ++r) {
-    double sum_sq = 0.0;
+    double ss = 0.0;
     for (int64_t c = 0; c < d; ++c) {
       const double xv = read_elem(x, x_dtype, r * d + c);
-      sum_sq += xv * xv;
+      ss += xv * xv;
     }
-    rr[r] = sqrt(sum_sq / (double)d + eps);
+    rr[r] = sqrt(ss / (double)d + eps);
     for (int64_t c = 0; c < d; ++c) {
       double acc = 0.0;
       for (int64_t j = 0; j < ncols; ++j) {

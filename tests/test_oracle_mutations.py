@@ -39,8 +39,8 @@ MUTATIONS = {
                                           "const double ds = (exp(x[j] - m) / l) * dp[j];"),
     "bwd_dk_missing_scale": ("dk[kv_base + e] += scale * ds * read_elem(q, q_dtype, q_base + e);",
                              "dk[kv_base + e] += ds * read_elem(q, q_dtype, q_base + e);"),
-    "bwd_dv_unnormalised": ("const double p = exp(scale * dot - stat_m[t]) / stat_l[t];",
-                            "const double p = exp(scale * dot - stat_m[t]);"),
+    "bwd_dv_unnormalised": ("const double p = exp(scale * qk - stat_m[t]) / stat_l[t];",
+                            "const double p = exp(scale * qk - stat_m[t]);"),
     "bwd_causal_boundary_exclusive": ("const int64_t j_end = pos[i] + 1 < j1 ? pos[i] + 1 : j1;",
                                       "const int64_t j_end = pos[i] < j1 ? pos[i] : j1;"),
     "bwd_gqa_modulo_mapping": ("for (int h = g * group; h < (g + 1) * group; ++h) {",
