@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define YOCO_ABI_VERSION 2
+#define YOCO_ABI_VERSION 3
 #define YOCO_MAX_SEQ 256
 
 /* Storage types. */
@@ -66,7 +66,7 @@ typedef enum yoco_status {
   YOCO_ERR_BAD_SHAPE = 2,    /* unsupported head_dim / group size / counts */
   YOCO_ERR_BAD_DTYPE = 3,    /* unsupported or mismatched storage type */
   YOCO_ERR_OUT_OF_RANGE = 4, /* rows or positions outside the cache */
-  YOCO_ERR_WORKSPACE = 5,    /* decode workspace too small */
+  YOCO_ERR_WORKSPACE = 5,    /* workspace too small */
   YOCO_ERR_HIP = 6,          /* HIP runtime error, or the device is not gfx950 */
   YOCO_ERR_BAD_VALUE = 7     /* bad scalar argument (eps, scale, split rows) */
 } yoco_status;
@@ -217,6 +217,42 @@ yoco_status yoco_cross_attn_prefill(const void *q, int32_t q_dtype, int64_t q_st
                                     int32_t n_q_heads, const yoco_kv_cache *cache, int32_t seq,
                                     float softmax_scale, void *o, int32_t o_dtype, float *lse,
                                     void *stream);
+
+/* Bytes of device workspace yoco_cross_attn_prefill_bwd needs for t query
+ * rows of n_q_heads heads: 2 * t * n_q_heads floats.  Errors: NULL_POINTER,
+ * BAD_SHAPE (t < 0, n_q_heads <= 0). */
+yoco_status yoco_cross_attn_prefill_bwd_workspace(int64_t t, int32_t n_q_heads, size_t *bytes);
+
+/* Backward of yoco_cross_attn_prefill for one cross layer (training): the
+ * gradient of [Notes] Eq. 3 with respect to the query and the shared K^/V^.
+ * [Deep] s.2.2: all cross layers read the same K^/V^, so their gradients
+ * sum over the layers; this call ADDS its layer's share to d_k and d_v
+ * (clear them before the first layer).
+ *
+ * For query row i at position p = q_start + i, head h, KV head g = h / G,
+ * with P_j = exp(softmax_scale <q, k_j> - lse) over rows j = 0..p and the
+ * upstream gradient dO of o:
+ *   dP_j = <dO, v_j>,  D = <dO, o>,  dS_j = P_j (dP_j - D)
+ *   d_q[i][h] = softmax_scale * sum_j dS_j k_j
+ *   d_k[j][g] += softmax_scale * dS_j q,   d_v[j][g] += P_j dO.
+ * q, d_o: [t][n_q_heads][head_dim] bf16; o: the forward's output, o_dtype
+ * (f32 or bf16); lse: [t][n_q_heads] fp32, the forward's lse (natural log);
+ * the cache must be bf16 and hold rows 0..q_start+t-1 of `seq`.
+ * d_q: [t][n_q_heads][head_dim] fp32, written.  d_k, d_v: [q_start+t][H_kv]
+ * [head_dim] fp32 (device), added to.  workspace: device memory of at least
+ * yoco_cross_attn_prefill_bwd_workspace bytes (per-row statistics; its
+ * contents on entry do not matter).
+ * P and dS are rounded to bf16 for the MFMA products, with fp32
+ * accumulation.  The result is bitwise reproducible (no atomics).  Calls on
+ * one stream that share d_k/d_v run in order; t == 0 is a no-op.
+ * Errors: NULL_POINTER; BAD_SHAPE (heads, seq); BAD_DTYPE (cache not bf16,
+ * o dtype); OUT_OF_RANGE (q_start < 0, t < 0, q_start + t > len_host[seq]);
+ * BAD_VALUE (scale); WORKSPACE (too small). */
+yoco_status yoco_cross_attn_prefill_bwd(const void *q, const void *o, int32_t o_dtype, const void *d_o,
+                                        const float *lse, int64_t q_start, int64_t t, int32_t n_q_heads,
+                                        const yoco_kv_cache *cache, int32_t seq, float softmax_scale,
+                                        float *d_q, float *d_k, float *d_v, void *workspace,
+                                        size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace yoco_cross_attn_decode needs for this cache,
  * query head count and split size, valid for any len_host up to

@@ -27,7 +27,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = _lib()
     names = _declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     for name in names:
         assert hasattr(lib, name), f"{name} declared in yoco.h but not exported"
 
@@ -242,3 +242,42 @@ def test_rope_entry_points_reject_bad_theta_and_positions():
     assert L.yoco_q_project_rope(FAKE, 1, 257, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 1, big, 0, 1e4, None) == \
         _status("YOCO_ERR_BAD_SHAPE")
     assert L.yoco_q_project_rope(FAKE, 1, 0, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 1, None, 0, 1e4, None) == 0
+
+
+def _bwd(c, **kw):
+    args = dict(q=FAKE, o=FAKE, o_dt=0, d_o=FAKE, lse=FAKE, q_start=0, t=8, hq=4, seq=0, scale=0.125,
+                d_q=FAKE, d_k=FAKE, d_v=FAKE, ws=FAKE, ws_bytes=1 << 20)
+    args.update(kw)
+    return _lib().yoco_cross_attn_prefill_bwd(args["q"], args["o"], args["o_dt"], args["d_o"], args["lse"],
+                                              args["q_start"], args["t"], args["hq"], ctypes.byref(c), args["seq"],
+                                              args["scale"], args["d_q"], args["d_k"], args["d_v"], args["ws"],
+                                              args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d_o=None), "YOCO_ERR_NULL_POINTER"),
+    (dict(lse=None), "YOCO_ERR_NULL_POINTER"),
+    (dict(d_k=None), "YOCO_ERR_NULL_POINTER"),
+    (dict(ws=None), "YOCO_ERR_NULL_POINTER"),
+    (dict(hq=3), "YOCO_ERR_BAD_SHAPE"),
+    (dict(seq=2), "YOCO_ERR_BAD_SHAPE"),
+    (dict(o_dt=7), "YOCO_ERR_BAD_DTYPE"),
+    (dict(scale=0.0), "YOCO_ERR_BAD_VALUE"),
+    (dict(q_start=5, t=8), "YOCO_ERR_OUT_OF_RANGE"),
+    (dict(t=-1), "YOCO_ERR_OUT_OF_RANGE"),
+    (dict(ws_bytes=2 * 8 * 4 * 4 - 1), "YOCO_ERR_WORKSPACE"),
+])
+def test_prefill_bwd_rejects(kw, status):
+    c, lens = _cache()
+    assert _bwd(c, **kw) == _status(status)
+    assert len(_lib().yoco_last_error()) > 0
+
+
+def test_prefill_bwd_needs_bf16_cache_and_sizes_workspace():
+    c, _ = _cache(dtype=0)
+    assert _bwd(c) == _status("YOCO_ERR_BAD_DTYPE")
+    c, _ = _cache()
+    assert _bwd(c, t=0, ws_bytes=0) == 0
+    out = ctypes.c_size_t(0)
+    assert _lib().yoco_cross_attn_prefill_bwd_workspace(1000, 24, ctypes.byref(out)) == 0
+    assert out.value == 2 * 1000 * 24 * 4

@@ -332,6 +332,14 @@ def make_prefill(n: int = 32768, n_q_heads: int = 24, n_kv_heads: int = 8,
                        head_dim=head_dim, dtype=dtype, peaked_rows=peaked)
 
 
+def make_grad(t: int, n_q_heads: int = 24, head_dim: int = 128, dtype: str = BF16, seed: int = 0,
+              layers: int = 1) -> list:
+    """Upstream gradients dO of the attention output for ``layers`` cross
+    layers: stream 10 + l, ``[t, H_q, d_h]`` N(0,1) each (a stand-in for the
+    gradient a loss would send back; no trained model here)."""
+    return [store(_normal(seed, 10 + l, (t, n_q_heads, head_dim)), dtype) for l in range(layers)]
+
+
 # ---------------------------------------------------------------------------
 # Projection workload at 3B-like widths.
 # ---------------------------------------------------------------------------

@@ -188,6 +188,49 @@ def cross_attn_prefill(q: torch.Tensor, cache: KVCache, seq: int = 0, q_start: i
     return (out, lse) if want_lse else out
 
 
+def prefill_bwd_workspace_bytes(t: int, n_q_heads: int) -> int:
+    out = ctypes.c_size_t(0)
+    check(lib().yoco_cross_attn_prefill_bwd_workspace(t, n_q_heads, ctypes.byref(out)))
+    return int(out.value)
+
+
+def cross_attn_prefill_bwd(q: torch.Tensor, o: torch.Tensor, d_o: torch.Tensor, lse: torch.Tensor,
+                           cache: KVCache, seq: int = 0, q_start: int = 0,
+                           softmax_scale: Optional[float] = None, d_q: Optional[torch.Tensor] = None,
+                           d_k: Optional[torch.Tensor] = None, d_v: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, stream=None):
+    """Backward of ``cross_attn_prefill`` for one layer: returns (d_q, d_k,
+    d_v).  d_k, d_v ``[q_start+t, H_kv, d_h]`` fp32 are ADDED to (zeros when
+    not given), so passing the same tensors for every cross layer sums the
+    layers' shares of the shared cache's gradient."""
+    _on_device(q, o, d_o, lse)
+    t, hq, dh = q.shape
+    scale = 1.0 / math.sqrt(dh) if softmax_scale is None else softmax_scale
+    rows = q_start + t
+    if d_q is None:
+        d_q = torch.empty((t, hq, dh), dtype=torch.float32, device=q.device)
+    if d_k is None:
+        d_k = torch.zeros((rows, cache.n_kv_heads, dh), dtype=torch.float32, device=q.device)
+    if d_v is None:
+        d_v = torch.zeros((rows, cache.n_kv_heads, dh), dtype=torch.float32, device=q.device)
+    for name, x in (("d_q", d_q), ("d_k", d_k), ("d_v", d_v)):
+        if x.dtype != torch.float32 or not x.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous float32 tensor")
+    if d_k.shape != (rows, cache.n_kv_heads, dh) or d_v.shape != d_k.shape or d_q.shape != (t, hq, dh):
+        raise ValueError("d_q must be [t, H_q, d_h]; d_k, d_v [q_start + t, H_kv, d_h]")
+    if lse.dtype != torch.float32 or lse.shape != (t, hq):
+        raise ValueError("lse must be the forward's float32 [t, H_q]")
+    nbytes = prefill_bwd_workspace_bytes(t, hq)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    s = cache.struct()
+    check(lib().yoco_cross_attn_prefill_bwd(_ptr(q), _ptr(o), _dt(o), _ptr(d_o), _ptr(lse), q_start, t, hq,
+                                            ctypes.byref(s), seq, scale, _ptr(d_q), _ptr(d_k), _ptr(d_v),
+                                            _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                            _stream(stream)))
+    return d_q, d_k, d_v
+
+
 def decode_workspace_bytes(cache: KVCache, n_q_heads: int, rows_per_split: int = 0) -> int:
     out = ctypes.c_size_t(0)
     s = cache.struct()

@@ -72,6 +72,11 @@ def _declare(lib):
     lib.yoco_q_project_rope.argtypes = [vp, i32, i64, i32, vp, f32, vp, i32, i32, i32, vp, i32, vp, i64, f64, vp]
     lib.yoco_cross_attn_prefill.restype = st
     lib.yoco_cross_attn_prefill.argtypes = [vp, i32, i64, i64, i32, cp, i32, f32, vp, i32, vp, vp]
+    lib.yoco_cross_attn_prefill_bwd_workspace.restype = st
+    lib.yoco_cross_attn_prefill_bwd_workspace.argtypes = [i64, i32, ctypes.POINTER(sz)]
+    lib.yoco_cross_attn_prefill_bwd.restype = st
+    lib.yoco_cross_attn_prefill_bwd.argtypes = [vp, vp, i32, vp, vp, i64, i64, i32, cp, i32, f32, vp, vp, vp,
+                                                vp, sz, vp]
     lib.yoco_cross_attn_decode_workspace.restype = st
     lib.yoco_cross_attn_decode_workspace.argtypes = [cp, i32, i64, ctypes.POINTER(sz)]
     lib.yoco_cross_attn_decode.restype = st

@@ -508,4 +508,64 @@ yoco_status yoco_cross_attn_decode(const void *q, int32_t q_dtype, int32_t n_q_h
                   "cross_attn_decode");
 }
 
+
+yoco_status yoco_cross_attn_prefill_bwd_workspace(int64_t t, int32_t n_q_heads, size_t *bytes) {
+  if (bytes == nullptr) return fail(YOCO_ERR_NULL_POINTER, "bytes is NULL");
+  if (t < 0 || n_q_heads <= 0) return fail(YOCO_ERR_BAD_SHAPE, "t %lld, n_q_heads %d", (long long)t, n_q_heads);
+  *bytes = static_cast<size_t>(2 * t * n_q_heads) * sizeof(float);
+  return ok();
+}
+
+yoco_status yoco_cross_attn_prefill_bwd(const void *q, const void *o, int32_t o_dtype, const void *d_o,
+                                        const float *lse, int64_t q_start, int64_t t, int32_t n_q_heads,
+                                        const yoco_kv_cache *cache, int32_t seq, float softmax_scale, float *d_q,
+                                        float *d_k, float *d_v, void *workspace, size_t workspace_bytes,
+                                        void *stream) {
+  yoco_status st = check_cache(cache);
+  if (st != YOCO_OK) return st;
+  if (q == nullptr || o == nullptr || d_o == nullptr || lse == nullptr || d_q == nullptr || d_k == nullptr ||
+      d_v == nullptr || workspace == nullptr)
+    return fail(YOCO_ERR_NULL_POINTER, "q, o, d_o, lse, d_q, d_k, d_v or workspace is NULL");
+  if ((st = check_heads(n_q_heads, cache->n_kv_heads)) != YOCO_OK) return st;
+  if (seq < 0 || seq >= cache->n_seq) return fail(YOCO_ERR_BAD_SHAPE, "seq %d outside [0, %d)", seq, cache->n_seq);
+  if (cache->dtype != YOCO_DT_BF16)
+    return fail(YOCO_ERR_BAD_DTYPE, "the backward runs on bf16 caches (cache dtype %d)", cache->dtype);
+  if (!dtype_ok(o_dtype)) return fail(YOCO_ERR_BAD_DTYPE, "o dtype %d unknown", o_dtype);
+  if ((st = check_scale(softmax_scale)) != YOCO_OK) return st;
+  const int64_t len = cache->len_host[seq];
+  if (q_start < 0 || t < 0 || len > cache->seq_capacity || q_start > len - t)
+    return fail(YOCO_ERR_OUT_OF_RANGE, "query rows at positions [%lld, %lld) exceed cache length %lld",
+                (long long)q_start, (long long)(q_start + t), (long long)len);
+  const size_t need = static_cast<size_t>(2 * t * n_q_heads) * sizeof(float);
+  if (workspace_bytes < need)
+    return fail(YOCO_ERR_WORKSPACE, "workspace %zu bytes < %zu (yoco_cross_attn_prefill_bwd_workspace)",
+                workspace_bytes, need);
+  if (t == 0) return ok();
+  if ((st = check_device()) != YOCO_OK) return st;
+
+  const int64_t slab = static_cast<int64_t>(seq) * cache->seq_capacity * cache->n_kv_heads * cache->head_dim;
+  yoco::BwdArgs a{};
+  a.q = q;
+  a.o = o;
+  a.d_o = d_o;
+  a.lse = lse;
+  a.k = static_cast<const char *>(cache->k) + slab * 2;
+  a.v = static_cast<const char *>(cache->v) + slab * 2;
+  a.d_q = d_q;
+  a.d_k = d_k;
+  a.d_v = d_v;
+  a.ws_d = static_cast<float *>(workspace);
+  a.ws_lse2 = static_cast<float *>(workspace) + t * n_q_heads;
+  a.q_start = q_start;
+  a.t = t;
+  a.kv_len = q_start + t;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = cache->n_kv_heads;
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.o_bf16 = (o_dtype == YOCO_DT_BF16) ? 1 : 0;
+  return launched(yoco::launch_prefill_bwd(a, cache->head_dim, static_cast<hipStream_t>(stream)),
+                  "cross_attn_prefill_bwd");
+}
+
 }  // extern "C"

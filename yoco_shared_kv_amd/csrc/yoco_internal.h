@@ -72,4 +72,29 @@ struct PrefillArgs {
 
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, int head_dim, hipStream_t s);
 
+// Backward of the prefill (bf16 operands, fp32 gradients).
+struct BwdArgs {
+  const void *q;      // [t][n_q_heads][head_dim] bf16
+  const void *o;      // [t][n_q_heads][head_dim] forward output, fp32 or bf16
+  const void *d_o;    // [t][n_q_heads][head_dim] bf16
+  const float *lse;   // [t][n_q_heads] natural log, from the forward
+  const void *k;      // sequence slab base: [capacity][H_kv][d_h] bf16
+  const void *v;
+  float *d_q;         // [t][n_q_heads][head_dim], written
+  float *d_k;         // [kv_len][H_kv][d_h], added to
+  float *d_v;
+  float *ws_d;        // [n_q_heads][t] workspace: <dO, o>
+  float *ws_lse2;     // [n_q_heads][t] workspace: lse * log2(e)
+  int64_t q_start;
+  int64_t t;
+  int64_t kv_len;     // q_start + t: the cache rows the block's rows see
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  float scale;
+  float scale_log2;
+  int32_t o_bf16;
+};
+
+hipError_t launch_prefill_bwd(const BwdArgs &a, int head_dim, hipStream_t s);
+
 }  // namespace yoco
