@@ -279,6 +279,49 @@ def bench_prefill(args, torch, y, W):
                 frac=tflops / BF16_DENSE_PEAK_TFLOPS)
 
 
+def bench_backward(args, torch, y, W):
+    """Backward of one cross layer's causal prefill at N=32768 (bf16 MFMA):
+    dQ written, dK/dV added into fp32 buffers shared by the layers."""
+    cfg = W.PREFILL_32K
+    n, hq, hkv, dh = cfg["n"], cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    log(f"generating backward workload N={n}")
+    c = W.make_prefill(**cfg)
+    cache = y.KVCache(1, n, hkv, dh, torch.bfloat16)
+    cache.k[0] = to_dev(c.k, torch)
+    cache.v[0] = to_dev(c.v, torch)
+    cache.len[0] = n
+    q = to_dev(c.q, torch)
+    d_o = to_dev(W.make_grad(n, hq, dh, seed=0)[0], torch)
+    stream = torch.cuda.current_stream()
+    o, lse = y.cross_attn_prefill(q, cache, want_lse=True, stream=stream)
+    d_q = torch.empty((n, hq, dh), dtype=torch.float32, device="cuda")
+    d_k = torch.zeros((n, hkv, dh), dtype=torch.float32, device="cuda")
+    d_v = torch.zeros_like(d_k)
+    ws = torch.empty(y.prefill_bwd_workspace_bytes(n, hq), dtype=torch.uint8, device="cuda")
+
+    def bwd():
+        y.cross_attn_prefill_bwd(q, o, d_o, lse, cache, d_q=d_q, d_k=d_k, d_v=d_v, workspace=ws, stream=stream)
+
+    for _ in range(3):
+        bwd()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.prefill_reps)]
+    for s_ev, e_ev in evs:
+        s_ev.record(stream)
+        bwd()
+        e_ev.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    avg = float(np.mean(ms))
+    # Five products per visible (row, key) pair: S (recomputed), dP, dV, dK
+    # and dQ, 2 * d_h flops each; 2.5 times the forward.
+    flops = 5.0 * dh * hq * n * (n + 1)
+    tflops = flops / (avg * 1e-3) / 1e12
+    log(f"prefill backward {avg:.3f} ms (p50 {pct(ms, 50):.3f}) -> {tflops:.1f} TFLOP/s")
+    return dict(ms=avg, ms_p10=pct(ms, 10), ms_p50=pct(ms, 50), ms_p90=pct(ms, 90), tflops=tflops, flops=flops)
+
+
 def bench_project(args, torch, y, W):
     """K^/V^ projection of a 32768-row prompt at 3B-like widths (3072 -> 2 x
     1024, bf16, matrix cores), with unit gain, with an fp32 gain, and with an
@@ -383,6 +426,7 @@ def main():
     dec = bench_decode(args, torch, y, W)
     pre = None if args.no_prefill else bench_prefill(args, torch, y, W)
     proj = None if args.no_prefill else bench_project(args, torch, y, W)
+    bwd = None if args.no_prefill else bench_backward(args, torch, y, W)
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec, W)
     # The committed counters were taken on the 128K workload.
     traffic, why = counter_traffic() if args.workload == "decode128k" else (None, "counters cover decode128k only")
@@ -466,6 +510,17 @@ def main():
             "without_early_exit_ms": None if pre is None else round(13 * pre["ms"], 3),
             "without_early_exit": "13 causal prefill launches over the whole prompt (the cross layers "
                                   "run for every position)",
+        }
+    if bwd is not None:
+        result["prefill_backward"] = {
+            "workload": "backward of one cross layer's causal prefill N=32768, H_q=24, H_kv=8, d_h=128, bf16 "
+                        "MFMA: dQ written, dK/dV added (fp32)",
+            "ms": round(bwd["ms"], 3),
+            "ms_p10_p50_p90": [round(bwd["ms_p10"], 3), round(bwd["ms_p50"], 3), round(bwd["ms_p90"], 3)],
+            "roofline": {"bound": "mfma", "achieved": round(bwd["tflops"], 1), "peak": BF16_DENSE_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(bwd["tflops"] / BF16_DENSE_PEAK_TFLOPS, 4),
+                         "flops_per_launch": bwd["flops"],
+                         "flops_convention": "5 products x 2 d_h per visible (row, key) pair"},
         }
     print(json.dumps(result), flush=True)
 
