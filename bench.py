@@ -181,6 +181,14 @@ def bench_decode(args, torch, y, W):
         flush_dst = torch.empty_like(flush_src)
     torch.cuda.synchronize()
 
+    # Three passes over the same step, each of args.steps steps:
+    #   plain:     no event inside the steps; the wall clock and one event pair
+    #              around the whole pass give ms_per_step (the headline);
+    #   per step:  one event pair around each step (its spread);
+    #   per launch: one event pair around each decode launch (the kernel's own
+    #              duration for the roofline).  Every recorded event sits
+    #              between two kernels on the stream and widens that gap, so
+    #              the instrumented passes are not used for the headline.
     n_ev = layers * args.steps
     ev_start = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     ev_end = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
@@ -188,36 +196,47 @@ def bench_decode(args, torch, y, W):
     cold_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(layers * args.cold_steps)]
 
-    def step(i, record, cold=None):
+    def step(i, record_step=None, record_launch=None, cold=None):
         cache.len[:] = lens - 1
-        if record is not None:
-            step_ev[record][0].record(stream)
+        if record_step is not None:
+            step_ev[record_step][0].record(stream)
         y.kv_append(cache, m_rows[i * n_seq:(i + 1) * n_seq], w_k, w_v, gain, 1e-6, stream=stream)
         for l in range(layers):
             if cold is not None:
                 flush_dst.copy_(flush_src)
                 cold_ev[cold * layers + l][0].record(stream)
-            if record is not None:
-                ev_start[record * layers + l].record(stream)
+            if record_launch is not None:
+                ev_start[record_launch * layers + l].record(stream)
             y.cross_attn_decode(q_layers[l], cache, workspace=ws, out=outs[l], stream=stream)
-            if record is not None:
-                ev_end[record * layers + l].record(stream)
+            if record_launch is not None:
+                ev_end[record_launch * layers + l].record(stream)
             if cold is not None:
                 cold_ev[cold * layers + l][1].record(stream)
-        if record is not None:
-            step_ev[record][1].record(stream)
+        if record_step is not None:
+            step_ev[record_step][1].record(stream)
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
-        step(i, None)
+        step(i)
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
+    pass_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     t0 = time.perf_counter()
+    pass_ev[0].record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, i)
+        step(args.warmup + i)
+    pass_ev[1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    gpu_ms_per_step = pass_ev[0].elapsed_time(pass_ev[1]) / args.steps
+    log(f"per-step and per-launch passes, {args.steps} steps each")
+    for i in range(args.steps):
+        step(args.warmup + i, record_step=i)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(args.warmup + i, record_launch=i)
+    torch.cuda.synchronize()
     kern_ms = [s_.elapsed_time(e_) for s_, e_ in zip(ev_start, ev_end)]
     step_ms = [s_.elapsed_time(e_) for s_, e_ in step_ev]
     kern_avg_ms = float(np.mean(kern_ms))
@@ -225,12 +244,12 @@ def bench_decode(args, torch, y, W):
     achieved_gbps = bytes_per_launch / (kern_avg_ms * 1e-3) / 1e9
     us_per_token_layer = ms_per_step * 1e3 / layers
     step_bytes = layers * bytes_per_launch + n_seq * 2 * d_model * hkv * dh * 2
-    log(f"decode step {ms_per_step:.3f} ms; {us_per_token_layer:.2f} us/token/layer; "
-        f"decode kernel avg {kern_avg_ms * 1e3:.2f} us -> {achieved_gbps:.0f} GB/s")
+    log(f"decode step {ms_per_step:.3f} ms (events: {gpu_ms_per_step:.3f}); {us_per_token_layer:.2f} "
+        f"us/token/layer; decode kernel avg {kern_avg_ms * 1e3:.2f} us -> {achieved_gbps:.0f} GB/s")
     cold = None
     if args.cold_steps > 0:
         for i in range(args.cold_steps):
-            step(args.warmup + args.steps + i, None, cold=i)
+            step(args.warmup + args.steps + i, cold=i)
         torch.cuda.synchronize()
         cold_ms = [s_.elapsed_time(e_) for s_, e_ in cold_ev]
         cold = dict(avg_launch_us=float(np.mean(cold_ms)) * 1e3, p50_launch_us=pct(cold_ms, 50) * 1e3,
@@ -238,6 +257,7 @@ def bench_decode(args, torch, y, W):
         log(f"cold decode (512 MiB flush before each launch): avg {cold['avg_launch_us']:.2f} us "
             f"-> {cold['GBps']:.0f} GB/s")
     return dict(case=case, cache=cache, q_layers=q_layers, outs=outs, ms_per_step=ms_per_step,
+                gpu_ms_per_step=gpu_ms_per_step,
                 us_per_token_layer=us_per_token_layer, kern_avg_us=kern_avg_ms * 1e3,
                 kern_p10_us=pct(kern_ms, 10) * 1e3, kern_p50_us=pct(kern_ms, 50) * 1e3,
                 kern_p90_us=pct(kern_ms, 90) * 1e3,
@@ -391,6 +411,49 @@ def bench_project(args, torch, y, W):
     return res
 
 
+def bench_project_bwd(args, torch, y, W):
+    """Backward of the shared K^/V^ projection of a 32768-row prompt at 3B
+    widths (bf16 M and weights, fp32 gain, fp32 upstream gradients as the
+    attention backward leaves them): d_M written, d_W_K, d_W_V, d_gain added."""
+    cfg = W.PROJECT_3B
+    log(f"generating projection backward workload N={cfg['n']}")
+    pc = W.make_project(**cfg, unit_gain=False)
+    n, d = pc.m.shape
+    ncols = pc.n_kv_heads * pc.head_dim
+    dz_k, dz_v = W.make_proj_grad(n, ncols, 2, dtype=W.F32, seed=0)
+    m, w_k, w_v = to_dev(pc.m, torch), to_dev(pc.w_k, torch), to_dev(pc.w_v, torch)
+    dzk, dzv = to_dev(dz_k, torch), to_dev(dz_v, torch)
+    gain = torch.from_numpy(pc.gain).cuda()
+    d_m = torch.empty((n, d), dtype=torch.float32, device="cuda")
+    d_wk = torch.zeros((d, ncols), dtype=torch.float32, device="cuda")
+    d_wv = torch.zeros_like(d_wk)
+    d_g = torch.zeros(d, dtype=torch.float32, device="cuda")
+    ws = torch.empty(y.project_bwd_workspace_bytes(n, d, ncols, 2), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def bwd():
+        y.kv_project_bwd(m, w_k, w_v, dzk, dzv, pc.n_kv_heads, pc.head_dim, gain=gain, eps=pc.eps, d_m=d_m,
+                         d_w_k=d_wk, d_w_v=d_wv, d_gain=d_g, workspace=ws, stream=stream)
+
+    for _ in range(3):
+        bwd()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.prefill_reps)]
+    for s_ev, e_ev in evs:
+        s_ev.record(stream)
+        bwd()
+        e_ev.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    avg = float(np.mean(ms))
+    # Two products of 2 * n * d * (2 * ncols) flops each: dy = dZ W^T and dW = y^T dZ.
+    flops = 2.0 * 2.0 * n * d * 2 * ncols
+    tflops = flops / (avg * 1e-3) / 1e12
+    log(f"kv_project backward {avg:.3f} ms (p50 {pct(ms, 50):.3f}) -> {tflops:.1f} TFLOP/s")
+    return dict(ms=avg, ms_p10=pct(ms, 10), ms_p50=pct(ms, 50), ms_p90=pct(ms, 90), tflops=tflops, flops=flops)
+
+
 def cpu_baseline(dec, W):
     import oracle
     case = dec["case"]
@@ -427,6 +490,7 @@ def main():
     pre = None if args.no_prefill else bench_prefill(args, torch, y, W)
     proj = None if args.no_prefill else bench_project(args, torch, y, W)
     bwd = None if args.no_prefill else bench_backward(args, torch, y, W)
+    pbwd = None if args.no_prefill else bench_project_bwd(args, torch, y, W)
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec, W)
     # The committed counters were taken on the 128K workload.
     traffic, why = counter_traffic() if args.workload == "decode128k" else (None, "counters cover decode128k only")
@@ -454,6 +518,7 @@ def main():
             "n_rows": int(dec["lens"].sum()), "layers": 13, "n_q_heads": 24, "n_kv_heads": 8, "head_dim": 128,
             "d_model": 3072, "batch": dec["n_seq"],
         },
+        "gpu_ms_per_step": round(dec["gpu_ms_per_step"], 4),
         "step_ms_p10_p50_p90": [round(dec["step_p10_ms"], 4), round(dec["step_p50_ms"], 4),
                                 round(dec["step_p90_ms"], 4)],
         "decode_hbm_GBps": round(dec["achieved_gbps"], 1),
@@ -521,6 +586,17 @@ def main():
                          "unit": "TFLOP/s", "frac": round(bwd["tflops"] / BF16_DENSE_PEAK_TFLOPS, 4),
                          "flops_per_launch": bwd["flops"],
                          "flops_convention": "5 products x 2 d_h per visible (row, key) pair"},
+        }
+    if pbwd is not None:
+        result["kv_project_backward"] = {
+            "workload": "backward of the K^/V^ projection of 32768 rows, 3072 -> 2 x 1024, bf16 MFMA (y and dz "
+                        "rounded to bf16), fp32 gain: d_M written, d_W_K, d_W_V, d_gain added (fp32)",
+            "ms": round(pbwd["ms"], 4),
+            "ms_p10_p50_p90": [round(pbwd["ms_p10"], 4), round(pbwd["ms_p50"], 4), round(pbwd["ms_p90"], 4)],
+            "roofline": {"bound": "mfma", "achieved": round(pbwd["tflops"], 1), "peak": BF16_DENSE_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(pbwd["tflops"] / BF16_DENSE_PEAK_TFLOPS, 4),
+                         "flops_per_launch": pbwd["flops"],
+                         "flops_convention": "dy = dZ W^T and dW = y^T dZ, 2 n d (2 ncols) flops each"},
         }
     print(json.dumps(result), flush=True)
 

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define YOCO_ABI_VERSION 3
+#define YOCO_ABI_VERSION 4
 #define YOCO_MAX_SEQ 256
 
 /* Storage types. */
@@ -253,6 +253,59 @@ yoco_status yoco_cross_attn_prefill_bwd(const void *q, const void *o, int32_t o_
                                         const yoco_kv_cache *cache, int32_t seq, float softmax_scale,
                                         float *d_q, float *d_k, float *d_v, void *workspace,
                                         size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace yoco_kv_project_bwd (n_out = 2, n_cols =
+ * n_kv_heads * head_dim) or yoco_q_project_bwd (n_out = 1, n_cols =
+ * n_q_heads * head_dim) needs for n input rows of width d_model.  The size
+ * depends on the shapes only.  Errors: NULL_POINTER; BAD_SHAPE (n < 0,
+ * d_model outside [1, 16384], n_cols < 1, n_out not 1 or 2). */
+yoco_status yoco_project_bwd_workspace(int64_t n, int32_t d_model, int32_t n_cols, int32_t n_out,
+                                       size_t *bytes);
+
+/* Backward of yoco_kv_project (training): the gradient of [Notes] Eq. 2,
+ * K^ = RMSNorm(M) W_K and V^ = RMSNorm(M) W_V with one norm shared by both.
+ * With y = m g / r, r = sqrt(mean_c m_c^2 + eps) per row, and the upstream
+ * gradients dz_k, dz_v of the row's K^ and V^ columns (for a shared cache:
+ * the sums over the cross layers that yoco_cross_attn_prefill_bwd adds up):
+ *   dy[c]     = sum_j dz_k[j] W_K[c][j] + sum_j dz_v[j] W_V[c][j]
+ *   d_m[c]    = g[c] dy[c] / r - m[c] / (d_model r^3) sum_c' g[c'] dy[c'] m[c']
+ *   d_w_k    += sum over rows of y^T dz_k   (likewise d_w_v)
+ *   d_gain[c] += sum over rows of dy[c] m[c] / r
+ * m: [n][d_model], m_dtype; gain: [d_model] fp32 or NULL (unit gain; then
+ * d_gain may still be requested); w_k, w_v: [d_model][n_kv_heads*head_dim],
+ * w_dtype; dz_k, dz_v: [n][n_kv_heads*head_dim] in dz_dtype (f32 or bf16;
+ * the [rows][H_kv][d_h] layout of the cache and of the attention backward's
+ * d_k, d_v).  d_m: [n][d_model] fp32, written.  d_w_k, d_w_v:
+ * [d_model][n_kv_heads*head_dim] fp32 and d_gain: [d_model] fp32 (or NULL to
+ * skip it) are ADDED to, so calls over several row blocks accumulate.
+ * With bf16 m and w, d_model % 256 == 0 and n_kv_heads*head_dim % 256 == 0
+ * the two products run on bf16 MFMA with fp32 accumulation, y and fp32 dz
+ * rounded to bf16 first; otherwise in fp32 arithmetic.  Results are bitwise
+ * reproducible (fixed reduction orders, no atomics).  The rows must not
+ * carry a rotary embedding (for a *_rope forward the caller passes dz_k
+ * turned back to the unrotated frame).  n == 0 is a no-op.
+ * workspace: device memory of at least yoco_project_bwd_workspace bytes
+ * (contents on entry do not matter).
+ * Errors: NULL_POINTER; BAD_SHAPE (n < 0, d_model outside [1, 16384],
+ * n_kv_heads outside [1, 64], head_dim); BAD_DTYPE; BAD_VALUE (eps);
+ * WORKSPACE (too small). */
+yoco_status yoco_kv_project_bwd(const void *m, int32_t m_dtype, int64_t n, int32_t d_model,
+                                const float *gain, float eps, const void *w_k, const void *w_v,
+                                int32_t w_dtype, int32_t n_kv_heads, int32_t head_dim,
+                                const void *dz_k, const void *dz_v, int32_t dz_dtype, float *d_m,
+                                float *d_w_k, float *d_w_v, float *d_gain, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/* Backward of yoco_q_project ([Notes] Eq. 3, Q^l = RMSNorm_l(X^l) W_Q^l):
+ * the same formulas with one weight.  x: [n][d_model]; w_q:
+ * [d_model][n_q_heads*head_dim]; dz_q: [n][n_q_heads][head_dim] (the
+ * attention backward's d_q); d_x written, d_w_q and d_gain added to.
+ * Errors as yoco_kv_project_bwd; n_q_heads outside [1, 4096] -> BAD_SHAPE. */
+yoco_status yoco_q_project_bwd(const void *x, int32_t x_dtype, int64_t n, int32_t d_model,
+                               const float *gain, float eps, const void *w_q, int32_t w_dtype,
+                               int32_t n_q_heads, int32_t head_dim, const void *dz_q,
+                               int32_t dz_dtype, float *d_x, float *d_w_q, float *d_gain,
+                               void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace yoco_cross_attn_decode needs for this cache,
  * query head count and split size, valid for any len_host up to

@@ -27,7 +27,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = _lib()
     names = _declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 17, names
     for name in names:
         assert hasattr(lib, name), f"{name} declared in yoco.h but not exported"
 
@@ -281,3 +281,60 @@ def test_prefill_bwd_needs_bf16_cache_and_sizes_workspace():
     out = ctypes.c_size_t(0)
     assert _lib().yoco_cross_attn_prefill_bwd_workspace(1000, 24, ctypes.byref(out)) == 0
     assert out.value == 2 * 1000 * 24 * 4
+
+
+def _pbwd(**kw):
+    args = dict(m=FAKE, m_dt=1, n=300, d=512, gain=None, eps=1e-6, wk=FAKE, wv=FAKE, w_dt=1, hkv=2, dh=128,
+                dzk=FAKE, dzv=FAKE, dz_dt=0, dm=FAKE, dwk=FAKE, dwv=FAKE, dg=None, ws=FAKE, ws_bytes=1 << 30)
+    args.update(kw)
+    a = args
+    return _lib().yoco_kv_project_bwd(a["m"], a["m_dt"], a["n"], a["d"], a["gain"], a["eps"], a["wk"], a["wv"],
+                                      a["w_dt"], a["hkv"], a["dh"], a["dzk"], a["dzv"], a["dz_dt"], a["dm"],
+                                      a["dwk"], a["dwv"], a["dg"], a["ws"], a["ws_bytes"], None)
+
+
+def _pbwd_ws(n, d, ncols, n_out):
+    out = ctypes.c_size_t(0)
+    st = _lib().yoco_project_bwd_workspace(n, d, ncols, n_out, ctypes.byref(out))
+    return st, out.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(m=None), "YOCO_ERR_NULL_POINTER"),
+    (dict(dzv=None), "YOCO_ERR_NULL_POINTER"),
+    (dict(dwk=None), "YOCO_ERR_NULL_POINTER"),
+    (dict(ws=None), "YOCO_ERR_NULL_POINTER"),
+    (dict(dm=None), "YOCO_ERR_NULL_POINTER"),
+    (dict(d=0), "YOCO_ERR_BAD_SHAPE"),
+    (dict(d=16385), "YOCO_ERR_BAD_SHAPE"),
+    (dict(n=-1), "YOCO_ERR_BAD_SHAPE"),
+    (dict(hkv=0), "YOCO_ERR_BAD_SHAPE"),
+    (dict(dh=96), "YOCO_ERR_BAD_SHAPE"),
+    (dict(dz_dt=3), "YOCO_ERR_BAD_DTYPE"),
+    (dict(w_dt=2), "YOCO_ERR_BAD_DTYPE"),
+    (dict(eps=-1.0), "YOCO_ERR_BAD_VALUE"),
+    (dict(ws_bytes=1024), "YOCO_ERR_WORKSPACE"),
+])
+def test_project_bwd_rejects(kw, status):
+    assert _pbwd(**kw) == _status(status)
+    assert len(_lib().yoco_last_error()) > 0
+
+
+def test_project_bwd_workspace_layout():
+    # matrix-core shapes: 1/r, y and dz in bf16, split partials, dgain shares
+    st, b = _pbwd_ws(32768, 3072, 1024, 2)
+    assert st == 0
+    splits = 8  # ceil(768 / (12 * 4 * 2)) tiles, 4096 rows each
+    expect = 32768 * 4 + 32768 * 3072 * 2 + 2 * 32768 * 1024 * 2 + splits * 2 * 3072 * 1024 * 4 + 512 * 3072 * 4
+    assert b == expect
+    # shapes the tiles do not cover: 1/r and dgain shares only (256-byte aligned)
+    st, b = _pbwd_ws(257, 256, 128, 2)
+    assert st == 0 and b == 1280 + 5 * 256 * 4
+    assert _pbwd_ws(10, 64, 128, 3)[0] == _status("YOCO_ERR_BAD_SHAPE")
+    st, b = _pbwd_ws(0, 512, 256, 2)
+    assert st == 0 and b == 0 and _pbwd(n=0, ws_bytes=0) == 0
+    L = _lib()
+    assert L.yoco_q_project_bwd(FAKE, 1, 4, 32, None, 1e-6, FAKE, 1, 4, 96, FAKE, 0, FAKE, FAKE, None, FAKE,
+                                1 << 20, None) == _status("YOCO_ERR_BAD_SHAPE")
+    assert L.yoco_q_project_bwd(FAKE, 1, 4, 32, None, 1e-6, None, 1, 4, 64, FAKE, 0, FAKE, FAKE, None, FAKE,
+                                1 << 20, None) == _status("YOCO_ERR_NULL_POINTER")

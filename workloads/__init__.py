@@ -340,6 +340,13 @@ def make_grad(t: int, n_q_heads: int = 24, head_dim: int = 128, dtype: str = BF1
     return [store(_normal(seed, 10 + l, (t, n_q_heads, head_dim)), dtype) for l in range(layers)]
 
 
+def make_proj_grad(n: int, n_cols: int, n_out: int = 2, dtype: str = F32, seed: int = 0) -> list:
+    """Upstream gradients dz_p ``[n, n_cols]`` of the projection outputs
+    (p < n_out; K^ then V^, or Q^): stream 20 + p, N(0,1) each (a stand-in for
+    what the cross layers' backward sends to the shared projection)."""
+    return [store(_normal(seed, 20 + p, (n, n_cols)), dtype) for p in range(n_out)]
+
+
 # ---------------------------------------------------------------------------
 # Projection workload at 3B-like widths.
 # ---------------------------------------------------------------------------

@@ -12,6 +12,9 @@ The functions mirror the C entry points:
 * ``q_project``       -> ``yoco_q_project``    (per-layer RMSNorm + Q^ projection)
 * ``cross_attn_prefill`` -> ``yoco_cross_attn_prefill`` (causal block over the cache)
 * ``cross_attn_decode``  -> ``yoco_cross_attn_decode``  (one token per sequence, split-N)
+* ``cross_attn_prefill_bwd`` -> ``yoco_cross_attn_prefill_bwd`` (training backward of one layer)
+* ``kv_project_bwd`` / ``q_project_bwd`` -> ``yoco_kv_project_bwd`` / ``yoco_q_project_bwd``
+  (backward of the fused RMSNorm + projections)
 """
 from __future__ import annotations
 
@@ -28,6 +31,8 @@ from ._native import (YOCO_DECODE_COUNTER_BYTES, YOCO_DT_BF16, YOCO_DT_F32, KVCa
 __all__ = [
     "KVCache", "YocoError", "kv_project", "kv_append", "q_project", "cross_attn_prefill",
     "cross_attn_decode", "decode_workspace", "decode_workspace_bytes", "kv_cache_bytes", "lib",
+    "cross_attn_prefill_bwd", "prefill_bwd_workspace_bytes", "kv_project_bwd", "q_project_bwd",
+    "project_bwd_workspace_bytes",
 ]
 
 _DT = {torch.float32: YOCO_DT_F32, torch.bfloat16: YOCO_DT_BF16}
@@ -229,6 +234,79 @@ def cross_attn_prefill_bwd(q: torch.Tensor, o: torch.Tensor, d_o: torch.Tensor, 
                                             _ptr(workspace), workspace.numel() * workspace.element_size(),
                                             _stream(stream)))
     return d_q, d_k, d_v
+
+
+def project_bwd_workspace_bytes(n: int, d_model: int, n_cols: int, n_out: int) -> int:
+    out = ctypes.c_size_t(0)
+    check(lib().yoco_project_bwd_workspace(n, d_model, n_cols, n_out, ctypes.byref(out)))
+    return int(out.value)
+
+
+def _grad_buffers(x, ws_bytes, weights, d_x, d_ws, d_gain, want_gain, workspace):
+    n, d = x.shape
+    if d_x is None:
+        d_x = torch.empty((n, d), dtype=torch.float32, device=x.device)
+    d_ws = [torch.zeros(w.shape, dtype=torch.float32, device=x.device) if g is None else g
+            for w, g in zip(weights, d_ws)]
+    if d_gain is None and want_gain:
+        d_gain = torch.zeros(d, dtype=torch.float32, device=x.device)
+    for name, t in [("d_x", d_x), ("d_gain", d_gain)] + [("d_w", g) for g in d_ws]:
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise TypeError(f"{name} must be a contiguous float32 tensor")
+    if d_x.shape != (n, d) or any(g.shape != w.shape for g, w in zip(d_ws, weights)):
+        raise ValueError("d_x must be [n, d_model] and each d_w the shape of its weight")
+    if d_gain is not None and d_gain.shape != (d,):
+        raise ValueError("d_gain must be [d_model]")
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    return d_x, d_ws, d_gain, workspace
+
+
+def kv_project_bwd(m: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor, dz_k: torch.Tensor,
+                   dz_v: torch.Tensor, n_kv_heads: int, head_dim: int, gain: Optional[torch.Tensor] = None,
+                   eps: float = 1e-6, d_m: Optional[torch.Tensor] = None, d_w_k: Optional[torch.Tensor] = None,
+                   d_w_v: Optional[torch.Tensor] = None, d_gain: Optional[torch.Tensor] = None,
+                   want_gain: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Backward of ``kv_project``: returns (d_m, d_w_k, d_w_v, d_gain).  d_m is
+    written; d_w_k, d_w_v and d_gain are ADDED to (zeros when not given;
+    d_gain is None unless given or ``want_gain``).  dz_k, dz_v:
+    ``[n, H_kv, d_h]`` or ``[n, H_kv*d_h]``, float32 or bfloat16."""
+    _on_device(m, w_k, w_v, dz_k, dz_v, gain)
+    if w_k.dtype != w_v.dtype or dz_k.dtype != dz_v.dtype:
+        raise TypeError("w_k/w_v and dz_k/dz_v must share a dtype")
+    n, d = m.shape
+    ncols = n_kv_heads * head_dim
+    if dz_k.numel() != n * ncols or dz_v.numel() != n * ncols:
+        raise ValueError(f"dz_k, dz_v must hold [n, {ncols}] values")
+    ws_bytes = project_bwd_workspace_bytes(n, d, ncols, 2)
+    d_m, (d_w_k, d_w_v), d_gain, workspace = _grad_buffers(m, ws_bytes, (w_k, w_v), d_m, (d_w_k, d_w_v), d_gain,
+                                                           want_gain, workspace)
+    check(lib().yoco_kv_project_bwd(_ptr(m), _dt(m), n, d, _ptr(gain), eps, _ptr(w_k), _ptr(w_v), _dt(w_k),
+                                    n_kv_heads, head_dim, _ptr(dz_k), _ptr(dz_v), _dt(dz_k), _ptr(d_m),
+                                    _ptr(d_w_k), _ptr(d_w_v), _ptr(d_gain), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)))
+    return d_m, d_w_k, d_w_v, d_gain
+
+
+def q_project_bwd(x: torch.Tensor, w_q: torch.Tensor, dz_q: torch.Tensor, n_q_heads: int, head_dim: int,
+                  gain: Optional[torch.Tensor] = None, eps: float = 1e-6, d_x: Optional[torch.Tensor] = None,
+                  d_w_q: Optional[torch.Tensor] = None, d_gain: Optional[torch.Tensor] = None,
+                  want_gain: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Backward of ``q_project``: returns (d_x, d_w_q, d_gain), with the
+    conventions of ``kv_project_bwd``."""
+    _on_device(x, w_q, dz_q, gain)
+    n, d = x.shape
+    ncols = n_q_heads * head_dim
+    if dz_q.numel() != n * ncols:
+        raise ValueError(f"dz_q must hold [n, {ncols}] values")
+    ws_bytes = project_bwd_workspace_bytes(n, d, ncols, 1)
+    d_x, (d_w_q,), d_gain, workspace = _grad_buffers(x, ws_bytes, (w_q,), d_x, (d_w_q,), d_gain, want_gain,
+                                                     workspace)
+    check(lib().yoco_q_project_bwd(_ptr(x), _dt(x), n, d, _ptr(gain), eps, _ptr(w_q), _dt(w_q), n_q_heads,
+                                   head_dim, _ptr(dz_q), _dt(dz_q), _ptr(d_x), _ptr(d_w_q), _ptr(d_gain),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)))
+    return d_x, d_w_q, d_gain
 
 
 def decode_workspace_bytes(cache: KVCache, n_q_heads: int, rows_per_split: int = 0) -> int:

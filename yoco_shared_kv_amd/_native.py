@@ -77,6 +77,14 @@ def _declare(lib):
     lib.yoco_cross_attn_prefill_bwd.restype = st
     lib.yoco_cross_attn_prefill_bwd.argtypes = [vp, vp, i32, vp, vp, i64, i64, i32, cp, i32, f32, vp, vp, vp,
                                                 vp, sz, vp]
+    lib.yoco_project_bwd_workspace.restype = st
+    lib.yoco_project_bwd_workspace.argtypes = [i64, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.yoco_kv_project_bwd.restype = st
+    lib.yoco_kv_project_bwd.argtypes = [vp, i32, i64, i32, vp, f32, vp, vp, i32, i32, i32, vp, vp, i32, vp, vp, vp,
+                                        vp, vp, sz, vp]
+    lib.yoco_q_project_bwd.restype = st
+    lib.yoco_q_project_bwd.argtypes = [vp, i32, i64, i32, vp, f32, vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, sz,
+                                       vp]
     lib.yoco_cross_attn_decode_workspace.restype = st
     lib.yoco_cross_attn_decode_workspace.argtypes = [cp, i32, i64, ctypes.POINTER(sz)]
     lib.yoco_cross_attn_decode.restype = st

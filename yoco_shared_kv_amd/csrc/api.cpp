@@ -569,3 +569,139 @@ yoco_status yoco_cross_attn_prefill_bwd(const void *q, const void *o, int32_t o_
 }
 
 }  // extern "C"
+
+namespace {
+
+// Workspace regions of the projection backward, each 256-byte aligned.  The
+// matrix-core regions are sized whenever the shapes allow that path, whatever
+// the storage types, so one size serves every call with these shapes.
+struct PbwdLayout {
+  size_t inv_r = 0, ybf = 0, dzb[2] = {0, 0}, dw_part = 0, dgain_part = 0, total = 0;
+  int32_t splits = 0, split_rows = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+PbwdLayout pbwd_layout(int64_t n, int32_t d, int32_t ncols, int32_t n_out) {
+  PbwdLayout L;
+  size_t off = 0;
+  L.inv_r = off;
+  off = align256(off + static_cast<size_t>(n) * 4);
+  const bool tiles = d % 256 == 0 && ncols % 256 == 0 && n > 0;
+  if (tiles) {
+    L.ybf = off;
+    off = align256(off + static_cast<size_t>(n) * d * 2);
+    for (int p = 0; p < n_out; ++p) {
+      L.dzb[p] = off;
+      off = align256(off + static_cast<size_t>(n) * ncols * 2);
+    }
+    yoco::project_bwd_split_plan(n, d, ncols, n_out, &L.splits, &L.split_rows);
+    L.dw_part = off;
+    off = align256(off + static_cast<size_t>(L.splits) * n_out * d * ncols * 4);
+  }
+  L.dgain_part = off;
+  off = align256(off + static_cast<size_t>((n + yoco::kProjBwdFinRows - 1) / yoco::kProjBwdFinRows) * d * 4);
+  L.total = off;
+  return L;
+}
+
+yoco_status project_bwd_impl(const void *x, int32_t x_dtype, int64_t n, int32_t d_model, const float *gain,
+                             float eps, const void *const w[2], int32_t w_dtype, int32_t ncols, int32_t n_out,
+                             const void *const dz[2], int32_t dz_dtype, float *d_x, float *const d_w[2],
+                             float *d_gain, void *workspace, size_t workspace_bytes, void *stream) {
+  if (x == nullptr || d_x == nullptr || workspace == nullptr)
+    return fail(YOCO_ERR_NULL_POINTER, "input, its gradient or workspace is NULL");
+  for (int p = 0; p < n_out; ++p) {
+    if (w[p] == nullptr || dz[p] == nullptr || d_w[p] == nullptr)
+      return fail(YOCO_ERR_NULL_POINTER, "a weight, an output gradient or a weight gradient is NULL");
+  }
+  if (n < 0 || d_model < 1 || d_model > yoco::kProjBwdMaxD)
+    return fail(YOCO_ERR_BAD_SHAPE, "n %lld must be >= 0 and d_model %d in [1, %d]", (long long)n, d_model,
+                yoco::kProjBwdMaxD);
+  if (!dtype_ok(x_dtype) || !dtype_ok(w_dtype) || !dtype_ok(dz_dtype))
+    return fail(YOCO_ERR_BAD_DTYPE, "input, weight or gradient dtype unknown");
+  yoco_status st = check_eps(eps);
+  if (st != YOCO_OK) return st;
+  const PbwdLayout L = pbwd_layout(n, d_model, ncols, n_out);
+  if (workspace_bytes < L.total)
+    return fail(YOCO_ERR_WORKSPACE, "workspace %zu bytes < %zu (yoco_project_bwd_workspace)", workspace_bytes,
+                L.total);
+  if (n == 0) return ok();
+  if ((st = check_device()) != YOCO_OK) return st;
+
+  char *ws = static_cast<char *>(workspace);
+  yoco::ProjBwdArgs a{};
+  a.x = x;
+  a.gain = gain;
+  a.dx = d_x;
+  a.dgain = d_gain;
+  for (int p = 0; p < n_out; ++p) {
+    a.w[p] = w[p];
+    a.dz[p] = dz[p];
+    a.dw[p] = d_w[p];
+  }
+  a.n = n;
+  a.d = d_model;
+  a.ncols = ncols;
+  a.n_out = n_out;
+  a.x_bf16 = x_dtype == YOCO_DT_BF16;
+  a.w_bf16 = w_dtype == YOCO_DT_BF16;
+  a.dz_bf16 = dz_dtype == YOCO_DT_BF16;
+  a.eps = eps;
+  a.inv_r = reinterpret_cast<float *>(ws + L.inv_r);
+  a.dgain_part = reinterpret_cast<float *>(ws + L.dgain_part);
+  a.mfma = yoco::project_bwd_mfma_applies(n, d_model, ncols, x_dtype, w_dtype) ? 1 : 0;
+  if (a.mfma) {
+    a.ybf = reinterpret_cast<uint16_t *>(ws + L.ybf);
+    for (int p = 0; p < n_out; ++p) {
+      a.dzb[p] = a.dz_bf16 ? static_cast<uint16_t *>(const_cast<void *>(dz[p]))
+                           : reinterpret_cast<uint16_t *>(ws + L.dzb[p]);
+    }
+    a.dw_part = reinterpret_cast<float *>(ws + L.dw_part);
+    a.splits = L.splits;
+    a.split_rows = L.split_rows;
+  }
+  return launched(yoco::launch_project_bwd(a, static_cast<hipStream_t>(stream)), "project_bwd");
+}
+
+}  // namespace
+
+extern "C" {
+
+yoco_status yoco_project_bwd_workspace(int64_t n, int32_t d_model, int32_t n_cols, int32_t n_out, size_t *bytes) {
+  if (bytes == nullptr) return fail(YOCO_ERR_NULL_POINTER, "bytes is NULL");
+  if (n < 0 || d_model < 1 || d_model > yoco::kProjBwdMaxD || n_cols < 1 || (n_out != 1 && n_out != 2))
+    return fail(YOCO_ERR_BAD_SHAPE, "n %lld, d_model %d, n_cols %d, n_out %d", (long long)n, d_model, n_cols, n_out);
+  *bytes = pbwd_layout(n, d_model, n_cols, n_out).total;
+  return ok();
+}
+
+yoco_status yoco_kv_project_bwd(const void *m, int32_t m_dtype, int64_t n, int32_t d_model, const float *gain,
+                                float eps, const void *w_k, const void *w_v, int32_t w_dtype, int32_t n_kv_heads,
+                                int32_t head_dim, const void *dz_k, const void *dz_v, int32_t dz_dtype, float *d_m,
+                                float *d_w_k, float *d_w_v, float *d_gain, void *workspace, size_t workspace_bytes,
+                                void *stream) {
+  if (n_kv_heads < 1 || n_kv_heads > yoco::kMaxKvHeads)
+    return fail(YOCO_ERR_BAD_SHAPE, "n_kv_heads %d outside [1, %d]", n_kv_heads, yoco::kMaxKvHeads);
+  if (!head_dim_ok(head_dim)) return fail(YOCO_ERR_BAD_SHAPE, "head_dim %d is not 64 or 128", head_dim);
+  const void *w[2] = {w_k, w_v};
+  const void *dz[2] = {dz_k, dz_v};
+  float *dw[2] = {d_w_k, d_w_v};
+  return project_bwd_impl(m, m_dtype, n, d_model, gain, eps, w, w_dtype, n_kv_heads * head_dim, 2, dz, dz_dtype,
+                          d_m, dw, d_gain, workspace, workspace_bytes, stream);
+}
+
+yoco_status yoco_q_project_bwd(const void *x, int32_t x_dtype, int64_t n, int32_t d_model, const float *gain,
+                               float eps, const void *w_q, int32_t w_dtype, int32_t n_q_heads, int32_t head_dim,
+                               const void *dz_q, int32_t dz_dtype, float *d_x, float *d_w_q, float *d_gain,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  if (n_q_heads < 1 || n_q_heads > 4096) return fail(YOCO_ERR_BAD_SHAPE, "n_q_heads %d outside [1, 4096]", n_q_heads);
+  if (!head_dim_ok(head_dim)) return fail(YOCO_ERR_BAD_SHAPE, "head_dim %d is not 64 or 128", head_dim);
+  const void *w[2] = {w_q, nullptr};
+  const void *dz[2] = {dz_q, nullptr};
+  float *dw[2] = {d_w_q, nullptr};
+  return project_bwd_impl(x, x_dtype, n, d_model, gain, eps, w, w_dtype, n_q_heads * head_dim, 1, dz, dz_dtype, d_x,
+                          dw, d_gain, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

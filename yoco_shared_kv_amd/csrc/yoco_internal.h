@@ -97,4 +97,39 @@ struct BwdArgs {
 
 hipError_t launch_prefill_bwd(const BwdArgs &a, int head_dim, hipStream_t s);
 
+// Backward of the fused RMSNorm + projection (training).  x, gain, W_p and
+// dz_p as in the forward; dx written, dW_p and dgain added to.  Workspace
+// regions (device): inv_r [n]; matrix-core path: ybf [n][d], dzb_p [n][ncols]
+// (or the caller's bf16 dz), dw_part [splits][n_out][d][ncols]; dgain_part
+// [ceil(n / kProjBwdFinRows)][d].
+constexpr int kProjBwdFinRows = 64;     // input rows per block of the dx kernel
+constexpr int kProjBwdMaxD = 16384;     // d_model bound of the dx kernel's registers
+struct ProjBwdArgs {
+  const void *x;             // [n][d]
+  const float *gain;         // [d] or null
+  const void *w[2];          // [d][ncols]
+  const void *dz[2];         // [n][ncols]
+  float *dx;                 // [n][d], written
+  float *dw[2];              // [d][ncols], added to
+  float *dgain;              // [d], added to, or null
+  float *inv_r;              // workspace [n]
+  uint16_t *ybf;             // workspace [n][d] bf16 (matrix-core path)
+  uint16_t *dzb[2];          // bf16 dz (matrix-core path)
+  float *dw_part;            // workspace (matrix-core path)
+  float *dgain_part;         // workspace
+  int64_t n;
+  int32_t d;
+  int32_t ncols;
+  int32_t n_out;
+  int32_t x_bf16, w_bf16, dz_bf16;
+  int32_t mfma;
+  int32_t splits;            // matrix-core dW: row splits
+  int32_t split_rows;        // rows per split (multiple of 64)
+  float eps;
+};
+
+bool project_bwd_mfma_applies(int64_t n, int32_t d, int32_t ncols, int x_dt, int w_dt);
+void project_bwd_split_plan(int64_t n, int32_t d, int32_t ncols, int32_t n_out, int32_t *splits, int32_t *rows);
+hipError_t launch_project_bwd(const ProjBwdArgs &a, hipStream_t s);
+
 }  // namespace yoco
