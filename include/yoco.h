@@ -258,7 +258,7 @@ yoco_status yoco_cross_attn_prefill_bwd(const void *q, const void *o, int32_t o_
  * n_kv_heads * head_dim) or yoco_q_project_bwd (n_out = 1, n_cols =
  * n_q_heads * head_dim) needs for n input rows of width d_model.  The size
  * depends on the shapes only.  Errors: NULL_POINTER; BAD_SHAPE (n < 0,
- * d_model outside [1, 16384], n_cols < 1, n_out not 1 or 2). */
+ * d_model outside [1, 4096], n_cols < 1, n_out not 1 or 2). */
 yoco_status yoco_project_bwd_workspace(int64_t n, int32_t d_model, int32_t n_cols, int32_t n_out,
                                        size_t *bytes);
 
@@ -286,7 +286,7 @@ yoco_status yoco_project_bwd_workspace(int64_t n, int32_t d_model, int32_t n_col
  * turned back to the unrotated frame).  n == 0 is a no-op.
  * workspace: device memory of at least yoco_project_bwd_workspace bytes
  * (contents on entry do not matter).
- * Errors: NULL_POINTER; BAD_SHAPE (n < 0, d_model outside [1, 16384],
+ * Errors: NULL_POINTER; BAD_SHAPE (n < 0, d_model outside [1, 4096],
  * n_kv_heads outside [1, 64], head_dim); BAD_DTYPE; BAD_VALUE (eps);
  * WORKSPACE (too small). */
 yoco_status yoco_kv_project_bwd(const void *m, int32_t m_dtype, int64_t n, int32_t d_model,

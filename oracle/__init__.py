@@ -20,6 +20,10 @@ query rows and heads).  This module only marshals numpy arrays to it:
                      K^ and V^ (K^/V^ gradients added, so layers sum).
 * ``project_bwd`` -- gradients of the shared projection with respect to M,
                      the norm gain, W_K and W_V.
+* ``gret_gate`` / ``gret`` / ``gret_step`` -- gated retention, the
+                     self-decoder's token mixer (YOCO reading notes, section
+                     2.2): the gate, the parallel form (Eq. 4, continuing from
+                     a given state) and one step of the recurrent form (Eq. 5).
 
 Inputs are the stored values: float32 arrays, bf16 kept as ``uint16`` bits,
 or float64 (for finite-difference checks).
@@ -99,6 +103,10 @@ class Oracle:
         lib.oracle_project_bwd.argtypes = [vp, i32, i64, i64, vp, dbl, vp, vp, i32, i64, vp, vp, i32,
                                            vp, vp, vp, vp]
         lib.oracle_project_bwd.restype = i32
+        lib.oracle_gret_gate.argtypes = [vp, i64, dbl, vp]
+        lib.oracle_gret.argtypes = [vp, vp, vp, i32, vp, i64, i32, i32, i32, vp, vp, i64, vp, vp]
+        lib.oracle_gret.restype = i32
+        lib.oracle_gret_step.argtypes = [vp, vp, vp, i32, vp, i64, i32, i32, i32, vp, vp]
         self.lib = lib
         self.path = path
 
@@ -269,6 +277,60 @@ class Oracle:
         pos = np.full(q.shape[0], length - 1, dtype=np.int64)
         return self.attention(q, pos, k[:length], v[:length], scale, want_lse)
 
+    def gret_gate(self, g: np.ndarray, tau: float) -> np.ndarray:
+        """gamma = sigmoid(g)^(1/tau) in fp64 (g: float32 gate logits)."""
+        g = np.ascontiguousarray(g, dtype=np.float32)
+        out = np.empty(g.shape, dtype=np.float64)
+        self.lib.oracle_gret_gate(_ptr(g), g.size, float(tau), _ptr(out))
+        return out
+
+    def gret(self, q: np.ndarray, k: np.ndarray, v: np.ndarray, gamma: np.ndarray, s_in=None,
+             rows=None, want_state: bool = False):
+        """Gated retention, parallel form, over a block: q, k ``[n, H, dk]``,
+        v ``[n, H, dv]`` (one storage type), gamma ``[n, H]`` fp64, s_in
+        ``[H, dk, dv]`` (the state before the block) or None.  Returns o
+        ``[n_rows, H, dv]`` (and the state after the block)."""
+        q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
+        n, heads, dk = q.shape
+        dv = v.shape[2]
+        if k.shape != q.shape or v.shape[:2] != (n, heads) or q.dtype != k.dtype or k.dtype != v.dtype:
+            raise ValueError("q, k must be [n, H, dk] and v [n, H, dv] of one dtype")
+        gamma = np.ascontiguousarray(gamma, dtype=np.float64)
+        if gamma.shape != (n, heads):
+            raise ValueError("gamma must be [n, H]")
+        sp = None
+        if s_in is not None:
+            s_in = np.ascontiguousarray(s_in, dtype=np.float64)
+            if s_in.shape != (heads, dk, dv):
+                raise ValueError("s_in must be [H, dk, dv]")
+            sp = _ptr(s_in)
+        r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+        n_rows = n if r is None else r.size
+        o = np.empty((n_rows, heads, dv), dtype=np.float64)
+        s_out = np.empty((heads, dk, dv), dtype=np.float64) if want_state else None
+        rc = self.lib.oracle_gret(_ptr(q), _ptr(k), _ptr(v), _code(q), _ptr(gamma), n, heads, dk, dv, sp,
+                                  None if r is None else _ptr(r), n_rows, _ptr(o),
+                                  None if s_out is None else _ptr(s_out))
+        if rc != 0:
+            raise ValueError("a row outside the block")
+        return (o, s_out) if want_state else o
+
+    def gret_step(self, q: np.ndarray, k: np.ndarray, v: np.ndarray, gamma: np.ndarray, state: np.ndarray):
+        """One recurrent step for each sequence: q, k ``[B, H, dk]``, v
+        ``[B, H, dv]``, gamma ``[B, H]``, state ``[B, H, dk, dv]`` fp64.
+        Returns (o ``[B, H, dv]``, the updated state)."""
+        q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
+        b, heads, dk = q.shape
+        dv = v.shape[2]
+        st = np.array(state, dtype=np.float64, copy=True, order="C")
+        if st.shape != (b, heads, dk, dv):
+            raise ValueError("state must be [B, H, dk, dv]")
+        gamma = np.ascontiguousarray(gamma, dtype=np.float64)
+        o = np.empty((b, heads, dv), dtype=np.float64)
+        self.lib.oracle_gret_step(_ptr(q), _ptr(k), _ptr(v), _code(q), _ptr(gamma), b, heads, dk, dv,
+                                  _ptr(st), _ptr(o))
+        return o, st
+
 
 def default() -> Oracle:
     """The oracle built from ``oracle.c`` beside this file (built if stale)."""
@@ -322,3 +384,15 @@ def attention_bwd(q, pos, k, v, dout, scale, dk=None, dv=None):
 
 def project_bwd(x, w_k, w_v, dz_k, dz_v, gain=None, eps: float = 1e-6):
     return default().project_bwd(x, w_k, w_v, dz_k, dz_v, gain, eps)
+
+
+def gret_gate(g, tau):
+    return default().gret_gate(g, tau)
+
+
+def gret(q, k, v, gamma, s_in=None, rows=None, want_state: bool = False):
+    return default().gret(q, k, v, gamma, s_in, rows, want_state)
+
+
+def gret_step(q, k, v, gamma, state):
+    return default().gret_step(q, k, v, gamma, state)

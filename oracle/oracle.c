@@ -487,3 +487,115 @@ int oracle_project_bwd(const void *x, int x_dtype, int64_t n, int64_t d, const f
   free(rr);
   return 0;
 }
+
+/* ---- Gated retention (gRet), the self-decoder's token mixer --------------
+ * [Notes] section 2.2, Eq. 4 (parallel form) and Eq. 5 (recurrent form);
+ * [Deep] section 3.1 (gated retention: head-wise data-controlled decay);
+ * [Blog] section 4 (the 2x2 state example).  Per head, with q_n, k_n of
+ * length dk, v_n of length dv and a scalar gate gamma_n:
+ *   gamma_n = sigmoid(g_n)^(1/tau)                              (Eq. 4)
+ *   D[n][m] = prod_{i=m+1..n} gamma_i  for m <= n, 0 otherwise
+ *   O       = (Q K^T (.) D) V                                    (Eq. 4)
+ *   S_n     = gamma_n S_{n-1} + k_n^T v_n,   O_n = q_n S_n      (Eq. 5)
+ * Positions count from 0 here (the pages count from 1).  The rotation of
+ * Q and K (Theta) is applied before these functions: they take q and k as
+ * they enter the products. */
+
+/* gamma[i] = sigmoid(g[i])^(1/tau), i < count. */
+void oracle_gret_gate(const float *g, int64_t count, double tau, double *gamma) {
+  for (int64_t i = 0; i < count; ++i) {
+    const double sig = 1.0 / (1.0 + exp(-(double)g[i]));
+    gamma[i] = pow(sig, 1.0 / tau);
+  }
+}
+
+/* Parallel form (Eq. 4) over a block of n positions of every head, starting
+ * from the state s_in that the recurrence (Eq. 5) held before the block
+ * (NULL: zero, a fresh sequence).  Unrolling Eq. 5 from that state gives
+ *   O_t = sum_{m<=t} D[t][m] (q_t . k_m) v_m + (prod_{i<=t} gamma_i) q_t s_in.
+ * D[t][m] is formed as a running product while m walks down from t.
+ * q, k: [n][heads][dk]; v: [n][heads][dv] (stored values, one dtype);
+ * gamma: [n][heads]; s_in: [heads][dk][dv] or NULL; rows: the positions to
+ * evaluate (NULL: all n), o: [n_rows][heads][dv].  s_out (NULL: skipped):
+ * [heads][dk][dv], the state after the block,
+ *   S = (prod_all gamma) s_in + sum_m D[n-1][m] k_m^T v_m.
+ * Returns 0, or -1 for a row outside [0, n). */
+int oracle_gret(const void *q, const void *k, const void *v, int dtype, const double *gamma, int64_t n,
+                int heads, int dk, int dv, const double *s_in, const int64_t *rows, int64_t n_rows,
+                double *o, double *s_out) {
+  if (rows == NULL) n_rows = n;
+  for (int64_t i = 0; i < n_rows; ++i) {
+    if (rows != NULL && (rows[i] < 0 || rows[i] >= n)) return -1;
+  }
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int64_t i = 0; i < n_rows; ++i) {
+    for (int h = 0; h < heads; ++h) {
+      const int64_t t = rows ? rows[i] : i;
+      double *out = o + (i * heads + h) * dv;
+      for (int e = 0; e < dv; ++e) out[e] = 0.0;
+      double decay = 1.0; /* D[t][m] for the current m */
+      for (int64_t m = t; m >= 0; --m) {
+        double dot = 0.0;
+        for (int c = 0; c < dk; ++c) {
+          dot += read_elem(q, dtype, (t * heads + h) * dk + c) * read_elem(k, dtype, (m * heads + h) * dk + c);
+        }
+        for (int e = 0; e < dv; ++e) out[e] += decay * dot * read_elem(v, dtype, (m * heads + h) * dv + e);
+        decay *= gamma[m * heads + h];
+      }
+      if (s_in != NULL) {
+        /* decay is now prod_{i=0..t} gamma_i */
+        const double *s = s_in + (int64_t)h * dk * dv;
+        for (int e = 0; e < dv; ++e) {
+          double acc = 0.0;
+          for (int c = 0; c < dk; ++c) acc += read_elem(q, dtype, (t * heads + h) * dk + c) * s[c * dv + e];
+          out[e] += decay * acc;
+        }
+      }
+    }
+  }
+  if (s_out != NULL) {
+#pragma omp parallel for schedule(static)
+    for (int h = 0; h < heads; ++h) {
+      double *s = s_out + (int64_t)h * dk * dv;
+      for (int64_t x = 0; x < (int64_t)dk * dv; ++x) s[x] = 0.0;
+      double decay = 1.0; /* D[n-1][m] */
+      for (int64_t m = n - 1; m >= 0; --m) {
+        for (int c = 0; c < dk; ++c) {
+          const double kc = decay * read_elem(k, dtype, (m * heads + h) * dk + c);
+          for (int e = 0; e < dv; ++e) s[c * dv + e] += kc * read_elem(v, dtype, (m * heads + h) * dv + e);
+        }
+        decay *= gamma[m * heads + h];
+      }
+      if (s_in != NULL) {
+        const double *si = s_in + (int64_t)h * dk * dv;
+        for (int64_t x = 0; x < (int64_t)dk * dv; ++x) s[x] += decay * si[x];
+      }
+    }
+  }
+  return 0;
+}
+
+/* One step of the recurrent form (Eq. 5) for n_seq sequences: per sequence b
+ * and head h, S <- gamma S + k^T v, then o = q S with the updated S.
+ * q, k: [n_seq][heads][dk]; v: [n_seq][heads][dv]; gamma: [n_seq][heads];
+ * state: [n_seq][heads][dk][dv], updated in place; o: [n_seq][heads][dv]. */
+void oracle_gret_step(const void *q, const void *k, const void *v, int dtype, const double *gamma,
+                      int64_t n_seq, int heads, int dk, int dv, double *state, double *o) {
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t b = 0; b < n_seq; ++b) {
+    for (int h = 0; h < heads; ++h) {
+      const int64_t bh = b * heads + h;
+      double *s = state + bh * dk * dv;
+      const double gm = gamma[bh];
+      for (int c = 0; c < dk; ++c) {
+        const double kc = read_elem(k, dtype, bh * dk + c);
+        for (int e = 0; e < dv; ++e) s[c * dv + e] = gm * s[c * dv + e] + kc * read_elem(v, dtype, bh * dv + e);
+      }
+      for (int e = 0; e < dv; ++e) {
+        double acc = 0.0;
+        for (int c = 0; c < dk; ++c) acc += read_elem(q, dtype, bh * dk + c) * s[c * dv + e];
+        o[bh * dv + e] = acc;
+      }
+    }
+  }
+}

@@ -604,6 +604,129 @@ def pin_project_bwd_library(orc):
     for name, a, b in zip(("dx", "dw_k", "dw_v", "dgain"), got, (xt.grad, wk.grad, wv.grad, gt.grad)):
         _close(a, b.numpy(), 1e-10, 1e-12, f"project {name} vs torch autograd")
 
+# ---------------------------------------------------------------------------
+# Gated retention (the self-decoder's token mixer)
+# ---------------------------------------------------------------------------
+GRET_GOLDEN = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden", "gret_worked_example.txt")
+
+
+def _gret_golden():
+    vals = {}
+    for line in open(GRET_GOLDEN):
+        if line.strip() and not line.startswith("#"):
+            name, *nums = line.split()
+            vals[name] = np.array([float(x) for x in nums], dtype=np.float64)
+    return vals
+
+
+def pin_gret_worked_example(orc):
+    """The blog's 2x2 example (section 4): state [[2,0],[0,2]], gate 0.5,
+    k = [1,0], v = [3,4] -> state [[4,4],[0,1]]; q = [1,0] reads [4,4].  Both
+    the recurrent step and the parallel form started from that state."""
+    g = _gret_golden()
+    q = g["q"].reshape(1, 1, 2)
+    k = g["k"].reshape(1, 1, 2)
+    v = g["v"].reshape(1, 1, 2)
+    gamma = g["gamma"].reshape(1, 1)
+    s0 = g["state_before"].reshape(1, 1, 2, 2)
+    o, s1 = orc.gret_step(q, k, v, gamma, s0)
+    _close(s1.reshape(4), g["state_after"], 0, 0, "gret step: state")
+    _close(o.reshape(2), g["o"], 0, 0, "gret step: output")
+    o, s1 = orc.gret(q, k, v, gamma, s_in=s0[0], want_state=True)
+    _close(s1.reshape(4), g["state_after"], 0, 0, "gret parallel: state")
+    _close(o.reshape(2), g["o"], 0, 0, "gret parallel: output")
+
+
+def pin_gret_two_token_state(orc):
+    """The reading notes' example (section 2.2): from S_0 = 0, two tokens give
+    S_2 = gamma_2 k_1^T v_1 + k_2^T v_2 -- the first token is decayed by the
+    second step's gate, the current token not at all."""
+    rng = _rng(40)
+    q = _grid(rng, (2, 1, 3)).astype(np.float64)
+    k = _grid(rng, (2, 1, 3)).astype(np.float64)
+    v = _grid(rng, (2, 1, 4)).astype(np.float64)
+    gamma = np.array([[0.75], [0.375]])
+    _, s = orc.gret(q, k, v, gamma, want_state=True)
+    want = gamma[1, 0] * np.outer(k[0, 0], v[0, 0]) + np.outer(k[1, 0], v[1, 0])
+    _close(s[0], want, 1e-15, 1e-15, "gret two-token state")
+
+
+def pin_gret_parallel_equals_recurrent(orc):
+    """Eq. 4 (parallel) and Eq. 5 (recurrent) give the same outputs and final
+    state, with and without a starting state."""
+    rng = _rng(41)
+    n, h, dk, dv = 23, 3, 5, 4
+    q = rng.standard_normal((n, h, dk))
+    k = rng.standard_normal((n, h, dk))
+    v = rng.standard_normal((n, h, dv))
+    gamma = rng.uniform(0.2, 1.0, (n, h))
+    for s0 in (None, rng.standard_normal((h, dk, dv))):
+        o, s = orc.gret(q, k, v, gamma, s_in=s0, want_state=True)
+        st = np.zeros((1, h, dk, dv)) if s0 is None else s0[None].copy()
+        for t in range(n):
+            ot, st = orc.gret_step(q[t:t + 1], k[t:t + 1], v[t:t + 1], gamma[t:t + 1], st)
+            _close(o[t], ot[0], 1e-12, 1e-12, f"gret parallel vs recurrent, row {t}")
+        _close(s, st[0], 1e-12, 1e-12, "gret parallel vs recurrent, final state")
+
+
+def pin_gret_unit_gate_is_causal_linear_attention(orc):
+    """With every gate 1 the decay matrix is the causal mask: O = tril(QK^T) V
+    (numpy fp64), and the state is K^T V."""
+    rng = _rng(42)
+    n, h, dk, dv = 17, 2, 6, 5
+    q = rng.standard_normal((n, h, dk))
+    k = rng.standard_normal((n, h, dk))
+    v = rng.standard_normal((n, h, dv))
+    o, s = orc.gret(q, k, v, np.ones((n, h)), want_state=True)
+    for hh in range(h):
+        want = np.tril(q[:, hh] @ k[:, hh].T) @ v[:, hh]
+        _close(o[:, hh], want, 1e-12, 1e-12, "gret unit gate outputs")
+        _close(s[hh], k[:, hh].T @ v[:, hh], 1e-12, 1e-12, "gret unit gate state")
+
+
+def pin_gret_zero_gate_keeps_current_token(orc):
+    """With every gate 0 nothing survives a step: O_t = (q_t . k_t) v_t and the
+    state is the last token's outer product."""
+    rng = _rng(43)
+    n, h, dk, dv = 9, 2, 4, 3
+    q = rng.standard_normal((n, h, dk))
+    k = rng.standard_normal((n, h, dk))
+    v = rng.standard_normal((n, h, dv))
+    s0 = rng.standard_normal((h, dk, dv))
+    o, s = orc.gret(q, k, v, np.zeros((n, h)), s_in=s0, want_state=True)
+    want = np.einsum("nhc,nhc->nh", q, k)[:, :, None] * v
+    _close(o, want, 1e-13, 1e-13, "gret zero gate outputs")
+    _close(s, np.einsum("hc,he->hce", k[-1], v[-1]), 1e-13, 1e-13, "gret zero gate state")
+
+
+def pin_gret_block_split(orc):
+    """Running a sequence as two blocks, the second starting from the first's
+    final state, equals one block (rows and final state); rows can be sampled."""
+    rng = _rng(44)
+    n, h, dk, dv = 40, 2, 8, 8
+    q = store(rng.standard_normal((n, h, dk)).astype(np.float32), BF16)
+    k = store(rng.standard_normal((n, h, dk)).astype(np.float32), BF16)
+    v = store(rng.standard_normal((n, h, dv)).astype(np.float32), BF16)
+    gamma = rng.uniform(0.5, 1.0, (n, h))
+    o, s = orc.gret(q, k, v, gamma, want_state=True)
+    cut = 13
+    o1, s1 = orc.gret(q[:cut], k[:cut], v[:cut], gamma[:cut], want_state=True)
+    o2, s2 = orc.gret(q[cut:], k[cut:], v[cut:], gamma[cut:], s_in=s1, want_state=True)
+    _close(np.concatenate([o1, o2]), o, 1e-12, 1e-12, "gret split outputs")
+    _close(s2, s, 1e-12, 1e-12, "gret split state")
+    rows = np.array([0, 5, 39, 12], dtype=np.int64)
+    _close(orc.gret(q, k, v, gamma, rows=rows), o[rows], 0, 0, "gret sampled rows")
+
+
+def pin_gret_gate_library(orc):
+    """gamma = sigmoid(g)^(1/tau) against scipy's logistic function."""
+    from scipy.special import expit
+    g = np.array([-30.0, -4.0, -0.5, 0.0, 0.25, 3.0, 20.0], dtype=np.float32)
+    for tau in (1.0, 16.0, 2.5):
+        _close(orc.gret_gate(g, tau), expit(g.astype(np.float64)) ** (1.0 / tau), 1e-14, 0, f"gret gate tau={tau}")
+    _close(orc.gret_gate(np.zeros(1, np.float32), 1.0), [0.5], 0, 0, "gret gate sigmoid(0)")
+
+
 ALL_PINS = [
     pin_rmsnorm_constant_row,
     pin_rmsnorm_one_hot,
@@ -638,4 +761,7 @@ ALL_PINS = [
     pin_project_bwd_finite_differences,
     pin_project_bwd_scale_invariance,
     pin_project_bwd_library,
+    pin_gret_worked_example, pin_gret_two_token_state, pin_gret_parallel_equals_recurrent,
+    pin_gret_unit_gate_is_causal_linear_attention, pin_gret_zero_gate_keeps_current_token,
+    pin_gret_block_split, pin_gret_gate_library,
 ]

@@ -306,7 +306,7 @@ def _pbwd_ws(n, d, ncols, n_out):
     (dict(ws=None), "YOCO_ERR_NULL_POINTER"),
     (dict(dm=None), "YOCO_ERR_NULL_POINTER"),
     (dict(d=0), "YOCO_ERR_BAD_SHAPE"),
-    (dict(d=16385), "YOCO_ERR_BAD_SHAPE"),
+    (dict(d=4097), "YOCO_ERR_BAD_SHAPE"),
     (dict(n=-1), "YOCO_ERR_BAD_SHAPE"),
     (dict(hkv=0), "YOCO_ERR_BAD_SHAPE"),
     (dict(dh=96), "YOCO_ERR_BAD_SHAPE"),

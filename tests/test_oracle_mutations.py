@@ -54,6 +54,18 @@ MUTATIONS = {
                               "ag += dy[r * d + c] * read_elem(x, x_dtype, r * d + c);"),
     "bwd_dw_uses_unnormalised_x": ("ak += y[r * d + c] * read_elem(dz_k, dz_dtype, r * ncols + j);",
                                    "ak += read_elem(x, x_dtype, r * d + c) * read_elem(dz_k, dz_dtype, r * ncols + j);"),
+    "gret_decay_applied_before_use": (
+        "        for (int e = 0; e < dv; ++e) out[e] += decay * dot * read_elem(v, dtype, (m * heads + h) * dv + e);\n        decay *= gamma[m * heads + h];",
+        "        decay *= gamma[m * heads + h];\n        for (int e = 0; e < dv; ++e) out[e] += decay * dot * read_elem(v, dtype, (m * heads + h) * dv + e);"),
+    "gret_gate_exponent_inverted": ("gamma[i] = pow(sig, 1.0 / tau);", "gamma[i] = pow(sig, tau);"),
+    "gret_start_state_not_decayed": ("out[e] += decay * acc;", "out[e] += acc;"),
+    "gret_step_reads_old_state": (
+        "s[c * dv + e] = gm * s[c * dv + e] + kc * read_elem(v, dtype, bh * dv + e);",
+        "s[c * dv + e] = s[c * dv + e];"),
+    "gret_state_outer_product_transposed": (
+        "for (int e = 0; e < dv; ++e) s[c * dv + e] += kc * read_elem(v, dtype, (m * heads + h) * dv + e);",
+        "for (int e = 0; e < dv; ++e) s[c * dv + e] += kc * read_elem(v, dtype, (m * heads + h) * dv + c % dv);"),
+    "gret_final_state_skips_first_token": ("for (int64_t m = n - 1; m >= 0; --m) {", "for (int64_t m = n - 1; m >= 1; --m) {"),
     "bwd_dy_weight_transposed": ("read_elem(w_k, w_dtype, c * ncols + j);", "read_elem(w_k, w_dtype, j * d + c);"),
 }
 

@@ -78,6 +78,7 @@ class KVCache:
         self.n_seq, self.capacity = n_seq, capacity
         self.n_kv_heads, self.head_dim, self.dtype = n_kv_heads, head_dim, dtype
         self._struct = None
+        self._key = None
 
     @classmethod
     def wrap(cls, k: torch.Tensor, v: torch.Tensor, lens) -> "KVCache":
@@ -90,10 +91,18 @@ class KVCache:
         obj.dtype = k.dtype
         obj.len = np.ascontiguousarray(np.asarray(lens, dtype=np.int64).reshape(obj.n_seq))
         obj._struct = None
+        obj._key = None
         return obj
 
     def struct(self) -> KVCacheStruct:
+        # The descriptor points at the tensors' storage and into ``len``; it is
+        # rebuilt whenever one of them has been replaced.
+        key = (self.k.data_ptr(), self.v.data_ptr(), id(self.len), self.capacity, self.n_seq)
+        if self._struct is not None and self._key == key:
+            return self._struct
         _on_device(self.k, self.v)
+        if self.len.dtype != np.int64 or not self.len.flags.c_contiguous or self.len.shape != (self.n_seq,):
+            raise ValueError("len must be a contiguous int64 array of n_seq entries")
         s = KVCacheStruct()
         s.k = self.k.data_ptr()
         s.v = self.v.data_ptr()
@@ -104,6 +113,7 @@ class KVCache:
         s.head_dim = self.head_dim
         s.dtype = _dt(self.k)
         self._struct = s  # keep alive with the numpy buffer it points into
+        self._key = key
         return s
 
 

@@ -95,6 +95,8 @@ def _declare(lib):
 def lib():
     """The loaded C library (raises if it was never built)."""
     global _lib
+    if _lib is not None:
+        return _lib
     with _lock:
         if _lib is None:
             if not os.path.exists(LIB_PATH):

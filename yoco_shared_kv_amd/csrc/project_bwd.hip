@@ -27,9 +27,10 @@
 //     their tiles are staged [64 rows][256] and read with ds_read_b64_tr_b16.
 //   * pbwd_dy_valu_kernel / pbwd_dw_valu_kernel: the same two products in
 //     fp32 arithmetic for fp32 inputs and for shapes the tiles do not cover.
-//   * pbwd_dx_kernel: per row, s = sum_c g dy/r x (one block reduction),
+//   * pbwd_dx_kernel: per row, s = sum_c g dy/r x (one wave reduction),
 //     then dx = g dy/r - x s / (d r^2) and the row block's share of dgain.
-//   * pbwd_dgain_reduce_kernel: adds the row blocks' dgain shares in order.
+//   * pbwd_dgain_reduce_kernel: adds the row blocks' dgain shares in a fixed
+//     order.
 #include "device_common.h"
 #include "yoco_internal.h"
 
@@ -526,62 +527,133 @@ __global__ __launch_bounds__(256) void pbwd_dw_valu_kernel(const ProjBwdArgs a) 
 // ---------------------------------------------------------------------------
 // Rows: dx = g dy/r - x s / (d r^2) with s = sum_c g dy/r x, and the row
 // block's share of dgain (sum over its rows of dy/r x).  dx holds dy/r on
-// entry.  256 threads take kFinRows rows; thread t owns columns t + 256 i.
+// entry.  A block of 4 waves takes kProjBwdFinRows rows; wave w handles rows
+// w, w+4, ... of the block, lane l owns the column groups l*4 + 256 i (four
+// consecutive columns each, when d % 4 == 0) or, for other widths, single
+// columns l + 64 (4 i + e).  The row sum is a wave reduction.  Each wave
+// keeps its dgain share in its own [d] slice of LDS (dynamic, 4 d floats);
+// the slices are added in wave order at the end.
 // ---------------------------------------------------------------------------
-template <typename TX, int SLOTS>
+template <typename TX>
 __global__ __launch_bounds__(256) void pbwd_dx_kernel(const ProjBwdArgs a) {
-  __shared__ float s_red[4];
-  const int tid = threadIdx.x;
+  extern __shared__ float s_dg[];  // [4][d]
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int d = a.d;
+  const bool vec = d % 4 == 0;
+  const int groups = (d + 255) / 256;
+  float *my_dg = s_dg + wave * d;
+  for (int c = lane; c < d; c += 64) my_dg[c] = 0.f;
+  // Column of element (i, e) of this lane.
+  auto column = [&](int i, int e) __attribute__((always_inline)) {
+    return vec ? lane * 4 + 256 * i + e : lane + 64 * (4 * i + e);
+  };
+  // dy/r, x and g of element group i of row r (zeros past the row's end).
+  auto load = [&](int64_t r, int i, float (&dv)[4], float (&xv)[4], float (&g)[4]) __attribute__((always_inline)) {
+    const float *dxr = a.dx + r * d;
+    if (vec) {
+      const int c = column(i, 0);
+      if (c < d) {
+        const float4 t = *reinterpret_cast<const float4 *>(dxr + c);
+        dv[0] = t.x, dv[1] = t.y, dv[2] = t.z, dv[3] = t.w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xv[e] = elem<TX>(a.x, r * d + c + e);
+        if (a.gain) {
+          const float4 gg = *reinterpret_cast<const float4 *>(a.gain + c);
+          g[0] = gg.x, g[1] = gg.y, g[2] = gg.z, g[3] = gg.w;
+        } else {
+          g[0] = g[1] = g[2] = g[3] = 1.f;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dv[e] = xv[e] = g[e] = 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = column(i, e);
+        dv[e] = (c < d) ? dxr[c] : 0.f;
+        xv[e] = (c < d) ? elem<TX>(a.x, r * d + c) : 0.f;
+        g[e] = (c < d) ? (a.gain ? a.gain[c] : 1.f) : 0.f;
+      }
+    }
+  };
   const int64_t r_begin = static_cast<int64_t>(blockIdx.x) * kProjBwdFinRows;
   const int64_t r_end = r_begin + kProjBwdFinRows < a.n ? r_begin + kProjBwdFinRows : a.n;
-  float g[SLOTS], dg[SLOTS];
-#pragma unroll
-  for (int i = 0; i < SLOTS; ++i) {
-    const int c = tid + 256 * i;
-    g[i] = (c < d) ? (a.gain ? a.gain[c] : 1.f) : 0.f;
-    dg[i] = 0.f;
-  }
-  for (int64_t r = r_begin; r < r_end; ++r) {
-    float *dxr = a.dx + r * d;
-    float xv[SLOTS], dv[SLOTS];
+  for (int64_t r = r_begin + wave; r < r_end; r += 4) {
     float s = 0.f;
+#pragma unroll 2
+    for (int i = 0; i < groups; ++i) {
+      float dv[4], xv[4], g[4];
+      load(r, i, dv, xv, g);
 #pragma unroll
-    for (int i = 0; i < SLOTS; ++i) {
-      const int c = tid + 256 * i;
-      xv[i] = (c < d) ? elem<TX>(a.x, r * d + c) : 0.f;
-      dv[i] = (c < d) ? dxr[c] : 0.f;
-      s = fmaf(g[i] * dv[i], xv[i], s);
+      for (int e = 0; e < 4; ++e) s = fmaf(g[e] * dv[e], xv[e], s);
     }
     s = pb::wave_sum(s);
-    if ((tid & 63) == 0) s_red[tid >> 6] = s;
-    __syncthreads();
-    s = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
-    __syncthreads();  // s_red is rewritten for the next row
     const float inv = a.inv_r[r];
     const float coef = inv * inv * s / static_cast<float>(d);
+    float *dxr = a.dx + r * d;
+    // Second sweep over the row (in cache): every lane has read all of its
+    // elements above, so the in-place stores cannot overtake a read.
+#pragma unroll 2
+    for (int i = 0; i < groups; ++i) {
+      float dv[4], xv[4], g[4], o[4];
+      load(r, i, dv, xv, g);
 #pragma unroll
-    for (int i = 0; i < SLOTS; ++i) {
-      const int c = tid + 256 * i;
-      if (c < d) dxr[c] = g[i] * dv[i] - xv[i] * coef;
-      dg[i] = fmaf(dv[i], xv[i], dg[i]);
+      for (int e = 0; e < 4; ++e) o[e] = g[e] * dv[e] - xv[e] * coef;
+      if (vec) {
+        const int c = column(i, 0);
+        if (c < d) {
+          *reinterpret_cast<float4 *>(dxr + c) = make_float4(o[0], o[1], o[2], o[3]);
+          float4 t = *reinterpret_cast<float4 *>(my_dg + c);
+          t.x = fmaf(dv[0], xv[0], t.x);
+          t.y = fmaf(dv[1], xv[1], t.y);
+          t.z = fmaf(dv[2], xv[2], t.z);
+          t.w = fmaf(dv[3], xv[3], t.w);
+          *reinterpret_cast<float4 *>(my_dg + c) = t;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = column(i, e);
+          if (c < d) {
+            dxr[c] = o[e];
+            my_dg[c] = fmaf(dv[e], xv[e], my_dg[c]);
+          }
+        }
+      }
     }
   }
   if (a.dgain == nullptr) return;
-#pragma unroll
-  for (int i = 0; i < SLOTS; ++i) {
-    const int c = tid + 256 * i;
-    if (c < d) a.dgain_part[static_cast<int64_t>(blockIdx.x) * d + c] = dg[i];
+  __syncthreads();
+  for (int c = threadIdx.x; c < d; c += 256) {
+    const float v = ((s_dg[c] + s_dg[d + c]) + s_dg[2 * d + c]) + s_dg[3 * d + c];
+    a.dgain_part[static_cast<int64_t>(blockIdx.x) * d + c] = v;
   }
 }
 
-// dgain[c] += sum over row blocks of their shares, in block order.
+// dgain[c] += sum over row blocks of their shares.  A block takes 16
+// columns; thread (slice, column) sums a contiguous run of row blocks, and
+// the 16 runs are added in order.
 __global__ __launch_bounds__(256) void pbwd_dgain_reduce_kernel(const ProjBwdArgs a, int n_blocks) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= a.d) return;
-  float s = a.dgain[c];
-  for (int b = 0; b < n_blocks; ++b) s += a.dgain_part[static_cast<int64_t>(b) * a.d + c];
-  a.dgain[c] = s;
+  __shared__ float s_part[16][16];
+  const int cl = threadIdx.x & 15;
+  const int slice = threadIdx.x >> 4;
+  const int c = blockIdx.x * 16 + cl;
+  const int per = (n_blocks + 15) / 16;
+  const int b0 = slice * per;
+  const int b1 = b0 + per < n_blocks ? b0 + per : n_blocks;
+  float s = 0.f;
+  if (c < a.d) {
+    for (int b = b0; b < b1; ++b) s += a.dgain_part[static_cast<int64_t>(b) * a.d + c];
+  }
+  s_part[slice][cl] = s;
+  __syncthreads();
+  if (slice == 0 && c < a.d) {
+    float t = a.dgain[c];
+    for (int k = 0; k < 16; ++k) t += s_part[k][cl];
+    a.dgain[c] = t;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -611,13 +683,8 @@ void project_bwd_split_plan(int64_t n, int32_t d, int32_t ncols, int32_t n_out, 
 template <typename TX>
 hipError_t launch_dx(const ProjBwdArgs &a, hipStream_t s) {
   const unsigned blocks = static_cast<unsigned>((a.n + kProjBwdFinRows - 1) / kProjBwdFinRows);
-  if (a.d <= 1024) {
-    hipLaunchKernelGGL((pbwd_dx_kernel<TX, 4>), dim3(blocks), dim3(256), 0, s, a);
-  } else if (a.d <= 4096) {
-    hipLaunchKernelGGL((pbwd_dx_kernel<TX, 16>), dim3(blocks), dim3(256), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((pbwd_dx_kernel<TX, 64>), dim3(blocks), dim3(256), 0, s, a);
-  }
+  const size_t lds = static_cast<size_t>(4) * a.d * sizeof(float);  // <= 64 KiB for d <= kProjBwdMaxD
+  hipLaunchKernelGGL((pbwd_dx_kernel<TX>), dim3(blocks), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
@@ -666,7 +733,7 @@ hipError_t launch_project_bwd(const ProjBwdArgs &a, hipStream_t s) {
   }
   if (e != hipSuccess || a.dgain == nullptr) return e;
   const int n_blocks = static_cast<int>((a.n + kProjBwdFinRows - 1) / kProjBwdFinRows);
-  hipLaunchKernelGGL(pbwd_dgain_reduce_kernel, dim3((a.d + 255) / 256), dim3(256), 0, s, a, n_blocks);
+  hipLaunchKernelGGL(pbwd_dgain_reduce_kernel, dim3((a.d + 15) / 16), dim3(256), 0, s, a, n_blocks);
   return hipGetLastError();
 }
 

@@ -103,7 +103,7 @@ hipError_t launch_prefill_bwd(const BwdArgs &a, int head_dim, hipStream_t s);
 // (or the caller's bf16 dz), dw_part [splits][n_out][d][ncols]; dgain_part
 // [ceil(n / kProjBwdFinRows)][d].
 constexpr int kProjBwdFinRows = 64;     // input rows per block of the dx kernel
-constexpr int kProjBwdMaxD = 16384;     // d_model bound of the dx kernel's registers
+constexpr int kProjBwdMaxD = 4096;      // d_model bound: the dx kernel keeps 4 x d floats in LDS (64 KiB)
 struct ProjBwdArgs {
   const void *x;             // [n][d]
   const float *gain;         // [d] or null
