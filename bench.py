@@ -454,6 +454,72 @@ def bench_project_bwd(args, torch, y, W):
     return dict(ms=avg, ms_p10=pct(ms, 10), ms_p50=pct(ms, 50), ms_p90=pct(ms, 90), tflops=tflops, flops=flops)
 
 
+def bench_gret(args, torch, y, W):
+    """Gated retention (the self-decoder's token mixer) at the 3B shapes:
+    the chunkwise prefill of 32768 positions x 24 heads of 128 (bf16), and
+    one generation step of 13 self layers (recurrent, fp32 states of
+    [24, 128, 128]) for batch 1."""
+    cfg = W.GRET_32K
+    log(f"generating gated-retention workload N={cfg['n']}")
+    c = W.make_gret(**cfg, dtype=W.BF16, seed=0)
+    n, heads, dh = cfg["n"], cfg["n_heads"], cfg["head_dim"]
+    q, k, v = to_dev(c.q, torch), to_dev(c.k, torch), to_dev(c.v, torch)
+    g = torch.from_numpy(c.gate).cuda()
+    o = torch.empty((n, heads, dh), dtype=torch.float32, device="cuda")
+    s_out = torch.empty((heads, dh, dh), dtype=torch.float32, device="cuda")
+    ws = torch.empty(y.gret_prefill_workspace_bytes(n, heads, dh, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def pre():
+        y.lib().yoco_gret_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), 1, g.data_ptr(), c.tau, n, heads, dh,
+                                  None, o.data_ptr(), s_out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                  stream.cuda_stream)
+
+    pre()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.prefill_reps)]
+    for s_ev, e_ev in evs:
+        s_ev.record(stream)
+        pre()
+        e_ev.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    avg = float(np.mean(ms))
+    # Algorithmic bytes: q, k, v (bf16) and the gate logits read once, o (fp32) written once.
+    alg = n * heads * (3 * dh * 2 + 4 + dh * 4)
+    gbps = alg / (avg * 1e-3) / 1e9
+    log(f"gret prefill {avg:.3f} ms -> {gbps:.0f} GB/s algorithmic")
+    # One generation step of 13 self layers, batch 1.
+    layers = 13
+    cd = W.make_gret(n=layers, n_heads=heads, head_dim=dh, dtype=W.BF16, seed=1)
+    qd, kd, vd = to_dev(cd.q, torch), to_dev(cd.k, torch), to_dev(cd.v, torch)
+    gd = torch.from_numpy(cd.gate).cuda()
+    states = torch.zeros((layers, 1, heads, dh, dh), dtype=torch.float32, device="cuda")
+    od = torch.empty((layers, 1, heads, dh), dtype=torch.float32, device="cuda")
+
+    def dec():
+        for l in range(layers):
+            y.gret_decode(qd[l:l + 1], kd[l:l + 1], vd[l:l + 1], gd[l:l + 1], cd.tau, states[l], out=od[l],
+                          stream=stream)
+
+    for _ in range(3):
+        dec()
+    torch.cuda.synchronize()
+    d_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.prefill_reps)]
+    for s_ev, e_ev in d_evs:
+        s_ev.record(stream)
+        dec()
+        e_ev.record(stream)
+    torch.cuda.synchronize()
+    dms = [a.elapsed_time(b) for a, b in d_evs]
+    davg = float(np.mean(dms))
+    log(f"gret decode step (13 layers) {davg * 1e3:.1f} us")
+    return dict(ms=avg, ms_p10=pct(ms, 10), ms_p50=pct(ms, 50), ms_p90=pct(ms, 90), gbps=gbps, bytes=alg,
+                decode_us=davg * 1e3, decode_p50_us=pct(dms, 50) * 1e3)
+
+
 def cpu_baseline(dec, W):
     import oracle
     case = dec["case"]
@@ -491,6 +557,7 @@ def main():
     proj = None if args.no_prefill else bench_project(args, torch, y, W)
     bwd = None if args.no_prefill else bench_backward(args, torch, y, W)
     pbwd = None if args.no_prefill else bench_project_bwd(args, torch, y, W)
+    gret = None if args.no_prefill else bench_gret(args, torch, y, W)
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec, W)
     # The committed counters were taken on the 128K workload.
     traffic, why = counter_traffic() if args.workload == "decode128k" else (None, "counters cover decode128k only")
@@ -598,6 +665,21 @@ def main():
                          "unit": "TFLOP/s", "frac": round(pbwd["tflops"] / BF16_DENSE_PEAK_TFLOPS, 4),
                          "flops_per_launch": pbwd["flops"],
                          "flops_convention": "dy = dZ W^T and dW = y^T dZ, 2 n d (2 ncols) flops each"},
+        }
+    if gret is not None:
+        result["gret_self_decoder"] = {
+            "workload": "gated retention at the 3B self-decoder shapes: chunkwise prefill of 32768 positions x 24 "
+                        "heads of 128 (bf16 q/k/v, fp32 gates, o and states; tau 16), and one generation step of "
+                        "13 self layers at batch 1 (recurrent, fp32 [24,128,128] states)",
+            "prefill_ms": round(gret["ms"], 4),
+            "prefill_ms_p10_p50_p90": [round(gret["ms_p10"], 4), round(gret["ms_p50"], 4), round(gret["ms_p90"], 4)],
+            "prefill_roofline": {"bound": "hbm", "achieved": round(gret["gbps"], 1), "peak": HBM_PEAK_GBPS,
+                                 "unit": "GB/s", "frac": round(gret["gbps"] / HBM_PEAK_GBPS, 4),
+                                 "bytes_per_launch": gret["bytes"],
+                                 "bytes_convention": "q, k, v (bf16) and gate logits read once, o (fp32) written "
+                                                     "once; chunk states are implementation traffic"},
+            "decode_step_us": round(gret["decode_us"], 2),
+            "decode_step_p50_us": round(gret["decode_p50_us"], 2),
         }
     print(json.dumps(result), flush=True)
 

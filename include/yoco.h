@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define YOCO_ABI_VERSION 4
+#define YOCO_ABI_VERSION 5
 #define YOCO_MAX_SEQ 256
 
 /* Storage types. */
@@ -347,6 +347,52 @@ yoco_status yoco_cross_attn_decode(const void *q, int32_t q_dtype, int32_t n_q_h
                                    const yoco_kv_cache *cache, float softmax_scale, float *o,
                                    float *lse, void *workspace, size_t workspace_bytes,
                                    int64_t rows_per_split, void *stream);
+
+/* ---- Gated retention (gRet), the self-decoder's token mixer -------------
+ * [Notes] "YOCO：You Only Cache Once 中文精读笔记" section 2.2, Eq. 4-5 and
+ * section 2.3 (chunkwise form); [Deep] section 3.1.  The self-decoder output
+ * M that yoco_kv_project turns into the shared cache comes from layers built
+ * around this mixer.  Per head, with q_t, k_t, v_t of length head_dim and
+ * the head-wise gate gamma_t = sigmoid(g_t)^(1/tau):
+ *   S_t = gamma_t S_{t-1} + k_t^T v_t,   o_t = q_t S_t             (Eq. 5)
+ * equal to O = (Q K^T (.) D) V, D[t][m] = prod_{i=m+1..t} gamma_i (Eq. 4).
+ * q and k enter as given (a position rotation, if any, is applied by the
+ * caller); the output is before the per-head normalisation, gate and W_O of
+ * the full layer.  States are fp32 [heads][head_dim][head_dim] per sequence
+ * (row index: key element, column: value element), outputs fp32.
+ * tau must be finite and > 0 (BAD_VALUE otherwise). */
+
+/* Bytes of device workspace yoco_gret_prefill needs: nonzero only for the
+ * chunkwise matrix-core path (bf16, head_dim 128).  Errors: NULL_POINTER,
+ * BAD_SHAPE, BAD_DTYPE. */
+yoco_status yoco_gret_prefill_workspace(int64_t n, int32_t n_heads, int32_t head_dim, int32_t dtype,
+                                        size_t *bytes);
+
+/* A block of n positions of one sequence (prefill, or the training forward
+ * of the mixer).  q, k, v: [n][n_heads][head_dim] in dtype; gate_logits:
+ * [n][n_heads] fp32 (g = x W_gamma); state_in: [n_heads][D][D] fp32, the
+ * state before the block, or NULL for a fresh sequence; o: [n][n_heads][D]
+ * fp32, written; state_out: [n_heads][D][D] fp32 (the state after the
+ * block, which yoco_gret_decode continues from), or NULL.  state_in and
+ * state_out must not overlap o.  bf16 with head_dim 128 runs the chunkwise
+ * form on MFMA (chunks of 128 positions; q.k scores and the carried state
+ * rounded to bf16 for the products, fp32 accumulation); other inputs run the
+ * recurrent form in fp32 (one workgroup per head, sequential over the
+ * positions).  n == 0 is a no-op.  Errors: NULL_POINTER; BAD_SHAPE; BAD_DTYPE;
+ * BAD_VALUE (tau); WORKSPACE. */
+yoco_status yoco_gret_prefill(const void *q, const void *k, const void *v, int32_t dtype,
+                              const float *gate_logits, float tau, int64_t n, int32_t n_heads,
+                              int32_t head_dim, const float *state_in, float *o, float *state_out,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* One generation step of every sequence: q, k, v: [n_seq][n_heads][D] in
+ * dtype, gate_logits: [n_seq][n_heads] fp32; state: [n_seq][n_heads][D][D]
+ * fp32, updated in place (S <- gamma S + k^T v); o: [n_seq][n_heads][D] fp32
+ * = q times the updated state.  n_seq == 0 is a no-op.  Errors as
+ * yoco_gret_prefill (state NULL -> NULL_POINTER). */
+yoco_status yoco_gret_decode(const void *q, const void *k, const void *v, int32_t dtype,
+                             const float *gate_logits, float tau, int32_t n_seq, int32_t n_heads,
+                             int32_t head_dim, float *state, float *o, void *stream);
 
 #ifdef __cplusplus
 }

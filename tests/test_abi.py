@@ -27,7 +27,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = _lib()
     names = _declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 20, names
     for name in names:
         assert hasattr(lib, name), f"{name} declared in yoco.h but not exported"
 
@@ -338,3 +338,38 @@ def test_project_bwd_workspace_layout():
                                 1 << 20, None) == _status("YOCO_ERR_BAD_SHAPE")
     assert L.yoco_q_project_bwd(FAKE, 1, 4, 32, None, 1e-6, None, 1, 4, 64, FAKE, 0, FAKE, FAKE, None, FAKE,
                                 1 << 20, None) == _status("YOCO_ERR_NULL_POINTER")
+
+
+def test_gret_rejects_and_sizes_workspace():
+    L = _lib()
+    def pre(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, dt=1, g=FAKE, tau=16.0, n=300, h=3, dh=128, s_in=None, o=FAKE, s_out=None,
+                 ws=FAKE, ws_bytes=1 << 30)
+        a.update(kw)
+        return L.yoco_gret_prefill(a["q"], a["k"], a["v"], a["dt"], a["g"], a["tau"], a["n"], a["h"], a["dh"],
+                                   a["s_in"], a["o"], a["s_out"], a["ws"], a["ws_bytes"], None)
+    assert pre(q=None) == _status("YOCO_ERR_NULL_POINTER")
+    assert pre(g=None) == _status("YOCO_ERR_NULL_POINTER")
+    assert pre(dh=96) == _status("YOCO_ERR_BAD_SHAPE")
+    assert pre(h=0) == _status("YOCO_ERR_BAD_SHAPE")
+    assert pre(n=-1) == _status("YOCO_ERR_BAD_SHAPE")
+    assert pre(dt=4) == _status("YOCO_ERR_BAD_DTYPE")
+    for tau in (0.0, -1.0, float("inf"), float("nan")):
+        assert pre(tau=tau) == _status("YOCO_ERR_BAD_VALUE")
+    assert pre(ws_bytes=100) == _status("YOCO_ERR_WORKSPACE")
+    assert pre(n=0) == 0
+    out = ctypes.c_size_t(0)
+    # chunkwise path: cumulative gates, chunk states (fp32), carried states (bf16), 256-byte aligned
+    assert L.yoco_gret_prefill_workspace(300, 3, 128, 1, ctypes.byref(out)) == 0
+    lcum = (300 * 3 * 4 + 255) // 256 * 256
+    assert out.value == lcum + 3 * 3 * 128 * 128 * 4 + 3 * 3 * 128 * 128 * 2
+    assert L.yoco_gret_prefill_workspace(300, 3, 128, 0, ctypes.byref(out)) == 0 and out.value == 0
+    assert L.yoco_gret_prefill_workspace(300, 3, 64, 1, ctypes.byref(out)) == 0 and out.value == 0
+    assert pre(dt=0, ws=None, ws_bytes=0) != _status("YOCO_ERR_WORKSPACE")
+    dec = lambda **kw: L.yoco_gret_decode(kw.get("q", FAKE), FAKE, FAKE, 1, FAKE, kw.get("tau", 16.0),
+                                         kw.get("b", 2), 3, kw.get("dh", 128), kw.get("st", FAKE), FAKE, None)
+    assert dec(st=None) == _status("YOCO_ERR_NULL_POINTER")
+    assert dec(dh=32) == _status("YOCO_ERR_BAD_SHAPE")
+    assert dec(b=-1) == _status("YOCO_ERR_BAD_SHAPE")
+    assert dec(tau=0.0) == _status("YOCO_ERR_BAD_VALUE")
+    assert dec(b=0) == 0

@@ -387,3 +387,34 @@ RAGGED_16 = dict(n_seq=16, lo=RAGGED_LO, hi=RAGGED_HI, n_q_heads=24, n_kv_heads=
                  head_dim=128, layers=13)
 NEEDLE_1M = dict(n_rows=1 << 20, n_q_heads=24, n_kv_heads=8, head_dim=128, layers=13)
 PROJECT_3B = dict(n=32768, d_model=3072, n_kv_heads=8, head_dim=128)
+
+
+# ---------------------------------------------------------------------------
+# Gated retention (self-decoder token mixer) at the 3B shapes: 24 heads of
+# 128 ([Blog] s.7: each self layer keeps a [24, 128, 128] state).
+# ---------------------------------------------------------------------------
+GRET_TAU = 16.0  # the pages give tau no value; 16 is the reading taken
+
+
+@dataclasses.dataclass
+class GretCase:
+    q: np.ndarray       # [n, H, D]
+    k: np.ndarray       # [n, H, D], scaled by D^-1/2 before storing
+    v: np.ndarray       # [n, H, D]
+    gate: np.ndarray    # [n, H] float32 logits
+    tau: float
+    dtype: str
+
+
+def make_gret(n: int = 32768, n_heads: int = 24, head_dim: int = 128, dtype: str = BF16, seed: int = 0,
+              tau: float = GRET_TAU, gate_mean: float = 0.0) -> GretCase:
+    """q, v ~ N(0,1); k ~ N(0,1) / sqrt(D); gate logits ~ N(gate_mean, 1).
+    Streams 30 q, 31 k, 32 v, 33 gate."""
+    q = store(_normal(seed, 30, (n, n_heads, head_dim)), dtype)
+    k = store(_normal(seed, 31, (n, n_heads, head_dim), 1.0 / math.sqrt(head_dim)), dtype)
+    v = store(_normal(seed, 32, (n, n_heads, head_dim)), dtype)
+    gate = (gate_mean + _normal(seed, 33, (n, n_heads))).astype(np.float32)
+    return GretCase(q=q, k=k, v=v, gate=gate, tau=tau, dtype=dtype)
+
+
+GRET_32K = dict(n=32768, n_heads=24, head_dim=128)

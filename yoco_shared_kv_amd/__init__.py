@@ -15,6 +15,8 @@ The functions mirror the C entry points:
 * ``cross_attn_prefill_bwd`` -> ``yoco_cross_attn_prefill_bwd`` (training backward of one layer)
 * ``kv_project_bwd`` / ``q_project_bwd`` -> ``yoco_kv_project_bwd`` / ``yoco_q_project_bwd``
   (backward of the fused RMSNorm + projections)
+* ``gret_prefill`` / ``gret_decode`` -> ``yoco_gret_prefill`` / ``yoco_gret_decode``
+  (gated retention, the self-decoder's token mixer: chunkwise block, recurrent step)
 """
 from __future__ import annotations
 
@@ -32,7 +34,7 @@ __all__ = [
     "KVCache", "YocoError", "kv_project", "kv_append", "q_project", "cross_attn_prefill",
     "cross_attn_decode", "decode_workspace", "decode_workspace_bytes", "kv_cache_bytes", "lib",
     "cross_attn_prefill_bwd", "prefill_bwd_workspace_bytes", "kv_project_bwd", "q_project_bwd",
-    "project_bwd_workspace_bytes",
+    "project_bwd_workspace_bytes", "gret_prefill", "gret_decode", "gret_prefill_workspace_bytes",
 ]
 
 _DT = {torch.float32: YOCO_DT_F32, torch.bfloat16: YOCO_DT_BF16}
@@ -317,6 +319,52 @@ def q_project_bwd(x: torch.Tensor, w_q: torch.Tensor, dz_q: torch.Tensor, n_q_he
                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
                                    _stream(stream)))
     return d_x, d_w_q, d_gain
+
+
+def gret_prefill_workspace_bytes(n: int, n_heads: int, head_dim: int, dtype: torch.dtype) -> int:
+    out = ctypes.c_size_t(0)
+    check(lib().yoco_gret_prefill_workspace(n, n_heads, head_dim, _DT.get(dtype, -1), ctypes.byref(out)))
+    return int(out.value)
+
+
+def gret_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate_logits: torch.Tensor, tau: float,
+                 state_in: Optional[torch.Tensor] = None, want_state: bool = False,
+                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Gated retention over a block: q, k, v ``[n, H, D]``, gate_logits
+    ``[n, H]`` fp32, state_in ``[H, D, D]`` fp32 or None.  Returns o
+    ``[n, H, D]`` fp32 (and the state after the block)."""
+    _on_device(q, k, v, gate_logits, state_in)
+    n, heads, dh = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must be matching [n, H, D] tensors")
+    if gate_logits.dtype != torch.float32 or gate_logits.shape != (n, heads):
+        raise ValueError("gate_logits must be float32 [n, H]")
+    if out is None:
+        out = torch.empty((n, heads, dh), dtype=torch.float32, device=q.device)
+    state_out = torch.empty((heads, dh, dh), dtype=torch.float32, device=q.device) if want_state else None
+    nbytes = gret_prefill_workspace_bytes(n, heads, dh, q.dtype)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().yoco_gret_prefill(_ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(gate_logits), float(tau), n, heads, dh,
+                                  _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(workspace), ws_bytes,
+                                  _stream(stream)))
+    return (out, state_out) if want_state else out
+
+
+def gret_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate_logits: torch.Tensor, tau: float,
+                state: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One recurrent step per sequence: q, k, v ``[B, H, D]``, gate_logits
+    ``[B, H]``, state ``[B, H, D, D]`` fp32 updated in place.  Returns o."""
+    _on_device(q, k, v, gate_logits, state)
+    b, heads, dh = q.shape
+    if state.dtype != torch.float32 or state.shape != (b, heads, dh, dh):
+        raise ValueError("state must be float32 [B, H, D, D]")
+    if out is None:
+        out = torch.empty((b, heads, dh), dtype=torch.float32, device=q.device)
+    check(lib().yoco_gret_decode(_ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(gate_logits), float(tau), b, heads, dh,
+                                 _ptr(state), _ptr(out), _stream(stream)))
+    return out
 
 
 def decode_workspace_bytes(cache: KVCache, n_q_heads: int, rows_per_split: int = 0) -> int:

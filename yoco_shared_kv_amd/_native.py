@@ -85,6 +85,12 @@ def _declare(lib):
     lib.yoco_q_project_bwd.restype = st
     lib.yoco_q_project_bwd.argtypes = [vp, i32, i64, i32, vp, f32, vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, sz,
                                        vp]
+    lib.yoco_gret_prefill_workspace.restype = st
+    lib.yoco_gret_prefill_workspace.argtypes = [i64, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.yoco_gret_prefill.restype = st
+    lib.yoco_gret_prefill.argtypes = [vp, vp, vp, i32, vp, f32, i64, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.yoco_gret_decode.restype = st
+    lib.yoco_gret_decode.argtypes = [vp, vp, vp, i32, vp, f32, i32, i32, i32, vp, vp, vp]
     lib.yoco_cross_attn_decode_workspace.restype = st
     lib.yoco_cross_attn_decode_workspace.argtypes = [cp, i32, i64, ctypes.POINTER(sz)]
     lib.yoco_cross_attn_decode.restype = st

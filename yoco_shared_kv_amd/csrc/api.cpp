@@ -705,3 +705,112 @@ yoco_status yoco_q_project_bwd(const void *x, int32_t x_dtype, int64_t n, int32_
 }
 
 }  // extern "C"
+
+namespace {
+
+// Workspace of the chunkwise gated-retention prefill, 256-byte aligned
+// regions: cumulative log gates, chunk states (fp32), carried states (bf16).
+struct GretLayout {
+  size_t lcum = 0, u = 0, rb = 0, total = 0;
+};
+
+GretLayout gret_layout(int64_t n, int32_t heads, int32_t head_dim, int32_t dtype) {
+  GretLayout L;
+  if (!yoco::gret_chunked_applies(dtype, head_dim) || n <= 0) return L;
+  const int64_t chunks = yoco::gret_n_chunks(n);
+  const size_t state = static_cast<size_t>(head_dim) * head_dim;
+  size_t off = 0;
+  L.lcum = off;
+  off = align256(off + static_cast<size_t>(n) * heads * 4);
+  L.u = off;
+  off = align256(off + static_cast<size_t>(chunks) * heads * state * 4);
+  L.rb = off;
+  off = align256(off + static_cast<size_t>(chunks) * heads * state * 2);
+  L.total = off;
+  return L;
+}
+
+yoco_status check_gret(const void *q, const void *k, const void *v, const float *gate, const float *o, int32_t dtype,
+                       int32_t heads, int32_t head_dim, float tau) {
+  if (q == nullptr || k == nullptr || v == nullptr || gate == nullptr || o == nullptr)
+    return fail(YOCO_ERR_NULL_POINTER, "q, k, v, gate_logits or o is NULL");
+  if (heads < 1 || heads > 4096) return fail(YOCO_ERR_BAD_SHAPE, "n_heads %d outside [1, 4096]", heads);
+  if (!head_dim_ok(head_dim)) return fail(YOCO_ERR_BAD_SHAPE, "head_dim %d is not 64 or 128", head_dim);
+  if (!dtype_ok(dtype)) return fail(YOCO_ERR_BAD_DTYPE, "dtype %d unknown", dtype);
+  if (!std::isfinite(tau) || tau <= 0.f) return fail(YOCO_ERR_BAD_VALUE, "tau %g must be finite and > 0", tau);
+  return YOCO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+yoco_status yoco_gret_prefill_workspace(int64_t n, int32_t n_heads, int32_t head_dim, int32_t dtype, size_t *bytes) {
+  if (bytes == nullptr) return fail(YOCO_ERR_NULL_POINTER, "bytes is NULL");
+  if (n < 0 || n_heads < 1 || !head_dim_ok(head_dim))
+    return fail(YOCO_ERR_BAD_SHAPE, "n %lld, n_heads %d, head_dim %d", (long long)n, n_heads, head_dim);
+  if (!dtype_ok(dtype)) return fail(YOCO_ERR_BAD_DTYPE, "dtype %d unknown", dtype);
+  *bytes = gret_layout(n, n_heads, head_dim, dtype).total;
+  return ok();
+}
+
+yoco_status yoco_gret_prefill(const void *q, const void *k, const void *v, int32_t dtype, const float *gate_logits,
+                              float tau, int64_t n, int32_t n_heads, int32_t head_dim, const float *state_in, float *o,
+                              float *state_out, void *workspace, size_t workspace_bytes, void *stream) {
+  yoco_status st = check_gret(q, k, v, gate_logits, o, dtype, n_heads, head_dim, tau);
+  if (st != YOCO_OK) return st;
+  if (n < 0) return fail(YOCO_ERR_BAD_SHAPE, "n %lld < 0", (long long)n);
+  const GretLayout L = gret_layout(n, n_heads, head_dim, dtype);
+  if (L.total > 0 && (workspace == nullptr || workspace_bytes < L.total))
+    return fail(YOCO_ERR_WORKSPACE, "workspace %zu bytes < %zu (yoco_gret_prefill_workspace)", workspace_bytes,
+                L.total);
+  if (n == 0) return ok();
+  if ((st = check_device()) != YOCO_OK) return st;
+  yoco::GretArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.gate = gate_logits;
+  a.state_in = state_in;
+  a.state_out = state_out;
+  a.o = o;
+  a.n_tokens = n;
+  a.heads = n_heads;
+  a.inv_tau = 1.0f / tau;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (L.total > 0) {
+    char *ws = static_cast<char *>(workspace);
+    a.lcum = reinterpret_cast<float *>(ws + L.lcum);
+    a.u = reinterpret_cast<float *>(ws + L.u);
+    a.rb = reinterpret_cast<uint16_t *>(ws + L.rb);
+    return launched(yoco::launch_gret_chunked(a, s), "gret_prefill");
+  }
+  return launched(yoco::launch_gret_recurrent(a, dtype, head_dim, 1, s), "gret_prefill");
+}
+
+yoco_status yoco_gret_decode(const void *q, const void *k, const void *v, int32_t dtype, const float *gate_logits,
+                             float tau, int32_t n_seq, int32_t n_heads, int32_t head_dim, float *state, float *o,
+                             void *stream) {
+  yoco_status st = check_gret(q, k, v, gate_logits, o, dtype, n_heads, head_dim, tau);
+  if (st != YOCO_OK) return st;
+  if (state == nullptr) return fail(YOCO_ERR_NULL_POINTER, "state is NULL");
+  if (n_seq < 0 || static_cast<int64_t>(n_seq) * n_heads > 0x7fffffff)
+    return fail(YOCO_ERR_BAD_SHAPE, "n_seq %d", n_seq);
+  if (n_seq == 0) return ok();
+  if ((st = check_device()) != YOCO_OK) return st;
+  yoco::GretArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.gate = gate_logits;
+  a.state_in = state;
+  a.state_out = state;
+  a.o = o;
+  a.n_tokens = 1;
+  a.heads = n_heads;
+  a.inv_tau = 1.0f / tau;
+  return launched(yoco::launch_gret_recurrent(a, dtype, head_dim, n_seq, static_cast<hipStream_t>(stream)),
+                  "gret_decode");
+}
+
+}  // extern "C"

@@ -1,0 +1,475 @@
+// Gated retention (gRet), the self-decoder's token mixer: recurrent steps
+// for generation and a chunkwise form on the matrix cores for prefill.
+//
+// What it computes ([Notes] "YOCO：You Only Cache Once 中文精读笔记" s.2.2
+// Eq. 4-5 and s.2.3; [Deep] "You Only Cache Once: Decoder-Decoder
+// Architectures for Language Models" s.3.1): per head, with q_t, k_t, v_t of
+// length D and the head-wise gate gamma_t = sigmoid(g_t)^(1/tau),
+//   S_t = gamma_t S_{t-1} + k_t^T v_t,   o_t = q_t S_t           (Eq. 5)
+// which equals the parallel form O = (Q K^T (.) D) V with
+// D[t][m] = prod_{i=m+1..t} gamma_i (Eq. 4).  Decays are handled as
+// cumulative sums of log gamma = logsigmoid(g) / tau, so every factor is
+// exp of a difference <= 0 (no division by a vanishing product).
+//
+// Recurrent path (gret_recurrent_kernel): one workgroup per (sequence,
+// head) keeps the D x D fp32 state in registers (thread t owns four columns
+// of D/32 or D/16 rows) and walks the tokens in order: state update, then
+// o = q S with a reduction over row groups through LDS.  Generation runs one
+// token per sequence; fp32 prefill runs all tokens of one sequence.
+//
+// Chunkwise path (bf16, D = 128), chunks of C = 128 positions
+// ([Notes] s.2.3: parallel inside a chunk, a state passed between chunks):
+//   with l_j the inclusive cumulative log gamma inside the chunk,
+//   U_c     = sum_k exp(l_C - l_k) k_k^T v_k                  (chunk's own state)
+//   R_{c+1} = exp(l_C) R_c + U_c,  R_0 = the start state       (state entering chunk c+1)
+//   O_j     = sum_{k<=j} exp(l_j - l_k) (q_j . k_k) v_k + exp(l_j) q_j R_c
+//   * gret_chunk_state_kernel: l for the chunk (a wave scan), then U_c on
+//     MFMA as K'^T V with K' = exp(l_C - l_k) k_k rounded to bf16; both
+//     operands come from row-major LDS tiles through transposed reads.
+//   * gret_scan_kernel: the sequential pass over chunks, elementwise over
+//     the state (R_c stored in bf16 for the output kernel, the last state
+//     in fp32), with the chunk states loaded a few chunks ahead.
+//   * gret_chunk_out_kernel: 4 waves x 32 query rows of a chunk.  The
+//     carried term O^T = R^T Q^T first (then each lane scales its query
+//     row by exp(l_j)), then per 32-key half S^T = K Q^T, P = S exp(l_j - l_k)
+//     masked to k <= j and rounded to bf16, O^T += V^T P^T -- the layout of
+//     the causal prefill kernel (one query row per lane, Q^T in registers).
+#include "attn_tiles.h"
+
+namespace yoco {
+namespace gr {
+constexpr int kChunk = 128;        // positions per chunk
+constexpr int kD = 128;            // head dim of the chunkwise path
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kSwz = 2;
+constexpr int kRowBytes = kD * 2;                    // 256
+constexpr int kTileBytes = kChunk * kRowBytes;       // 32 KiB: [128][128] bf16
+constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // 8 one-KiB loads
+constexpr int kScanAhead = 4;      // chunk states in flight in the scan
+}  // namespace gr
+
+// log gamma = logsigmoid(g) / tau = (min(g, 0) - log1p(exp(-|g|))) / tau.
+__device__ __forceinline__ float gret_log_gate(float g, float inv_tau) {
+  return (fminf(g, 0.f) - log1pf(expf(-fabsf(g)))) * inv_tau;
+}
+
+// ---------------------------------------------------------------------------
+// Recurrent steps.  Thread t owns state columns 4*(t % (D/4)) .. +3 of rows
+// t / (D/4) + G*i (G = 256 / (D/4) row groups, D/G rows each).
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256) void gret_recurrent_kernel(const GretArgs a) {
+  constexpr int kColThreads = D / 4;
+  constexpr int kGroups = 256 / kColThreads;
+  constexpr int kRows = D / kGroups;
+  __shared__ float s_q[D], s_k[D], s_v[D];
+  __shared__ float s_o[kGroups][D];
+  const int tid = threadIdx.x;
+  const int c0 = (tid % kColThreads) * 4;
+  const int grp = tid / kColThreads;
+  const int b = blockIdx.x / a.heads;
+  const int h = blockIdx.x % a.heads;
+  const int64_t sbase = (static_cast<int64_t>(b) * a.heads + h) * D * D;
+  float S[kRows][4];
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    const int row = grp + kGroups * i;
+    if (a.state_in != nullptr) {
+      const float4 t = *reinterpret_cast<const float4 *>(a.state_in + sbase + row * D + c0);
+      S[i][0] = t.x, S[i][1] = t.y, S[i][2] = t.z, S[i][3] = t.w;
+    } else {
+      S[i][0] = S[i][1] = S[i][2] = S[i][3] = 0.f;
+    }
+  }
+  for (int64_t t = 0; t < a.n_tokens; ++t) {
+    const int64_t tok = (static_cast<int64_t>(b) * a.n_tokens + t) * a.heads + h;
+    __syncthreads();  // the previous token's reads of s_q/s_k/s_v/s_o are done
+    if (tid < D) {
+      s_q[tid] = load_elem(static_cast<const T *>(a.q) + tok * D + tid);
+      s_k[tid] = load_elem(static_cast<const T *>(a.k) + tok * D + tid);
+      s_v[tid] = load_elem(static_cast<const T *>(a.v) + tok * D + tid);
+    }
+    const float gamma = expf(gret_log_gate(a.gate[tok], a.inv_tau));
+    __syncthreads();
+    float vv[4], o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vv[e] = s_v[c0 + e];
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      const int row = grp + kGroups * i;
+      const float kr = s_k[row], qr = s_q[row];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        S[i][e] = fmaf(gamma, S[i][e], kr * vv[e]);
+        o[e] = fmaf(qr, S[i][e], o[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s_o[grp][c0 + e] = o[e];
+    __syncthreads();
+    if (tid < D) {
+      float acc = 0.f;
+#pragma unroll
+      for (int g2 = 0; g2 < kGroups; ++g2) acc += s_o[g2][tid];
+      a.o[tok * D + tid] = acc;
+    }
+  }
+  if (a.state_out == nullptr) return;
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    const int row = grp + kGroups * i;
+    *reinterpret_cast<float4 *>(a.state_out + sbase + row * D + c0) = make_float4(S[i][0], S[i][1], S[i][2], S[i][3]);
+  }
+}
+
+namespace gr {
+// Direct-to-LDS staging of a [128][128] bf16 tile whose row r starts at
+// base + r * stride (elements): load i of wave w fills 1 KiB block
+// b = w * kLoadsPerWave + i = rows 4b .. 4b+3; lane L writes (row 4b + L/16,
+// slot L%16) holding global chunk slot ^ row_xor(row).  The descriptor ends
+// with row rows-1, so rows past it land as zeros.
+__device__ __forceinline__ void stage_rows(char *dst, const bf16_t *base, int stride, int rows, int wave, int lane) {
+  const int bytes = rows > 0 ? ((rows - 1) * stride + kD) * 2 : 0;
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(base), 0, bytes, kBufferFlags);
+#pragma unroll
+  for (int i = 0; i < kLoadsPerWave; ++i) {
+    const int blk = wave * kLoadsPerWave + i;
+    const int row = blk * 4 + (lane >> 4);
+    const int chunk = (lane & 15) ^ row_xor<kD, kSwz>(row);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(dst + blk * 1024), 16,
+                                             static_cast<uint32_t>(row * stride * 2 + chunk * 16), 0, 0, 0);
+  }
+}
+
+// Transposed reads of a row-major [k][128] tile: the A (or B) fragment for
+// output index tile `dt` (32 wide) and k step ks (16 deep): lane i of each
+// 16-lane group receives 4 consecutive k rows of index dt*32 + (group&1)*16
+// + i per read, two reads per fragment.  The order of k within the step is
+// free as long as both operands of a product agree:
+//   kSplitHalves: lanes 0..31 take k rows 0..7 of the step, 32..63 rows
+//                 8..15 (the order of a 16-byte read of a k-contiguous row);
+//   kInterleave:  lanes 0..31 take rows 0..3 and 8..11, 32..63 rows 4..7
+//                 and 12..15 (the order of the 32x32 accumulator rows, so a
+//                 score accumulator serves directly as the other operand).
+enum TrOrder { kSplitHalves = 0, kInterleave = 1 };
+struct TrFrag {
+  int off[2][4];
+  __device__ __forceinline__ void init(int lane, TrOrder order) {
+    const int grp = lane >> 4;
+    const int src_a = lane & 3;
+    const int src_j = (lane >> 2) & 3;
+    const int krow = order == kSplitHalves ? (grp >> 1) * 8 + src_j : (grp >> 1) * 4 + src_j;
+    const int second = order == kSplitHalves ? 4 : 8;
+    const int col = (grp & 1) * 16 + src_a * 4;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) off[r][d] = swz<kD, kSwz>(krow + second * r, d * 32 + col);
+    }
+  }
+  __device__ __forceinline__ bf16x8_t read(const char *tile, int dt, int ks) const {
+    Frag8 f;
+    f.s4[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t *)(tile + off[0][dt] + ks * 16 * kRowBytes));
+    f.s4[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t *)(tile + off[1][dt] + ks * 16 * kRowBytes));
+    return f.v;
+  }
+};
+}  // namespace gr
+
+// ---------------------------------------------------------------------------
+// Per (chunk, head): l (inclusive cumulative log gamma inside the chunk) to
+// the workspace, and U_c = sum_k exp(l_C - l_k) k_k^T v_k (fp32).
+// Wave w computes U rows (key dims) 32w .. 32w+31, all 128 value dims.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(gr::kThreads) void gret_chunk_state_kernel(const GretArgs a) {
+  using namespace gr;
+  __shared__ __attribute__((aligned(1024))) char lds_k[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v[kTileBytes];
+  __shared__ float s_w[kChunk];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int chunk = blockIdx.x / a.heads;
+  const int h = blockIdx.x % a.heads;
+  const int64_t t0 = static_cast<int64_t>(chunk) * kChunk;
+  const int rows = a.n_tokens - t0 < kChunk ? static_cast<int>(a.n_tokens - t0) : kChunk;
+  const int stride = a.heads * kD;
+  const bf16_t *kg = static_cast<const bf16_t *>(a.k) + (t0 * a.heads + h) * kD;
+  const bf16_t *vg = static_cast<const bf16_t *>(a.v) + (t0 * a.heads + h) * kD;
+  stage_rows(lds_v, vg, stride, rows, wave, lane);
+
+  // Wave 0: the chunk's cumulative log gates (lane holds positions 2L, 2L+1).
+  if (wave == 0) {
+    float l0 = 0.f, l1 = 0.f;
+    const int p0 = 2 * lane, p1 = 2 * lane + 1;
+    if (p0 < rows) l0 = gret_log_gate(a.gate[(t0 + p0) * a.heads + h], a.inv_tau);
+    if (p1 < rows) l1 = gret_log_gate(a.gate[(t0 + p1) * a.heads + h], a.inv_tau);
+    l1 += l0;
+    float incl = l1;  // inclusive scan of the pair sums over lanes
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+      const float o = __shfl_up(incl, s, 64);
+      if (lane >= s) incl += o;
+    }
+    const float excl = incl - l1;
+    const float c0v = excl + l0, c1v = excl + l1;
+    const float last = __shfl(incl, 63, 64);  // l_C (rows past the chunk add 0)
+    if (p0 < rows) a.lcum[(t0 + p0) * a.heads + h] = c0v;
+    if (p1 < rows) a.lcum[(t0 + p1) * a.heads + h] = c1v;
+    s_w[p0] = p0 < rows ? expf(last - c0v) : 0.f;
+    s_w[p1] = p1 < rows ? expf(last - c1v) : 0.f;
+  }
+  __syncthreads();
+  // K' = exp(l_C - l_k) k_k in bf16, staged through registers.
+#pragma unroll
+  for (int i = 0; i < kChunk * 16 / kThreads; ++i) {
+    const int piece = i * kThreads + tid;
+    const int row = piece >> 4;
+    const int ch = piece & 15;
+    Frag8 f;
+    f.u = make_uint4(0, 0, 0, 0);
+    if (row < rows) {
+      const uint4 raw = ld16(kg + static_cast<int64_t>(row) * stride + ch * 8);
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      const float sc = s_w[row];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f.w[j] = cvt_pk_bf16(bf16_lo(w[j]) * sc, bf16_hi(w[j]) * sc);
+    }
+    *reinterpret_cast<uint4 *>(lds_k + swz<kD, kSwz>(row, ch * 8)) = f.u;
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  TrFrag fr;  // both operands of K'^T V use the same k order
+  fr.init(lane, kSplitHalves);
+  floatx16 acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
+  }
+#pragma unroll
+  for (int ks = 0; ks < kChunk / 16; ++ks) {
+    const bf16x8_t af = fr.read(lds_k, wave, ks);  // K'^T rows 32*wave + lane%32
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, fr.read(lds_v, t, ks), acc[t], 0, 0, 0);
+  }
+  // acc[t] element e: U row 32*wave + (e/4)*8 + half*4 + e%4, column t*32 + lane%32.
+  float *u = a.u + (static_cast<int64_t>(chunk) * a.heads + h) * kD * kD;
+  const int half = lane >> 5;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = wave * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+      u[row * kD + t * 32 + (lane & 31)] = acc[t][e];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The pass over chunks: R_0 = start state, R_{c+1} = exp(l_C) R_c + U_c.
+// Thread owns 4 consecutive state elements of one head; R_c goes out in bf16
+// (for the output kernel), the state after the last chunk in fp32.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gret_scan_kernel(const GretArgs a, int n_chunks) {
+  using namespace gr;
+  constexpr int kPerHead = kD * kD / 4;  // float4s per state
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<int64_t>(a.heads) * kPerHead) return;
+  const int h = static_cast<int>(idx / kPerHead);
+  const int e4 = static_cast<int>(idx % kPerHead);
+  float4 r = a.state_in ? reinterpret_cast<const float4 *>(a.state_in + static_cast<int64_t>(h) * kD * kD)[e4]
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+  auto u_at = [&](int c) __attribute__((always_inline)) {
+    return reinterpret_cast<const float4 *>(a.u + (static_cast<int64_t>(c) * a.heads + h) * kD * kD)[e4];
+  };
+  auto lc_at = [&](int c) __attribute__((always_inline)) {
+    const int64_t last = (static_cast<int64_t>(c) + 1) * kChunk - 1 < a.n_tokens - 1
+                             ? (static_cast<int64_t>(c) + 1) * kChunk - 1 : a.n_tokens - 1;
+    return a.lcum[last * a.heads + h];
+  };
+  float4 ring[kScanAhead];
+  float lring[kScanAhead];
+#pragma unroll
+  for (int j = 0; j < kScanAhead; ++j) {
+    if (j < n_chunks) {
+      ring[j] = u_at(j);
+      lring[j] = lc_at(j);
+    }
+  }
+  for (int c0 = 0; c0 < n_chunks; c0 += kScanAhead) {
+#pragma unroll
+    for (int j = 0; j < kScanAhead; ++j) {
+      const int c = c0 + j;
+      if (c < n_chunks) {
+        uint2 packed;
+        packed.x = cvt_pk_bf16(r.x, r.y);
+        packed.y = cvt_pk_bf16(r.z, r.w);
+        reinterpret_cast<uint2 *>(a.rb + (static_cast<int64_t>(c) * a.heads + h) * kD * kD)[e4] = packed;
+        const float dec = expf(lring[j]);
+        const float4 u = ring[j];
+        r.x = fmaf(dec, r.x, u.x);
+        r.y = fmaf(dec, r.y, u.y);
+        r.z = fmaf(dec, r.z, u.z);
+        r.w = fmaf(dec, r.w, u.w);
+        if (c + kScanAhead < n_chunks) {
+          ring[j] = u_at(c + kScanAhead);
+          lring[j] = lc_at(c + kScanAhead);
+        }
+      }
+    }
+  }
+  if (a.state_out) reinterpret_cast<float4 *>(a.state_out + static_cast<int64_t>(h) * kD * kD)[e4] = r;
+}
+
+// ---------------------------------------------------------------------------
+// Outputs of one chunk of one head: wave w owns query rows 32w .. 32w+31.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(gr::kThreads) void gret_chunk_out_kernel(const GretArgs a) {
+  using namespace gr;
+  __shared__ __attribute__((aligned(1024))) char lds_k[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_r[kTileBytes];
+  __shared__ float s_l[kChunk];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  // Chunks in reverse order, so the ragged last chunk does not run last.
+  const int n_chunks = static_cast<int>((a.n_tokens + kChunk - 1) / kChunk);
+  const int chunk = n_chunks - 1 - static_cast<int>(blockIdx.x / a.heads);
+  const int h = blockIdx.x % a.heads;
+  const int64_t t0 = static_cast<int64_t>(chunk) * kChunk;
+  const int rows = a.n_tokens - t0 < kChunk ? static_cast<int>(a.n_tokens - t0) : kChunk;
+  const int stride = a.heads * kD;
+  const bf16_t *kg = static_cast<const bf16_t *>(a.k) + (t0 * a.heads + h) * kD;
+  const bf16_t *vg = static_cast<const bf16_t *>(a.v) + (t0 * a.heads + h) * kD;
+  const bf16_t *rg = a.rb + (static_cast<int64_t>(chunk) * a.heads + h) * kD * kD;
+  stage_rows(lds_r, rg, kD, kChunk, wave, lane);
+  stage_rows(lds_k, kg, stride, rows, wave, lane);
+  stage_rows(lds_v, vg, stride, rows, wave, lane);
+  if (tid < kChunk) s_l[tid] = tid < rows ? a.lcum[(t0 + tid) * a.heads + h] : 0.f;
+
+  // Q^T as the B operand: lane holds query row 32*wave + col, dims ks*16 + half*8 .. +8.
+  const int my_row = wave * 32 + col;
+  const bool row_valid = my_row < rows;
+  Frag8 qf[kD / 16];
+  {
+    const bf16_t *qp = static_cast<const bf16_t *>(a.q) + ((t0 + (row_valid ? my_row : 0)) * a.heads + h) * kD + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) qf[ks].u = row_valid ? ld16(qp + ks * 16) : make_uint4(0, 0, 0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  TrFrag fr, fv;
+  fr.init(lane, kSplitHalves);  // R^T against Q^T (16-byte reads of q rows)
+  fv.init(lane, kInterleave);   // V^T against P^T (the score accumulator order)
+  floatx16 oacc[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[d][e] = 0.f;
+  }
+  // Carried state: O^T = R^T Q^T, then row j times exp(l_j).
+#pragma unroll
+  for (int ks = 0; ks < kD / 16; ++ks) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.read(lds_r, d, ks), qf[ks].v, oacc[d], 0, 0, 0);
+  }
+  const float l_row = s_l[row_valid ? my_row : 0];
+  const float carry = expf(l_row);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[d][e] *= carry;
+  }
+  // Inside the chunk: 32-key halves u = 0 .. wave (keys <= the wave's rows).
+  int koff[kD / 16];
+#pragma unroll
+  for (int ks = 0; ks < kD / 16; ++ks) koff[ks] = swz<kD, kSwz>(col, ks * 16 + half * 8);
+  for (int u = 0; u <= wave; ++u) {
+    floatx16 s;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] = 0.f;
+    const char *tk = lds_k + u * 32 * kRowBytes;
+#pragma unroll
+    for (int ks = 0; ks < kD / 16; ++ks) {
+      Frag8 kf;
+      kf.u = *reinterpret_cast<const uint4 *>(tk + koff[ks]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v, qf[ks].v, s, 0, 0, 0);
+    }
+    // S^T element e is key 32u + (e/4)*8 + half*4 + e%4 of query row my_row.
+    Frag8 p[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float pv[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int e = kk * 8 + 2 * j + x;
+          const int key = u * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+          pv[x] = (key <= my_row) ? s[e] * expf(l_row - s_l[key]) : 0.f;
+        }
+        p[kk].w[j] = cvt_pk_bf16(pv[0], pv[1]);
+      }
+    }
+    // O^T += V^T P^T over the half's two 16-key steps.
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv.read(lds_v + u * 32 * kRowBytes, d, kk), p[kk].v, oacc[d], 0, 0, 0);
+      }
+    }
+  }
+  if (!row_valid) return;
+  // oacc[d] element e is value dim d*32 + (e/4)*8 + half*4 + e%4 of row my_row.
+  float *op = a.o + ((t0 + my_row) * a.heads + h) * kD;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      *reinterpret_cast<float4 *>(op + d * 32 + i4 * 8 + half * 4) =
+          make_float4(oacc[d][i4 * 4 + 0], oacc[d][i4 * 4 + 1], oacc[d][i4 * 4 + 2], oacc[d][i4 * 4 + 3]);
+    }
+  }
+}
+
+bool gret_chunked_applies(int dtype, int head_dim) { return dtype == YOCO_DT_BF16 && head_dim == gr::kD; }
+
+int64_t gret_n_chunks(int64_t n) { return (n + gr::kChunk - 1) / gr::kChunk; }
+
+hipError_t launch_gret_recurrent(const GretArgs &a, int dtype, int head_dim, int n_seq, hipStream_t s) {
+  const unsigned blocks = static_cast<unsigned>(n_seq) * a.heads;
+  if (dtype == YOCO_DT_BF16) {
+    if (head_dim == 128) hipLaunchKernelGGL((gret_recurrent_kernel<bf16_t, 128>), dim3(blocks), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gret_recurrent_kernel<bf16_t, 64>), dim3(blocks), dim3(256), 0, s, a);
+  } else {
+    if (head_dim == 128) hipLaunchKernelGGL((gret_recurrent_kernel<float, 128>), dim3(blocks), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gret_recurrent_kernel<float, 64>), dim3(blocks), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gret_chunked(const GretArgs &a, hipStream_t s) {
+  const int64_t n_chunks = gret_n_chunks(a.n_tokens);
+  const int64_t blocks = n_chunks * a.heads;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gret_chunk_state_kernel, dim3(static_cast<unsigned>(blocks)), dim3(gr::kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t scan_threads = static_cast<int64_t>(a.heads) * gr::kD * gr::kD / 4;
+  hipLaunchKernelGGL(gret_scan_kernel, dim3(static_cast<unsigned>((scan_threads + 255) / 256)), dim3(256), 0, s, a,
+                     static_cast<int>(n_chunks));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(gret_chunk_out_kernel, dim3(static_cast<unsigned>(blocks)), dim3(gr::kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace yoco

@@ -132,4 +132,31 @@ bool project_bwd_mfma_applies(int64_t n, int32_t d, int32_t ncols, int x_dt, int
 void project_bwd_split_plan(int64_t n, int32_t d, int32_t ncols, int32_t n_out, int32_t *splits, int32_t *rows);
 hipError_t launch_project_bwd(const ProjBwdArgs &a, hipStream_t s);
 
+// Gated retention (self-decoder token mixer).  Token t of sequence b is
+// element (b * n_tokens + t) of q, k, v ([..][heads][D]), gate ([..][heads])
+// and o; one of n_seq and n_tokens is 1.  States are [n_seq][heads][D][D]
+// fp32 (state_in may be null: zero; state_out may be null; they may alias).
+// Chunkwise path workspace: lcum [n_tokens][heads] fp32, u [chunks][heads]
+// [D][D] fp32, rb [chunks][heads][D][D] bf16.
+struct GretArgs {
+  const void *q;
+  const void *k;
+  const void *v;
+  const float *gate;
+  const float *state_in;
+  float *state_out;
+  float *o;
+  float *lcum;
+  float *u;
+  uint16_t *rb;
+  int64_t n_tokens;
+  int32_t heads;
+  float inv_tau;
+};
+
+bool gret_chunked_applies(int dtype, int head_dim);
+int64_t gret_n_chunks(int64_t n);
+hipError_t launch_gret_recurrent(const GretArgs &a, int dtype, int head_dim, int n_seq, hipStream_t s);
+hipError_t launch_gret_chunked(const GretArgs &a, hipStream_t s);
+
 }  // namespace yoco
