@@ -296,7 +296,29 @@ def bench_prefill(args, torch, y, W):
     tflops = flops / (avg * 1e-3) / 1e12
     log(f"prefill {avg:.3f} ms (p50 {pct(ms, 50):.3f}) -> {tflops:.1f} TFLOP/s")
     return dict(ms=avg, ms_p10=pct(ms, 10), ms_p50=pct(ms, 50), ms_p90=pct(ms, 90), tflops=tflops, flops=flops,
-                frac=tflops / BF16_DENSE_PEAK_TFLOPS)
+                frac=tflops / BF16_DENSE_PEAK_TFLOPS, case=c)
+
+
+def sampled_rows(n, count):
+    """Rows spread evenly over [0, n): the centres of `count` equal strata."""
+    return ((np.arange(count) + 0.5) * n / count).astype(np.int64)
+
+
+def causal_cpu_baseline(name, run_rows, n, count):
+    """Time an oracle call on `count` sampled query rows of a causal workload
+    of n rows and extrapolate to all n rows: the work of row r is
+    proportional to its r + 1 visible keys."""
+    import oracle
+    rows = sampled_rows(n, count)
+    t0 = time.perf_counter()
+    run_rows(rows)
+    dt = time.perf_counter() - t0
+    frac = float(np.sum(rows + 1)) / (n * (n + 1) / 2.0)
+    full_ms = dt / frac * 1e3
+    log(f"cpu baseline ({name}): {count} sampled rows in {dt:.2f} s -> {full_ms / 1e3:.1f} s extrapolated")
+    return {"value": round(full_ms, 1), "unit": "ms", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{count} query rows spread evenly over the {n} positions, every head, timed "
+                      f"({dt:.2f} s wall, {frac * 100:.3f}% of the causal work) and extrapolated to all rows"}
 
 
 def bench_backward(args, torch, y, W):
@@ -517,7 +539,7 @@ def bench_gret(args, torch, y, W):
     davg = float(np.mean(dms))
     log(f"gret decode step (13 layers) {davg * 1e3:.1f} us")
     return dict(ms=avg, ms_p10=pct(ms, 10), ms_p50=pct(ms, 50), ms_p90=pct(ms, 90), gbps=gbps, bytes=alg,
-                decode_us=davg * 1e3, decode_p50_us=pct(dms, 50) * 1e3)
+                decode_us=davg * 1e3, decode_p50_us=pct(dms, 50) * 1e3, case=c)
 
 
 def cpu_baseline(dec, W):
@@ -559,6 +581,18 @@ def main():
     pbwd = None if args.no_prefill else bench_project_bwd(args, torch, y, W)
     gret = None if args.no_prefill else bench_gret(args, torch, y, W)
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec, W)
+    pre_cpu = gret_cpu = None
+    if not args.no_cpu_baseline and pre is not None:
+        import oracle
+        c = pre["case"]
+        pre_cpu = causal_cpu_baseline(
+            "prefill", lambda rows: oracle.prefill(c.q, 0, c.k, c.v, c.softmax_scale, rows=rows), c.k.shape[0], 48)
+    if not args.no_cpu_baseline and gret is not None:
+        import oracle
+        gc = gret["case"]
+        gamma = oracle.gret_gate(gc.gate, gc.tau)
+        gret_cpu = causal_cpu_baseline(
+            "gated retention", lambda rows: oracle.gret(gc.q, gc.k, gc.v, gamma, rows=rows), gc.q.shape[0], 48)
     # The committed counters were taken on the 128K workload.
     traffic, why = counter_traffic() if args.workload == "decode128k" else (None, "counters cover decode128k only")
     if why:
@@ -622,6 +656,7 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(pre["tflops"], 1),
                          "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(pre["frac"], 4), "flops_per_launch": pre["flops"]},
+            "cpu_baseline": pre_cpu,
         }
     if proj is not None:
         u = proj["unit_gain"]
@@ -678,6 +713,7 @@ def main():
                                  "bytes_per_launch": gret["bytes"],
                                  "bytes_convention": "q, k, v (bf16) and gate logits read once, o (fp32) written "
                                                      "once; chunk states are implementation traffic"},
+            "prefill_cpu_baseline": gret_cpu,
             "decode_step_us": round(gret["decode_us"], 2),
             "decode_step_p50_us": round(gret["decode_p50_us"], 2),
         }

@@ -20,9 +20,11 @@
 //     on MFMA (Q^T and dO^T in registers), dS^T formed in the accumulator
 //     layout (one query row per lane), then dQ^T += K^T dS^T with K^T read
 //     transposed from LDS.
-//   * bwd_dkdv_kernel: one workgroup per (128 cache rows, KV head), one wave
-//     per SIMD, each wave owning 32 cache rows whose K^T and V^T fragments
-//     stay in registers.  Query rows of the G query heads stream through LDS
+//   * bwd_dkdv_kernel: one workgroup per (128 cache rows, KV head), 4 waves,
+//     two workgroups per CU (so two waves per SIMD: one wave's exp and dS
+//     work runs while the other's products occupy the matrix core), each
+//     wave owning 32 cache rows whose K^T and V^T fragments stay in
+//     registers.  Query rows of the G query heads stream through LDS
 //     in tiles of 64 (Q, dO, lse, D).  Per 32-row half: S = Q K^T and
 //     dP = dO V^T (one cache row per lane), P and dS formed there, then
 //     dV += P^T dO and dK += dS^T Q with dO and Q read transposed from LDS.
@@ -33,7 +35,7 @@
 namespace yoco {
 
 namespace bw {
-constexpr int kKvWaves = 4;                  // dK/dV workgroup: one wave per SIMD
+constexpr int kKvWaves = 4;                  // dK/dV workgroup: 4 waves, two workgroups per CU
 constexpr int kKeysPerWave = 32;
 constexpr int kBlockKeys = kKvWaves * kKeysPerWave;  // 128 cache rows per workgroup
 constexpr int kKvThreads = kKvWaves * 64;
@@ -298,7 +300,7 @@ struct KvStage {
 };
 
 template <int DH>
-__global__ __launch_bounds__(bw::kKvThreads, 1) void bwd_dkdv_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(bw::kKvThreads, 2) void bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int SWZ = bw::kSwizzle;
   using S = PrefillShape<DH>;
   __shared__ __attribute__((aligned(1024))) char lds_q0[S::kTileBytes];
@@ -378,9 +380,10 @@ __global__ __launch_bounds__(bw::kKvThreads, 1) void bwd_dkdv_kernel(const BwdAr
     }
   }
 
-  int roff[S::KSTEPS];
-#pragma unroll
-  for (int ks = 0; ks < S::KSTEPS; ++ks) roff[ks] = swz<DH, SWZ>(col, ks * 16 + half * 8);
+  // Row-read offsets are recomputed at each use (a few integer ops) rather
+  // than held in registers.
+  const int rx = row_xor<DH, SWZ>(col);
+  const int rbase = col * S::kRowBytes;
   const int grp = lane >> 4;
   const int src_a = lane & 3;
   const int src_j = (lane >> 2) & 3;
@@ -394,7 +397,7 @@ __global__ __launch_bounds__(bw::kKvThreads, 1) void bwd_dkdv_kernel(const BwdAr
   }
   auto read_rows = [&](const char *tile, int ks) __attribute__((always_inline)) {
     Frag8 f;
-    f.u = *reinterpret_cast<const uint4 *>(tile + roff[ks]);
+    f.u = *reinterpret_cast<const uint4 *>(tile + rbase + (((2 * ks + half) ^ rx) << 4));
     return f;
   };
   auto read_tr = [&](const char *tile, int d, int kk) __attribute__((always_inline)) {
