@@ -32,8 +32,9 @@
 //   * gret_chunk_out_kernel: 4 waves x 32 query rows of a chunk.  The
 //     carried term O^T = R^T Q^T first (then each lane scales its query
 //     row by exp(l_j)), then per 32-key half S^T = K Q^T, P = S exp(l_j - l_k)
-//     masked to k <= j and rounded to bf16, O^T += V^T P^T -- the layout of
-//     the causal prefill kernel (one query row per lane, Q^T in registers).
+//     masked to k <= j and rounded to bf16 (formed while V loads into the
+//     buffer R_c held), then O^T += V^T P^T -- the layout of the causal
+//     prefill kernel (one query row per lane, Q^T in registers).
 #include "attn_tiles.h"
 
 namespace yoco {
@@ -46,7 +47,7 @@ constexpr int kSwz = 2;
 constexpr int kRowBytes = kD * 2;                    // 256
 constexpr int kTileBytes = kChunk * kRowBytes;       // 32 KiB: [128][128] bf16
 constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // 8 one-KiB loads
-constexpr int kScanAhead = 4;      // chunk states in flight in the scan
+constexpr int kScanAhead = 16;     // chunk states in flight per thread in the scan
 }  // namespace gr
 
 // log gamma = logsigmoid(g) / tau = (min(g, 0) - log1p(exp(-|g|))) / tau.
@@ -327,12 +328,14 @@ __global__ __launch_bounds__(256) void gret_scan_kernel(const GretArgs a, int n_
 
 // ---------------------------------------------------------------------------
 // Outputs of one chunk of one head: wave w owns query rows 32w .. 32w+31.
+// 64 KiB of LDS (two workgroups per CU): the carried state R_c is staged into
+// the buffer that V takes afterwards, so V loads while the scores of the
+// chunk are formed.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(gr::kThreads) void gret_chunk_out_kernel(const GretArgs a) {
+__global__ __launch_bounds__(gr::kThreads, 2) void gret_chunk_out_kernel(const GretArgs a) {
   using namespace gr;
   __shared__ __attribute__((aligned(1024))) char lds_k[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_v[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_r[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_rv[kTileBytes];  // R_c, then V
   __shared__ float s_l[kChunk];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -349,9 +352,8 @@ __global__ __launch_bounds__(gr::kThreads) void gret_chunk_out_kernel(const Gret
   const bf16_t *kg = static_cast<const bf16_t *>(a.k) + (t0 * a.heads + h) * kD;
   const bf16_t *vg = static_cast<const bf16_t *>(a.v) + (t0 * a.heads + h) * kD;
   const bf16_t *rg = a.rb + (static_cast<int64_t>(chunk) * a.heads + h) * kD * kD;
-  stage_rows(lds_r, rg, kD, kChunk, wave, lane);
+  stage_rows(lds_rv, rg, kD, kChunk, wave, lane);
   stage_rows(lds_k, kg, stride, rows, wave, lane);
-  stage_rows(lds_v, vg, stride, rows, wave, lane);
   if (tid < kChunk) s_l[tid] = tid < rows ? a.lcum[(t0 + tid) * a.heads + h] : 0.f;
 
   // Q^T as the B operand: lane holds query row 32*wave + col, dims ks*16 + half*8 .. +8.
@@ -379,7 +381,7 @@ __global__ __launch_bounds__(gr::kThreads) void gret_chunk_out_kernel(const Gret
 #pragma unroll
   for (int ks = 0; ks < kD / 16; ++ks) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d) oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.read(lds_r, d, ks), qf[ks].v, oacc[d], 0, 0, 0);
+    for (int d = 0; d < 4; ++d) oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.read(lds_rv, d, ks), qf[ks].v, oacc[d], 0, 0, 0);
   }
   const float l_row = s_l[row_valid ? my_row : 0];
   const float carry = expf(l_row);
@@ -388,11 +390,18 @@ __global__ __launch_bounds__(gr::kThreads) void gret_chunk_out_kernel(const Gret
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[d][e] *= carry;
   }
-  // Inside the chunk: 32-key halves u = 0 .. wave (keys <= the wave's rows).
+  __syncthreads();  // every wave is done with R_c; V takes its buffer
+  stage_rows(lds_rv, vg, stride, rows, wave, lane);
+
+  // Scores of the chunk while V loads: 32-key halves u = 0 .. wave (keys <=
+  // the wave's rows), P = S exp(l_j - l_k) masked to k <= j, in bf16.
   int koff[kD / 16];
 #pragma unroll
   for (int ks = 0; ks < kD / 16; ++ks) koff[ks] = swz<kD, kSwz>(col, ks * 16 + half * 8);
-  for (int u = 0; u <= wave; ++u) {
+  Frag8 p[kWaves][2];
+#pragma unroll
+  for (int u = 0; u < kWaves; ++u) {
+    if (u > wave) break;
     floatx16 s;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.f;
@@ -404,7 +413,6 @@ __global__ __launch_bounds__(gr::kThreads) void gret_chunk_out_kernel(const Gret
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v, qf[ks].v, s, 0, 0, 0);
     }
     // S^T element e is key 32u + (e/4)*8 + half*4 + e%4 of query row my_row.
-    Frag8 p[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
@@ -416,15 +424,21 @@ __global__ __launch_bounds__(gr::kThreads) void gret_chunk_out_kernel(const Gret
           const int key = u * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
           pv[x] = (key <= my_row) ? s[e] * expf(l_row - s_l[key]) : 0.f;
         }
-        p[kk].w[j] = cvt_pk_bf16(pv[0], pv[1]);
+        p[u][kk].w[j] = cvt_pk_bf16(pv[0], pv[1]);
       }
     }
-    // O^T += V^T P^T over the half's two 16-key steps.
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // V has landed for every wave
+  // O^T += V^T P^T over each half's two 16-key steps.
+#pragma unroll
+  for (int u = 0; u < kWaves; ++u) {
+    if (u > wave) break;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv.read(lds_v + u * 32 * kRowBytes, d, kk), p[kk].v, oacc[d], 0, 0, 0);
+        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv.read(lds_rv + u * 32 * kRowBytes, d, kk), p[u][kk].v, oacc[d], 0, 0, 0);
       }
     }
   }

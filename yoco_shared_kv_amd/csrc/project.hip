@@ -18,12 +18,13 @@
 //    with fp32 FMA.
 //  * rows <= 8 (generation-time append, per-token Q): the work is a
 //    matrix-vector product bound by reading W once, so one 1024-thread
-//    workgroup (512 for 8 rows) owns a 64-column strip of one weight for all
-//    d_model rows.
-//    Each 8-lane group reads one 128-byte line of a W row per load (a wave
-//    covers 8 rows, the workgroup 128 rows per pass), multiplies it by the
-//    LDS-resident x*gain of every input row, and the per-lane partial sums
-//    are reduced across lanes (shuffles) and waves (LDS) in a fixed order.
+//    workgroup (512 for 8 rows) owns a 16-column strip of one weight for all
+//    d_model rows (128 workgroups for a 3072 x 1024 pair of weights).
+//    Each 2-lane pair reads 32 bytes of a W row per load (a wave covers 32
+//    rows, the workgroup 512 rows per pass, so a 3072-row weight is one pass
+//    of loads in flight), multiplies them by the LDS-resident x*gain of every
+//    input row, and the per-lane partial sums are reduced across lanes
+//    (shuffles) and waves (LDS) in a fixed order.
 //    Rows run in launches of up to 8 (fewer when d_model is large, since a
 //    launch stages x*gain in at most 48 KiB of LDS).
 // Destination rows are either contiguous (a cache slab or a Q buffer) or, for
@@ -152,13 +153,15 @@ __global__ __launch_bounds__(pj::kThreads) void project_kernel(const ProjArgs a)
 namespace pg {
 // 16 waves (8 for 8 input rows, whose accumulators need the larger
 // per-lane register budget of a 512-thread workgroup).
+constexpr int kCols = 16;            // columns per workgroup: 2 lanes x 8 columns per W row
+constexpr int kLanesPerRow = kCols / 8;
+constexpr int kRowSlots = 64 / kLanesPerRow;  // W rows one wave reads per load
 template <int NR>
 struct Shape {
   static constexpr int kWaves = (NR == 8) ? 8 : 16;
   static constexpr int kThreads = kWaves * 64;
-  static constexpr int kRowsPerPass = kWaves * 8;
+  static constexpr int kRowsPerPass = kWaves * kRowSlots;
 };
-constexpr int kCols = 64;            // columns per workgroup (8 lanes x 8 bf16 / fp32 pairs)
 constexpr int kMaxRows = 8;
 constexpr int kMaxXBytes = 48 * 1024;  // dynamic LDS for x * gain (within the default 64 KiB)
 constexpr int kMaxChunks = 4;          // launches per call before the tiled kernel takes over
@@ -229,8 +232,8 @@ __global__ __launch_bounds__(pg::Shape<NR>::kThreads) void project_small_kernel(
   }
   __syncthreads();
 
-  const int c8 = lane & 7;        // 8-column chunk of the strip
-  const int rslot = lane >> 3;    // row within the wave's 8 rows
+  const int c8 = lane % kLanesPerRow;  // 8-column chunk of the strip
+  const int rslot = lane / kLanesPerRow;  // row within the wave's kRowSlots rows
   float acc[NR][8];
 #pragma unroll
   for (int r = 0; r < NR; ++r)
@@ -244,7 +247,7 @@ __global__ __launch_bounds__(pg::Shape<NR>::kThreads) void project_small_kernel(
     float wv[kUnroll][8];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int k = k0 + u * kRowsPerPass + wave * 8 + rslot;
+      const int k = k0 + u * kRowsPerPass + wave * kRowSlots + rslot;
       if (k < d) {
         load_w8<TW>(wcol + static_cast<int64_t>(k) * a.ncols, wv[u]);
       } else {
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(pg::Shape<NR>::kThreads) void project_small_kernel(
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int k = k0 + u * kRowsPerPass + wave * 8 + rslot;
+      const int k = k0 + u * kRowsPerPass + wave * kRowSlots + rslot;
       if (k < d) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
@@ -266,9 +269,10 @@ __global__ __launch_bounds__(pg::Shape<NR>::kThreads) void project_small_kernel(
     }
   }
 
-  // Reduce over the 8 row slots of the wave (lane bits 3..5), then waves.
+  // Reduce over the row slots of the wave (the lane bits above the chunk),
+  // then over the waves.
 #pragma unroll
-  for (int sft = 8; sft < 64; sft <<= 1) {
+  for (int sft = kLanesPerRow; sft < 64; sft <<= 1) {
 #pragma unroll
     for (int r = 0; r < NR; ++r)
 #pragma unroll
