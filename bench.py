@@ -493,9 +493,10 @@ def bench_gret(args, torch, y, W):
     stream = torch.cuda.current_stream()
 
     def pre():
-        y.lib().yoco_gret_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), 1, g.data_ptr(), c.tau, n, heads, dh,
-                                  None, o.data_ptr(), s_out.data_ptr(), ws.data_ptr(), ws.numel(),
-                                  stream.cuda_stream)
+        if y.lib().yoco_gret_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), 1, g.data_ptr(), c.tau, n, heads, dh,
+                                     None, o.data_ptr(), s_out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                     stream.cuda_stream) != 0:
+            raise RuntimeError(y.lib().yoco_last_error().decode())
 
     pre()
     torch.cuda.synchronize()
@@ -520,10 +521,17 @@ def bench_gret(args, torch, y, W):
     states = torch.zeros((layers, 1, heads, dh, dh), dtype=torch.float32, device="cuda")
     od = torch.empty((layers, 1, heads, dh), dtype=torch.float32, device="cuda")
 
+    # Pointers marshalled once: the step is 13 calls of the C entry point.
+    lib = y.lib()
+    es = 2  # bf16 element size
+    args = [(qd.data_ptr() + l * heads * dh * es, kd.data_ptr() + l * heads * dh * es,
+             vd.data_ptr() + l * heads * dh * es, gd.data_ptr() + l * heads * 4, states[l].data_ptr(),
+             od[l].data_ptr()) for l in range(layers)]
+
     def dec():
-        for l in range(layers):
-            y.gret_decode(qd[l:l + 1], kd[l:l + 1], vd[l:l + 1], gd[l:l + 1], cd.tau, states[l], out=od[l],
-                          stream=stream)
+        for qp, kp, vp, gp, sp, op in args:
+            if lib.yoco_gret_decode(qp, kp, vp, 1, gp, cd.tau, 1, heads, dh, sp, op, stream.cuda_stream) != 0:
+                raise RuntimeError(lib.yoco_last_error().decode())
 
     for _ in range(3):
         dec()

@@ -11,11 +11,12 @@
 // cumulative sums of log gamma = logsigmoid(g) / tau, so every factor is
 // exp of a difference <= 0 (no division by a vanishing product).
 //
-// Recurrent path (gret_recurrent_kernel): one workgroup per (sequence,
-// head) keeps the D x D fp32 state in registers (thread t owns four columns
-// of D/32 or D/16 rows) and walks the tokens in order: state update, then
-// o = q S with a reduction over row groups through LDS.  Generation runs one
-// token per sequence; fp32 prefill runs all tokens of one sequence.
+// Recurrent path (gret_recurrent_kernel): the state's columns evolve
+// independently, so one workgroup per (sequence, head, 16 state columns)
+// keeps its D x 16 slice of the fp32 state in registers and walks the tokens
+// in order: state update, then o = q S for its columns with a reduction over
+// rows (shuffles, then LDS).  Generation runs one token per sequence; fp32
+// prefill runs all tokens of one sequence.
 //
 // Chunkwise path (bf16, D = 128), chunks of C = 128 positions
 // ([Notes] s.2.3: parallel inside a chunk, a state passed between chunks):
@@ -56,21 +57,34 @@ __device__ __forceinline__ float gret_log_gate(float g, float inv_tau) {
 }
 
 // ---------------------------------------------------------------------------
-// Recurrent steps.  Thread t owns state columns 4*(t % (D/4)) .. +3 of rows
-// t / (D/4) + G*i (G = 256 / (D/4) row groups, D/G rows each).
+// Recurrent steps.  Column e of the state evolves on its own (S_t[:, e] =
+// gamma_t S_{t-1}[:, e] + k_t v_t[e]) and o_t[e] = q_t S_t[:, e] reads only
+// that column, so a workgroup owns kGretCols columns of one (sequence, head)
+// state for all D rows: thread t holds four consecutive columns
+// 4 * (t % 4) .. +3 of rows t / 4 + 64 i.  The row sum of o goes through
+// shuffles inside each wave (lane bits 2..5) and then LDS across the four
+// waves, in a fixed order.
 // ---------------------------------------------------------------------------
+constexpr int kGretCols = 16;
 template <typename T, int D>
 __global__ __launch_bounds__(256) void gret_recurrent_kernel(const GretArgs a) {
-  constexpr int kColThreads = D / 4;
-  constexpr int kGroups = 256 / kColThreads;
-  constexpr int kRows = D / kGroups;
-  __shared__ float s_q[D], s_k[D], s_v[D];
-  __shared__ float s_o[kGroups][D];
+  constexpr int kColThreads = kGretCols / 4;        // 4 threads per row
+  constexpr int kGroups = 256 / kColThreads;        // 64 row groups
+  constexpr int kRows = D / kGroups;                // rows per thread
+  constexpr int kBlocks = D / kGretCols;            // column blocks per head
+  static_assert(kRows >= 1 && D % kGroups == 0, "state rows");
+  __shared__ float s_q[D], s_k[D], s_v[kGretCols];
+  __shared__ float s_o[4][kGretCols];
   const int tid = threadIdx.x;
-  const int c0 = (tid % kColThreads) * 4;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c_local = (tid % kColThreads) * 4;
   const int grp = tid / kColThreads;
-  const int b = blockIdx.x / a.heads;
-  const int h = blockIdx.x % a.heads;
+  const int cblk = blockIdx.x % kBlocks;
+  const int bh = blockIdx.x / kBlocks;
+  const int b = bh / a.heads;
+  const int h = bh % a.heads;
+  const int c0 = cblk * kGretCols + c_local;  // this thread's first state column
   const int64_t sbase = (static_cast<int64_t>(b) * a.heads + h) * D * D;
   float S[kRows][4];
 #pragma unroll
@@ -89,13 +103,13 @@ __global__ __launch_bounds__(256) void gret_recurrent_kernel(const GretArgs a) {
     if (tid < D) {
       s_q[tid] = load_elem(static_cast<const T *>(a.q) + tok * D + tid);
       s_k[tid] = load_elem(static_cast<const T *>(a.k) + tok * D + tid);
-      s_v[tid] = load_elem(static_cast<const T *>(a.v) + tok * D + tid);
     }
+    if (tid < kGretCols) s_v[tid] = load_elem(static_cast<const T *>(a.v) + tok * D + cblk * kGretCols + tid);
     const float gamma = expf(gret_log_gate(a.gate[tok], a.inv_tau));
     __syncthreads();
     float vv[4], o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) vv[e] = s_v[c0 + e];
+    for (int e = 0; e < 4; ++e) vv[e] = s_v[c_local + e];
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
       const int row = grp + kGroups * i;
@@ -106,14 +120,20 @@ __global__ __launch_bounds__(256) void gret_recurrent_kernel(const GretArgs a) {
         o[e] = fmaf(qr, S[i][e], o[e]);
       }
     }
+    // Sum over the 16 row groups of the wave (lane bits 2..5), then waves.
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s_o[grp][c0 + e] = o[e];
+    for (int sft = kColThreads; sft < 64; sft <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] += __shfl_xor(o[e], sft, 64);
+    }
+    if (lane < kColThreads) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s_o[wave][c_local + e] = o[e];
+    }
     __syncthreads();
-    if (tid < D) {
-      float acc = 0.f;
-#pragma unroll
-      for (int g2 = 0; g2 < kGroups; ++g2) acc += s_o[g2][tid];
-      a.o[tok * D + tid] = acc;
+    if (tid < kGretCols) {
+      const float acc = ((s_o[0][tid] + s_o[1][tid]) + s_o[2][tid]) + s_o[3][tid];
+      a.o[tok * D + cblk * kGretCols + tid] = acc;
     }
   }
   if (a.state_out == nullptr) return;
@@ -460,7 +480,9 @@ bool gret_chunked_applies(int dtype, int head_dim) { return dtype == YOCO_DT_BF1
 int64_t gret_n_chunks(int64_t n) { return (n + gr::kChunk - 1) / gr::kChunk; }
 
 hipError_t launch_gret_recurrent(const GretArgs &a, int dtype, int head_dim, int n_seq, hipStream_t s) {
-  const unsigned blocks = static_cast<unsigned>(n_seq) * a.heads;
+  const int64_t blocks64 = static_cast<int64_t>(n_seq) * a.heads * (head_dim / kGretCols);
+  if (blocks64 > 0x7fffffff) return hipErrorInvalidValue;
+  const unsigned blocks = static_cast<unsigned>(blocks64);
   if (dtype == YOCO_DT_BF16) {
     if (head_dim == 128) hipLaunchKernelGGL((gret_recurrent_kernel<bf16_t, 128>), dim3(blocks), dim3(256), 0, s, a);
     else hipLaunchKernelGGL((gret_recurrent_kernel<bf16_t, 64>), dim3(blocks), dim3(256), 0, s, a);
