@@ -524,12 +524,12 @@ def bench_gret(args, torch, y, W):
     # Pointers marshalled once: the step is 13 calls of the C entry point.
     lib = y.lib()
     es = 2  # bf16 element size
-    args = [(qd.data_ptr() + l * heads * dh * es, kd.data_ptr() + l * heads * dh * es,
-             vd.data_ptr() + l * heads * dh * es, gd.data_ptr() + l * heads * 4, states[l].data_ptr(),
-             od[l].data_ptr()) for l in range(layers)]
+    call_args = [(qd.data_ptr() + l * heads * dh * es, kd.data_ptr() + l * heads * dh * es,
+                  vd.data_ptr() + l * heads * dh * es, gd.data_ptr() + l * heads * 4, states[l].data_ptr(),
+                  od[l].data_ptr()) for l in range(layers)]
 
     def dec():
-        for qp, kp, vp, gp, sp, op in args:
+        for qp, kp, vp, gp, sp, op in call_args:
             if lib.yoco_gret_decode(qp, kp, vp, 1, gp, cd.tau, 1, heads, dh, sp, op, stream.cuda_stream) != 0:
                 raise RuntimeError(lib.yoco_last_error().decode())
 

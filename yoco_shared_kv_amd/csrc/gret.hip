@@ -97,15 +97,29 @@ __global__ __launch_bounds__(256) void gret_recurrent_kernel(const GretArgs a) {
       S[i][0] = S[i][1] = S[i][2] = S[i][3] = 0.f;
     }
   }
+  // Token t's q, k, v and gate are loaded one token ahead (token 0 together
+  // with the state), so a step waits for at most one memory round trip.
+  float nq = 0.f, nk = 0.f, nv = 0.f, ng = 0.f;
+  auto fetch = [&](int64_t t) __attribute__((always_inline)) {
+    const int64_t tok = (static_cast<int64_t>(b) * a.n_tokens + t) * a.heads + h;
+    if (tid < D) {
+      nq = load_elem(static_cast<const T *>(a.q) + tok * D + tid);
+      nk = load_elem(static_cast<const T *>(a.k) + tok * D + tid);
+    }
+    if (tid < kGretCols) nv = load_elem(static_cast<const T *>(a.v) + tok * D + cblk * kGretCols + tid);
+    ng = a.gate[tok];
+  };
+  if (a.n_tokens > 0) fetch(0);
   for (int64_t t = 0; t < a.n_tokens; ++t) {
     const int64_t tok = (static_cast<int64_t>(b) * a.n_tokens + t) * a.heads + h;
     __syncthreads();  // the previous token's reads of s_q/s_k/s_v/s_o are done
     if (tid < D) {
-      s_q[tid] = load_elem(static_cast<const T *>(a.q) + tok * D + tid);
-      s_k[tid] = load_elem(static_cast<const T *>(a.k) + tok * D + tid);
+      s_q[tid] = nq;
+      s_k[tid] = nk;
     }
-    if (tid < kGretCols) s_v[tid] = load_elem(static_cast<const T *>(a.v) + tok * D + cblk * kGretCols + tid);
-    const float gamma = expf(gret_log_gate(a.gate[tok], a.inv_tau));
+    if (tid < kGretCols) s_v[tid] = nv;
+    const float gamma = expf(gret_log_gate(ng, a.inv_tau));
+    if (t + 1 < a.n_tokens) fetch(t + 1);
     __syncthreads();
     float vv[4], o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll

@@ -205,35 +205,69 @@ __global__ __launch_bounds__(pg::Shape<NR>::kThreads) void project_small_kernel(
   const int d = a.d;
   const TX *x = static_cast<const TX *>(a.x);
   const TW *w = static_cast<const TW *>(a.w[out_id]);
-
-  // Stage x * gain (fp32) and reduce the row norms: wave r handles row r.
-  for (int idx = tid; idx < NR * d; idx += kThreads) {
-    const int r = idx / d;
-    const int c = idx - r * d;
-    float v = 0.f;
-    if (r < nr) {
-      v = load_elem<TX>(x + (row_base + r) * d + c);
-      if (a.gain != nullptr) v *= a.gain[c];
+  const int c8 = lane % kLanesPerRow;     // 8-column chunk of the strip
+  const int rslot = lane / kLanesPerRow;  // row within the wave's kRowSlots rows
+  constexpr int kUnroll = (NR <= 2) ? 8 : 4;
+  const TW *wcol = w + strip * kCols + c8 * 8;
+  float wv[kUnroll][8];
+  auto load_batch = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int k = k0 + u * kRowsPerPass + wave * kRowSlots + rslot;
+      load_w8<TW>(wcol + static_cast<int64_t>(k < d ? k : d - 1) * a.ncols, wv[u]);
     }
-    s_x[idx] = v;
-  }
-  if (wave < NR) {
-    float ss = 0.f;
-    if (wave < nr) {
-      const TX *xr = x + (row_base + wave) * d;
-      for (int c = lane; c < d; c += 64) {
-        const float v = load_elem<TX>(xr + c);
-        ss = fmaf(v, v, ss);
-      }
+  };
+  load_batch(0);
+
+  // Stage x * gain (fp32); the same loads give each thread's share of the
+  // row sums of squares, which reduce over lanes (shuffles) and then waves
+  // (LDS, in wave order).
+  __shared__ float s_ss[kWaves][NR];
+  float ssp[NR];
+#pragma unroll
+  for (int rr = 0; rr < NR; ++rr) ssp[rr] = 0.f;
+  // Four elements per thread per round: the loads of a round are issued
+  // before any of them is used (addresses clamped into the input, values
+  // past it replaced by zero), so a round costs one memory round trip.
+  constexpr int kStage = 4;
+  for (int base = tid; base < NR * d; base += kStage * kThreads) {
+    float v[kStage], g[kStage];
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) {
+      const int idx = base + j * kThreads;
+      const int r = idx / d;
+      const int c = idx - r * d;
+      const int rc = r < nr ? r : 0;
+      const int cc = idx < NR * d ? c : 0;
+      v[j] = load_elem<TX>(x + (row_base + rc) * d + cc);
+      g[j] = a.gain != nullptr ? a.gain[cc] : 1.f;
     }
 #pragma unroll
-    for (int sft = 32; sft >= 1; sft >>= 1) ss += shfl_xor_f(ss, sft);
-    if (lane == 0) s_inv_rms[wave] = 1.0f / sqrtf(ss / static_cast<float>(d) + a.eps);
+    for (int j = 0; j < kStage; ++j) {
+      const int idx = base + j * kThreads;
+      const int r = idx / d;
+      const float vj = (idx < NR * d && r < nr) ? v[j] : 0.f;
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr) ssp[rr] = (r == rr) ? fmaf(vj, vj, ssp[rr]) : ssp[rr];
+      if (idx < NR * d) s_x[idx] = vj * g[j];
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < NR; ++rr) {
+    float t = ssp[rr];
+#pragma unroll
+    for (int sft = 32; sft >= 1; sft >>= 1) t += shfl_xor_f(t, sft);
+    if (lane == 0) s_ss[wave][rr] = t;
+  }
+  __syncthreads();
+  if (tid < NR) {
+    float ss = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves; ++w2) ss += s_ss[w2][tid];
+    s_inv_rms[tid] = 1.0f / sqrtf(ss / static_cast<float>(d) + a.eps);
   }
   __syncthreads();
 
-  const int c8 = lane % kLanesPerRow;  // 8-column chunk of the strip
-  const int rslot = lane / kLanesPerRow;  // row within the wave's kRowSlots rows
   float acc[NR][8];
 #pragma unroll
   for (int r = 0; r < NR; ++r)
@@ -241,30 +275,23 @@ __global__ __launch_bounds__(pg::Shape<NR>::kThreads) void project_small_kernel(
     for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
 
   // W rows in flight per lane; fewer for more input rows (more accumulators).
-  constexpr int kUnroll = (NR <= 2) ? 8 : 4;
-  const TW *wcol = w + strip * kCols + c8 * 8;
+  // All kUnroll loads of a batch are issued before the first is used: rows
+  // past d read row d-1 and are zeroed afterwards (no branch around a load).
+  // The first batch is issued before x is staged (one batch covers
+  // d <= 4096 for up to two input rows); later batches at the top of their
+  // iteration.
   for (int k0 = 0; k0 < d; k0 += kRowsPerPass * kUnroll) {
-    float wv[kUnroll][8];
+    if (k0 > 0) load_batch(k0);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int k = k0 + u * kRowsPerPass + wave * kRowSlots + rslot;
-      if (k < d) {
-        load_w8<TW>(wcol + static_cast<int64_t>(k) * a.ncols, wv[u]);
-      } else {
+      const bool in = k < d;
+      const int kc = in ? k : d - 1;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) wv[u][e] = 0.f;
-      }
-    }
+      for (int r = 0; r < NR; ++r) {
+        const float xv = in ? s_x[r * d + kc] : 0.f;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int k = k0 + u * kRowsPerPass + wave * kRowSlots + rslot;
-      if (k < d) {
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          const float xv = s_x[r * d + k];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(xv, wv[u][e], acc[r][e]);
-        }
+        for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(xv, wv[u][e], acc[r][e]);
       }
     }
   }
