@@ -15,6 +15,7 @@ import torch
 import oracle
 import workloads as W
 from tests.gpu_helpers import assert_parity, assert_projection_bf16, to_dev, to_stored
+from workloads import as_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -412,3 +413,35 @@ def test_q_project_single_token():
     gain = (1 + 0.1 * r.standard_normal(3072)).astype(np.float32)
     q = y.q_project(to_dev(x), to_dev(wq), 24, 128, torch.from_numpy(gain).cuda(), out_dtype=torch.float32)
     assert_parity(to_stored(q).reshape(1, -1), orc().project(x, wq, gain), bf16=False, what="Q^ (fp32 out)")
+
+
+def test_decode_and_append_at_the_sequence_limit():
+    """YOCO_MAX_SEQ (256) sequences of mixed lengths 1..600: one appended row
+    per sequence, then a decode step of every sequence against the oracle."""
+    print("decode + append, 256 sequences", flush=True)
+    n_seq, hkv, dh, hq, d = 256, 2, 64, 6, 128
+    r = rng(77)
+    lens = r.integers(1, 600, n_seq)
+    lens[0], lens[1] = 1, 0  # a one-row slab and an empty one that the append fills
+    ks = [W.store(r.standard_normal((max(L, 1), hkv, dh)).astype(np.float32), W.BF16) for L in lens]
+    vs = [W.store(r.standard_normal((max(L, 1), hkv, dh)).astype(np.float32), W.BF16) for L in lens]
+    cache = make_cache_from(ks, vs, 640, W.BF16)
+    cache.len[:] = lens
+    m_new = W.store(r.standard_normal((n_seq, d)).astype(np.float32), W.BF16)
+    w_k = W.store((r.standard_normal((d, hkv * dh)) / math.sqrt(d)).astype(np.float32), W.BF16)
+    w_v = W.store((r.standard_normal((d, hkv * dh)) / math.sqrt(d)).astype(np.float32), W.BF16)
+    y.kv_append(cache, to_dev(m_new), to_dev(w_k), to_dev(w_v))
+    assert cache.len.tolist() == (lens + 1).tolist()
+    q = W.store(r.standard_normal((n_seq, hq, dh)).astype(np.float32), W.BF16)
+    o = to_stored(y.cross_attn_decode(to_dev(q), cache, 1 / math.sqrt(dh)))
+    k_all = to_stored(cache.k)
+    v_all = to_stored(cache.v)
+    new_k = orc().project(m_new, w_k, None, 1e-6).reshape(n_seq, hkv, dh)
+    for b in range(n_seq):
+        L = int(lens[b]) + 1
+        kb, vb = k_all[b, :L], v_all[b, :L]
+        assert_projection_bf16(kb[L - 1].reshape(1, -1), new_k[b].reshape(1, -1),
+                               np.abs(orc().rmsnorm(m_new[b:b + 1])) @ np.abs(as_f32(w_k).astype(np.float64)),
+                               d, what=f"appended K^ row of sequence {b}")
+        ro = orc().decode(q[b:b + 1], L, kb, vb, 1 / math.sqrt(dh))
+        assert_parity(o[b], ro[0], bf16=True, what=f"decode seq {b} len {L}")
