@@ -165,6 +165,7 @@ struct Shape {
 constexpr int kMaxRows = 8;
 constexpr int kMaxXBytes = 48 * 1024;  // dynamic LDS for x * gain (within the default 64 KiB)
 constexpr int kMaxChunks = 4;          // launches per call before the tiled kernel takes over
+constexpr int kXcds = 8;               // workgroups are dealt to the XCDs round-robin
 }  // namespace pg
 
 // W loads of 8 consecutive columns as fp32.
@@ -199,9 +200,15 @@ __global__ __launch_bounds__(pg::Shape<NR>::kThreads) void project_small_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  // Consecutive workgroups go to consecutive XCDs, and each XCD has its own
+  // L2: XCD x takes a contiguous run of strips, so the 128-byte lines of a W
+  // row that several strips share are fetched into one L2, not into four.
   const int n_strips = a.ncols / kCols;
-  const int strip = blockIdx.x % n_strips;
-  const int out_id = blockIdx.x / n_strips;
+  const int per_xcd = (n_strips * a.n_out + kXcds - 1) / kXcds;
+  const int linear = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (linear >= n_strips * a.n_out) return;
+  const int strip = linear % n_strips;
+  const int out_id = linear / n_strips;
   const int d = a.d;
   const TX *x = static_cast<const TX *>(a.x);
   const TW *w = static_cast<const TW *>(a.w[out_id]);
@@ -354,7 +361,8 @@ static bool use_small(const ProjArgs &a) {
 
 template <typename TX, typename TW, typename TO>
 static hipError_t launch_project_small(const ProjArgs &a, hipStream_t s) {
-  const unsigned int blocks = static_cast<unsigned int>((a.ncols / pg::kCols) * a.n_out);
+  const unsigned int per_xcd = static_cast<unsigned int>(((a.ncols / pg::kCols) * a.n_out + pg::kXcds - 1) / pg::kXcds);
+  const unsigned int blocks = per_xcd * pg::kXcds;
   const int chunk = small_chunk_rows(a.d);
   for (int64_t base = 0; base < a.n; base += chunk) {
     const int nr = static_cast<int>(a.n - base < chunk ? a.n - base : chunk);
