@@ -48,6 +48,9 @@ def _dev(c):
     (300, 3, 128, W.BF16, 16.0, False),   # chunkwise: 3 chunks, ragged last one
     (300, 3, 128, W.BF16, 16.0, True),    # ... continuing from a start state
     (1000, 2, 128, W.BF16, 1.0, True),    # strong decay: carried factors underflow across chunks
+    (2500, 2, 128, W.BF16, 4.0, True),    # 20 chunks: groups of 8, 8 and 4 chunks, ragged last chunk
+    (2049, 1, 128, W.BF16, 16.0, False),  # 17 chunks: the last group is one chunk of one position
+    (3000, 2, 128, W.BF16, 1.0, False),   # strong decay across groups
     (128, 2, 128, W.BF16, 16.0, False),   # exactly one chunk
     (1, 2, 128, W.BF16, 16.0, True),      # one position
     (257, 2, 64, W.BF16, 16.0, True),     # head dim 64: recurrent path on bf16 values

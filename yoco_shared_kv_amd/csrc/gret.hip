@@ -24,18 +24,30 @@
 //   U_c     = sum_k exp(l_C - l_k) k_k^T v_k                  (chunk's own state)
 //   R_{c+1} = exp(l_C) R_c + U_c,  R_0 = the start state       (state entering chunk c+1)
 //   O_j     = sum_{k<=j} exp(l_j - l_k) (q_j . k_k) v_k + exp(l_j) q_j R_c
-//   * gret_chunk_state_kernel: l for the chunk (a wave scan), then U_c on
-//     MFMA as K'^T V with K' = exp(l_C - l_k) k_k rounded to bf16; both
-//     operands come from row-major LDS tiles through transposed reads.
-//   * gret_scan_kernel: the sequential pass over chunks, elementwise over
-//     the state (R_c stored in bf16 for the output kernel, the last state
-//     in fp32), with the chunk states loaded a few chunks ahead.
-//   * gret_chunk_out_kernel: 4 waves x 32 query rows of a chunk.  The
-//     carried term O^T = R^T Q^T first (then each lane scales its query
-//     row by exp(l_j)), then per 32-key half S^T = K Q^T, P = S exp(l_j - l_k)
-//     masked to k <= j and rounded to bf16 (formed while V loads into the
-//     buffer R_c held), then O^T += V^T P^T -- the layout of the causal
-//     prefill kernel (one query row per lane, Q^T in registers).
+// The pass over chunks is split in two levels, so no per-chunk fp32 state
+// ever goes to memory: chunks form groups of kGroup; inside group g the
+// same recurrence started from zero gives A_c, the group's total T_g and
+// its decay Lambda_g, and then S_{g+1} = exp(Lambda_g) S_g + T_g (S_0 the
+// start state) gives R_c = A_c + exp(delta_c) S_g, delta_c the log decay
+// from the group's start to chunk c.
+//   * gret_group_state_kernel: one workgroup per (group, head) walks the
+//     group's chunks with A in the MFMA accumulators: l for the chunk (a
+//     wave scan), A_c out in bf16, then A <- exp(l_C) A + K'^T V with
+//     K' = exp(l_C - l_k) k_k rounded to bf16 (weights applied to the
+//     transposed K fragments), both operands from row-major LDS tiles.
+//   * gret_group_scan_kernel: the short pass over groups, elementwise over
+//     the state (S_g in fp32, the last state to state_out).
+//   * gret_chunk_out_kernel: 4 waves x 32 query rows of a chunk.  R_c is
+//     formed in fp32 from A_c and S_g and rounded to bf16 into LDS; the
+//     carried term O^T = R^T Q^T comes first (then each lane scales its
+//     query row by exp(l_j)), then per 32-key half S^T = K Q^T,
+//     P = S exp(l_j - l_k) masked to k <= j and rounded to bf16 (formed
+//     while V loads into the buffer R_c held), then O^T += V^T P^T -- the
+//     layout of the causal prefill kernel (one query row per lane, Q^T in
+//     registers).
+// The stored states are transposed ([value dim][key dim]): the output
+// kernel then reads R^T rows with plain 16-byte LDS reads, and the state
+// kernel writes four consecutive key dims per lane.
 #include "attn_tiles.h"
 
 namespace yoco {
@@ -48,7 +60,8 @@ constexpr int kSwz = 2;
 constexpr int kRowBytes = kD * 2;                    // 256
 constexpr int kTileBytes = kChunk * kRowBytes;       // 32 KiB: [128][128] bf16
 constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // 8 one-KiB loads
-constexpr int kScanAhead = 16;     // chunk states in flight per thread in the scan
+constexpr int kGroup = 8;          // chunks per group of the state kernel
+constexpr int kScanAhead = 8;      // group states in flight per thread in the scan
 }  // namespace gr
 
 // log gamma = logsigmoid(g) / tau = (min(g, 0) - log1p(exp(-|g|))) / tau.
@@ -191,178 +204,228 @@ __device__ __forceinline__ void stage_rows(char *dst, const bf16_t *base, int st
 enum TrOrder { kSplitHalves = 0, kInterleave = 1 };
 struct TrFrag {
   int off[2][4];
-  __device__ __forceinline__ void init(int lane, TrOrder order) {
+  // Byte offset of read r (0, 1) of index tile dt for this lane.
+  static __device__ __forceinline__ int offset(int lane, TrOrder order, int r, int dt) {
     const int grp = lane >> 4;
     const int src_a = lane & 3;
     const int src_j = (lane >> 2) & 3;
     const int krow = order == kSplitHalves ? (grp >> 1) * 8 + src_j : (grp >> 1) * 4 + src_j;
     const int second = order == kSplitHalves ? 4 : 8;
     const int col = (grp & 1) * 16 + src_a * 4;
+    return swz<kD, kSwz>(krow + second * r, dt * 32 + col);
+  }
+  __device__ __forceinline__ void init(int lane, TrOrder order) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
 #pragma unroll
-      for (int d = 0; d < 4; ++d) off[r][d] = swz<kD, kSwz>(krow + second * r, d * 32 + col);
+      for (int d = 0; d < 4; ++d) off[r][d] = offset(lane, order, r, d);
     }
   }
-  __device__ __forceinline__ bf16x8_t read(const char *tile, int dt, int ks) const {
+  static __device__ __forceinline__ bf16x8_t read_at(const char *tile, int off0, int off1, int ks) {
     Frag8 f;
-    f.s4[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t *)(tile + off[0][dt] + ks * 16 * kRowBytes));
-    f.s4[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t *)(tile + off[1][dt] + ks * 16 * kRowBytes));
+    f.s4[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t *)(tile + off0 + ks * 16 * kRowBytes));
+    f.s4[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t *)(tile + off1 + ks * 16 * kRowBytes));
     return f.v;
+  }
+  __device__ __forceinline__ bf16x8_t read(const char *tile, int dt, int ks) const {
+    return read_at(tile, off[0][dt], off[1][dt], ks);
   }
 };
 }  // namespace gr
 
 // ---------------------------------------------------------------------------
-// Per (chunk, head): l (inclusive cumulative log gamma inside the chunk) to
-// the workspace, and U_c = sum_k exp(l_C - l_k) k_k^T v_k (fp32).
-// Wave w computes U rows (key dims) 32w .. 32w+31, all 128 value dims.
+// Per (group of kGroup chunks, head), walking the group's chunks in order:
+// l (inclusive cumulative log gamma inside each chunk) and the log decay
+// from the group's start to each chunk (delta_c) go to the workspace; the
+// group-local state A_c (state before chunk c, counted from zero at the
+// group's start) goes out in bf16 for every chunk but the group's first,
+// A_{c+1} = exp(l_C) A_c + K'^T V with K' = exp(l_C - l_k) k_k rounded to
+// bf16, and the group's total T_g = A after its last chunk in fp32, with
+// its log decay Lambda_g.  A lives in the MFMA accumulators: wave w owns
+// rows (key dims) 32w .. 32w+31, all 128 value dims.  States are stored
+// transposed ([value dim][key dim]), the layout the output kernel reads.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(gr::kThreads) void gret_chunk_state_kernel(const GretArgs a) {
+__global__ __launch_bounds__(gr::kThreads, 2) void gret_group_state_kernel(const GretArgs a) {
   using namespace gr;
   __shared__ __attribute__((aligned(1024))) char lds_k[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_v[kTileBytes];
-  __shared__ float s_w[kChunk];
+  __shared__ __attribute__((aligned(16))) float s_w[kChunk];
+  __shared__ float s_lc;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int chunk = blockIdx.x / a.heads;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int g = blockIdx.x / a.heads;
   const int h = blockIdx.x % a.heads;
-  const int64_t t0 = static_cast<int64_t>(chunk) * kChunk;
-  const int rows = a.n_tokens - t0 < kChunk ? static_cast<int>(a.n_tokens - t0) : kChunk;
+  const int n_chunks = static_cast<int>((a.n_tokens + kChunk - 1) / kChunk);
+  const int c_begin = g * kGroup;
+  const int c_end = c_begin + kGroup < n_chunks ? c_begin + kGroup : n_chunks;
   const int stride = a.heads * kD;
-  const bf16_t *kg = static_cast<const bf16_t *>(a.k) + (t0 * a.heads + h) * kD;
-  const bf16_t *vg = static_cast<const bf16_t *>(a.v) + (t0 * a.heads + h) * kD;
-  stage_rows(lds_v, vg, stride, rows, wave, lane);
 
-  // Wave 0: the chunk's cumulative log gates (lane holds positions 2L, 2L+1).
-  if (wave == 0) {
-    float l0 = 0.f, l1 = 0.f;
-    const int p0 = 2 * lane, p1 = 2 * lane + 1;
-    if (p0 < rows) l0 = gret_log_gate(a.gate[(t0 + p0) * a.heads + h], a.inv_tau);
-    if (p1 < rows) l1 = gret_log_gate(a.gate[(t0 + p1) * a.heads + h], a.inv_tau);
-    l1 += l0;
-    float incl = l1;  // inclusive scan of the pair sums over lanes
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) {
-      const float o = __shfl_up(incl, s, 64);
-      if (lane >= s) incl += o;
-    }
-    const float excl = incl - l1;
-    const float c0v = excl + l0, c1v = excl + l1;
-    const float last = __shfl(incl, 63, 64);  // l_C (rows past the chunk add 0)
-    if (p0 < rows) a.lcum[(t0 + p0) * a.heads + h] = c0v;
-    if (p1 < rows) a.lcum[(t0 + p1) * a.heads + h] = c1v;
-    s_w[p0] = p0 < rows ? expf(last - c0v) : 0.f;
-    s_w[p1] = p1 < rows ? expf(last - c1v) : 0.f;
-  }
-  __syncthreads();
-  // K' = exp(l_C - l_k) k_k in bf16, staged through registers.
-#pragma unroll
-  for (int i = 0; i < kChunk * 16 / kThreads; ++i) {
-    const int piece = i * kThreads + tid;
-    const int row = piece >> 4;
-    const int ch = piece & 15;
-    Frag8 f;
-    f.u = make_uint4(0, 0, 0, 0);
-    if (row < rows) {
-      const uint4 raw = ld16(kg + static_cast<int64_t>(row) * stride + ch * 8);
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-      const float sc = s_w[row];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) f.w[j] = cvt_pk_bf16(bf16_lo(w[j]) * sc, bf16_hi(w[j]) * sc);
-    }
-    *reinterpret_cast<uint4 *>(lds_k + swz<kD, kSwz>(row, ch * 8)) = f.u;
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  TrFrag fr;  // both operands of K'^T V use the same k order
+  TrFrag fr;  // both operands of K'^T V in the same k order
   fr.init(lane, kSplitHalves);
+  // This wave's K^T fragment offsets (index tile = wave), kept out of the
+  // per-tile table so no register array is indexed at run time.
+  const int ka0 = TrFrag::offset(lane, kSplitHalves, 0, wave);
+  const int ka1 = TrFrag::offset(lane, kSplitHalves, 1, wave);
   floatx16 acc[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
   }
+  float delta = 0.f;  // log decay from the group's start to chunk c
+  for (int c = c_begin; c < c_end; ++c) {
+    const int64_t t0 = static_cast<int64_t>(c) * kChunk;
+    const int rows = a.n_tokens - t0 < kChunk ? static_cast<int>(a.n_tokens - t0) : kChunk;
+    stage_rows(lds_k, static_cast<const bf16_t *>(a.k) + (t0 * a.heads + h) * kD, stride, rows, wave, lane);
+    stage_rows(lds_v, static_cast<const bf16_t *>(a.v) + (t0 * a.heads + h) * kD, stride, rows, wave, lane);
+    // Wave 0, while the tiles load: the chunk's cumulative log gates (lane
+    // holds positions 2L, 2L+1) and the key weights exp(l_C - l_k).
+    if (wave == 0) {
+      float l0 = 0.f, l1 = 0.f;
+      const int p0 = 2 * lane, p1 = 2 * lane + 1;
+      if (p0 < rows) l0 = gret_log_gate(a.gate[(t0 + p0) * a.heads + h], a.inv_tau);
+      if (p1 < rows) l1 = gret_log_gate(a.gate[(t0 + p1) * a.heads + h], a.inv_tau);
+      l1 += l0;
+      float incl = l1;  // inclusive scan of the pair sums over lanes
 #pragma unroll
-  for (int ks = 0; ks < kChunk / 16; ++ks) {
-    const bf16x8_t af = fr.read(lds_k, wave, ks);  // K'^T rows 32*wave + lane%32
+      for (int sft = 1; sft < 64; sft <<= 1) {
+        const float o = __shfl_up(incl, sft, 64);
+        if (lane >= sft) incl += o;
+      }
+      const float excl = incl - l1;
+      const float c0v = excl + l0, c1v = excl + l1;
+      const float last = __shfl(incl, 63, 64);  // l_C (rows past the chunk add 0)
+      if (p0 < rows) a.lcum[(t0 + p0) * a.heads + h] = c0v;
+      if (p1 < rows) a.lcum[(t0 + p1) * a.heads + h] = c1v;
+      s_w[p0] = p0 < rows ? expf(last - c0v) : 0.f;
+      s_w[p1] = p1 < rows ? expf(last - c1v) : 0.f;
+      if (lane == 0) {
+        s_lc = last;
+        a.cdec[static_cast<int64_t>(c) * a.heads + h] = delta;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const float lc = s_lc;
+    // A_c out (bf16, transposed): acc[t] element e is A row (key dim)
+    // 32*wave + (e/4)*8 + half*4 + e%4, column (value dim) t*32 + col, so a
+    // lane's four consecutive e are four consecutive key dims: 8-byte stores.
+    if (c > c_begin) {
+      uint16_t *rl = a.rl + (static_cast<int64_t>(c) * a.heads + h) * kD * kD;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, fr.read(lds_v, t, ks), acc[t], 0, 0, 0);
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          uint2 pk;
+          pk.x = cvt_pk_bf16(acc[t][q4 * 4 + 0], acc[t][q4 * 4 + 1]);
+          pk.y = cvt_pk_bf16(acc[t][q4 * 4 + 2], acc[t][q4 * 4 + 3]);
+          *reinterpret_cast<uint2 *>(rl + (t * 32 + col) * kD + wave * 32 + q4 * 8 + half * 4) = pk;
+        }
+      }
+    }
+    const float dec = expf(lc);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[t][e] *= dec;
+    }
+    delta += lc;
+#pragma unroll
+    for (int ks = 0; ks < kChunk / 16; ++ks) {
+      // The K^T fragment holds key rows ks*16 + half*8 + i (i = 0..7) of
+      // key dim 32*wave + col; each is weighted and rounded to bf16.
+      Frag8 af;
+      af.v = TrFrag::read_at(lds_k, ka0, ka1, ks);
+      const float4 w0 = *reinterpret_cast<const float4 *>(s_w + ks * 16 + half * 8);
+      const float4 w1 = *reinterpret_cast<const float4 *>(s_w + ks * 16 + half * 8 + 4);
+      af.w[0] = cvt_pk_bf16(bf16_lo(af.w[0]) * w0.x, bf16_hi(af.w[0]) * w0.y);
+      af.w[1] = cvt_pk_bf16(bf16_lo(af.w[1]) * w0.z, bf16_hi(af.w[1]) * w0.w);
+      af.w[2] = cvt_pk_bf16(bf16_lo(af.w[2]) * w1.x, bf16_hi(af.w[2]) * w1.y);
+      af.w[3] = cvt_pk_bf16(bf16_lo(af.w[3]) * w1.z, bf16_hi(af.w[3]) * w1.w);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af.v, fr.read(lds_v, t, ks), acc[t], 0, 0, 0);
+    }
+    __syncthreads();  // the next chunk's tiles take the buffers
   }
-  // acc[t] element e: U row 32*wave + (e/4)*8 + half*4 + e%4, column t*32 + lane%32.
-  float *u = a.u + (static_cast<int64_t>(chunk) * a.heads + h) * kD * kD;
-  const int half = lane >> 5;
+  // T_g (fp32, transposed) and Lambda_g.
+  float *tg = a.tg + (static_cast<int64_t>(g) * a.heads + h) * kD * kD;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int row = wave * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-      u[row * kD + t * 32 + (lane & 31)] = acc[t][e];
+    for (int q4 = 0; q4 < 4; ++q4) {
+      *reinterpret_cast<float4 *>(tg + (t * 32 + col) * kD + wave * 32 + q4 * 8 + half * 4) =
+          make_float4(acc[t][q4 * 4 + 0], acc[t][q4 * 4 + 1], acc[t][q4 * 4 + 2], acc[t][q4 * 4 + 3]);
     }
   }
+  if (tid == 0) a.gdec[static_cast<int64_t>(g) * a.heads + h] = delta;
 }
 
 // ---------------------------------------------------------------------------
-// The pass over chunks: R_0 = start state, R_{c+1} = exp(l_C) R_c + U_c.
-// Thread owns 4 consecutive state elements of one head; R_c goes out in bf16
-// (for the output kernel), the state after the last chunk in fp32.
+// The pass over groups: S_0 = start state, S_{g+1} = exp(Lambda_g) S_g + T_g.
+// Thread owns 4 consecutive elements of one head's transposed state; S_g
+// goes out in fp32 for the output kernel, the state after the last group
+// (untransposed) to state_out.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void gret_scan_kernel(const GretArgs a, int n_chunks) {
+__global__ __launch_bounds__(256) void gret_group_scan_kernel(const GretArgs a, int n_groups) {
   using namespace gr;
   constexpr int kPerHead = kD * kD / 4;  // float4s per state
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= static_cast<int64_t>(a.heads) * kPerHead) return;
   const int h = static_cast<int>(idx / kPerHead);
   const int e4 = static_cast<int>(idx % kPerHead);
-  float4 r = a.state_in ? reinterpret_cast<const float4 *>(a.state_in + static_cast<int64_t>(h) * kD * kD)[e4]
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
-  auto u_at = [&](int c) __attribute__((always_inline)) {
-    return reinterpret_cast<const float4 *>(a.u + (static_cast<int64_t>(c) * a.heads + h) * kD * kD)[e4];
-  };
-  auto lc_at = [&](int c) __attribute__((always_inline)) {
-    const int64_t last = (static_cast<int64_t>(c) + 1) * kChunk - 1 < a.n_tokens - 1
-                             ? (static_cast<int64_t>(c) + 1) * kChunk - 1 : a.n_tokens - 1;
-    return a.lcum[last * a.heads + h];
+  const int vdim = e4 / (kD / 4);         // row of the transposed state
+  const int kdim = (e4 % (kD / 4)) * 4;   // first of its four key dims
+  float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (a.state_in) {
+    const float *si = a.state_in + static_cast<int64_t>(h) * kD * kD + vdim;
+    r = make_float4(si[(kdim + 0) * kD], si[(kdim + 1) * kD], si[(kdim + 2) * kD], si[(kdim + 3) * kD]);
+  }
+  auto t_at = [&](int gg) __attribute__((always_inline)) {
+    return reinterpret_cast<const float4 *>(a.tg + (static_cast<int64_t>(gg) * a.heads + h) * kD * kD)[e4];
   };
   float4 ring[kScanAhead];
   float lring[kScanAhead];
 #pragma unroll
   for (int j = 0; j < kScanAhead; ++j) {
-    if (j < n_chunks) {
-      ring[j] = u_at(j);
-      lring[j] = lc_at(j);
+    if (j < n_groups) {
+      ring[j] = t_at(j);
+      lring[j] = a.gdec[static_cast<int64_t>(j) * a.heads + h];
     }
   }
-  for (int c0 = 0; c0 < n_chunks; c0 += kScanAhead) {
+  for (int g0 = 0; g0 < n_groups; g0 += kScanAhead) {
 #pragma unroll
     for (int j = 0; j < kScanAhead; ++j) {
-      const int c = c0 + j;
-      if (c < n_chunks) {
-        uint2 packed;
-        packed.x = cvt_pk_bf16(r.x, r.y);
-        packed.y = cvt_pk_bf16(r.z, r.w);
-        reinterpret_cast<uint2 *>(a.rb + (static_cast<int64_t>(c) * a.heads + h) * kD * kD)[e4] = packed;
+      const int gg = g0 + j;
+      if (gg < n_groups) {
+        reinterpret_cast<float4 *>(a.sg + (static_cast<int64_t>(gg) * a.heads + h) * kD * kD)[e4] = r;
         const float dec = expf(lring[j]);
-        const float4 u = ring[j];
-        r.x = fmaf(dec, r.x, u.x);
-        r.y = fmaf(dec, r.y, u.y);
-        r.z = fmaf(dec, r.z, u.z);
-        r.w = fmaf(dec, r.w, u.w);
-        if (c + kScanAhead < n_chunks) {
-          ring[j] = u_at(c + kScanAhead);
-          lring[j] = lc_at(c + kScanAhead);
+        const float4 t = ring[j];
+        r.x = fmaf(dec, r.x, t.x);
+        r.y = fmaf(dec, r.y, t.y);
+        r.z = fmaf(dec, r.z, t.z);
+        r.w = fmaf(dec, r.w, t.w);
+        if (gg + kScanAhead < n_groups) {
+          ring[j] = t_at(gg + kScanAhead);
+          lring[j] = a.gdec[static_cast<int64_t>(gg + kScanAhead) * a.heads + h];
         }
       }
     }
   }
-  if (a.state_out) reinterpret_cast<float4 *>(a.state_out + static_cast<int64_t>(h) * kD * kD)[e4] = r;
+  if (a.state_out) {
+    float *so = a.state_out + static_cast<int64_t>(h) * kD * kD + vdim;
+    so[(kdim + 0) * kD] = r.x;
+    so[(kdim + 1) * kD] = r.y;
+    so[(kdim + 2) * kD] = r.z;
+    so[(kdim + 3) * kD] = r.w;
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Outputs of one chunk of one head: wave w owns query rows 32w .. 32w+31.
-// 64 KiB of LDS (two workgroups per CU): the carried state R_c is staged into
+// 64 KiB of LDS (two workgroups per CU): the carried state R_c is formed in
 // the buffer that V takes afterwards, so V loads while the scores of the
 // chunk are formed.
 // ---------------------------------------------------------------------------
@@ -385,10 +448,32 @@ __global__ __launch_bounds__(gr::kThreads, 2) void gret_chunk_out_kernel(const G
   const int stride = a.heads * kD;
   const bf16_t *kg = static_cast<const bf16_t *>(a.k) + (t0 * a.heads + h) * kD;
   const bf16_t *vg = static_cast<const bf16_t *>(a.v) + (t0 * a.heads + h) * kD;
-  const bf16_t *rg = a.rb + (static_cast<int64_t>(chunk) * a.heads + h) * kD * kD;
-  stage_rows(lds_rv, rg, kD, kChunk, wave, lane);
   stage_rows(lds_k, kg, stride, rows, wave, lane);
   if (tid < kChunk) s_l[tid] = tid < rows ? a.lcum[(t0 + tid) * a.heads + h] : 0.f;
+  // R_c = A_c + exp(delta_c) S_g (transposed: row = value dim), formed in
+  // fp32 and rounded to bf16 into LDS; A_c is zero for a group's first chunk.
+  {
+    const int g = chunk / kGroup;
+    const bool first = chunk == g * kGroup;
+    const float dec = expf(a.cdec[static_cast<int64_t>(chunk) * a.heads + h]);
+    const float *sg = a.sg + (static_cast<int64_t>(g) * a.heads + h) * kD * kD;
+    const uint16_t *rl = a.rl + (static_cast<int64_t>(chunk) * a.heads + h) * kD * kD;
+#pragma unroll
+    for (int i = 0; i < kD * 16 / kThreads; ++i) {
+      const int piece = i * kThreads + tid;
+      const int row = piece >> 4;
+      const int ch = piece & 15;
+      const float4 s0 = *reinterpret_cast<const float4 *>(sg + row * kD + ch * 8);
+      const float4 s1 = *reinterpret_cast<const float4 *>(sg + row * kD + ch * 8 + 4);
+      Frag8 r;
+      r.u = first ? make_uint4(0, 0, 0, 0) : ld16(reinterpret_cast<const bf16_t *>(rl) + row * kD + ch * 8);
+      r.w[0] = cvt_pk_bf16(fmaf(dec, s0.x, bf16_lo(r.w[0])), fmaf(dec, s0.y, bf16_hi(r.w[0])));
+      r.w[1] = cvt_pk_bf16(fmaf(dec, s0.z, bf16_lo(r.w[1])), fmaf(dec, s0.w, bf16_hi(r.w[1])));
+      r.w[2] = cvt_pk_bf16(fmaf(dec, s1.x, bf16_lo(r.w[2])), fmaf(dec, s1.y, bf16_hi(r.w[2])));
+      r.w[3] = cvt_pk_bf16(fmaf(dec, s1.z, bf16_lo(r.w[3])), fmaf(dec, s1.w, bf16_hi(r.w[3])));
+      *reinterpret_cast<uint4 *>(lds_rv + swz<kD, kSwz>(row, ch * 8)) = r.u;
+    }
+  }
 
   // Q^T as the B operand: lane holds query row 32*wave + col, dims ks*16 + half*8 .. +8.
   const int my_row = wave * 32 + col;
@@ -402,20 +487,27 @@ __global__ __launch_bounds__(gr::kThreads, 2) void gret_chunk_out_kernel(const G
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  TrFrag fr, fv;
-  fr.init(lane, kSplitHalves);  // R^T against Q^T (16-byte reads of q rows)
+  TrFrag fv;
   fv.init(lane, kInterleave);   // V^T against P^T (the score accumulator order)
+  int koff[kD / 16];            // 16-byte reads of a row-major [.][128] tile: row col, dims ks*16 + half*8
+#pragma unroll
+  for (int ks = 0; ks < kD / 16; ++ks) koff[ks] = swz<kD, kSwz>(col, ks * 16 + half * 8);
   floatx16 oacc[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[d][e] = 0.f;
   }
-  // Carried state: O^T = R^T Q^T, then row j times exp(l_j).
+  // Carried state: O^T = R^T Q^T (R^T rows d*32 + col from 16-byte reads),
+  // then row j times exp(l_j).
 #pragma unroll
   for (int ks = 0; ks < kD / 16; ++ks) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d) oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.read(lds_rv, d, ks), qf[ks].v, oacc[d], 0, 0, 0);
+    for (int d = 0; d < 4; ++d) {
+      Frag8 rf;
+      rf.u = *reinterpret_cast<const uint4 *>(lds_rv + d * 32 * kRowBytes + koff[ks]);
+      oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf.v, qf[ks].v, oacc[d], 0, 0, 0);
+    }
   }
   const float l_row = s_l[row_valid ? my_row : 0];
   const float carry = expf(l_row);
@@ -429,9 +521,6 @@ __global__ __launch_bounds__(gr::kThreads, 2) void gret_chunk_out_kernel(const G
 
   // Scores of the chunk while V loads: 32-key halves u = 0 .. wave (keys <=
   // the wave's rows), P = S exp(l_j - l_k) masked to k <= j, in bf16.
-  int koff[kD / 16];
-#pragma unroll
-  for (int ks = 0; ks < kD / 16; ++ks) koff[ks] = swz<kD, kSwz>(col, ks * 16 + half * 8);
   Frag8 p[kWaves][2];
 #pragma unroll
   for (int u = 0; u < kWaves; ++u) {
@@ -493,6 +582,8 @@ bool gret_chunked_applies(int dtype, int head_dim) { return dtype == YOCO_DT_BF1
 
 int64_t gret_n_chunks(int64_t n) { return (n + gr::kChunk - 1) / gr::kChunk; }
 
+int64_t gret_n_groups(int64_t n) { return (gret_n_chunks(n) + gr::kGroup - 1) / gr::kGroup; }
+
 hipError_t launch_gret_recurrent(const GretArgs &a, int dtype, int head_dim, int n_seq, hipStream_t s) {
   const int64_t blocks64 = static_cast<int64_t>(n_seq) * a.heads * (head_dim / kGretCols);
   if (blocks64 > 0x7fffffff) return hipErrorInvalidValue;
@@ -509,14 +600,16 @@ hipError_t launch_gret_recurrent(const GretArgs &a, int dtype, int head_dim, int
 
 hipError_t launch_gret_chunked(const GretArgs &a, hipStream_t s) {
   const int64_t n_chunks = gret_n_chunks(a.n_tokens);
+  const int64_t n_groups = gret_n_groups(a.n_tokens);
   const int64_t blocks = n_chunks * a.heads;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gret_chunk_state_kernel, dim3(static_cast<unsigned>(blocks)), dim3(gr::kThreads), 0, s, a);
+  hipLaunchKernelGGL(gret_group_state_kernel, dim3(static_cast<unsigned>(n_groups * a.heads)), dim3(gr::kThreads), 0,
+                     s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t scan_threads = static_cast<int64_t>(a.heads) * gr::kD * gr::kD / 4;
-  hipLaunchKernelGGL(gret_scan_kernel, dim3(static_cast<unsigned>((scan_threads + 255) / 256)), dim3(256), 0, s, a,
-                     static_cast<int>(n_chunks));
+  hipLaunchKernelGGL(gret_group_scan_kernel, dim3(static_cast<unsigned>((scan_threads + 255) / 256)), dim3(256), 0, s,
+                     a, static_cast<int>(n_groups));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(gret_chunk_out_kernel, dim3(static_cast<unsigned>(blocks)), dim3(gr::kThreads), 0, s, a);
   return hipGetLastError();

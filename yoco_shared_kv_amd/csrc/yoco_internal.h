@@ -146,9 +146,12 @@ struct GretArgs {
   const float *state_in;
   float *state_out;
   float *o;
-  float *lcum;
-  float *u;
-  uint16_t *rb;
+  float *lcum;      // [n][heads] inclusive cumulative log gates inside each chunk
+  float *cdec;      // [chunks][heads] log decay from the chunk's group start to the chunk
+  float *gdec;      // [groups][heads] log decay over each group
+  uint16_t *rl;     // [chunks][heads][D][D] bf16 group-local state before each chunk (transposed)
+  float *tg;        // [groups][heads][D][D] group-local state after each group (transposed)
+  float *sg;        // [groups][heads][D][D] state entering each group (transposed)
   int64_t n_tokens;
   int32_t heads;
   float inv_tau;
@@ -156,6 +159,7 @@ struct GretArgs {
 
 bool gret_chunked_applies(int dtype, int head_dim);
 int64_t gret_n_chunks(int64_t n);
+int64_t gret_n_groups(int64_t n);
 hipError_t launch_gret_recurrent(const GretArgs &a, int dtype, int head_dim, int n_seq, hipStream_t s);
 hipError_t launch_gret_chunked(const GretArgs &a, hipStream_t s);
 
