@@ -74,6 +74,10 @@ def _gpu_kv(pc, dz_k, dz_v, gain, init=None, d_gain=True):
     (300, 512, 2, 128, W.BF16, W.BF16, False, TOL_MFMA),
     (700, 256, 4, 64, W.BF16, W.F32, True, TOL_MFMA),    # two row splits of the d_W product
     (1, 256, 2, 128, W.BF16, W.F32, True, TOL_MFMA),     # one row
+    (130, 768, 2, 128, W.BF16, W.F32, True, TOL_MFMA),   # the row kernels' last column groups half past d
+    (64, 3584, 2, 128, W.BF16, W.F32, True, TOL_MFMA),   # d > 3072: the general row kernel after the MFMA products
+    (100, 320, 2, 64, W.F32, W.F32, True, TOL_F32),      # d % 256 != 0: the general row kernel, 4-column groups
+    (90, 130, 1, 64, W.F32, W.F32, True, TOL_F32),       # odd width: single columns
 ])
 def test_kv_project_bwd_matches_oracle(n, d, hkv, dh, dtype, dz_dtype, gain, tol):
     print(f"kv_project_bwd n={n} d={d} hkv={hkv} dh={dh} {dtype} dz {dz_dtype} gain={gain}", flush=True)

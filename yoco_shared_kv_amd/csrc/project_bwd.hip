@@ -228,6 +228,87 @@ __global__ __launch_bounds__(256) void pbwd_prep_kernel(const ProjBwdArgs a) {
   }
 }
 
+// The same on the matrix-core path (bf16 x, d % 256 == 0, d <= 512 GX):
+// every load of a row is issued before the first is used, x stays in
+// registers between the sum of squares and y, and dz is converted four
+// 8-column groups per batch.  Same arithmetic, in the same order.
+template <int GX>
+__global__ __launch_bounds__(256) void pbwd_prep_rows_kernel(const ProjBwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= a.n) return;
+  const int d = a.d;
+  const bf16_t *xr = static_cast<const bf16_t *>(a.x) + row * d;
+  uint4 xw[GX];
+#pragma unroll
+  for (int i = 0; i < GX; ++i) {
+    const int c = lane * 8 + 512 * i;
+    xw[i] = c < d ? ld16(xr + c) : make_uint4(0, 0, 0, 0);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < GX; ++i) {
+    const uint32_t ww[4] = {xw[i].x, xw[i].y, xw[i].z, xw[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ss = fmaf(bf16_lo(ww[j]), bf16_lo(ww[j]), ss);
+      ss = fmaf(bf16_hi(ww[j]), bf16_hi(ww[j]), ss);
+    }
+  }
+  ss = pb::wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / static_cast<float>(d) + a.eps);
+  if (lane == 0) a.inv_r[row] = inv;
+  bf16_t *yr = a.ybf + row * d;
+#pragma unroll
+  for (int i = 0; i < GX; ++i) {
+    const int c = lane * 8 + 512 * i;
+    if (c >= d) continue;
+    const uint32_t ww[4] = {xw[i].x, xw[i].y, xw[i].z, xw[i].w};
+    float g[8];
+    if (a.gain) {
+      const float4 g0 = *reinterpret_cast<const float4 *>(a.gain + c);
+      const float4 g1 = *reinterpret_cast<const float4 *>(a.gain + c + 4);
+      g[0] = g0.x, g[1] = g0.y, g[2] = g0.z, g[3] = g0.w, g[4] = g1.x, g[5] = g1.y, g[6] = g1.z, g[7] = g1.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) g[j] = 1.f;
+    }
+    uint4 o;
+    uint32_t *ow = reinterpret_cast<uint32_t *>(&o);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ow[j] = pb::cvt_pk_bf16(bf16_lo(ww[j]) * g[2 * j] * inv, bf16_hi(ww[j]) * g[2 * j + 1] * inv);
+    *reinterpret_cast<uint4 *>(yr + c) = o;
+  }
+  if (a.dz_bf16) return;
+  constexpr int kBatch = 4;
+  for (int p = 0; p < a.n_out; ++p) {
+    const float *zr = static_cast<const float *>(a.dz[p]) + row * a.ncols;
+    bf16_t *zb = a.dzb[p] + row * a.ncols;
+    for (int c0 = lane * 8; c0 < a.ncols; c0 += 512 * kBatch) {
+      uint4 u[kBatch][2];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int c = c0 + 512 * b;
+        if (c < a.ncols) {
+          u[b][0] = ld16(zr + c);
+          u[b][1] = ld16(zr + c + 4);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int c = c0 + 512 * b;
+        if (c >= a.ncols) continue;
+        uint4 o;
+        o.x = pb::cvt_pk_bf16(__uint_as_float(u[b][0].x), __uint_as_float(u[b][0].y));
+        o.y = pb::cvt_pk_bf16(__uint_as_float(u[b][0].z), __uint_as_float(u[b][0].w));
+        o.z = pb::cvt_pk_bf16(__uint_as_float(u[b][1].x), __uint_as_float(u[b][1].y));
+        o.w = pb::cvt_pk_bf16(__uint_as_float(u[b][1].z), __uint_as_float(u[b][1].w));
+        *reinterpret_cast<uint4 *>(zb + c) = o;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dy^T = W dz^T on the matrix cores; stores dy / r into dx.
 // Tile: 256 model columns c (A = W_p rows) x 256 input rows r (B = dz_p
@@ -632,6 +713,91 @@ __global__ __launch_bounds__(256) void pbwd_dx_kernel(const ProjBwdArgs a) {
   }
 }
 
+// The same for d % 256 == 0 with G = d / 256 <= 12 column groups per lane: a row's
+// loads are all issued before the first is used and both sweeps run from
+// registers; the gain and the wave's dgain share stay in registers across
+// its rows.  Same arithmetic, in the same order.
+template <typename TX, int G>
+__global__ __launch_bounds__(256) void pbwd_dx_rows_kernel(const ProjBwdArgs a) {
+  extern __shared__ float s_dg[];  // [4][d]
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int d = a.d;
+  float g[G][4], dg[G][4];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    if (a.gain) {
+      const float4 gg = *reinterpret_cast<const float4 *>(a.gain + lane * 4 + 256 * i);
+      g[i][0] = gg.x, g[i][1] = gg.y, g[i][2] = gg.z, g[i][3] = gg.w;
+    } else {
+      g[i][0] = g[i][1] = g[i][2] = g[i][3] = 1.f;
+    }
+    dg[i][0] = dg[i][1] = dg[i][2] = dg[i][3] = 0.f;
+  }
+  const int64_t r_begin = static_cast<int64_t>(blockIdx.x) * kProjBwdFinRows;
+  const int64_t r_end = r_begin + kProjBwdFinRows < a.n ? r_begin + kProjBwdFinRows : a.n;
+  for (int64_t r = r_begin + wave; r < r_end; r += 4) {
+    float *dxr = a.dx + r * d;
+    float4 dv[G];
+    float xv[G][4];
+    if constexpr (sizeof(TX) == 2) {
+      uint2 xw[G];
+      const bf16_t *xr = static_cast<const bf16_t *>(a.x) + r * d;
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        dv[i] = *reinterpret_cast<const float4 *>(dxr + lane * 4 + 256 * i);
+        xw[i] = *reinterpret_cast<const uint2 *>(xr + lane * 4 + 256 * i);
+      }
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        xv[i][0] = bf16_lo(xw[i].x), xv[i][1] = bf16_hi(xw[i].x);
+        xv[i][2] = bf16_lo(xw[i].y), xv[i][3] = bf16_hi(xw[i].y);
+      }
+    } else {
+      float4 xw[G];
+      const float *xr = static_cast<const float *>(a.x) + r * d;
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        dv[i] = *reinterpret_cast<const float4 *>(dxr + lane * 4 + 256 * i);
+        xw[i] = *reinterpret_cast<const float4 *>(xr + lane * 4 + 256 * i);
+      }
+#pragma unroll
+      for (int i = 0; i < G; ++i) xv[i][0] = xw[i].x, xv[i][1] = xw[i].y, xv[i][2] = xw[i].z, xv[i][3] = xw[i].w;
+    }
+    float s = 0.f;
+    float gd[G][4];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const float dvv[4] = {dv[i].x, dv[i].y, dv[i].z, dv[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        gd[i][e] = g[i][e] * dvv[e];
+        s = fmaf(gd[i][e], xv[i][e], s);
+        dg[i][e] = fmaf(dvv[e], xv[i][e], dg[i][e]);
+      }
+    }
+    s = pb::wave_sum(s);
+    const float inv = a.inv_r[r];
+    const float coef = inv * inv * s / static_cast<float>(d);
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      *reinterpret_cast<float4 *>(dxr + lane * 4 + 256 * i) =
+          make_float4(gd[i][0] - xv[i][0] * coef, gd[i][1] - xv[i][1] * coef, gd[i][2] - xv[i][2] * coef,
+                      gd[i][3] - xv[i][3] * coef);
+    }
+  }
+  if (a.dgain == nullptr) return;
+  float *my_dg = s_dg + wave * d;
+#pragma unroll
+  for (int i = 0; i < G; ++i)
+    *reinterpret_cast<float4 *>(my_dg + lane * 4 + 256 * i) = make_float4(dg[i][0], dg[i][1], dg[i][2], dg[i][3]);
+  __syncthreads();
+  for (int c = threadIdx.x; c < d; c += 256) {
+    const float v = ((s_dg[c] + s_dg[d + c]) + s_dg[2 * d + c]) + s_dg[3 * d + c];
+    a.dgain_part[static_cast<int64_t>(blockIdx.x) * d + c] = v;
+  }
+}
+
 // dgain[c] += sum over row blocks of their shares.  A block takes 16
 // columns; thread (slice, column) sums a contiguous run of row blocks, and
 // the 16 runs are added in order.
@@ -680,11 +846,54 @@ void project_bwd_split_plan(int64_t n, int32_t d, int32_t ncols, int32_t n_out, 
   *splits = static_cast<int32_t>((n + r - 1) / r);
 }
 
+template <typename TX, int G>
+static void launch_dx_rows(const ProjBwdArgs &a, unsigned blocks, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL((pbwd_dx_rows_kernel<TX, G>), dim3(blocks), dim3(256), lds, s, a);
+}
+
 template <typename TX>
 hipError_t launch_dx(const ProjBwdArgs &a, hipStream_t s) {
   const unsigned blocks = static_cast<unsigned>((a.n + kProjBwdFinRows - 1) / kProjBwdFinRows);
   const size_t lds = static_cast<size_t>(4) * a.d * sizeof(float);  // <= 64 KiB for d <= kProjBwdMaxD
-  hipLaunchKernelGGL((pbwd_dx_kernel<TX>), dim3(blocks), dim3(256), lds, s, a);
+  // Past 12 column groups the row kernel's registers allow one wave per SIMD.
+  if (a.d % 256 != 0 || a.d > 12 * 256) {
+    hipLaunchKernelGGL((pbwd_dx_kernel<TX>), dim3(blocks), dim3(256), lds, s, a);
+    return hipGetLastError();
+  }
+  switch (a.d / 256) {
+    case 1: launch_dx_rows<TX, 1>(a, blocks, lds, s); break;
+    case 2: launch_dx_rows<TX, 2>(a, blocks, lds, s); break;
+    case 3: launch_dx_rows<TX, 3>(a, blocks, lds, s); break;
+    case 4: launch_dx_rows<TX, 4>(a, blocks, lds, s); break;
+    case 5: launch_dx_rows<TX, 5>(a, blocks, lds, s); break;
+    case 6: launch_dx_rows<TX, 6>(a, blocks, lds, s); break;
+    case 7: launch_dx_rows<TX, 7>(a, blocks, lds, s); break;
+    case 8: launch_dx_rows<TX, 8>(a, blocks, lds, s); break;
+    case 9: launch_dx_rows<TX, 9>(a, blocks, lds, s); break;
+    case 10: launch_dx_rows<TX, 10>(a, blocks, lds, s); break;
+    case 11: launch_dx_rows<TX, 11>(a, blocks, lds, s); break;
+    default: launch_dx_rows<TX, 12>(a, blocks, lds, s); break;
+  }
+  return hipGetLastError();
+}
+
+static hipError_t launch_prep(const ProjBwdArgs &a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((a.n + 3) / 4));
+  if (!a.mfma) {
+    hipLaunchKernelGGL(pbwd_prep_kernel, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  // the matrix-core path has d % 256 == 0 and d <= kProjBwdMaxD
+  switch ((a.d + 511) / 512) {
+    case 1: hipLaunchKernelGGL((pbwd_prep_rows_kernel<1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((pbwd_prep_rows_kernel<2>), grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((pbwd_prep_rows_kernel<3>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((pbwd_prep_rows_kernel<4>), grid, dim3(256), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((pbwd_prep_rows_kernel<5>), grid, dim3(256), 0, s, a); break;
+    case 6: hipLaunchKernelGGL((pbwd_prep_rows_kernel<6>), grid, dim3(256), 0, s, a); break;
+    case 7: hipLaunchKernelGGL((pbwd_prep_rows_kernel<7>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((pbwd_prep_rows_kernel<8>), grid, dim3(256), 0, s, a); break;
+  }
   return hipGetLastError();
 }
 
@@ -704,8 +913,7 @@ hipError_t launch_valu_products_z(const ProjBwdArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_project_bwd(const ProjBwdArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(pbwd_prep_kernel, dim3(static_cast<unsigned>((a.n + 3) / 4)), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_prep(a, s);
   if (e != hipSuccess) return e;
   if (a.mfma) {
     const int64_t rtiles = (a.n + pb::kTile - 1) / pb::kTile;
