@@ -32,6 +32,11 @@
  *     length is unchanged; yoco_last_error() gives the reason.
  *   - Row-major layouts; element [a][b][c] of an [A][B][C] array sits at
  *     offset (a*B + b)*C + c.
+ *   - Alignment: every device array is 16-byte aligned (hipMalloc and torch
+ *     allocations are 256-byte aligned; row slices keep it when a row is a
+ *     multiple of 16 bytes), except the per-row or per-head scalar arrays
+ *     (lse, gate_logits), which need 4 bytes.  Any other pointer is rejected
+ *     with YOCO_ERR_ALIGNMENT before anything is enqueued.
  *   - head_dim is 64 or 128; H_q must be a multiple of H_kv with group size
  *     G = H_q / H_kv in {1, 2, 3, 4, 6, 8}.  Query head h reads KV head
  *     floor(h / G).
@@ -51,7 +56,7 @@
 extern "C" {
 #endif
 
-#define YOCO_ABI_VERSION 5
+#define YOCO_ABI_VERSION 6
 #define YOCO_MAX_SEQ 256
 
 /* Storage types. */
@@ -68,7 +73,8 @@ typedef enum yoco_status {
   YOCO_ERR_OUT_OF_RANGE = 4, /* rows or positions outside the cache */
   YOCO_ERR_WORKSPACE = 5,    /* workspace too small */
   YOCO_ERR_HIP = 6,          /* HIP runtime error, or the device is not gfx950 */
-  YOCO_ERR_BAD_VALUE = 7     /* bad scalar argument (eps, scale, split rows) */
+  YOCO_ERR_BAD_VALUE = 7,    /* bad scalar argument (eps, scale, split rows) */
+  YOCO_ERR_ALIGNMENT = 8     /* a device pointer breaks the alignment rule below */
 } yoco_status;
 
 /* The shared global K^/V^ cache ([Notes] Eq. 2; [Blog] section 7): ONE copy,

@@ -376,3 +376,48 @@ def test_gret_rejects_and_sizes_workspace():
     assert dec(b=-1) == _status("YOCO_ERR_BAD_SHAPE")
     assert dec(tau=0.0) == _status("YOCO_ERR_BAD_VALUE")
     assert dec(b=0) == 0
+
+
+def test_status_table_matches_header():
+    from yoco_shared_kv_amd._native import STATUS
+    text = open(HEADER).read()
+    codes = {int(v): k for k, v in re.findall(r"\b(YOCO_(?:OK|ERR_[A-Z_]+)) = (\d+)", text)}
+    assert codes == STATUS
+
+
+MIS = ctypes.c_void_p(0x1008)   # 8-byte but not 16-byte aligned
+MIS4 = ctypes.c_void_p(0x1002)  # not 4-byte aligned
+AL4 = ctypes.c_void_p(0x1004)   # 4-byte aligned
+
+
+def test_misaligned_pointers_rejected():
+    L = _lib()
+    bad = _status("YOCO_ERR_ALIGNMENT")
+    c, lens = _cache()
+    assert _project(c, m=MIS) == bad
+    assert _project(c, gain=MIS) == bad
+    assert lens.tolist() == [10, 20]
+    assert "aligned" in L.yoco_last_error().decode()
+    c.k = MIS
+    assert _project(c) == bad
+    c, lens = _cache()
+    assert L.yoco_kv_append(FAKE, 1, 32, None, 1e-6, FAKE, MIS, 1, ctypes.byref(c), None) == bad
+    assert lens.tolist() == [10, 20]
+    assert L.yoco_q_project(FAKE, 1, 4, 32, None, 1e-6, FAKE, 1, 4, 64, MIS, 1, None) == bad
+    assert L.yoco_cross_attn_prefill(MIS, 1, 0, 4, 4, ctypes.byref(c), 0, 0.125, FAKE, 0, None, None) == bad
+    assert L.yoco_cross_attn_prefill(FAKE, 1, 0, 4, 4, ctypes.byref(c), 0, 0.125, FAKE, 0, MIS4, None) == bad
+    assert L.yoco_cross_attn_decode(FAKE, 1, 4, ctypes.byref(c), 0.125, MIS, None, FAKE, 1 << 30, 0, None) == bad
+    assert L.yoco_cross_attn_decode(FAKE, 1, 4, ctypes.byref(c), 0.125, FAKE, None, MIS, 1 << 30, 0, None) == bad
+    assert _bwd(c, d_v=MIS) == bad
+    assert _bwd(c, lse=MIS4) == bad
+    assert _pbwd(dzv=MIS) == bad
+    assert _pbwd(dm=MIS) == bad
+    # 4-byte scalar arrays pass the alignment check (and fail later only for other reasons)
+    assert _bwd(c, lse=AL4, ws_bytes=16) == _status("YOCO_ERR_WORKSPACE")
+    gret = lambda **kw: L.yoco_gret_prefill(kw.get("q", FAKE), FAKE, FAKE, 1, kw.get("g", FAKE), 16.0, 300, 3, 128,
+                                           kw.get("s_in"), FAKE, None, FAKE, kw.get("ws_bytes", 1 << 30), None)
+    assert gret(q=MIS) == bad
+    assert gret(s_in=MIS) == bad
+    assert gret(g=MIS4) == bad
+    assert gret(g=AL4, ws_bytes=100) == _status("YOCO_ERR_WORKSPACE")
+    assert L.yoco_gret_decode(FAKE, FAKE, FAKE, 1, FAKE, 16.0, 2, 3, 128, MIS, FAKE, None) == bad

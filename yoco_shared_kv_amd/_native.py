@@ -20,6 +20,7 @@ YOCO_DECODE_COUNTER_BYTES = YOCO_MAX_SEQ * 64 * 4
 STATUS = {
     0: "YOCO_OK", 1: "YOCO_ERR_NULL_POINTER", 2: "YOCO_ERR_BAD_SHAPE", 3: "YOCO_ERR_BAD_DTYPE",
     4: "YOCO_ERR_OUT_OF_RANGE", 5: "YOCO_ERR_WORKSPACE", 6: "YOCO_ERR_HIP", 7: "YOCO_ERR_BAD_VALUE",
+    8: "YOCO_ERR_ALIGNMENT",
 }
 
 

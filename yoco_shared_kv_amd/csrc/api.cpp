@@ -5,6 +5,8 @@
 
 #include <atomic>
 #include <cmath>
+#include <cstdint>
+#include <initializer_list>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -61,9 +63,25 @@ yoco_status launched(hipError_t e, const char *what) {
   return ok();
 }
 
+// The kernels move tensors with 16-byte vector loads and stores, and
+// per-row or per-head scalars with 4-byte ones.
+struct Named {
+  const void *p;
+  const char *name;
+};
+
+yoco_status check_aligned(std::initializer_list<Named> ptrs, unsigned align) {
+  for (const Named &x : ptrs) {
+    if (x.p != nullptr && (reinterpret_cast<uintptr_t>(x.p) & (align - 1)) != 0)
+      return fail(YOCO_ERR_ALIGNMENT, "%s (%p) is not %u-byte aligned", x.name, x.p, align);
+  }
+  return YOCO_OK;
+}
+
 yoco_status check_cache(const yoco_kv_cache *c) {
   if (c == nullptr) return fail(YOCO_ERR_NULL_POINTER, "cache is NULL");
   if (c->k == nullptr || c->v == nullptr) return fail(YOCO_ERR_NULL_POINTER, "cache k or v is NULL");
+  if (check_aligned({{c->k, "cache k"}, {c->v, "cache v"}}, 16) != YOCO_OK) return YOCO_ERR_ALIGNMENT;
   if (c->len_host == nullptr) return fail(YOCO_ERR_NULL_POINTER, "cache len_host is NULL");
   if (c->n_seq < 1 || c->n_seq > YOCO_MAX_SEQ)
     return fail(YOCO_ERR_BAD_SHAPE, "n_seq %d outside [1, %d]", c->n_seq, YOCO_MAX_SEQ);
@@ -214,6 +232,7 @@ yoco_status kv_project_impl(const void *m, int32_t m_dtype, int64_t n, int32_t d
   yoco_status st = check_cache(cache);
   if (st != YOCO_OK) return st;
   if (m == nullptr || w_k == nullptr || w_v == nullptr) return fail(YOCO_ERR_NULL_POINTER, "m, w_k or w_v is NULL");
+  if ((st = check_aligned({{m, "m"}, {w_k, "w_k"}, {w_v, "w_v"}, {gain, "gain"}}, 16)) != YOCO_OK) return st;
   if (d_model < 1) return fail(YOCO_ERR_BAD_SHAPE, "d_model %d < 1", d_model);
   if (seq < 0 || seq >= cache->n_seq) return fail(YOCO_ERR_BAD_SHAPE, "seq %d outside [0, %d)", seq, cache->n_seq);
   if (!dtype_ok(m_dtype) || !dtype_ok(w_dtype)) return fail(YOCO_ERR_BAD_DTYPE, "m or w dtype unknown");
@@ -255,6 +274,7 @@ yoco_status kv_append_impl(const void *m_new, int32_t m_dtype, int32_t d_model, 
   if (st != YOCO_OK) return st;
   if (m_new == nullptr || w_k == nullptr || w_v == nullptr)
     return fail(YOCO_ERR_NULL_POINTER, "m_new, w_k or w_v is NULL");
+  if ((st = check_aligned({{m_new, "m_new"}, {w_k, "w_k"}, {w_v, "w_v"}, {gain, "gain"}}, 16)) != YOCO_OK) return st;
   if (d_model < 1) return fail(YOCO_ERR_BAD_SHAPE, "d_model %d < 1", d_model);
   if (!dtype_ok(m_dtype) || !dtype_ok(w_dtype)) return fail(YOCO_ERR_BAD_DTYPE, "m or w dtype unknown");
   if ((st = check_eps(eps)) != YOCO_OK) return st;
@@ -296,6 +316,8 @@ yoco_status q_project_impl(const void *x, int32_t x_dtype, int64_t n, int32_t d_
                            float eps, const void *w_q, int32_t w_dtype, int32_t n_q_heads, int32_t head_dim,
                            void *q_out, int32_t q_dtype, const RopeSpec &rope, void *stream) {
   if (x == nullptr || w_q == nullptr || q_out == nullptr) return fail(YOCO_ERR_NULL_POINTER, "x, w_q or q_out is NULL");
+  if (check_aligned({{x, "x"}, {w_q, "w_q"}, {gain, "gain"}, {q_out, "q_out"}}, 16) != YOCO_OK)
+    return YOCO_ERR_ALIGNMENT;
   if (d_model < 1 || n_q_heads < 1 || n < 0) return fail(YOCO_ERR_BAD_SHAPE, "d_model, n_q_heads and n must be positive");
   if (!head_dim_ok(head_dim)) return fail(YOCO_ERR_BAD_SHAPE, "head_dim %d is not 64 or 128", head_dim);
   if (!dtype_ok(x_dtype) || !dtype_ok(w_dtype) || !dtype_ok(q_dtype))
@@ -407,6 +429,8 @@ yoco_status yoco_cross_attn_prefill(const void *q, int32_t q_dtype, int64_t q_st
   yoco_status st = check_cache(cache);
   if (st != YOCO_OK) return st;
   if (q == nullptr || o == nullptr) return fail(YOCO_ERR_NULL_POINTER, "q or o is NULL");
+  if ((st = check_aligned({{q, "q"}, {o, "o"}}, 16)) != YOCO_OK) return st;
+  if ((st = check_aligned({{lse, "lse"}}, 4)) != YOCO_OK) return st;
   if ((st = check_heads(n_q_heads, cache->n_kv_heads)) != YOCO_OK) return st;
   if (seq < 0 || seq >= cache->n_seq) return fail(YOCO_ERR_BAD_SHAPE, "seq %d outside [0, %d)", seq, cache->n_seq);
   if (q_dtype != cache->dtype) return fail(YOCO_ERR_BAD_DTYPE, "q dtype %d differs from cache dtype %d", q_dtype, cache->dtype);
@@ -456,6 +480,8 @@ yoco_status yoco_cross_attn_decode(const void *q, int32_t q_dtype, int32_t n_q_h
   if (st != YOCO_OK) return st;
   if (q == nullptr || o == nullptr || workspace == nullptr)
     return fail(YOCO_ERR_NULL_POINTER, "q, o or workspace is NULL");
+  if ((st = check_aligned({{q, "q"}, {o, "o"}, {workspace, "workspace"}}, 16)) != YOCO_OK) return st;
+  if ((st = check_aligned({{lse, "lse"}}, 4)) != YOCO_OK) return st;
   if ((st = check_heads(n_q_heads, cache->n_kv_heads)) != YOCO_OK) return st;
   if (q_dtype != cache->dtype) return fail(YOCO_ERR_BAD_DTYPE, "q dtype %d differs from cache dtype %d", q_dtype, cache->dtype);
   if ((st = check_scale(softmax_scale)) != YOCO_OK) return st;
@@ -526,6 +552,10 @@ yoco_status yoco_cross_attn_prefill_bwd(const void *q, const void *o, int32_t o_
   if (q == nullptr || o == nullptr || d_o == nullptr || lse == nullptr || d_q == nullptr || d_k == nullptr ||
       d_v == nullptr || workspace == nullptr)
     return fail(YOCO_ERR_NULL_POINTER, "q, o, d_o, lse, d_q, d_k, d_v or workspace is NULL");
+  if ((st = check_aligned({{q, "q"}, {o, "o"}, {d_o, "d_o"}, {d_q, "d_q"}, {d_k, "d_k"}, {d_v, "d_v"},
+                           {workspace, "workspace"}}, 16)) != YOCO_OK)
+    return st;
+  if ((st = check_aligned({{lse, "lse"}}, 4)) != YOCO_OK) return st;
   if ((st = check_heads(n_q_heads, cache->n_kv_heads)) != YOCO_OK) return st;
   if (seq < 0 || seq >= cache->n_seq) return fail(YOCO_ERR_BAD_SHAPE, "seq %d outside [0, %d)", seq, cache->n_seq);
   if (cache->dtype != YOCO_DT_BF16)
@@ -614,6 +644,13 @@ yoco_status project_bwd_impl(const void *x, int32_t x_dtype, int64_t n, int32_t 
   for (int p = 0; p < n_out; ++p) {
     if (w[p] == nullptr || dz[p] == nullptr || d_w[p] == nullptr)
       return fail(YOCO_ERR_NULL_POINTER, "a weight, an output gradient or a weight gradient is NULL");
+  }
+  if (check_aligned({{x, "input"}, {gain, "gain"}, {d_x, "input gradient"}, {d_gain, "d_gain"},
+                     {workspace, "workspace"}}, 16) != YOCO_OK)
+    return YOCO_ERR_ALIGNMENT;
+  for (int p = 0; p < n_out; ++p) {
+    if (check_aligned({{w[p], "weight"}, {dz[p], "output gradient"}, {d_w[p], "weight gradient"}}, 16) != YOCO_OK)
+      return YOCO_ERR_ALIGNMENT;
   }
   if (n < 0 || d_model < 1 || d_model > yoco::kProjBwdMaxD)
     return fail(YOCO_ERR_BAD_SHAPE, "n %lld must be >= 0 and d_model %d in [1, %d]", (long long)n, d_model,
@@ -743,6 +780,8 @@ yoco_status check_gret(const void *q, const void *k, const void *v, const float 
                        int32_t heads, int32_t head_dim, float tau) {
   if (q == nullptr || k == nullptr || v == nullptr || gate == nullptr || o == nullptr)
     return fail(YOCO_ERR_NULL_POINTER, "q, k, v, gate_logits or o is NULL");
+  if (check_aligned({{q, "q"}, {k, "k"}, {v, "v"}, {o, "o"}}, 16) != YOCO_OK) return YOCO_ERR_ALIGNMENT;
+  if (check_aligned({{gate, "gate_logits"}}, 4) != YOCO_OK) return YOCO_ERR_ALIGNMENT;
   if (heads < 1 || heads > 4096) return fail(YOCO_ERR_BAD_SHAPE, "n_heads %d outside [1, 4096]", heads);
   if (!head_dim_ok(head_dim)) return fail(YOCO_ERR_BAD_SHAPE, "head_dim %d is not 64 or 128", head_dim);
   if (!dtype_ok(dtype)) return fail(YOCO_ERR_BAD_DTYPE, "dtype %d unknown", dtype);
@@ -769,6 +808,9 @@ yoco_status yoco_gret_prefill(const void *q, const void *k, const void *v, int32
   yoco_status st = check_gret(q, k, v, gate_logits, o, dtype, n_heads, head_dim, tau);
   if (st != YOCO_OK) return st;
   if (n < 0) return fail(YOCO_ERR_BAD_SHAPE, "n %lld < 0", (long long)n);
+  if ((st = check_aligned({{state_in, "state_in"}, {state_out, "state_out"}, {workspace, "workspace"}}, 16)) !=
+      YOCO_OK)
+    return st;
   const GretLayout L = gret_layout(n, n_heads, head_dim, dtype);
   if (L.total > 0 && (workspace == nullptr || workspace_bytes < L.total))
     return fail(YOCO_ERR_WORKSPACE, "workspace %zu bytes < %zu (yoco_gret_prefill_workspace)", workspace_bytes,
@@ -806,6 +848,7 @@ yoco_status yoco_gret_decode(const void *q, const void *k, const void *v, int32_
   yoco_status st = check_gret(q, k, v, gate_logits, o, dtype, n_heads, head_dim, tau);
   if (st != YOCO_OK) return st;
   if (state == nullptr) return fail(YOCO_ERR_NULL_POINTER, "state is NULL");
+  if ((st = check_aligned({{state, "state"}}, 16)) != YOCO_OK) return st;
   if (n_seq < 0 || static_cast<int64_t>(n_seq) * n_heads > 0x7fffffff)
     return fail(YOCO_ERR_BAD_SHAPE, "n_seq %d", n_seq);
   if (n_seq == 0) return ok();
