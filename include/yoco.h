@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define YOCO_ABI_VERSION 6
+#define YOCO_ABI_VERSION 7
 #define YOCO_MAX_SEQ 256
 
 /* Storage types. */
@@ -79,7 +79,8 @@ typedef enum yoco_status {
 
 /* The shared global K^/V^ cache ([Notes] Eq. 2; [Blog] section 7): ONE copy,
  * read by every cross layer.  k and v are each
- * [n_seq][seq_capacity][n_kv_heads][head_dim] in `dtype`.  len_host[b]
+ * [n_seq][seq_capacity][n_kv_heads][head_dim] in `dtype`, rows possibly
+ * padded to row_stride elements (layout below).  len_host[b]
  * (HOST memory) is the number of valid rows of sequence b; the project and
  * append calls advance it when they enqueue their writes.  Lowering
  * len_host[b] truncates a sequence (e.g. to roll back speculative tokens). */
@@ -92,7 +93,17 @@ typedef struct yoco_kv_cache {
   int32_t n_kv_heads;   /* >= 1 */
   int32_t head_dim;     /* 64 or 128 */
   int32_t dtype;        /* yoco_dtype of k and v */
+  int64_t row_stride;   /* elements from one cache row to the next (see below) */
 } yoco_kv_cache;
+
+/* Cache layout.  Element e of KV head g at row r of sequence b sits at
+ *   ((b * seq_capacity + r) * row_stride + g * head_dim + e)
+ * of k (and of v).  row_stride 0 means dense rows (n_kv_heads * head_dim);
+ * otherwise row_stride >= n_kv_heads * head_dim, a multiple of 16 bytes and
+ * at most 2^20 elements, and the elements past n_kv_heads * head_dim are
+ * never read or written.  The logical cache is [n_seq][capacity][H_kv][d_h]
+ * either way; padding only moves each row in memory.
+ * yoco_kv_cache_row_stride gives the stride the kernels stream fastest. */
 
 /* Returns YOCO_ABI_VERSION of the built library. */
 int yoco_abi_version(void);
@@ -102,12 +113,26 @@ int yoco_abi_version(void);
 const char *yoco_last_error(void);
 
 /* Host-only helper: bytes of ONE of the k / v tensors of a cache with these
- * dimensions (2 * this value for the whole cache).  For 131072 rows, 8 KV
- * heads, head dim 128 in bf16 the pair is 2*131072*8*128*2 B = 0.5 GiB, the
- * size [Blog] section 7 prints for the shared cache.  Errors: NULL bytes ->
- * NULL_POINTER; non-positive sizes -> BAD_SHAPE; unknown dtype -> BAD_DTYPE. */
+ * dimensions and row stride (0: dense rows; 2 * this value for the whole
+ * cache).  Dense, 131072 rows, 8 KV heads, head dim 128 in bf16 give the
+ * pair 2*131072*8*128*2 B = 0.5 GiB, the size [Blog] section 7 prints for the
+ * shared cache.  Errors: NULL bytes -> NULL_POINTER; non-positive sizes or a
+ * row stride outside the rule above -> BAD_SHAPE; unknown dtype ->
+ * BAD_DTYPE. */
 yoco_status yoco_kv_cache_bytes(int32_t n_seq, int64_t seq_capacity, int32_t n_kv_heads,
-                                int32_t head_dim, int32_t dtype, size_t *bytes);
+                                int32_t head_dim, int32_t dtype, int64_t row_stride, size_t *bytes);
+
+/* Host-only helper: the row stride (elements) the kernels stream fastest.
+ * Rows of 1 KiB or more whose size is a multiple of 512 bytes get 128 bytes
+ * of padding: with dense rows every KV head's block sits at the same offset
+ * in every row, and under a full decode some of those offsets stream 20-30%
+ * slower than others (measured on MI355X); the padding walks each head's
+ * block through the offsets from row to row.  Other rows stay dense.  At 8
+ * KV heads x 128 in bf16 the rows grow from 2048 to 2176 bytes (6.25%).
+ * Errors: NULL row_stride -> NULL_POINTER; non-positive sizes -> BAD_SHAPE;
+ * unknown dtype -> BAD_DTYPE. */
+yoco_status yoco_kv_cache_row_stride(int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                                     int64_t *row_stride);
 
 /* Shared K^/V^ projection with one cache write ([Notes] Eq. 2; [Blog]
  * section 7: computed once in the cross-decoder front and written before the

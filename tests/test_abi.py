@@ -27,7 +27,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = _lib()
     names = _declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     for name in names:
         assert hasattr(lib, name), f"{name} declared in yoco.h but not exported"
 
@@ -51,6 +51,34 @@ def test_kv_cache_bytes_matches_printed_size():
     with pytest.raises(y.YocoError) as e:
         y.kv_cache_bytes(0, 1, 1, 64)
     assert e.value.name == "YOCO_ERR_BAD_SHAPE"
+
+
+def test_cache_row_stride_rule():
+    """Rows of >= 1 KiB whose size is a multiple of 512 B get 128 B of padding;
+    others stay dense.  The byte count follows the stride; bad strides are
+    rejected."""
+    import yoco_shared_kv_amd as y
+    import torch
+    bf, f32 = torch.bfloat16, torch.float32
+    assert y.kv_cache_row_stride(8, 128, bf) == 8 * 128 + 64       # 2048 B rows -> 2176 B
+    assert y.kv_cache_row_stride(4, 128, bf) == 4 * 128 + 64       # 1 KiB
+    assert y.kv_cache_row_stride(8, 128, f32) == 8 * 128 + 32      # 4 KiB rows, 128 B of fp32
+    assert y.kv_cache_row_stride(2, 128, bf) == 2 * 128            # 512 B: dense
+    assert y.kv_cache_row_stride(1, 128, bf) == 128
+    assert y.kv_cache_row_stride(3, 128, bf) == 3 * 128            # 768 B: not a multiple of 512
+    assert y.kv_cache_row_stride(6, 128, bf) == 6 * 128 + 64       # 1536 B
+    assert y.kv_cache_bytes(1, 131072, 8, 128, bf, row_stride=1088) == 131072 * 1088 * 2
+    assert y.kv_cache_bytes(2, 10, 8, 128, f32, row_stride=0) == 2 * 10 * 1024 * 4
+    for rs in (1023, 1028, (1 << 20) + 8, -8):                     # short, not 16 B, too long, negative
+        with pytest.raises(y.YocoError) as e:
+            y.kv_cache_bytes(1, 10, 8, 128, bf, row_stride=rs)
+        assert e.value.name == "YOCO_ERR_BAD_SHAPE"
+    c, lens = _cache(hkv=2, dh=64)
+    c.row_stride = 130                                             # 260 B rows: not a multiple of 16 B
+    assert _project(c) == _status("YOCO_ERR_BAD_SHAPE")
+    c.row_stride = 64                                              # shorter than the 128-element row
+    assert _project(c) == _status("YOCO_ERR_BAD_SHAPE")
+    assert lens.tolist() == [10, 20]
 
 
 # ---- error paths with placeholder pointers (never dereferenced) ----------

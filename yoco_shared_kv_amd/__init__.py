@@ -32,7 +32,8 @@ from ._native import (YOCO_DECODE_COUNTER_BYTES, YOCO_DT_BF16, YOCO_DT_F32, KVCa
 
 __all__ = [
     "KVCache", "YocoError", "kv_project", "kv_append", "q_project", "cross_attn_prefill",
-    "cross_attn_decode", "decode_workspace", "decode_workspace_bytes", "kv_cache_bytes", "lib",
+    "cross_attn_decode", "decode_workspace", "decode_workspace_bytes", "kv_cache_bytes",
+    "kv_cache_row_stride", "lib",
     "cross_attn_prefill_bwd", "prefill_bwd_workspace_bytes", "kv_project_bwd", "q_project_bwd",
     "project_bwd_workspace_bytes", "gret_prefill", "gret_decode", "gret_prefill_workspace_bytes",
 ]
@@ -68,29 +69,42 @@ def _on_device(*ts):
 
 class KVCache:
     """The one shared K^/V^ cache: k, v ``[n_seq, capacity, H_kv, d_h]`` on the
-    device plus host lengths ``len`` (numpy int64, advanced by project/append)."""
+    device plus host lengths ``len`` (numpy int64, advanced by project/append).
+    With ``padded`` (the default) each row is stored at the row stride
+    ``yoco_kv_cache_row_stride`` recommends, so k and v are views into larger
+    buffers whose rows end in a few unused elements."""
 
     def __init__(self, n_seq: int, capacity: int, n_kv_heads: int, head_dim: int,
-                 dtype: torch.dtype = torch.bfloat16, device="cuda", zero: bool = False):
+                 dtype: torch.dtype = torch.bfloat16, device="cuda", zero: bool = False, padded: bool = True):
         alloc = torch.zeros if zero else torch.empty
-        shape = (n_seq, capacity, n_kv_heads, head_dim)
-        self.k = alloc(shape, dtype=dtype, device=device)
-        self.v = alloc(shape, dtype=dtype, device=device)
+        dense = n_kv_heads * head_dim
+        rs = kv_cache_row_stride(n_kv_heads, head_dim, dtype) if padded else dense
+        self._k_rows = alloc((n_seq, capacity, rs), dtype=dtype, device=device)
+        self._v_rows = alloc((n_seq, capacity, rs), dtype=dtype, device=device)
+        self.k = self._k_rows[:, :, :dense].unflatten(2, (n_kv_heads, head_dim))
+        self.v = self._v_rows[:, :, :dense].unflatten(2, (n_kv_heads, head_dim))
         self.len = np.zeros(n_seq, dtype=np.int64)
         self.n_seq, self.capacity = n_seq, capacity
         self.n_kv_heads, self.head_dim, self.dtype = n_kv_heads, head_dim, dtype
+        self.row_stride = rs
         self._struct = None
         self._key = None
 
     @classmethod
     def wrap(cls, k: torch.Tensor, v: torch.Tensor, lens) -> "KVCache":
-        """Use existing k/v tensors ``[n_seq, capacity, H_kv, d_h]``."""
+        """Use existing k/v tensors ``[n_seq, capacity, H_kv, d_h]`` (dense, or
+        rows padded: any stride along capacity, the rest packed)."""
         obj = cls.__new__(cls)
-        if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 4:
+        if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 4 or k.stride() != v.stride():
             raise ValueError("k and v must be matching [n_seq, capacity, H_kv, d_h] tensors")
+        n_seq, cap, hkv, dh = k.shape
+        rs = k.stride(1)
+        if k.stride(3) != 1 or k.stride(2) != dh or rs < hkv * dh or k.stride(0) != cap * rs:
+            raise ValueError("k and v rows must be packed [H_kv, d_h] blocks at one row stride")
         obj.k, obj.v = k, v
-        obj.n_seq, obj.capacity, obj.n_kv_heads, obj.head_dim = k.shape
+        obj.n_seq, obj.capacity, obj.n_kv_heads, obj.head_dim = n_seq, cap, hkv, dh
         obj.dtype = k.dtype
+        obj.row_stride = rs
         obj.len = np.ascontiguousarray(np.asarray(lens, dtype=np.int64).reshape(obj.n_seq))
         obj._struct = None
         obj._key = None
@@ -114,17 +128,25 @@ class KVCache:
         s.n_kv_heads = self.n_kv_heads
         s.head_dim = self.head_dim
         s.dtype = _dt(self.k)
+        s.row_stride = self.row_stride
         self._struct = s  # keep alive with the numpy buffer it points into
         self._key = key
         return s
 
 
 def kv_cache_bytes(n_seq: int, capacity: int, n_kv_heads: int, head_dim: int,
-                   dtype: torch.dtype = torch.bfloat16) -> int:
+                   dtype: torch.dtype = torch.bfloat16, row_stride: int = 0) -> int:
     """Bytes of one of k / v (host-only; see ``yoco_kv_cache_bytes``)."""
     out = ctypes.c_size_t(0)
-    check(lib().yoco_kv_cache_bytes(n_seq, capacity, n_kv_heads, head_dim,
-                                    _DT.get(dtype, -1), ctypes.byref(out)))
+    check(lib().yoco_kv_cache_bytes(n_seq, capacity, n_kv_heads, head_dim, _DT.get(dtype, -1), row_stride,
+                                    ctypes.byref(out)))
+    return int(out.value)
+
+
+def kv_cache_row_stride(n_kv_heads: int, head_dim: int, dtype: torch.dtype = torch.bfloat16) -> int:
+    """Row stride (elements) the kernels stream fastest (``yoco_kv_cache_row_stride``)."""
+    out = ctypes.c_int64(0)
+    check(lib().yoco_kv_cache_row_stride(n_kv_heads, head_dim, _DT.get(dtype, -1), ctypes.byref(out)))
     return int(out.value)
 
 

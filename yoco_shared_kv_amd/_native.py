@@ -41,6 +41,7 @@ class KVCacheStruct(ctypes.Structure):
         ("n_kv_heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+        ("row_stride", ctypes.c_int64),
     ]
 
 
@@ -57,7 +58,9 @@ def _declare(lib):
     lib.yoco_last_error.restype = ctypes.c_char_p
     lib.yoco_last_error.argtypes = []
     lib.yoco_kv_cache_bytes.restype = st
-    lib.yoco_kv_cache_bytes.argtypes = [i32, i64, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.yoco_kv_cache_bytes.argtypes = [i32, i64, i32, i32, i32, i64, ctypes.POINTER(sz)]
+    lib.yoco_kv_cache_row_stride.restype = st
+    lib.yoco_kv_cache_row_stride.argtypes = [i32, i32, i32, ctypes.POINTER(i64)]
     lib.yoco_kv_project.restype = st
     lib.yoco_kv_project.argtypes = [vp, i32, i64, i32, vp, f32, vp, vp, i32, cp, i32, i64, vp]
     lib.yoco_kv_append.restype = st

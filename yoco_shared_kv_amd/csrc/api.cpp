@@ -78,6 +78,22 @@ yoco_status check_aligned(std::initializer_list<Named> ptrs, unsigned align) {
   return YOCO_OK;
 }
 
+constexpr int64_t kMaxRowStride = int64_t(1) << 20;
+
+yoco_status check_row_stride(int64_t rs, int32_t n_kv_heads, int32_t head_dim, int32_t dtype) {
+  if (rs == 0) return YOCO_OK;
+  const int64_t dense = static_cast<int64_t>(n_kv_heads) * head_dim;
+  if (rs < dense || rs > kMaxRowStride || (rs * static_cast<int64_t>(dtype_size(dtype))) % 16 != 0)
+    return fail(YOCO_ERR_BAD_SHAPE, "row_stride %lld: must be 0 or in [%lld, %lld] with rows a multiple of 16 bytes",
+                (long long)rs, (long long)dense, (long long)kMaxRowStride);
+  return YOCO_OK;
+}
+
+// Elements from one cache row to the next.
+int64_t row_stride_of(const yoco_kv_cache *c) {
+  return c->row_stride != 0 ? c->row_stride : static_cast<int64_t>(c->n_kv_heads) * c->head_dim;
+}
+
 yoco_status check_cache(const yoco_kv_cache *c) {
   if (c == nullptr) return fail(YOCO_ERR_NULL_POINTER, "cache is NULL");
   if (c->k == nullptr || c->v == nullptr) return fail(YOCO_ERR_NULL_POINTER, "cache k or v is NULL");
@@ -91,7 +107,7 @@ yoco_status check_cache(const yoco_kv_cache *c) {
   if (c->seq_capacity < 1 || c->seq_capacity > (int64_t(1) << 31) - 1)
     return fail(YOCO_ERR_BAD_SHAPE, "seq_capacity %lld outside [1, 2^31)", (long long)c->seq_capacity);
   if (!dtype_ok(c->dtype)) return fail(YOCO_ERR_BAD_DTYPE, "cache dtype %d unknown", c->dtype);
-  return YOCO_OK;
+  return check_row_stride(c->row_stride, c->n_kv_heads, c->head_dim, c->dtype);
 }
 
 yoco_status check_eps(float eps) {
@@ -190,13 +206,27 @@ int yoco_abi_version(void) { return YOCO_ABI_VERSION; }
 const char *yoco_last_error(void) { return g_err; }
 
 yoco_status yoco_kv_cache_bytes(int32_t n_seq, int64_t seq_capacity, int32_t n_kv_heads, int32_t head_dim,
-                                int32_t dtype, size_t *bytes) {
+                                int32_t dtype, int64_t row_stride, size_t *bytes) {
   if (bytes == nullptr) return fail(YOCO_ERR_NULL_POINTER, "bytes is NULL");
   if (n_seq < 1 || seq_capacity < 1 || n_kv_heads < 1 || head_dim < 1)
     return fail(YOCO_ERR_BAD_SHAPE, "cache dimensions must be positive");
   if (!dtype_ok(dtype)) return fail(YOCO_ERR_BAD_DTYPE, "dtype %d unknown", dtype);
-  *bytes = static_cast<size_t>(n_seq) * static_cast<size_t>(seq_capacity) * n_kv_heads * head_dim *
+  yoco_status st = check_row_stride(row_stride, n_kv_heads, head_dim, dtype);
+  if (st != YOCO_OK) return st;
+  const int64_t rs = row_stride != 0 ? row_stride : static_cast<int64_t>(n_kv_heads) * head_dim;
+  *bytes = static_cast<size_t>(n_seq) * static_cast<size_t>(seq_capacity) * static_cast<size_t>(rs) *
            dtype_size(dtype);
+  return ok();
+}
+
+yoco_status yoco_kv_cache_row_stride(int32_t n_kv_heads, int32_t head_dim, int32_t dtype, int64_t *row_stride) {
+  if (row_stride == nullptr) return fail(YOCO_ERR_NULL_POINTER, "row_stride is NULL");
+  if (n_kv_heads < 1 || head_dim < 1) return fail(YOCO_ERR_BAD_SHAPE, "cache dimensions must be positive");
+  if (!dtype_ok(dtype)) return fail(YOCO_ERR_BAD_DTYPE, "dtype %d unknown", dtype);
+  const int64_t dense = static_cast<int64_t>(n_kv_heads) * head_dim;
+  const int64_t esz = static_cast<int64_t>(dtype_size(dtype));
+  const int64_t bytes = dense * esz;
+  *row_stride = (bytes >= 1024 && bytes % 512 == 0) ? dense + 128 / esz : dense;
   return ok();
 }
 
@@ -255,6 +285,7 @@ yoco_status kv_project_impl(const void *m, int32_t m_dtype, int64_t n, int32_t d
   a.dst_row_base = static_cast<int64_t>(seq) * cache->seq_capacity + row_start;
   a.d = d_model;
   a.ncols = cache->n_kv_heads * cache->head_dim;
+  a.out_stride = row_stride_of(cache);
   a.n_out = 2;
   a.indexed = 0;
   a.eps = eps;
@@ -298,6 +329,7 @@ yoco_status kv_append_impl(const void *m_new, int32_t m_dtype, int32_t d_model, 
   a.dst_row_base = 0;
   a.d = d_model;
   a.ncols = cache->n_kv_heads * cache->head_dim;
+  a.out_stride = row_stride_of(cache);
   a.n_out = 2;
   a.indexed = 1;
   a.eps = eps;
@@ -351,6 +383,7 @@ yoco_status q_project_impl(const void *x, int32_t x_dtype, int64_t n, int32_t d_
   a.dst_row_base = 0;
   a.d = d_model;
   a.ncols = n_q_heads * head_dim;
+  a.out_stride = a.ncols;
   a.n_out = 1;
   a.indexed = 0;
   a.eps = eps;
@@ -444,7 +477,7 @@ yoco_status yoco_cross_attn_prefill(const void *q, int32_t q_dtype, int64_t q_st
   if ((st = check_device()) != YOCO_OK) return st;
 
   const size_t esz = dtype_size(cache->dtype);
-  const int64_t slab = static_cast<int64_t>(seq) * cache->seq_capacity * cache->n_kv_heads * cache->head_dim;
+  const int64_t slab = static_cast<int64_t>(seq) * cache->seq_capacity * row_stride_of(cache);
   yoco::PrefillArgs a{};
   a.q = q;
   a.k = static_cast<const char *>(cache->k) + slab * esz;
@@ -456,6 +489,7 @@ yoco_status yoco_cross_attn_prefill(const void *q, int32_t q_dtype, int64_t q_st
   a.kv_len = len;
   a.n_q_heads = n_q_heads;
   a.n_kv_heads = cache->n_kv_heads;
+  a.kv_row_stride = static_cast<int32_t>(row_stride_of(cache));
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.o_bf16 = (o_dtype == YOCO_DT_BF16) ? 1 : 0;
   return launched(yoco::launch_prefill(a, cache->dtype, cache->head_dim, static_cast<hipStream_t>(stream)),
@@ -523,7 +557,8 @@ yoco_status yoco_cross_attn_decode(const void *q, int32_t q_dtype, int32_t n_q_h
   a.counters = static_cast<unsigned int *>(workspace);
   a.part_acc = reinterpret_cast<float *>(static_cast<char *>(workspace) + YOCO_DECODE_COUNTER_BYTES);
   a.part_ml = nullptr;
-  a.seq_stride = cache->seq_capacity * cache->n_kv_heads * cache->head_dim;
+  a.row_stride = row_stride_of(cache);
+  a.seq_stride = cache->seq_capacity * a.row_stride;
   a.n_seq = cache->n_seq;
   a.n_kv_heads = cache->n_kv_heads;
   a.n_q_heads = n_q_heads;
@@ -573,7 +608,7 @@ yoco_status yoco_cross_attn_prefill_bwd(const void *q, const void *o, int32_t o_
   if (t == 0) return ok();
   if ((st = check_device()) != YOCO_OK) return st;
 
-  const int64_t slab = static_cast<int64_t>(seq) * cache->seq_capacity * cache->n_kv_heads * cache->head_dim;
+  const int64_t slab = static_cast<int64_t>(seq) * cache->seq_capacity * row_stride_of(cache);
   yoco::BwdArgs a{};
   a.q = q;
   a.o = o;
@@ -591,6 +626,7 @@ yoco_status yoco_cross_attn_prefill_bwd(const void *q, const void *o, int32_t o_
   a.kv_len = q_start + t;
   a.n_q_heads = n_q_heads;
   a.n_kv_heads = cache->n_kv_heads;
+  a.kv_row_stride = static_cast<int32_t>(row_stride_of(cache));
   a.scale = softmax_scale;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.o_bf16 = (o_dtype == YOCO_DT_BF16) ? 1 : 0;

@@ -116,10 +116,12 @@ __device__ __forceinline__ void stage_tile(char *lds_dst, const bf16_t *src, int
   using S = PrefillShape<DH>;
   // Bytes from the tile start to the end of row kv_len-1 of this head; a
   // staged tile always starts at or before that row.
-  const int tile_bytes = pf::kKeyTile * row_stride * 2;
-  const int valid = ((kv_len - 1 - key0) * row_stride + DH) * 2;
+  // (64-bit: the distance to the last row can pass 2 GiB in long slabs.)
+  const int64_t tile_bytes = static_cast<int64_t>(pf::kKeyTile) * row_stride * 2;
+  const int64_t valid = (static_cast<int64_t>(kv_len - 1 - key0) * row_stride + DH) * 2;
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t *>(src + (int64_t)key0 * row_stride), 0, min(valid, tile_bytes), kBufferFlags);
+      const_cast<bf16_t *>(src + (int64_t)key0 * row_stride), 0, static_cast<int>(min(valid, tile_bytes)),
+      kBufferFlags);
 #pragma unroll
   for (int i = 0; i < S::kLoadsPerWave; ++i) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)(lds_dst + (wave * S::kLoadsPerWave + i) * 1024), 16,

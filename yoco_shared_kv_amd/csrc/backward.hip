@@ -122,7 +122,7 @@ __global__ __launch_bounds__(pf::kThreads, 1) void bwd_dq_kernel(const BwdArgs a
   const int h = g * group + slot_on_xcd % group;
 
   const int64_t row_stride_q = (int64_t)a.n_q_heads * DH;
-  const int row_stride_kv = a.n_kv_heads * DH;
+  const int row_stride_kv = a.kv_row_stride;
   const bf16_t *kg = static_cast<const bf16_t *>(a.k) + g * DH;
   const bf16_t *vg = static_cast<const bf16_t *>(a.v) + g * DH;
 
@@ -287,10 +287,11 @@ struct KvStage {
   // past the end land as zeros.
   __device__ __forceinline__ void tile(char *lds_dst, const bf16_t *src, int64_t row_stride, int row0, int n_rows,
                                        int wave) const {
-    const int valid = (n_rows - row0) * static_cast<int>(row_stride) * 2;
-    const int tile_bytes = bw::kQTile * static_cast<int>(row_stride) * 2;
+    const int64_t valid = static_cast<int64_t>(n_rows - row0) * row_stride * 2;
+    const int64_t tile_bytes = static_cast<int64_t>(bw::kQTile) * row_stride * 2;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16_t *>(src + (int64_t)row0 * row_stride), 0, max(0, min(valid, tile_bytes)), kBufferFlags);
+        const_cast<bf16_t *>(src + (int64_t)row0 * row_stride), 0,
+        static_cast<int>(max(int64_t(0), min(valid, tile_bytes))), kBufferFlags);
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)(lds_dst + (wave * kLoadsPerWave + i) * 1024), 16,
@@ -337,7 +338,8 @@ __global__ __launch_bounds__(bw::kKvThreads, 2) void bwd_dkdv_kernel(const BwdAr
   const bool wave_active = key0 < kv_len;
 
   const int64_t row_stride_q = (int64_t)a.n_q_heads * DH;
-  const int64_t row_stride_kv = (int64_t)a.n_kv_heads * DH;
+  const int64_t row_stride_kv = a.kv_row_stride;               // cache rows
+  const int64_t row_stride_dkv = (int64_t)a.n_kv_heads * DH;   // d_k, d_v rows (dense)
 
   // Query rows that see this block: positions >= key_blk0.
   const int r_first = max(0, key_blk0 - q_start);
@@ -490,7 +492,7 @@ __global__ __launch_bounds__(bw::kKvThreads, 2) void bwd_dkdv_kernel(const BwdAr
     for (int i = 0; i < 16; ++i) {
       const int key = key0 + (i >> 2) * 8 + half * 4 + (i & 3);
       if (key < kv_len) {
-        const int64_t e = (int64_t)key * row_stride_kv + (int64_t)g * DH + d * 32 + col;
+        const int64_t e = (int64_t)key * row_stride_dkv + (int64_t)g * DH + d * 32 + col;
         a.d_k[e] += dk[d][i] * a.scale;
         a.d_v[e] += dv[d][i];
       }

@@ -28,7 +28,8 @@ struct DecodeArgs {
   unsigned int *counters; // [YOCO_MAX_SEQ][kMaxKvHeads]
   float *part_ml;         // [total_splits][n_kv_heads][G][2]
   float *part_acc;        // [total_splits][n_kv_heads][G][head_dim]
-  int64_t seq_stride;     // elements between sequence slabs (capacity*H_kv*d_h)
+  int64_t seq_stride;     // elements between sequence slabs (capacity * row_stride)
+  int64_t row_stride;     // elements between cache rows (>= H_kv * d_h)
   int32_t n_seq;
   int32_t n_kv_heads;
   int32_t n_q_heads;

@@ -249,7 +249,7 @@ __global__ __launch_bounds__(TUNE::NW * 64) void decode_kernel(const DecodeArgs 
   const int row_begin = (ws - first_split) * a.split_rows;
   const int nrows = min(a.split_rows, a.len[b] - row_begin);
 
-  const int64_t row_stride = (int64_t)H * DH;
+  const int64_t row_stride = a.row_stride;
   const T *kbase = static_cast<const T *>(a.k) + b * a.seq_stride + row_begin * row_stride + g * DH;
   const T *vbase = static_cast<const T *>(a.v) + b * a.seq_stride + row_begin * row_stride + g * DH;
 

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const Pre
   const int h = g * group + slot_on_xcd % group;
 
   const int64_t row_stride_q = (int64_t)a.n_q_heads * DH;
-  const int row_stride_kv = a.n_kv_heads * DH;
+  const int row_stride_kv = a.kv_row_stride;
   const bf16_t *qg = static_cast<const bf16_t *>(a.q);
   const bf16_t *kg = static_cast<const bf16_t *>(a.k) + g * DH;
   const bf16_t *vg = static_cast<const bf16_t *>(a.v) + g * DH;
@@ -453,7 +453,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillArgs a) {
   const int64_t last_pos = a.q_start + last_row;
 
   const int64_t rs_q = (int64_t)a.n_q_heads * DH;
-  const int64_t rs_kv = (int64_t)a.n_kv_heads * DH;
+  const int64_t rs_kv = a.kv_row_stride;
   const float *qp = static_cast<const float *>(a.q) + (valid ? row : 0) * rs_q + (int64_t)h * DH;
   const float *kg = static_cast<const float *>(a.k) + g * DH;
   const float *vg = static_cast<const float *>(a.v) + g * DH;

@@ -133,7 +133,7 @@ __global__ __launch_bounds__(pj::kThreads) void project_kernel(const ProjArgs a)
     if (row >= a.n) continue;
     const int64_t dst = a.indexed ? a.dst_rows[row] : a.dst_row_base + row;
     const float inv = s_inv_rms[rr];
-    TO *orow = out + dst * a.ncols + col_tile * BN + tx * 4;
+    TO *orow = out + dst * a.out_stride + col_tile * BN + tx * 4;
     float v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) v[j] = acc[i][j] * inv;
@@ -340,8 +340,8 @@ __global__ __launch_bounds__(pg::Shape<NR>::kThreads) void project_small_kernel(
       rope_turn(v0, v1, proj_row_pos(a, row), rope_rev(pair, a.head_dim, a.rope_log2_theta));
     }
     const int64_t dst = a.indexed ? a.dst_rows[row] : a.dst_row_base + row;
-    store_elem<TO>(out + dst * a.ncols + strip * kCols + col, v0);
-    store_elem<TO>(out + dst * a.ncols + strip * kCols + col + 1, v1);
+    store_elem<TO>(out + dst * a.out_stride + strip * kCols + col, v0);
+    store_elem<TO>(out + dst * a.out_stride + strip * kCols + col + 1, v1);
   }
 }
 

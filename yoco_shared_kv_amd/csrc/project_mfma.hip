@@ -284,7 +284,7 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
     const int r = wr * 64 + s2 * 32 + col;
     if (r >= rows_here) continue;
     const float inv = 1.0f / sqrtf(ss / static_cast<float>(d) + a.eps);
-    bf16_t *orow = out + (a.dst_row_base + row0 + r) * a.ncols + col0 + wc * 128;
+    bf16_t *orow = out + (a.dst_row_base + row0 + r) * a.out_stride + col0 + wc * 128;
     const int64_t pos = rope ? proj_row_pos(a, row0 + r) : 0;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {

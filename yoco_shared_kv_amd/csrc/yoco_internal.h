@@ -16,7 +16,8 @@ namespace yoco {
 // Fused RMSNorm + projection (shared K/V, per-layer Q, append).
 // Output row r of the input goes to destination row dst_row(r):
 //   contiguous: dst_row_base + r;   indexed: dst_rows[r] (r < YOCO_MAX_SEQ).
-// Destination element (row, col) is out[p][row * ncols + col] for weight p.
+// Destination element (row, col) is out[p][row * out_stride + col] for
+// weight p (out_stride >= ncols: padded cache rows).
 // ---------------------------------------------------------------------------
 struct ProjArgs {
   const void *x;
@@ -27,6 +28,7 @@ struct ProjArgs {
   int64_t dst_row_base;      // contiguous mode
   int32_t d;                 // d_model
   int32_t ncols;             // columns per weight (H*d_h)
+  int64_t out_stride;        // elements between destination rows
   int32_t n_out;             // 1 (Q) or 2 (K and V)
   int32_t indexed;           // 1: use dst_rows
   float eps;
@@ -66,6 +68,7 @@ struct PrefillArgs {
   int64_t kv_len;     // rows of the slab that hold data (len_host[seq])
   int32_t n_q_heads;
   int32_t n_kv_heads;
+  int32_t kv_row_stride;  // elements between cache rows
   float scale_log2;
   int32_t o_bf16;
 };
@@ -81,7 +84,7 @@ struct BwdArgs {
   const void *k;      // sequence slab base: [capacity][H_kv][d_h] bf16
   const void *v;
   float *d_q;         // [t][n_q_heads][head_dim], written
-  float *d_k;         // [kv_len][H_kv][d_h], added to
+  float *d_k;         // [kv_len][H_kv][d_h] (dense rows), added to
   float *d_v;
   float *ws_d;        // [n_q_heads][t] workspace: <dO, o>
   float *ws_lse2;     // [n_q_heads][t] workspace: lse * log2(e)
@@ -90,6 +93,7 @@ struct BwdArgs {
   int64_t kv_len;     // q_start + t: the cache rows the block's rows see
   int32_t n_q_heads;
   int32_t n_kv_heads;
+  int32_t kv_row_stride;  // elements between cache rows (k, v)
   float scale;
   float scale_log2;
   int32_t o_bf16;
