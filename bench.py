@@ -299,6 +299,18 @@ def bench_prefill(args, torch, y, W):
                 frac=tflops / BF16_DENSE_PEAK_TFLOPS, case=c)
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def sampled_rows(n, count):
     """Rows spread evenly over [0, n): the centres of `count` equal strata."""
     return ((np.arange(count) + 0.5) * n / count).astype(np.int64)
@@ -316,8 +328,8 @@ def causal_cpu_baseline(name, run_rows, n, count):
     frac = float(np.sum(rows + 1)) / (n * (n + 1) / 2.0)
     full_ms = dt / frac * 1e3
     log(f"cpu baseline ({name}): {count} sampled rows in {dt:.2f} s -> {full_ms / 1e3:.1f} s extrapolated")
-    return {"value": round(full_ms, 1), "unit": "ms", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{count} query rows spread evenly over the {n} positions, every head, timed "
+    return {"value": round(full_ms, 1), "unit": "ms", "cores": oracle.num_threads(), "cpu": cpu_model(),
+            "kind": "oracle", "sample": f"{count} query rows spread evenly over the {n} positions, every head, timed "
                       f"({dt:.2f} s wall, {frac * 100:.3f}% of the causal work) and extrapolated to all rows"}
 
 
@@ -560,7 +572,7 @@ def cpu_baseline(dec, W):
     for b, n in enumerate(case.lens):
         oracle.decode(case.q[:, b], int(n), case.k[b], case.v[b], case.softmax_scale)
     dt = time.perf_counter() - t0
-    return {"value": dt * 1e6 / case.layers, "unit": "us/token/layer", "cores": threads,
+    return {"value": dt * 1e6 / case.layers, "unit": "us/token/layer", "cores": threads, "cpu": cpu_model(),
             "kind": "oracle",
             "sample": f"one full decode step: 13 layers x 24 query heads over all {rows} cache rows of "
                       f"{len(case.lens)} sequence(s) (fp64, {dt:.2f} s wall)"}
