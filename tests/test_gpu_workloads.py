@@ -9,7 +9,8 @@ benchmark times (library-chosen split size, fp32 outputs):
 * ragged decode, 16 sequences of 8192..131072 rows: layers 0 and 12 against
   the oracle (all sequences, all heads);
 * decode over 2^20 rows with a planted needle per KV head: the needle check
-  for all 13 layers and oracle parity for layers 0 and 7;
+  for all 13 layers and oracle parity for layers 0 and 7; a prefill block of
+  the last 64 positions over the same cache (the decode's row and the oracle);
 * K^/V^ projection of 32768 rows at 3B-like widths (3072 -> 2 x 1024, matrix
   cores): a seeded sample of rows against the fp64 projection, every value
   finite, and the cache rows outside the range untouched.
@@ -127,7 +128,22 @@ def test_needle_1m():
     for l in (0, 7):
         ref = oracle.decode(case.q[l:l + 1, 0], n, case.k[0], v_all, case.softmax_scale)
         assert_parity(outs[l], ref[0], bf16=True, what=f"needle layer {l}")
+        if l == 0:
+            ref0 = ref[0]
     say(f"needle 1M: worst cos(o, V_needle) {worst_cos:.5f}")
+    # A prefill block of the last 64 positions over the same 2^20 rows: its
+    # first key tiles lie more than 2 GiB of cache before the last row, so
+    # this covers the 64-bit range arithmetic of the tile loads.  The last
+    # block row carries layer 0's query (= the decode at len n), the first
+    # a random query at position n-64.
+    rng = np.random.default_rng(21)
+    qb = W.store(rng.standard_normal((64, case.n_q_heads, case.head_dim)).astype(np.float32), W.BF16)
+    qb[63] = case.q[0, 0]
+    ob = to_stored(y.cross_attn_prefill(to_dev(qb), cache, 0, n - 64, case.softmax_scale))
+    assert_parity(ob[63], ref0, bf16=True, what="prefill row at position n-1")
+    ref_first = oracle.decode(qb[0:1], n - 63, case.k[0], v_all, case.softmax_scale)
+    assert_parity(ob[0], ref_first[0], bf16=True, what="prefill row at position n-64")
+    say("needle 1M: prefill of the last 64 positions matches the decode and the oracle")
 
 
 def test_kv_project_3b_sampled_rows():
