@@ -55,8 +55,8 @@ constexpr int kXTileBytes = kRows * kXRowBytes;  // 32 KiB
 constexpr int kWRowBytes = 128 * 2;             // one half: 128 columns
 constexpr int kWHalfBytes = kK * kWRowBytes;    // 16 KiB
 constexpr int kXLoads = kXTileBytes / 1024 / kWaves;     // 1 KiB loads per wave per stage
-constexpr int kWLoads = 2 * kWHalfBytes / 1024 / kWaves;
 constexpr int kXcds = 8;
+constexpr int64_t kNarrowBelowTiles = 256;      // 256-column tiles fill the device from this many
 constexpr int32_t kBufferFlags = 0x00020000;    // raw buffer, 32-bit data format
 
 union Frag8 {
@@ -85,13 +85,30 @@ __device__ __forceinline__ int w_off(int k, int col) {
 
 }  // namespace pm
 
-template <bool kGain>
+// NCOLS: output columns per workgroup, 256 (waves own 64 rows x 128
+// columns) or 128 (64 x 64; twice the workgroups for short inputs, at more
+// LDS reads per MFMA).
+template <int NCOLS>
+struct PmShape {
+  static constexpr int kColsT = NCOLS;
+  static constexpr int kHalves = NCOLS / 128;                           // [64][128] W half tiles per stage
+  static constexpr int kWLoadsT = kHalves * pm::kWHalfBytes / 1024 / pm::kWaves;
+  static constexpr int kWaveCols = NCOLS / 2;                           // columns of one wave
+  static constexpr int NT = kWaveCols / 32;                             // 32-column accumulator tiles per wave
+};
+
+template <bool kGain, int NCOLS>
 __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const ProjArgs a) {
   using namespace pm;
+  using Sh = PmShape<NCOLS>;
+  constexpr int kColsT = Sh::kColsT;
+  constexpr int kHalves = Sh::kHalves;
+  constexpr int kWaveCols = Sh::kWaveCols;
+  constexpr int NT = Sh::NT;
   __shared__ __attribute__((aligned(1024))) char lds_x0[kXTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_x1[kXTileBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_w0[2 * kWHalfBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_w1[2 * kWHalfBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_w0[kHalves * kWHalfBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_w1[kHalves * kWHalfBytes];
   __shared__ __attribute__((aligned(1024))) float lds_g0[256];
   __shared__ __attribute__((aligned(1024))) float lds_g1[256];
   __shared__ double lds_rev[64];  // RoPE turns per position, per pair of a head
@@ -103,7 +120,7 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
 
   // Block -> (row tile, column tile): the column tiles of one row tile run
   // on consecutive slots of one XCD, so their x rows are shared in its L2.
-  const int col_tiles_per_out = a.ncols / kCols;
+  const int col_tiles_per_out = a.ncols / kColsT;
   const int col_tiles = col_tiles_per_out * a.n_out;
   const int row_tiles = static_cast<int>((a.n + kRows - 1) / kRows);
   const int xcd = blockIdx.x % kXcds;
@@ -112,7 +129,7 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
   if (row_tile >= row_tiles) return;
   const int ct = slot % col_tiles;
   const int p = ct / col_tiles_per_out;
-  const int col0 = (ct % col_tiles_per_out) * kCols;
+  const int col0 = (ct % col_tiles_per_out) * kColsT;
   const int64_t row0 = static_cast<int64_t>(row_tile) * kRows;
   const int rows_here = a.n - row0 < kRows ? static_cast<int>(a.n - row0) : kRows;
   const int d = a.d;
@@ -131,7 +148,11 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
   // lane L -> row b*8 + L/8, LDS slot L%8 holding global chunk slot^(row%8).
   // W block b (4 rows of half b/16): lane L -> row (b%16)*4 + L/16, slot
   // L%16 holding global chunk slot^w_xor(row).
-  uint32_t xsoff[kXLoads], wsoff[kWLoads];
+  // (wsoff has its 256-column size for both widths: host compilation drops
+  // the kernel's instantiation when the buffer-load builtins below see an
+  // operand whose type depends on NCOLS.)
+  constexpr int kWLoadsMax = 2 * kWHalfBytes / 1024 / kWaves;
+  uint32_t xsoff[kXLoads], wsoff[kWLoadsMax];
 #pragma unroll
   for (int i = 0; i < kXLoads; ++i) {
     const int row = (wave * kXLoads + i) * 8 + (lane >> 3);
@@ -139,8 +160,8 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
     xsoff[i] = static_cast<uint32_t>(row * d * 2 + chunk * 16);
   }
 #pragma unroll
-  for (int i = 0; i < kWLoads; ++i) {
-    const int blk = wave * kWLoads + i;
+  for (int i = 0; i < kWLoadsMax; ++i) {
+    const int blk = wave * Sh::kWLoadsT + (i < Sh::kWLoadsT ? i : 0);
     const int k = (blk & 15) * 4 + (lane >> 4);
     const int chunk = (lane & 15) ^ w_xor(k);
     wsoff[i] = static_cast<uint32_t>((k * a.ncols + (blk >> 4) * 128) * 2 + chunk * 16);
@@ -154,8 +175,9 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
     }
     const uint32_t wbase = (k0 * a.ncols + col0) * 2;
 #pragma unroll
-    for (int i = 0; i < kWLoads; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_t *)(wdst + (wave * kWLoads + i) * 1024), 16, wsoff[i],
+    for (int i = 0; i < kWLoadsMax; ++i) {
+      if (i >= Sh::kWLoadsT) break;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_t *)(wdst + (wave * Sh::kWLoadsT + i) * 1024), 16, wsoff[i],
                                                wbase, 0, 0);
     }
     if constexpr (kGain) {
@@ -166,7 +188,7 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
     }
   };
 
-  // Wave tile: rows wr*64 + s*32 (s = 0, 1), columns wc*128 + t*32 (t = 0..3).
+  // Wave tile: rows wr*64 + s*32 (s = 0, 1), columns wc*kWaveCols + t*32 (t < NT).
   const int wr = wave & 3;
   const int wc = wave >> 2;
   // B (x^T) read: row wr*64 + s*32 + col, chunk 2*ks + half; row % 8 = col % 8.
@@ -182,16 +204,19 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
   const int src_j = (lane >> 2) & 3;
   const int krow = (grp >> 1) * 8 + src_j;
   const int ccol = (grp & 1) * 16 + src_a * 4;
-  int woff[2][4];
+  // The wave's columns start in W half tile (wc*kWaveCols)/128 at column
+  // (wc*kWaveCols)%128 of that half.
+  int woff[2][NT];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) woff[r][t] = wc * kWHalfBytes + w_off(krow + 4 * r, t * 32 + ccol);
+    for (int t = 0; t < NT; ++t)
+      woff[r][t] = (wc * kWaveCols / 128) * kWHalfBytes + w_off(krow + 4 * r, (wc * kWaveCols) % 128 + t * 32 + ccol);
   }
 
-  floatx16 acc[4][2];
+  floatx16 acc[NT][2];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < NT; ++t) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
@@ -206,9 +231,9 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
       Frag8 b[2];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) b[s2].u = *reinterpret_cast<const uint4 *>(xt + xoff[ks] + s2 * 32 * kXRowBytes);
-      Frag8 af[4];
+      Frag8 af[Sh::NT];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < Sh::NT; ++t) {
         af[t].s4[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t *)(wt + woff[0][t] + ks * 16 * kWRowBytes));
         af[t].s4[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t *)(wt + woff[1][t] + ks * 16 * kWRowBytes));
       }
@@ -232,14 +257,14 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
             lo.w[j] = cvt_pk_bf16(x0 - __uint_as_float(hi.w[j] << 16), x1 - __uint_as_float(hi.w[j] & 0xffff0000u));
           }
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
+          for (int t = 0; t < Sh::NT; ++t) {
             acc[t][s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t].v, hi.v, acc[t][s2], 0, 0, 0);
             acc[t][s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t].v, lo.v, acc[t][s2], 0, 0, 0);
           }
         }
       } else {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < Sh::NT; ++t) {
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
             acc[t][s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t].v, b[s2].v, acc[t][s2], 0, 0, 0);
@@ -284,16 +309,16 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
     const int r = wr * 64 + s2 * 32 + col;
     if (r >= rows_here) continue;
     const float inv = 1.0f / sqrtf(ss / static_cast<float>(d) + a.eps);
-    bf16_t *orow = out + (a.dst_row_base + row0 + r) * a.out_stride + col0 + wc * 128;
+    bf16_t *orow = out + (a.dst_row_base + row0 + r) * a.out_stride + col0 + wc * kWaveCols;
     const int64_t pos = rope ? proj_row_pos(a, row0 + r) : 0;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < NT; ++t) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         float v0 = acc[t][s2][i4 * 4 + 0] * inv, v1 = acc[t][s2][i4 * 4 + 1] * inv;
         float v2 = acc[t][s2][i4 * 4 + 2] * inv, v3 = acc[t][s2][i4 * 4 + 3] * inv;
         if (rope) {
-          const int pair = ((col0 + wc * 128 + t * 32 + i4 * 8 + half * 4) % a.head_dim) >> 1;
+          const int pair = ((col0 + wc * kWaveCols + t * 32 + i4 * 8 + half * 4) % a.head_dim) >> 1;
           rope_turn(v0, v1, pos, lds_rev[pair]);
           rope_turn(v2, v3, pos, lds_rev[pair + 1]);
         }
@@ -313,17 +338,28 @@ bool project_mfma_applies(const ProjArgs &a, int x_dt, int w_dt, int o_dt) {
          static_cast<int64_t>(pm::kRows) * a.d * 2 < (int64_t(1) << 31);
 }
 
-hipError_t launch_project_mfma(const ProjArgs &a, hipStream_t s) {
-  const int64_t row_tiles = (a.n + pm::kRows - 1) / pm::kRows;
-  const int64_t col_tiles = static_cast<int64_t>(a.ncols / pm::kCols) * a.n_out;
+template <int NCOLS>
+static hipError_t launch_project_mfma_t(const ProjArgs &a, int64_t row_tiles, hipStream_t s) {
+  const int64_t col_tiles = static_cast<int64_t>(a.ncols / NCOLS) * a.n_out;
   const int64_t blocks = (row_tiles + pm::kXcds - 1) / pm::kXcds * pm::kXcds * col_tiles;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (a.gain != nullptr) {
-    hipLaunchKernelGGL(project_mfma_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(pm::kThreads), 0, s, a);
+    hipLaunchKernelGGL((project_mfma_kernel<true, NCOLS>), dim3(static_cast<unsigned>(blocks)), dim3(pm::kThreads), 0,
+                       s, a);
   } else {
-    hipLaunchKernelGGL(project_mfma_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(pm::kThreads), 0, s, a);
+    hipLaunchKernelGGL((project_mfma_kernel<false, NCOLS>), dim3(static_cast<unsigned>(blocks)), dim3(pm::kThreads), 0,
+                       s, a);
   }
   return hipGetLastError();
+}
+
+// 256-column tiles unless they leave CUs idle (fewer tiles than the 256 CUs
+// of the device, e.g. 4096 rows at 2 x 1024 columns): then 128-column tiles.
+hipError_t launch_project_mfma(const ProjArgs &a, hipStream_t s) {
+  const int64_t row_tiles = (a.n + pm::kRows - 1) / pm::kRows;
+  const int64_t tiles256 = row_tiles * (a.ncols / pm::kCols) * a.n_out;
+  if (tiles256 < pm::kNarrowBelowTiles) return launch_project_mfma_t<128>(a, row_tiles, s);
+  return launch_project_mfma_t<256>(a, row_tiles, s);
 }
 
 }  // namespace yoco
