@@ -81,26 +81,60 @@ DECODE_SOURCES = (
 )
 
 
-def decode_source_digest():
+PREFILL_COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "prefill_32k_counters.md")
+PREFILL_SOURCES = (
+    "yoco_shared_kv_amd/csrc/prefill.hip",
+    "yoco_shared_kv_amd/csrc/attn_tiles.h",
+    "yoco_shared_kv_amd/csrc/device_common.h",
+)
+
+
+def _digest(sources):
     h = hashlib.sha256()
-    for rel in DECODE_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(rel.encode() + b"\0" + f.read())
     return h.hexdigest()
+
+
+def decode_source_digest():
+    return _digest(DECODE_SOURCES)
+
+
+def prefill_source_digest():
+    return _digest(PREFILL_SOURCES)
+
+
+def _summary_json(path):
+    try:
+        text = open(path).read()
+    except OSError:
+        return None, "no counter summary"
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if m is None:
+        return None, "counter summary has no json block"
+    return json.loads(m.group(1)), None
+
+
+def prefill_mfma_busy():
+    """Fraction of the prefill kernel's cycles its matrix cores were busy, from
+    the committed counter summary: SQ_VALU_MFMA_BUSY_CYCLES (summed over the
+    SIMDs) over SIMDs x GRBM_GUI_ACTIVE per XCD; or (None, reason)."""
+    rec, why = _summary_json(PREFILL_COUNTER_SUMMARY)
+    if rec is None:
+        return None, why
+    if rec["prefill_source_sha256"] != prefill_source_digest():
+        return None, "prefill kernel sources changed since the counters were taken"
+    return rec["mfma_busy_cycles"] / (rec["simds"] * rec["gui_active_cycles"] / rec["xcds"]), None
 
 
 def counter_traffic():
     """HBM bytes per decode launch from the committed counter summary, or
     (None, reason).  FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each
     scaled by COPY_BYTES over what the same counter read for the plain copy."""
-    try:
-        text = open(COUNTER_SUMMARY).read()
-    except OSError:
-        return None, "no counter summary"
-    m = re.search(r"```json\n(.*?)\n```", text, re.S)
-    if m is None:
-        return None, "counter summary has no json block"
-    rec = json.loads(m.group(1))
+    rec, why = _summary_json(COUNTER_SUMMARY)
+    if rec is None:
+        return None, why
     if rec["decode_source_sha256"] != decode_source_digest():
         return None, "decode kernel sources changed since the counters were taken"
     fetch_scale = rec["copy_bytes"] / (rec["copy_fetch_kib"] * 1024)
@@ -669,13 +703,20 @@ def main():
         "cpu_baseline": cpu,
     }
     if pre is not None:
+        busy, busy_why = prefill_mfma_busy()
+        if busy_why:
+            log(f"prefill.roofline.mfma_busy is null: {busy_why}")
         result["prefill"] = {
             "workload": "causal prefill N=32768, H_q=24, H_kv=8, d_h=128, bf16 MFMA, fp32 out",
             "ms": round(pre["ms"], 3), "tflops": round(pre["tflops"], 1),
             "ms_p10_p50_p90": [round(pre["ms_p10"], 3), round(pre["ms_p50"], 3), round(pre["ms_p90"], 3)],
             "roofline": {"bound": "mfma", "achieved": round(pre["tflops"], 1),
                          "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(pre["frac"], 4), "flops_per_launch": pre["flops"]},
+                         "frac": round(pre["frac"], 4), "flops_per_launch": pre["flops"],
+                         "mfma_busy": None if busy is None else round(busy, 4),
+                         "mfma_busy_unit": "fraction of the kernel's cycles the matrix cores were busy "
+                                           "(SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs x GRBM_GUI_ACTIVE per "
+                                           "XCD, committed counters)"},
             "cpu_baseline": pre_cpu,
         }
     if proj is not None:

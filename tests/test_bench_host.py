@@ -49,3 +49,19 @@ def test_committed_summary_parses():
         pytest.skip(why)
     # the decode launch reads K^ and V^ once: counters must not fall below that
     assert traffic >= 2 * 131072 * 8 * 128 * 2
+
+
+def test_committed_prefill_counters_parse():
+    busy, why = bench.prefill_mfma_busy()
+    if why is not None:
+        pytest.skip(why)
+    assert 0.3 < busy <= 1.0
+
+
+def test_prefill_busy_null_once_sources_change(tmp_path, monkeypatch):
+    p = tmp_path / "pf.md"
+    p.write_text('```json\n{"prefill_source_sha256": "' + "0" * 64 + '", "mfma_busy_cycles": 1, '
+                 '"gui_active_cycles": 8, "simds": 1, "xcds": 8}\n```\n')
+    monkeypatch.setattr(bench, "PREFILL_COUNTER_SUMMARY", str(p))
+    busy, why = bench.prefill_mfma_busy()
+    assert busy is None and "changed" in why
