@@ -449,3 +449,23 @@ def test_misaligned_pointers_rejected():
     assert gret(g=MIS4) == bad
     assert gret(g=AL4, ws_bytes=100) == _status("YOCO_ERR_WORKSPACE")
     assert L.yoco_gret_decode(FAKE, FAKE, FAKE, 1, FAKE, 16.0, 2, 3, 128, MIS, FAKE, None) == bad
+
+
+def test_kvcache_wrap_reads_the_row_stride():
+    """KVCache.wrap takes dense or row-padded [n_seq, capacity, H_kv, d_h]
+    tensors and rejects layouts whose heads are not packed inside a row
+    (host tensors: only the layout logic runs)."""
+    import torch
+    import yoco_shared_kv_amd as y
+    dense = torch.zeros(2, 5, 8, 128, dtype=torch.bfloat16)
+    assert y.KVCache.wrap(dense, dense.clone(), [1, 2]).row_stride == 1024
+    rows = torch.zeros(2, 5, 1088, dtype=torch.bfloat16)
+    padded = rows[:, :, :1024].unflatten(2, (8, 128))
+    assert y.KVCache.wrap(padded, rows.clone()[:, :, :1024].unflatten(2, (8, 128)), [1, 2]).row_stride == 1088
+    one = torch.zeros(1, 1, 8, 128, dtype=torch.bfloat16)
+    assert y.KVCache.wrap(one, one.clone(), [0]).row_stride == 1024
+    swapped = torch.zeros(2, 5, 128, 8, dtype=torch.bfloat16).transpose(2, 3)
+    with pytest.raises(ValueError):
+        y.KVCache.wrap(swapped, swapped, [1, 1])
+    with pytest.raises(ValueError):
+        y.KVCache.wrap(dense, padded, [1, 1])                     # k and v strides differ

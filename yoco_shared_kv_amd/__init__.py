@@ -98,8 +98,11 @@ class KVCache:
         if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 4 or k.stride() != v.stride():
             raise ValueError("k and v must be matching [n_seq, capacity, H_kv, d_h] tensors")
         n_seq, cap, hkv, dh = k.shape
-        rs = k.stride(1)
-        if k.stride(3) != 1 or k.stride(2) != dh or rs < hkv * dh or k.stride(0) != cap * rs:
+        # (the stride of a dimension of size 1 carries no layout: rows are
+        # then dense, and one sequence needs no slab stride)
+        rs = k.stride(1) if cap > 1 else (k.stride(0) if n_seq > 1 else hkv * dh)
+        if (k.stride(3) != 1 or (hkv > 1 and k.stride(2) != dh) or rs < hkv * dh
+                or (n_seq > 1 and k.stride(0) != cap * rs)):
             raise ValueError("k and v rows must be packed [H_kv, d_h] blocks at one row stride")
         obj.k, obj.v = k, v
         obj.n_seq, obj.capacity, obj.n_kv_heads, obj.head_dim = n_seq, cap, hkv, dh
