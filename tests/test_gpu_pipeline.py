@@ -44,6 +44,21 @@ def test_chunked_kv_project_equals_one_shot():
     assert torch.equal(chunked.k, one.k) and torch.equal(chunked.v, one.v)
 
 
+def test_wide_and_narrow_projection_tiles_agree_bitwise():
+    """16384 rows take 256-column tiles (512 tiles); 2048-row chunks take
+    128-column tiles (64 tiles, fewer than the CUs).  Each output element
+    sees the same products in the same order, so the caches agree bitwise."""
+    p = W.make_project(n=16384, d_model=1024, n_kv_heads=8, head_dim=128, unit_gain=False, seed=33)
+    m, w_k, w_v = to_dev(p.m), to_dev(p.w_k), to_dev(p.w_v)
+    gain = torch.from_numpy(p.gain).cuda()
+    wide = y.KVCache(1, 16384, 8, 128, torch.bfloat16, zero=True)
+    y.kv_project(wide, m, w_k, w_v, gain, p.eps)
+    narrow = y.KVCache(1, 16384, 8, 128, torch.bfloat16, zero=True)
+    for s, e in _chunks(16384, 2048):
+        y.kv_project(narrow, m[s:e], w_k, w_v, gain, p.eps, row_start=s)
+    assert torch.equal(wide.k, narrow.k) and torch.equal(wide.v, narrow.v)
+
+
 def test_chunked_prefill_equals_one_shot():
     c = W.make_prefill(n=2000, n_q_heads=6, n_kv_heads=2, head_dim=128, seed=32)
     cache = y.KVCache(1, 2000, 2, 128, torch.bfloat16)
