@@ -66,6 +66,8 @@ def parse_args():
     p.add_argument("--prefill-reps", type=int, default=20)
     p.add_argument("--prefill-warmup", type=int, default=6)
     p.add_argument("--copy-calibration", action="store_true")
+    p.add_argument("--dense-rows", action="store_true",
+                   help="decode cache with dense rows instead of the library's padded row stride (for comparison)")
     return p.parse_args()
 
 
@@ -196,7 +198,8 @@ def bench_decode(args, torch, y, W):
     proj = W.make_project(n=(args.warmup + args.steps + args.cold_steps) * n_seq, d_model=d_model,
                           n_kv_heads=hkv, head_dim=dh, seed=1)
 
-    cache = y.KVCache(n_seq, cap, hkv, dh, torch.bfloat16)
+    cache = y.KVCache(n_seq, cap, hkv, dh, torch.bfloat16, padded=not args.dense_rows)
+    log(f"cache rows: {cache.row_stride} elements ({'dense' if cache.row_stride == hkv * dh else 'padded'})")
     for b in range(n_seq):
         cache.k[b, :lens[b]] = to_dev(case.k[b], torch)
         cache.v[b, :lens[b]] = to_dev(case.v[b], torch)
@@ -297,7 +300,8 @@ def bench_decode(args, torch, y, W):
                 kern_p90_us=pct(kern_ms, 90) * 1e3,
                 step_p10_ms=pct(step_ms, 10), step_p50_ms=pct(step_ms, 50), step_p90_ms=pct(step_ms, 90),
                 achieved_gbps=achieved_gbps, bytes_per_launch=bytes_per_launch,
-                step_gbps=step_bytes / (ms_per_step * 1e-3) / 1e9, cold=cold, n_seq=n_seq, lens=lens)
+                step_gbps=step_bytes / (ms_per_step * 1e-3) / 1e9, cold=cold, n_seq=n_seq, lens=lens,
+                row_stride=cache.row_stride)
 
 
 def bench_prefill(args, torch, y, W):
@@ -649,6 +653,8 @@ def main():
             "gated retention", lambda rows: oracle.gret(gc.q, gc.k, gc.v, gamma, rows=rows), gc.q.shape[0], 48)
     # The committed counters were taken on the 128K workload.
     traffic, why = counter_traffic() if args.workload == "decode128k" else (None, "counters cover decode128k only")
+    if args.dense_rows and why is None:
+        traffic, why = None, "counters were taken on padded cache rows"
     if why:
         log(f"roofline.traffic is null: {why}")
     metric = "cross-attn decode us/token/layer at N=128K (shared bf16 K^/V^, 13 layers)"
@@ -671,7 +677,7 @@ def main():
         "config": {
             "workload": WORKLOADS[args.workload][2],
             "n_rows": int(dec["lens"].sum()), "layers": 13, "n_q_heads": 24, "n_kv_heads": 8, "head_dim": 128,
-            "d_model": 3072, "batch": dec["n_seq"],
+            "d_model": 3072, "batch": dec["n_seq"], "cache_row_stride": dec["row_stride"],
         },
         "gpu_ms_per_step": round(dec["gpu_ms_per_step"], 4),
         "step_ms_p10_p50_p90": [round(dec["step_p10_ms"], 4), round(dec["step_p50_ms"], 4),
