@@ -24,7 +24,7 @@
 // far below the fp32 accumulation error; without a gain x enters as stored.
 //
 // A workgroup is 8 waves and computes 256 input rows x 256 output columns of
-// one weight; wave (wr, wc) owns rows wr*64.. and columns wc*128... The
+// one weight, in wave tiles of 64 x 128 (32 x 256 with a gain).  The
 // reduction runs in slices of 64, staged global -> LDS with 16-byte buffer
 // loads to LDS, two stages deep: x slice [256][64] (128-byte rows, chunk
 // index XOR row%8), W slice [64][256] as two [64][128] halves (256-byte rows,
@@ -85,26 +85,33 @@ __device__ __forceinline__ int w_off(int k, int col) {
 
 }  // namespace pm
 
-// NCOLS: output columns per workgroup, 256 (waves own 64 rows x 128
-// columns) or 128 (64 x 64; twice the workgroups for short inputs, at more
-// LDS reads per MFMA).
-template <int NCOLS>
+// NCOLS: output columns per workgroup, 256 or 128 (twice the workgroups for
+// short inputs, at more LDS reads per MFMA).
+// Wave tiles: without a gain each wave owns 64 rows x NCOLS/2 columns (4 x 2
+// waves); with a gain each wave owns 32 rows x NCOLS columns (8 x 1 waves),
+// so every x fragment is split into hi + lo by one wave only, for twice the
+// W reads per MFMA.  The MFMAs of an output element are the same in both.
+template <int NCOLS, bool kGain>
 struct PmShape {
   static constexpr int kColsT = NCOLS;
   static constexpr int kHalves = NCOLS / 128;                           // [64][128] W half tiles per stage
   static constexpr int kWLoadsT = kHalves * pm::kWHalfBytes / 1024 / pm::kWaves;
-  static constexpr int kWaveCols = NCOLS / 2;                           // columns of one wave
+  static constexpr int kRB = kGain ? 1 : 2;                             // 32-row blocks per wave
+  static constexpr int kWavesR = pm::kWaves / kRB;                      // waves along the rows
+  static constexpr int kWaveRows = 32 * kRB;
+  static constexpr int kWaveCols = NCOLS / kRB;                         // columns of one wave
   static constexpr int NT = kWaveCols / 32;                             // 32-column accumulator tiles per wave
 };
 
 template <bool kGain, int NCOLS>
 __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const ProjArgs a) {
   using namespace pm;
-  using Sh = PmShape<NCOLS>;
+  using Sh = PmShape<NCOLS, kGain>;
   constexpr int kColsT = Sh::kColsT;
   constexpr int kHalves = Sh::kHalves;
   constexpr int kWaveCols = Sh::kWaveCols;
   constexpr int NT = Sh::NT;
+  constexpr int kRB = Sh::kRB;
   __shared__ __attribute__((aligned(1024))) char lds_x0[kXTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_x1[kXTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_w0[kHalves * kWHalfBytes];
@@ -188,13 +195,13 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
     }
   };
 
-  // Wave tile: rows wr*64 + s*32 (s = 0, 1), columns wc*kWaveCols + t*32 (t < NT).
-  const int wr = wave & 3;
-  const int wc = wave >> 2;
+  // Wave tile: rows wr*kWaveRows + s*32 (s < kRB), columns wc*kWaveCols + t*32 (t < NT).
+  const int wr = wave % Sh::kWavesR;
+  const int wc = wave / Sh::kWavesR;
   // B (x^T) read: row wr*64 + s*32 + col, chunk 2*ks + half; row % 8 = col % 8.
   int xoff[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) xoff[ks] = (wr * 64 + col) * kXRowBytes + (((2 * ks + half) ^ (col & 7)) << 4);
+  for (int ks = 0; ks < 4; ++ks) xoff[ks] = (wr * Sh::kWaveRows + col) * kXRowBytes + (((2 * ks + half) ^ (col & 7)) << 4);
   // A (W^T) reads: in each 16-lane group, source lane a + 4j points at k row
   // kb + j, columns cb + 4a .. +3, and lane i of the group receives k rows
   // kb..kb+3 of column cb + i.  Lanes 0..31 take k rows 0..7 of the step (two
@@ -204,41 +211,44 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
   const int src_j = (lane >> 2) & 3;
   const int krow = (grp >> 1) * 8 + src_j;
   const int ccol = (grp & 1) * 16 + src_a * 4;
-  // The wave's columns start in W half tile (wc*kWaveCols)/128 at column
-  // (wc*kWaveCols)%128 of that half.
+  // Column tile t of the wave (32 columns from cw = wc*kWaveCols + t*32)
+  // sits in W half tile cw/128 at column cw%128 of that half.
   int woff[2][NT];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
-      woff[r][t] = (wc * kWaveCols / 128) * kWHalfBytes + w_off(krow + 4 * r, (wc * kWaveCols) % 128 + t * 32 + ccol);
+      woff[r][t] = ((wc * kWaveCols + t * 32) / 128) * kWHalfBytes +
+                   w_off(krow + 4 * r, (wc * kWaveCols + t * 32) % 128 + ccol);
   }
 
-  floatx16 acc[NT][2];
+  floatx16 acc[NT][kRB];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
+    for (int s2 = 0; s2 < kRB; ++s2) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[t][s2][i] = 0.f;
     }
   }
-  float sumsq[2] = {0.f, 0.f};
+  float sumsq[kRB];
+#pragma unroll
+  for (int s2 = 0; s2 < kRB; ++s2) sumsq[s2] = 0.f;
 
   auto compute = [&](const char *xt, const char *wt, const float *gt) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      Frag8 b[2];
+      Frag8 b[kRB];
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) b[s2].u = *reinterpret_cast<const uint4 *>(xt + xoff[ks] + s2 * 32 * kXRowBytes);
-      Frag8 af[Sh::NT];
+      for (int s2 = 0; s2 < kRB; ++s2) b[s2].u = *reinterpret_cast<const uint4 *>(xt + xoff[ks] + s2 * 32 * kXRowBytes);
+      Frag8 af[NT];
 #pragma unroll
-      for (int t = 0; t < Sh::NT; ++t) {
+      for (int t = 0; t < NT; ++t) {
         af[t].s4[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t *)(wt + woff[0][t] + ks * 16 * kWRowBytes));
         af[t].s4[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t *)(wt + woff[1][t] + ks * 16 * kWRowBytes));
       }
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
+      for (int s2 = 0; s2 < kRB; ++s2) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) sumsq[s2] = dot2_bf16(b[s2].w[j], b[s2].w[j], sumsq[s2]);
       }
@@ -247,7 +257,7 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
         const float4 g1 = *reinterpret_cast<const float4 *>(gt + ks * 16 + half * 8 + 4);
         const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
+        for (int s2 = 0; s2 < kRB; ++s2) {
           Frag8 hi, lo;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -257,16 +267,16 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
             lo.w[j] = cvt_pk_bf16(x0 - __uint_as_float(hi.w[j] << 16), x1 - __uint_as_float(hi.w[j] & 0xffff0000u));
           }
 #pragma unroll
-          for (int t = 0; t < Sh::NT; ++t) {
+          for (int t = 0; t < NT; ++t) {
             acc[t][s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t].v, hi.v, acc[t][s2], 0, 0, 0);
             acc[t][s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t].v, lo.v, acc[t][s2], 0, 0, 0);
           }
         }
       } else {
 #pragma unroll
-        for (int t = 0; t < Sh::NT; ++t) {
+        for (int t = 0; t < NT; ++t) {
 #pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
+          for (int s2 = 0; s2 < kRB; ++s2) {
             acc[t][s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t].v, b[s2].v, acc[t][s2], 0, 0, 0);
           }
         }
@@ -304,9 +314,9 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
   }
   bf16_t *out = static_cast<bf16_t *>(a.out[p]);
 #pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2) {
+  for (int s2 = 0; s2 < kRB; ++s2) {
     const float ss = sumsq[s2] + shfl_xor_f(sumsq[s2], 32);
-    const int r = wr * 64 + s2 * 32 + col;
+    const int r = wr * Sh::kWaveRows + s2 * 32 + col;
     if (r >= rows_here) continue;
     const float inv = 1.0f / sqrtf(ss / static_cast<float>(d) + a.eps);
     bf16_t *orow = out + (a.dst_row_base + row0 + r) * a.out_stride + col0 + wc * kWaveCols;
