@@ -198,7 +198,7 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
   // Wave tile: rows wr*kWaveRows + s*32 (s < kRB), columns wc*kWaveCols + t*32 (t < NT).
   const int wr = wave % Sh::kWavesR;
   const int wc = wave / Sh::kWavesR;
-  // B (x^T) read: row wr*64 + s*32 + col, chunk 2*ks + half; row % 8 = col % 8.
+  // B (x^T) read: row wr*kWaveRows + s*32 + col, chunk 2*ks + half; row % 8 = col % 8.
   int xoff[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) xoff[ks] = (wr * Sh::kWaveRows + col) * kXRowBytes + (((2 * ks + half) ^ (col & 7)) << 4);
@@ -304,8 +304,8 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
   }
 
   // Epilogue: acc[t][s2] element i is output column
-  //   col0 + wc*128 + t*32 + (i/4)*8 + half*4 + (i%4)
-  // of input row row0 + wr*64 + s2*32 + col.  With RoPE, columns (2i, 2i+1)
+  //   col0 + wc*kWaveCols + t*32 + (i/4)*8 + half*4 + (i%4)
+  // of input row row0 + wr*kWaveRows + s2*32 + col.  With RoPE, columns (2i, 2i+1)
   // of a head sit in elements (i4*4 + 2j, i4*4 + 2j + 1) of the same lane.
   const bool rope = a.rope_out == p;  // block-uniform
   if (rope) {
