@@ -44,17 +44,21 @@ def test_chunked_kv_project_equals_one_shot():
     assert torch.equal(chunked.k, one.k) and torch.equal(chunked.v, one.v)
 
 
-def test_wide_and_narrow_projection_tiles_agree_bitwise():
-    """16384 rows take 256-column tiles (512 tiles); 2048-row chunks take
-    128-column tiles (64 tiles, fewer than the CUs).  Each output element
+@pytest.mark.parametrize("with_gain", [True, False])
+def test_wide_and_narrow_projection_tiles_agree_bitwise(with_gain):
+    """16300 rows take 256-column tiles (512 tiles); 2048-row chunks take
+    128-column tiles (64 tiles, fewer than the CUs), the last chunk ragged.
+    The wave tiles differ with and without a gain, but each output element
     sees the same products in the same order, so the caches agree bitwise."""
-    p = W.make_project(n=16384, d_model=1024, n_kv_heads=8, head_dim=128, unit_gain=False, seed=33)
+    n = 16300
+    print(f"pipeline: wide vs narrow tiles, gain={with_gain}", flush=True)
+    p = W.make_project(n=n, d_model=1024, n_kv_heads=8, head_dim=128, unit_gain=False, seed=33)
     m, w_k, w_v = to_dev(p.m), to_dev(p.w_k), to_dev(p.w_v)
-    gain = torch.from_numpy(p.gain).cuda()
-    wide = y.KVCache(1, 16384, 8, 128, torch.bfloat16, zero=True)
+    gain = torch.from_numpy(p.gain).cuda() if with_gain else None
+    wide = y.KVCache(1, n, 8, 128, torch.bfloat16, zero=True)
     y.kv_project(wide, m, w_k, w_v, gain, p.eps)
-    narrow = y.KVCache(1, 16384, 8, 128, torch.bfloat16, zero=True)
-    for s, e in _chunks(16384, 2048):
+    narrow = y.KVCache(1, n, 8, 128, torch.bfloat16, zero=True)
+    for s, e in _chunks(n, 2048):
         y.kv_project(narrow, m[s:e], w_k, w_v, gain, p.eps, row_start=s)
     assert torch.equal(wide.k, narrow.k) and torch.equal(wide.v, narrow.v)
 
