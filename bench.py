@@ -208,6 +208,8 @@ def bench_decode(args, torch, y, W):
     w_k, w_v = to_dev(proj.w_k, torch), to_dev(proj.w_v, torch)
     gain = torch.ones(d_model, dtype=torch.float32, device="cuda")
     ws = y.decode_workspace(cache, hq)
+    pws = torch.zeros(max(1, y.project_workspace_bytes(n_seq, d_model, hkv * dh, 2)), dtype=torch.uint8,
+                      device="cuda")
     outs = [torch.empty((n_seq, hq, dh), dtype=torch.float32, device="cuda") for _ in range(layers)]
     stream = torch.cuda.current_stream()
     # Cold variant: a 512 MiB copy between layer calls evicts every cache level
@@ -237,7 +239,7 @@ def bench_decode(args, torch, y, W):
         cache.len[:] = lens - 1
         if record_step is not None:
             step_ev[record_step][0].record(stream)
-        y.kv_append(cache, m_rows[i * n_seq:(i + 1) * n_seq], w_k, w_v, gain, 1e-6, stream=stream)
+        y.kv_append(cache, m_rows[i * n_seq:(i + 1) * n_seq], w_k, w_v, gain, 1e-6, stream=stream, workspace=pws)
         for l in range(layers):
             if cold is not None:
                 flush_dst.copy_(flush_src)
@@ -349,26 +351,34 @@ def cpu_model():
     return None
 
 
-def sampled_rows(n, count):
-    """Rows spread evenly over [0, n): the centres of `count` equal strata."""
-    return ((np.arange(count) + 0.5) * n / count).astype(np.int64)
+def stratified_rows(n, per_decile, seed=0):
+    """Rows 0, 1 and n-1 plus `per_decile` distinct seeded rows in each tenth
+    of the positions [0, n)."""
+    rng = np.random.default_rng(seed)
+    rows = {0, 1, n - 1}
+    for d in range(10):
+        lo, hi = d * n // 10, (d + 1) * n // 10
+        rows.update(int(r) for r in rng.choice(np.arange(lo, hi), min(per_decile, hi - lo), replace=False))
+    return np.array(sorted(rows), dtype=np.int64)
 
 
-def causal_cpu_baseline(name, run_rows, n, count):
-    """Time an oracle call on `count` sampled query rows of a causal workload
-    of n rows and extrapolate to all n rows: the work of row r is
+def causal_cpu_baseline(name, run_rows, n, per_decile):
+    """Time an oracle call on a stratified sample of query rows of a causal
+    workload of n rows and extrapolate to all n rows: the work of row r is
     proportional to its r + 1 visible keys."""
     import oracle
-    rows = sampled_rows(n, count)
+    rows = stratified_rows(n, per_decile)
     t0 = time.perf_counter()
     run_rows(rows)
     dt = time.perf_counter() - t0
     frac = float(np.sum(rows + 1)) / (n * (n + 1) / 2.0)
     full_ms = dt / frac * 1e3
-    log(f"cpu baseline ({name}): {count} sampled rows in {dt:.2f} s -> {full_ms / 1e3:.1f} s extrapolated")
+    log(f"cpu baseline ({name}): {rows.size} sampled rows in {dt:.2f} s -> {full_ms / 1e3:.1f} s extrapolated")
     return {"value": round(full_ms, 1), "unit": "ms", "cores": oracle.num_threads(), "cpu": cpu_model(),
-            "kind": "oracle", "sample": f"{count} query rows spread evenly over the {n} positions, every head, timed "
-                      f"({dt:.2f} s wall, {frac * 100:.3f}% of the causal work) and extrapolated to all rows"}
+            "kind": "oracle",
+            "sample": f"rows 0, 1, {n - 1} and {per_decile} seeded rows per position decile ({rows.size} query rows "
+                      f"of {n}), every head, timed ({dt:.2f} s wall, {frac * 100:.3f}% of the causal work) and "
+                      f"extrapolated to all rows"}
 
 
 def bench_backward(args, torch, y, W):
@@ -453,7 +463,11 @@ def bench_project(args, torch, y, W):
     w_q = [to_dev(W.store((rng.standard_normal((d, hq * dh)) / math.sqrt(d)).astype(np.float32), W.BF16), torch)
            for _ in range(layers)]
     ws = y.decode_workspace(cache, hq)
+    ncols = pc.n_kv_heads * pc.head_dim
+    pws = torch.zeros(max(y.project_workspace_bytes(1, d, ncols, 2), y.project_workspace_bytes(1, d, hq * dh, 1)),
+                      dtype=torch.uint8, device="cuda")
     outs = [torch.empty((1, hq, dh), dtype=torch.float32, device="cuda") for _ in range(layers)]
+    qs = [torch.empty((1, hq, dh), dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
     chunk = 4096
 
     def pipeline():
@@ -461,9 +475,9 @@ def bench_project(args, torch, y, W):
         for s0 in range(0, n - 1, chunk):
             e0 = min(s0 + chunk, n - 1)
             y.kv_project(cache, m[s0:e0], w_k, w_v, gain, pc.eps, row_start=s0, stream=stream)
-        y.kv_append(cache, m[n - 1:n], w_k, w_v, gain, pc.eps, stream=stream)
+        y.kv_append(cache, m[n - 1:n], w_k, w_v, gain, pc.eps, stream=stream, workspace=pws)
         for l in range(layers):
-            q = y.q_project(x_last[l], w_q[l], hq, dh, stream=stream)
+            q = y.q_project(x_last[l], w_q[l], hq, dh, out=qs[l], stream=stream, workspace=pws)
             y.cross_attn_decode(q, cache, workspace=ws, out=outs[l], stream=stream)
 
     pipeline()
@@ -480,6 +494,41 @@ def bench_project(args, torch, y, W):
     res["early_exit_p50_ms"] = pct(ee, 50)
     log(f"early-exit prefill at N={n} (chunked projection + append + 13 x (q_project + decode)): "
         f"{res['early_exit_ms']:.3f} ms")
+
+    # The one-row projections of generation: the append of one K^/V^ row
+    # (W_K and W_V read once) and one layer's query row (W_Q read once).  A
+    # call through the Python binding costs more host time than the kernel
+    # takes, so 50 launches are captured into a HIP graph and the graph is
+    # replayed between one event pair (the kernels' back-to-back time).
+    reps, replays = 50, 4
+    one = {}
+    for name, wbytes in (("append", 2 * d * ncols * 2), ("query", d * hq * dh * 2)):
+        def launch(s_):
+            if name == "append":
+                cache.len[0] = n - 1
+                y.kv_append(cache, m[n - 1:n], w_k, w_v, gain, pc.eps, stream=s_, workspace=pws)
+            else:
+                y.q_project(x_last[0], w_q[0], hq, dh, gain=gain, out=qs[0], stream=s_, workspace=pws)
+        for _ in range(5):
+            launch(stream)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(reps):
+                launch(None)          # the capturing stream
+        graph.replay()
+        torch.cuda.synchronize()
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_ev.record(stream)
+        for _ in range(replays):
+            graph.replay()
+        b_ev.record(stream)
+        torch.cuda.synchronize()
+        us = a_ev.elapsed_time(b_ev) * 1e3 / (reps * replays)
+        del graph
+        one[name] = dict(us=us, bytes=wbytes, GBps=wbytes / (us * 1e-6) / 1e9)
+        log(f"one-row {name} projection: {us:.2f} us per launch -> {one[name]['GBps']:.0f} GB/s of weights")
+    res["one_row"] = one
     return res
 
 
@@ -644,13 +693,13 @@ def main():
         import oracle
         c = pre["case"]
         pre_cpu = causal_cpu_baseline(
-            "prefill", lambda rows: oracle.prefill(c.q, 0, c.k, c.v, c.softmax_scale, rows=rows), c.k.shape[0], 48)
+            "prefill", lambda rows: oracle.prefill(c.q, 0, c.k, c.v, c.softmax_scale, rows=rows), c.k.shape[0], 128)
     if not args.no_cpu_baseline and gret is not None:
         import oracle
         gc = gret["case"]
         gamma = oracle.gret_gate(gc.gate, gc.tau)
         gret_cpu = causal_cpu_baseline(
-            "gated retention", lambda rows: oracle.gret(gc.q, gc.k, gc.v, gamma, rows=rows), gc.q.shape[0], 48)
+            "gated retention", lambda rows: oracle.gret(gc.q, gc.k, gc.v, gamma, rows=rows), gc.q.shape[0], 8)
     # The committed counters were taken on the 128K workload.
     traffic, why = counter_traffic() if args.workload == "decode128k" else (None, "counters cover decode128k only")
     if args.dense_rows and why is None:
@@ -746,6 +795,21 @@ def main():
             "without_early_exit": "13 causal prefill launches over the whole prompt (the cross layers "
                                   "run for every position)",
         }
+        one = proj["one_row"]
+        result["one_row_projection"] = {
+            "workload": "generation-time projections of one row at 3B widths (bf16 weights, fp32 gain, RMSNorm "
+                        "fused): the K^/V^ append (3072 -> 2 x 1024) and one layer's query (3072 -> 24 x 128); "
+                        "weights split over their d_model rows across the chip",
+            "timing": "50 launches captured in a HIP graph, HIP events around 4 replays (no host time "
+                      "between launches)",
+        }
+        for name in ("append", "query"):
+            e = one[name]
+            result["one_row_projection"][name] = {
+                "us": round(e["us"], 2), "weight_bytes": e["bytes"],
+                "roofline": {"bound": "hbm", "achieved": round(e["GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                             "frac": round(e["GBps"] / HBM_PEAK_GBPS, 4)},
+            }
     if bwd is not None:
         result["prefill_backward"] = {
             "workload": "backward of one cross layer's causal prefill N=32768, H_q=24, H_kv=8, d_h=128, bf16 "

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define YOCO_ABI_VERSION 7
+#define YOCO_ABI_VERSION 8
 #define YOCO_MAX_SEQ 256
 
 /* Storage types. */
@@ -150,14 +150,18 @@ yoco_status yoco_kv_cache_row_stride(int32_t n_kv_heads, int32_t head_dim, int32
  * Writes k/v rows row_start .. row_start+n-1 of `seq` in the cache dtype,
  * then sets len_host[seq] = max(len_host[seq], row_start + n).
  * n == 0 is a successful no-op.
+ * workspace / workspace_bytes: see "Few-row projections" below (NULL, 0
+ * is always valid).
  * Errors: NULL m/w_k/w_v/cache/cache->k/v/len_host -> NULL_POINTER;
  * d_model < 1, bad cache dims, seq outside [0, n_seq) -> BAD_SHAPE;
  * dtype codes -> BAD_DTYPE; row_start < 0 or row_start + n > seq_capacity ->
- * OUT_OF_RANGE; eps < 0 or not finite -> BAD_VALUE. */
+ * OUT_OF_RANGE; eps < 0 or not finite -> BAD_VALUE; WORKSPACE (given but
+ * too small for a call that uses it). */
 yoco_status yoco_kv_project(const void *m, int32_t m_dtype, int64_t n, int32_t d_model,
                             const float *gain, float eps, const void *w_k, const void *w_v,
                             int32_t w_dtype, yoco_kv_cache *cache, int32_t seq,
-                            int64_t row_start, void *stream);
+                            int64_t row_start, void *workspace, size_t workspace_bytes,
+                            void *stream);
 
 /* Generation-time append ([Notes] section 2.1 and section 2.5: each new token
  * goes through the self-decoder and its K/V row is appended to the shared
@@ -169,7 +173,8 @@ yoco_status yoco_kv_project(const void *m, int32_t m_dtype, int64_t n, int32_t d
  * len_host[b] < 0 -> OUT_OF_RANGE (and nothing is written). */
 yoco_status yoco_kv_append(const void *m_new, int32_t m_dtype, int32_t d_model,
                            const float *gain, float eps, const void *w_k, const void *w_v,
-                           int32_t w_dtype, yoco_kv_cache *cache, void *stream);
+                           int32_t w_dtype, yoco_kv_cache *cache, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /* Per-layer query projection ([Notes] Eq. 3: Q^l = LN(X^l) W_Q^l with the
  * layer's own norm; [Blog] section 7: each cross layer projects only its Q).
@@ -177,11 +182,39 @@ yoco_status yoco_kv_append(const void *m_new, int32_t m_dtype, int32_t d_model,
  * w_q: [d_model][n_q_heads*head_dim]; q_out: [n][n_q_heads][head_dim] in
  * q_dtype (f32 or bf16).  n == 0 is a no-op.
  * Errors: NULL_POINTER, BAD_SHAPE (head_dim not 64/128, counts < 1),
- * BAD_DTYPE, BAD_VALUE (eps). */
+ * BAD_DTYPE, BAD_VALUE (eps), WORKSPACE. */
 yoco_status yoco_q_project(const void *x, int32_t x_dtype, int64_t n, int32_t d_model,
                            const float *gain, float eps, const void *w_q, int32_t w_dtype,
                            int32_t n_q_heads, int32_t head_dim, void *q_out, int32_t q_dtype,
-                           void *stream);
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Few-row projections (generation: one appended row per sequence, one query
+ * row per layer).  With at most 8 input rows the projection is a
+ * matrix-vector product bound by reading W once.  Given a workspace, the
+ * calls above (and their _rope forms) with 1..32 input rows split W's
+ * d_model rows over about 512 workgroups that each stream whole 256-byte
+ * row segments, and the last workgroup of each column block adds the
+ * partials in a fixed order (bitwise reproducible); without one (NULL, 0)
+ * the same rows run on a kernel that needs no workspace and streams W
+ * several times slower.  The workspace is device memory of at least the
+ * size yoco_project_workspace reports for the call's shapes; its first
+ * YOCO_PROJECT_COUNTER_BYTES bytes are arrival counters that must be zero
+ * before the first call, and every completed call leaves them zero (so
+ * zero-filling it once at allocation is enough).  Calls that share a
+ * workspace must not overlap in time (same stream, or synchronized).  Calls
+ * whose shapes do not use the path ignore the workspace. */
+#define YOCO_PROJECT_COUNTER_BYTES 16384
+
+/* Bytes of workspace a projection of n input rows of width d_model to
+ * n_out weights of n_cols columns (K^ and V^: n_out 2, n_cols
+ * n_kv_heads*head_dim; Q^: n_out 1, n_cols n_q_heads*head_dim) in w_dtype
+ * uses; 0 when those shapes do not use the few-row path (n outside
+ * [1, 32], n_cols not a multiple of 128 bf16 / 64 fp32 columns, or more
+ * than 128 such column blocks over the n_out weights).
+ * Host-only.  Errors: NULL_POINTER; BAD_SHAPE (n < 0, d_model < 1,
+ * n_cols < 1, n_out not 1 or 2); BAD_DTYPE. */
+yoco_status yoco_project_workspace(int64_t n, int32_t d_model, int32_t n_cols, int32_t n_out,
+                                   int32_t w_dtype, size_t *bytes);
 
 /* Rotary position embedding on the projections ([Blog] "NeurIPS'24 | YOCO:
  * 长上下文 LLM 为什么不必每层都存一份 KV Cache?" section 7: the shared projection
@@ -206,14 +239,15 @@ yoco_status yoco_q_project(const void *x, int32_t x_dtype, int64_t n, int32_t d_
 yoco_status yoco_kv_project_rope(const void *m, int32_t m_dtype, int64_t n, int32_t d_model,
                                  const float *gain, float eps, const void *w_k, const void *w_v,
                                  int32_t w_dtype, yoco_kv_cache *cache, int32_t seq,
-                                 int64_t row_start, double rope_theta, void *stream);
+                                 int64_t row_start, double rope_theta, void *workspace,
+                                 size_t workspace_bytes, void *stream);
 
 /* yoco_kv_append with the new K^ row of sequence b rotated at position
  * len_host[b] (its cache row). */
 yoco_status yoco_kv_append_rope(const void *m_new, int32_t m_dtype, int32_t d_model,
                                 const float *gain, float eps, const void *w_k, const void *w_v,
                                 int32_t w_dtype, yoco_kv_cache *cache, double rope_theta,
-                                void *stream);
+                                void *workspace, size_t workspace_bytes, void *stream);
 
 /* yoco_q_project with query row r rotated at position pos_host[r] (a HOST
  * array of n >= 0 positions, n <= YOCO_MAX_SEQ, else BAD_SHAPE; decode: the
@@ -223,7 +257,14 @@ yoco_status yoco_q_project_rope(const void *x, int32_t x_dtype, int64_t n, int32
                                 const float *gain, float eps, const void *w_q, int32_t w_dtype,
                                 int32_t n_q_heads, int32_t head_dim, void *q_out,
                                 int32_t q_dtype, const int64_t *pos_host, int64_t pos0,
-                                double rope_theta, void *stream);
+                                double rope_theta, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/* Host-only helper: the softmax scale 1/sqrt(head_dim) of [Blog] section 2
+ * (o_t = softmax(q_t K^T / sqrt(d_h)) V), the scale the attention calls below
+ * use in the pages' method; the calls take the scale explicitly.  Errors:
+ * NULL scale -> NULL_POINTER; head_dim < 1 -> BAD_SHAPE. */
+yoco_status yoco_default_softmax_scale(int32_t head_dim, float *scale);
 
 /* Causal cross-attention over the shared cache for a block of query rows
  * (prefill / training forward: [Notes] Eq. 3 with the causal mask; [Blog]

@@ -27,7 +27,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = _lib()
     names = _declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 23, names
     for name in names:
         assert hasattr(lib, name), f"{name} declared in yoco.h but not exported"
 
@@ -101,11 +101,12 @@ def _status(name):
 
 
 def _project(c, **kw):
-    args = dict(m=FAKE, m_dt=1, n=4, d=32, gain=None, eps=1e-6, wk=FAKE, wv=FAKE, w_dt=1, seq=0, row_start=0)
+    args = dict(m=FAKE, m_dt=1, n=4, d=32, gain=None, eps=1e-6, wk=FAKE, wv=FAKE, w_dt=1, seq=0, row_start=0,
+                ws=None, ws_bytes=0)
     args.update(kw)
     return _lib().yoco_kv_project(args["m"], args["m_dt"], args["n"], args["d"], args["gain"], args["eps"],
                                   args["wk"], args["wv"], args["w_dt"], ctypes.byref(c), args["seq"],
-                                  args["row_start"], None)
+                                  args["row_start"], args["ws"], args["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -153,13 +154,13 @@ def test_cache_pointers_required():
     c, _ = _cache()
     c.k = None
     assert _project(c) == _status("YOCO_ERR_NULL_POINTER")
-    assert _lib().yoco_kv_project(FAKE, 1, 4, 32, None, 1e-6, FAKE, FAKE, 1, None, 0, 0, None) == \
+    assert _lib().yoco_kv_project(FAKE, 1, 4, 32, None, 1e-6, FAKE, FAKE, 1, None, 0, 0, None, 0, None) == \
         _status("YOCO_ERR_NULL_POINTER")
 
 
 def test_append_at_capacity_rejected_and_lengths_kept():
     c, lens = _cache(lens=(10, 64))
-    st = _lib().yoco_kv_append(FAKE, 1, 32, None, 1e-6, FAKE, FAKE, 1, ctypes.byref(c), None)
+    st = _lib().yoco_kv_append(FAKE, 1, 32, None, 1e-6, FAKE, FAKE, 1, ctypes.byref(c), None, 0, None)
     assert st == _status("YOCO_ERR_OUT_OF_RANGE")
     assert lens.tolist() == [10, 64]
 
@@ -230,10 +231,10 @@ def test_decode_rejects():
 
 def test_q_project_rejects():
     L = _lib()
-    assert L.yoco_q_project(FAKE, 1, 4, 32, None, 1e-6, FAKE, 1, 4, 96, FAKE, 1, None) == _status("YOCO_ERR_BAD_SHAPE")
-    assert L.yoco_q_project(None, 1, 4, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 1, None) == _status("YOCO_ERR_NULL_POINTER")
-    assert L.yoco_q_project(FAKE, 1, 4, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 2, None) == _status("YOCO_ERR_BAD_DTYPE")
-    assert L.yoco_q_project(FAKE, 1, 0, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 1, None) == 0
+    assert L.yoco_q_project(FAKE, 1, 4, 32, None, 1e-6, FAKE, 1, 4, 96, FAKE, 1, None, 0, None) == _status("YOCO_ERR_BAD_SHAPE")
+    assert L.yoco_q_project(None, 1, 4, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 1, None, 0, None) == _status("YOCO_ERR_NULL_POINTER")
+    assert L.yoco_q_project(FAKE, 1, 4, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 2, None, 0, None) == _status("YOCO_ERR_BAD_DTYPE")
+    assert L.yoco_q_project(FAKE, 1, 0, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 1, None, 0, None) == 0
 
 
 @pytest.mark.skipif(gpu_available(), reason="checks the no-GPU failure mode")
@@ -256,20 +257,21 @@ def test_rope_entry_points_reject_bad_theta_and_positions():
     L = _lib()
     c, lens = _cache()
     for theta in (0.0, 1.0, 0.5, float("inf"), float("nan")):
-        st = L.yoco_kv_project_rope(FAKE, 1, 4, 32, None, 1e-6, FAKE, FAKE, 1, ctypes.byref(c), 0, 0, theta, None)
+        st = L.yoco_kv_project_rope(FAKE, 1, 4, 32, None, 1e-6, FAKE, FAKE, 1, ctypes.byref(c), 0, 0, theta, None, 0,
+                                    None)
         assert st == _status("YOCO_ERR_BAD_VALUE"), theta
-        st = L.yoco_kv_append_rope(FAKE, 1, 32, None, 1e-6, FAKE, FAKE, 1, ctypes.byref(c), theta, None)
+        st = L.yoco_kv_append_rope(FAKE, 1, 32, None, 1e-6, FAKE, FAKE, 1, ctypes.byref(c), theta, None, 0, None)
         assert st == _status("YOCO_ERR_BAD_VALUE"), theta
     assert lens.tolist() == [10, 20]
     pos = (ctypes.c_int64 * 3)(5, -1, 7)
-    assert L.yoco_q_project_rope(FAKE, 1, 3, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 1, pos, 0, 1e4, None) == \
+    assert L.yoco_q_project_rope(FAKE, 1, 3, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 1, pos, 0, 1e4, None, 0, None) == \
         _status("YOCO_ERR_OUT_OF_RANGE")
-    assert L.yoco_q_project_rope(FAKE, 1, 3, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 1, None, -2, 1e4, None) == \
+    assert L.yoco_q_project_rope(FAKE, 1, 3, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 1, None, -2, 1e4, None, 0, None) == \
         _status("YOCO_ERR_OUT_OF_RANGE")
     big = (ctypes.c_int64 * 257)()
-    assert L.yoco_q_project_rope(FAKE, 1, 257, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 1, big, 0, 1e4, None) == \
+    assert L.yoco_q_project_rope(FAKE, 1, 257, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 1, big, 0, 1e4, None, 0, None) == \
         _status("YOCO_ERR_BAD_SHAPE")
-    assert L.yoco_q_project_rope(FAKE, 1, 0, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 1, None, 0, 1e4, None) == 0
+    assert L.yoco_q_project_rope(FAKE, 1, 0, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 1, None, 0, 1e4, None, 0, None) == 0
 
 
 def _bwd(c, **kw):
@@ -429,9 +431,9 @@ def test_misaligned_pointers_rejected():
     c.k = MIS
     assert _project(c) == bad
     c, lens = _cache()
-    assert L.yoco_kv_append(FAKE, 1, 32, None, 1e-6, FAKE, MIS, 1, ctypes.byref(c), None) == bad
+    assert L.yoco_kv_append(FAKE, 1, 32, None, 1e-6, FAKE, MIS, 1, ctypes.byref(c), None, 0, None) == bad
     assert lens.tolist() == [10, 20]
-    assert L.yoco_q_project(FAKE, 1, 4, 32, None, 1e-6, FAKE, 1, 4, 64, MIS, 1, None) == bad
+    assert L.yoco_q_project(FAKE, 1, 4, 32, None, 1e-6, FAKE, 1, 4, 64, MIS, 1, None, 0, None) == bad
     assert L.yoco_cross_attn_prefill(MIS, 1, 0, 4, 4, ctypes.byref(c), 0, 0.125, FAKE, 0, None, None) == bad
     assert L.yoco_cross_attn_prefill(FAKE, 1, 0, 4, 4, ctypes.byref(c), 0, 0.125, FAKE, 0, MIS4, None) == bad
     assert L.yoco_cross_attn_decode(FAKE, 1, 4, ctypes.byref(c), 0.125, MIS, None, FAKE, 1 << 30, 0, None) == bad
@@ -469,3 +471,100 @@ def test_kvcache_wrap_reads_the_row_stride():
         y.KVCache.wrap(swapped, swapped, [1, 1])
     with pytest.raises(ValueError):
         y.KVCache.wrap(dense, padded, [1, 1])                     # k and v strides differ
+
+
+def test_project_workspace_sizes_and_rules():
+    L = _lib()
+    out = ctypes.c_size_t(0)
+    # one appended row at 3B widths: K^ and V^ of 8 heads x 128, bf16 weights
+    assert L.yoco_project_workspace(1, 3072, 1024, 2, 1, ctypes.byref(out)) == 0
+    kv = out.value
+    assert kv > 16384 and (kv - 16384) % 16 == 0
+    # the partials are sized for a launch of 8 rows whatever n is (1..32)
+    for n in (2, 8, 32):
+        assert L.yoco_project_workspace(n, 3072, 1024, 2, 1, ctypes.byref(out)) == 0 and out.value == kv
+    # shapes that do not take the few-row path need none
+    for args in ((33, 3072, 1024, 2, 1), (0, 3072, 1024, 2, 1), (1, 256, 96, 1, 1), (1, 256, 32, 1, 0)):
+        assert L.yoco_project_workspace(*args, ctypes.byref(out)) == 0 and out.value == 0, args
+    assert L.yoco_project_workspace(1, 256, 64, 1, 0, ctypes.byref(out)) == 0 and out.value > 16384
+    # at most 128 column blocks (one arrival counter per 128-byte line of the 16 KiB)
+    assert L.yoco_project_workspace(1, 256, 128 * 64, 2, 1, ctypes.byref(out)) == 0 and out.value > 0
+    assert L.yoco_project_workspace(1, 256, 130 * 64, 2, 1, ctypes.byref(out)) == 0 and out.value == 0
+    assert L.yoco_project_workspace(1, 0, 1024, 2, 1, ctypes.byref(out)) == _status("YOCO_ERR_BAD_SHAPE")
+    assert L.yoco_project_workspace(1, 64, 1024, 3, 1, ctypes.byref(out)) == _status("YOCO_ERR_BAD_SHAPE")
+    assert L.yoco_project_workspace(1, 64, 1024, 2, 7, ctypes.byref(out)) == _status("YOCO_ERR_BAD_DTYPE")
+    assert L.yoco_project_workspace(1, 64, 1024, 2, 1, None) == _status("YOCO_ERR_NULL_POINTER")
+
+    # A workspace that is given but too small for a call that uses it is an
+    # error before anything is enqueued; a misaligned one too.
+    c, lens = _cache()   # 2 sequences, 2 KV heads x 64
+    need = ctypes.c_size_t(0)
+    ncols = c.n_kv_heads * c.head_dim
+    assert L.yoco_project_workspace(4, 32, ncols, 2, 1, ctypes.byref(need)) == 0
+    if need.value:
+        assert _project(c, ws=FAKE, ws_bytes=need.value - 1) == _status("YOCO_ERR_WORKSPACE")
+        assert _project(c, ws=MIS, ws_bytes=need.value) == _status("YOCO_ERR_ALIGNMENT")
+        st = L.yoco_kv_append(FAKE, 1, 32, None, 1e-6, FAKE, FAKE, 1, ctypes.byref(c), FAKE, 16, None)
+        assert st == _status("YOCO_ERR_WORKSPACE")
+    assert lens.tolist() == [10, 20]
+    assert L.yoco_q_project(FAKE, 1, 4, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 1, FAKE, 16, None) == \
+        _status("YOCO_ERR_WORKSPACE")
+
+
+def test_default_softmax_scale():
+    L = _lib()
+    out = ctypes.c_float(0.0)
+    for dh in (64, 128):
+        assert L.yoco_default_softmax_scale(dh, ctypes.byref(out)) == 0
+        assert out.value == np.float32(1.0 / np.sqrt(dh))
+    assert L.yoco_default_softmax_scale(0, ctypes.byref(out)) == _status("YOCO_ERR_BAD_SHAPE")
+    assert L.yoco_default_softmax_scale(128, None) == _status("YOCO_ERR_NULL_POINTER")
+
+
+def test_binding_checks_shapes_before_the_library():
+    """The C ABI sees raw pointers only, so the binding checks every tensor
+    against the cache and the weights (host tensors: nothing reaches the
+    device)."""
+    import torch
+    import yoco_shared_kv_amd as y
+    k = torch.zeros(2, 16, 8, 64, dtype=torch.bfloat16)
+    cache = y.KVCache.wrap(k, k.clone(), [4, 4])
+    with pytest.raises(ValueError, match="q must be"):
+        y.cross_attn_decode(torch.zeros(3, 8, 64, dtype=torch.bfloat16), cache)
+    with pytest.raises(ValueError, match="q must be"):
+        y.cross_attn_decode(torch.zeros(2, 8, 128, dtype=torch.bfloat16), cache)
+    with pytest.raises(ValueError, match="out must"):
+        y.cross_attn_decode(torch.zeros(2, 8, 64, dtype=torch.bfloat16), cache, out=torch.zeros(2, 8, 32))
+    with pytest.raises(TypeError, match="out must"):
+        y.cross_attn_decode(torch.zeros(2, 8, 64, dtype=torch.bfloat16), cache,
+                            out=torch.zeros(2, 8, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="m_new must be"):
+        y.kv_append(cache, torch.zeros(1, 32), torch.zeros(32, 512), torch.zeros(32, 512))
+    with pytest.raises(ValueError, match="weight must"):
+        y.kv_append(cache, torch.zeros(2, 32), torch.zeros(32, 256), torch.zeros(32, 512))
+    with pytest.raises(ValueError, match="weight must"):
+        y.kv_project(cache, torch.zeros(5, 32), torch.zeros(32, 512), torch.zeros(16, 512))
+    with pytest.raises(ValueError, match="gain must"):
+        y.kv_project(cache, torch.zeros(5, 32), torch.zeros(32, 512), torch.zeros(32, 512), torch.ones(16))
+    with pytest.raises(ValueError, match="weight must"):
+        y.q_project(torch.zeros(2, 32), torch.zeros(32, 200), 4, 64)
+    with pytest.raises(ValueError, match="q must be"):
+        y.cross_attn_prefill(torch.zeros(4, 8, 128, dtype=torch.bfloat16), cache)
+
+
+def test_cache_descriptor_follows_a_replaced_length_array(monkeypatch):
+    """The descriptor keeps the length array it points into and is rebuilt
+    when ``len`` is a different array, even one at a reused address."""
+    import torch
+    import yoco_shared_kv_amd as y
+    monkeypatch.setattr(y, "_on_device", lambda *ts: None)
+    k = torch.zeros(2, 16, 8, 64, dtype=torch.bfloat16)
+    cache = y.KVCache.wrap(k, k.clone(), [4, 4])
+    addr = lambda s: ctypes.cast(s.len_host, ctypes.c_void_p).value
+    s1 = cache.struct()
+    assert addr(s1) == cache.len.ctypes.data
+    for _ in range(3):
+        cache.len = np.array([5, 6], dtype=np.int64)
+        s2 = cache.struct()
+        assert addr(s2) == cache.len.ctypes.data
+        assert cache.struct() is s2

@@ -8,11 +8,16 @@ products, which accumulate in fp32, so each gradient tensor must have a
 relative L2 error <= 5e-3 and no element off by more than 1% of the tensor's
 largest magnitude.
 
-Full size (causal N=32768, 24/8 heads, d_h=128): dQ on sampled rows; dK, dV
-exactly on the last 64 cache rows (every query row that sees them is then
-known); and over all rows the softmax identities sum_j dK_j = 0 (to 2e-2 of
-each column's L2 norm) and sum_j dV_j = sum of dO over the query rows and
-heads of each KV head.
+Full size (causal N=32768, 24/8 heads, d_h=128):
+* with the dense seeded dO: dQ on sampled rows; dK, dV exactly on the last 64
+  cache rows (every query row that sees them is then known); and over all
+  rows the softmax identities sum_j dK_j = 0 (to 2e-2 of each column's L2
+  norm) and sum_j dV_j = sum of dO over the query rows and heads of each KV
+  head;
+* with dO non-zero on 65 rows spread over all positions: dK and dV of every
+  cache row element by element (the zero rows add exactly nothing), dQ of
+  those rows, and exactly zero dQ elsewhere.
+Every element of dQ, dK and dV is also compared at N=4096 with 24/8 heads.
 """
 import math
 
@@ -172,3 +177,55 @@ def test_backward_full_size_sampled():
     # near 1; measured 7e-3.
     assert float((sk / col).max()) <= 2e-2, "sum_j dK_j is not ~0 relative to the column norms"
     assert_grad(sv, want, "sum_j dV_j vs sum of dO")
+
+
+def test_backward_full_size_sparse_upstream_every_cache_row():
+    """At the full size, dO is the seeded gradient on 65 query rows (one in
+    each 512-row stretch, plus N-1) and zero on every other row.  The rows
+    with zero dO add exactly nothing (dP = D = 0, so dS = 0 and P dO = 0),
+    so the oracle over those 65 rows alone gives the exact dK and dV of
+    every one of the 32768 cache rows: all of them are compared element by
+    element, and each cache row's sum runs over every query tile after it.
+    dQ of the 65 rows is compared too, and every other row's dQ must be
+    exactly zero."""
+    cfg = W.PREFILL_32K
+    c = W.make_prefill(**cfg)
+    n, hq, hkv, dh = cfg["n"], cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    print(f"backward full size, sparse upstream gradient, n={n}", flush=True)
+    cache, q, o, lse = _forward(c)
+    rng = np.random.default_rng(55)
+    rows = np.unique(np.concatenate([[int(rng.integers(b, b + 512)) for b in range(0, n, 512)], [n - 1]]))
+    dense = W.make_grad(n, hq, dh, seed=0)[0]
+    d_o = np.zeros_like(dense)
+    d_o[rows] = dense[rows]
+    d_q, d_k, d_v = y.cross_attn_prefill_bwd(q, o, to_dev(d_o), lse, cache)
+    torch.cuda.synchronize()
+    dq, dk, dv = to_stored(d_q), to_stored(d_k), to_stored(d_v)
+    rq, rk, rv = oracle.attention_bwd(c.q[rows], rows, c.k, c.v, d_o[rows], c.softmax_scale)
+    assert_grad(dk, rk, "dK, all cache rows")
+    assert_grad(dv, rv, "dV, all cache rows")
+    assert_grad(dq[rows], rq, "dQ of the rows with a gradient")
+    others = np.ones(n, dtype=bool)
+    others[rows] = False
+    assert not np.any(dq[others]), "dQ of a row with zero upstream gradient is not zero"
+    print(f"sparse upstream: {rows.size} rows; dK rel-L2 "
+          f"{np.linalg.norm(dk - rk) / np.linalg.norm(rk):.2e}, dV rel-L2 "
+          f"{np.linalg.norm(dv - rv) / np.linalg.norm(rv):.2e}", flush=True)
+
+
+def test_backward_4096_full_tensors():
+    """Every element of dQ, dK and dV at N=4096 with the 3B head layout
+    (24 query heads over 8 KV heads, d_h 128): 16 query tiles of 256 rows and
+    32 cache-row blocks of 128, so the dK/dV kernel's accumulation over many
+    query tiles is compared element by element."""
+    n, hq, hkv, dh = 4096, 24, 8, 128
+    c = W.make_prefill(n=n, n_q_heads=hq, n_kv_heads=hkv, head_dim=dh, seed=56)
+    print(f"backward full tensors n={n} hq={hq} hkv={hkv}", flush=True)
+    cache, q, o, lse = _forward(c)
+    d_o = W.make_grad(n, hq, dh, seed=56)[0]
+    d_q, d_k, d_v = y.cross_attn_prefill_bwd(q, o, to_dev(d_o), lse, cache)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_bwd(c.q, np.arange(n), c.k, c.v, d_o, c.softmax_scale)
+    assert_grad(to_stored(d_q), rq, "dQ")
+    assert_grad(to_stored(d_k), rk, "dK")
+    assert_grad(to_stored(d_v), rv, "dV")

@@ -123,7 +123,24 @@ def test_decode_parity(dtype, dh, hq, hkv, lens, rows):
     ks, vs, q = _decode_case(dtype, dh, hq, hkv, lens)
     cache = make_cache_from(ks, vs, max(lens) + 5, dtype)
     s = 1 / math.sqrt(dh)
-    o, lse = y.cross_attn_decode(to_dev(q), cache, s, rows_per_split=rows, want_lse=True)
+    n_seq = len(lens)
+    # Guard bands: the outputs are views into NaN-filled buffers with a row
+    # before and after, and the workspace is followed by a 64 KiB pattern;
+    # the decode must write only its [n_seq, H_q, d_h] and [n_seq, H_q]
+    # outputs and stay inside the workspace size the library reports.
+    o_buf = torch.full((n_seq + 2, hq, dh), float("nan"), dtype=torch.float32, device="cuda")
+    lse_buf = torch.full((n_seq + 2, hq), float("nan"), dtype=torch.float32, device="cuda")
+    ws_bytes = y.decode_workspace_bytes(cache, hq, rows)
+    guard = 64 * 1024
+    ws_buf = torch.zeros(ws_bytes + guard, dtype=torch.uint8, device="cuda")
+    ws_buf[ws_bytes:] = 0xA5
+    o, lse = y.cross_attn_decode(to_dev(q), cache, s, workspace=ws_buf[:ws_bytes], rows_per_split=rows,
+                                 out=o_buf[1:n_seq + 1], lse_out=lse_buf[1:n_seq + 1], want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.isnan(o_buf[0]).all() and torch.isnan(o_buf[n_seq + 1]).all(), "decode wrote outside o"
+    assert torch.isnan(lse_buf[0]).all() and torch.isnan(lse_buf[n_seq + 1]).all(), "decode wrote outside lse"
+    assert bool((ws_buf[ws_bytes:] == 0xA5).all()), "decode wrote past its workspace"
+    assert not bool(ws_buf[:64 * 1024].any()), "decode left an arrival counter non-zero"
     o, lse = to_stored(o), to_stored(lse)
     for b, L in enumerate(lens):
         ro, rl = orc().decode(q[b:b + 1], L, ks[b], vs[b], s, want_lse=True)
@@ -190,6 +207,10 @@ PREFILL_CASES = [
     (W.BF16, 128, 3, 1, 1000, 999, 1),
     (W.BF16, 64, 8, 2, 129, 0, 129),
     (W.BF16, 128, 4, 2, 900, 250, 130),
+    (W.BF16, 128, 12, 2, 333, 0, 333),      # group of 6
+    (W.BF16, 128, 48, 8, 300, 40, 260),     # group of 6 at 8 KV heads
+    (W.BF16, 128, 8, 1, 290, 30, 260),      # group of 8
+    (W.BF16, 64, 16, 2, 515, 0, 515),       # group of 8, head_dim 64
     (W.F32, 64, 4, 2, 300, 0, 300),
     (W.F32, 128, 2, 2, 200, 50, 100),
 ]
@@ -379,19 +400,21 @@ def test_q_project_bf16_parity():
     assert_projection_bf16(to_stored(q).reshape(33, -1), orc().project(x, wq), abs_terms, 3072, "Q^")
 
 
+@pytest.mark.parametrize("split_rows", [True, False], ids=["split-W", "strips"])
 @pytest.mark.parametrize("dtype,n,d", [(W.BF16, 1, 3072), (W.BF16, 5, 3072), (W.BF16, 13, 3072),
                                        (W.BF16, 16, 3072), (W.F32, 1, 256), (W.F32, 8, 256),
-                                       (W.F32, 30, 512), (W.BF16, 3, 8192)])
-def test_small_row_projection_parity(dtype, n, d):
-    """Few-row projections (generation-time append and per-token queries) run
-    on the matrix-vector kernel, in launches of up to 8 rows."""
+                                       (W.F32, 30, 512), (W.BF16, 3, 8192), (W.BF16, 32, 200)])
+def test_small_row_projection_parity(dtype, n, d, split_rows):
+    """Few-row projections (generation-time append and per-token queries), in
+    launches of up to 8 rows: with a workspace on the kernel that splits W's
+    rows over the whole chip, without one on the column-strip kernel."""
     p = W.make_project(n=n, d_model=d, dtype=dtype, unit_gain=False, seed=24)
     tdt = torch.bfloat16 if dtype == W.BF16 else torch.float32
     cache = y.KVCache(1, n + 7, 8, 128, tdt)
     cache.k.fill_(7.0)
     cache.v.fill_(7.0)
     y.kv_project(cache, to_dev(p.m), to_dev(p.w_k), to_dev(p.w_v), torch.from_numpy(p.gain).cuda(), p.eps,
-                 row_start=3)
+                 row_start=3, workspace=None if split_rows else False)
     k = to_stored(cache.k[0, 3:3 + n]).reshape(n, -1)
     v = to_stored(cache.v[0, 3:3 + n]).reshape(n, -1)
     rk = orc().project(p.m, p.w_k, p.gain, p.eps)

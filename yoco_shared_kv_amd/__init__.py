@@ -20,8 +20,9 @@ The functions mirror the C entry points:
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
-import math
+import threading
 from typing import Optional
 
 import numpy as np
@@ -33,7 +34,7 @@ from ._native import (YOCO_DECODE_COUNTER_BYTES, YOCO_DT_BF16, YOCO_DT_F32, KVCa
 __all__ = [
     "KVCache", "YocoError", "kv_project", "kv_append", "q_project", "cross_attn_prefill",
     "cross_attn_decode", "decode_workspace", "decode_workspace_bytes", "kv_cache_bytes",
-    "kv_cache_row_stride", "lib",
+    "kv_cache_row_stride", "lib", "project_workspace_bytes", "default_softmax_scale",
     "cross_attn_prefill_bwd", "prefill_bwd_workspace_bytes", "kv_project_bwd", "q_project_bwd",
     "project_bwd_workspace_bytes", "gret_prefill", "gret_decode", "gret_prefill_workspace_bytes",
 ]
@@ -67,6 +68,56 @@ def _on_device(*ts):
             raise ValueError("inputs must be device tensors")
 
 
+def _on(stream):
+    """Temporaries of a call are allocated (and zero-filled) on the stream
+    its kernels run on, so the fill is ordered before them and the caching
+    allocator does not hand the memory to other streams while they run."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
+def _check_shape(name: str, t: Optional[torch.Tensor], shape, dtype=None) -> None:
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _check_weights(d: int, ncols: int, gain, *ws) -> None:
+    for w in ws:
+        _check_shape("weight", w, (d, ncols))
+    _check_shape("gain", gain, (d,), torch.float32)
+
+
+# Few-row projection workspaces, one per (device, stream): calls on one
+# stream never overlap, and the library leaves the arrival counters zero
+# after each call, so a zero-filled buffer can be reused by every later call
+# on its stream.
+_scratch_lock = threading.Lock()
+_scratch: dict = {}
+
+
+def _stream_scratch(device: torch.device, stream, nbytes: int) -> Optional[torch.Tensor]:
+    if nbytes <= 0:
+        return None
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    key = (device.index if device.index is not None else torch.cuda.current_device(), s.cuda_stream)
+    with _scratch_lock:
+        buf = _scratch.get(key)
+        if buf is None or buf.numel() < nbytes:
+            with torch.cuda.stream(s):
+                buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+            _scratch[key] = buf
+        return buf
+
+
+def _ws_args(ws: Optional[torch.Tensor]):
+    if ws is None:
+        return None, 0
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
 class KVCache:
     """The one shared K^/V^ cache: k, v ``[n_seq, capacity, H_kv, d_h]`` on the
     device plus host lengths ``len`` (numpy int64, advanced by project/append).
@@ -89,6 +140,7 @@ class KVCache:
         self.row_stride = rs
         self._struct = None
         self._key = None
+        self._len_ref = None
 
     @classmethod
     def wrap(cls, k: torch.Tensor, v: torch.Tensor, lens) -> "KVCache":
@@ -111,13 +163,17 @@ class KVCache:
         obj.len = np.ascontiguousarray(np.asarray(lens, dtype=np.int64).reshape(obj.n_seq))
         obj._struct = None
         obj._key = None
+        obj._len_ref = None
         return obj
 
     def struct(self) -> KVCacheStruct:
         # The descriptor points at the tensors' storage and into ``len``; it is
         # rebuilt whenever one of them has been replaced.
-        key = (self.k.data_ptr(), self.v.data_ptr(), id(self.len), self.capacity, self.n_seq)
-        if self._struct is not None and self._key == key:
+        # ``len`` is compared by identity, and the descriptor keeps a reference
+        # to the array its len_host points into, so a replaced array can never
+        # be mistaken for the one the descriptor was built on.
+        key = (self.k.data_ptr(), self.v.data_ptr(), self.capacity, self.n_seq)
+        if self._struct is not None and self._key == key and self._len_ref is self.len:
             return self._struct
         _on_device(self.k, self.v)
         if self.len.dtype != np.int64 or not self.len.flags.c_contiguous or self.len.shape != (self.n_seq,):
@@ -132,8 +188,9 @@ class KVCache:
         s.head_dim = self.head_dim
         s.dtype = _dt(self.k)
         s.row_stride = self.row_stride
-        self._struct = s  # keep alive with the numpy buffer it points into
+        self._struct = s
         self._key = key
+        self._len_ref = self.len  # keeps the array len_host points into alive
         return s
 
 
@@ -153,54 +210,101 @@ def kv_cache_row_stride(n_kv_heads: int, head_dim: int, dtype: torch.dtype = tor
     return int(out.value)
 
 
+def project_workspace_bytes(n: int, d_model: int, n_cols: int, n_out: int,
+                            w_dtype: torch.dtype = torch.bfloat16) -> int:
+    """Workspace bytes of the few-row projection path (``yoco_project_workspace``;
+    0 when these shapes do not use it)."""
+    out = ctypes.c_size_t(0)
+    check(lib().yoco_project_workspace(n, d_model, n_cols, n_out, _DT.get(w_dtype, -1), ctypes.byref(out)))
+    return int(out.value)
+
+
+def default_softmax_scale(head_dim: int) -> float:
+    """The pages' softmax scale 1/sqrt(d_h) (``yoco_default_softmax_scale``)."""
+    out = ctypes.c_float(0.0)
+    check(lib().yoco_default_softmax_scale(head_dim, ctypes.byref(out)))
+    return float(out.value)
+
+
+def _proj_workspace(x: torch.Tensor, n: int, d: int, ncols: int, n_out: int, w: torch.Tensor, workspace, stream):
+    """Workspace of a projection call: the caller's tensor; None (the
+    default) for this stream's shared one when the call takes the few-row
+    path; False for none (few rows then run on the kernel that needs no
+    workspace)."""
+    if workspace is False:
+        return None
+    if workspace is not None:
+        return workspace
+    return _stream_scratch(x.device, stream, project_workspace_bytes(n, d, ncols, n_out, w.dtype))
+
+
 def kv_project(cache: KVCache, m: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor,
                gain: Optional[torch.Tensor] = None, eps: float = 1e-6, seq: int = 0,
-               row_start: int = 0, stream=None, rope_theta: Optional[float] = None) -> None:
+               row_start: int = 0, stream=None, rope_theta: Optional[float] = None,
+               workspace: Optional[torch.Tensor] = None) -> None:
     """RMSNorm(M) W_K and RMSNorm(M) W_V into cache rows [row_start, row_start+n);
     with ``rope_theta``, K^ row r is rotated at position row_start + r."""
-    _on_device(m, w_k, w_v, gain)
+    if m.dim() != 2:
+        raise ValueError("m must be [n, d_model]")
+    n, d = m.shape
+    ncols = cache.n_kv_heads * cache.head_dim
     if w_k.dtype != w_v.dtype:
         raise TypeError("w_k and w_v must share a dtype")
-    n, d = m.shape
+    _check_weights(d, ncols, gain, w_k, w_v)
+    _on_device(m, w_k, w_v, gain)
     s = cache.struct()
+    ws, ws_bytes = _ws_args(_proj_workspace(m, n, d, ncols, 2, w_k, workspace, stream))
     args = (_ptr(m), _dt(m), n, d, _ptr(gain), eps, _ptr(w_k), _ptr(w_v), _dt(w_k), ctypes.byref(s), seq, row_start)
     if rope_theta is None:
-        check(lib().yoco_kv_project(*args, _stream(stream)))
+        check(lib().yoco_kv_project(*args, ws, ws_bytes, _stream(stream)))
     else:
-        check(lib().yoco_kv_project_rope(*args, float(rope_theta), _stream(stream)))
+        check(lib().yoco_kv_project_rope(*args, float(rope_theta), ws, ws_bytes, _stream(stream)))
 
 
 def kv_append(cache: KVCache, m_new: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor,
               gain: Optional[torch.Tensor] = None, eps: float = 1e-6, stream=None,
-              rope_theta: Optional[float] = None) -> None:
+              rope_theta: Optional[float] = None, workspace: Optional[torch.Tensor] = None) -> None:
     """Project one new row per sequence (m_new ``[n_seq, d_model]``) and append it;
     with ``rope_theta``, the new K^ row of sequence b is rotated at position len[b]."""
-    _on_device(m_new, w_k, w_v, gain)
+    if m_new.dim() != 2 or m_new.shape[0] != cache.n_seq:
+        raise ValueError(f"m_new must be [{cache.n_seq}, d_model] (one row per sequence), got {tuple(m_new.shape)}")
+    d = m_new.shape[1]
+    ncols = cache.n_kv_heads * cache.head_dim
     if w_k.dtype != w_v.dtype:
         raise TypeError("w_k and w_v must share a dtype")
+    _check_weights(d, ncols, gain, w_k, w_v)
+    _on_device(m_new, w_k, w_v, gain)
     s = cache.struct()
-    args = (_ptr(m_new), _dt(m_new), m_new.shape[1], _ptr(gain), eps, _ptr(w_k), _ptr(w_v), _dt(w_k),
-            ctypes.byref(s))
+    ws, ws_bytes = _ws_args(_proj_workspace(m_new, cache.n_seq, d, ncols, 2, w_k, workspace, stream))
+    args = (_ptr(m_new), _dt(m_new), d, _ptr(gain), eps, _ptr(w_k), _ptr(w_v), _dt(w_k), ctypes.byref(s))
     if rope_theta is None:
-        check(lib().yoco_kv_append(*args, _stream(stream)))
+        check(lib().yoco_kv_append(*args, ws, ws_bytes, _stream(stream)))
     else:
-        check(lib().yoco_kv_append_rope(*args, float(rope_theta), _stream(stream)))
+        check(lib().yoco_kv_append_rope(*args, float(rope_theta), ws, ws_bytes, _stream(stream)))
 
 
 def q_project(x: torch.Tensor, w_q: torch.Tensor, n_q_heads: int, head_dim: int,
               gain: Optional[torch.Tensor] = None, eps: float = 1e-6,
               out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
               stream=None, rope_theta: Optional[float] = None, positions=None,
-              pos0: int = 0) -> torch.Tensor:
+              pos0: int = 0, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """RMSNorm_l(X) W_Q^l -> ``[n, H_q, d_h]``; with ``rope_theta``, row r is
     rotated at position ``positions[r]`` (host sequence) or pos0 + r."""
-    _on_device(x, w_q, gain)
+    if x.dim() != 2:
+        raise ValueError("x must be [n, d_model]")
     n, d = x.shape
-    if out is None:
-        out = torch.empty((n, n_q_heads, head_dim), dtype=out_dtype or x.dtype, device=x.device)
+    ncols = n_q_heads * head_dim
+    _check_weights(d, ncols, gain, w_q)
+    if out is not None:
+        _check_shape("out", out, (n, n_q_heads, head_dim))
+    _on_device(x, w_q, gain, out)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((n, n_q_heads, head_dim), dtype=out_dtype or x.dtype, device=x.device)
+        ws, ws_bytes = _ws_args(_proj_workspace(x, n, d, ncols, 1, w_q, workspace, stream))
     args = (_ptr(x), _dt(x), n, d, _ptr(gain), eps, _ptr(w_q), _dt(w_q), n_q_heads, head_dim, _ptr(out), _dt(out))
     if rope_theta is None:
-        check(lib().yoco_q_project(*args, _stream(stream)))
+        check(lib().yoco_q_project(*args, ws, ws_bytes, _stream(stream)))
     else:
         pos = None
         if positions is not None:
@@ -208,26 +312,40 @@ def q_project(x: torch.Tensor, w_q: torch.Tensor, n_q_heads: int, head_dim: int,
             if pos.shape != (n,):
                 raise ValueError(f"positions must hold {n} entries")
         pos_ptr = None if pos is None else pos.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
-        check(lib().yoco_q_project_rope(*args, pos_ptr, int(pos0), float(rope_theta), _stream(stream)))
+        check(lib().yoco_q_project_rope(*args, pos_ptr, int(pos0), float(rope_theta), ws, ws_bytes,
+                                        _stream(stream)))
     return out
+
+
+def _scale(softmax_scale, head_dim: int) -> float:
+    return default_softmax_scale(head_dim) if softmax_scale is None else float(softmax_scale)
 
 
 def cross_attn_prefill(q: torch.Tensor, cache: KVCache, seq: int = 0, q_start: int = 0,
                        softmax_scale: Optional[float] = None,
                        out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None,
-                       want_lse: bool = False, stream=None):
+                       want_lse: bool = False, stream=None, lse_out: Optional[torch.Tensor] = None):
     """Causal attention of q ``[t, H_q, d_h]`` (row i at position q_start+i)
-    over sequence ``seq`` of the shared cache.  Returns o (and lse)."""
-    _on_device(q)
+    over sequence ``seq`` of the shared cache.  Returns o (and lse).  The
+    scale defaults to the library's 1/sqrt(d_h)."""
+    if q.dim() != 3 or q.shape[2] != cache.head_dim:
+        raise ValueError(f"q must be [t, H_q, {cache.head_dim}], got {tuple(q.shape)}")
     t, hq, dh = q.shape
-    scale = 1.0 / math.sqrt(dh) if softmax_scale is None else softmax_scale
-    if out is None:
-        out = torch.empty((t, hq, dh), dtype=out_dtype, device=q.device)
-    lse = torch.empty((t, hq), dtype=torch.float32, device=q.device) if want_lse else None
+    if out is not None:
+        _check_shape("out", out, (t, hq, dh))
+    _check_shape("lse_out", lse_out, (t, hq), torch.float32)
+    _on_device(q, out, lse_out)
+    scale = _scale(softmax_scale, dh)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((t, hq, dh), dtype=out_dtype, device=q.device)
+        lse = lse_out
+        if lse is None and want_lse:
+            lse = torch.empty((t, hq), dtype=torch.float32, device=q.device)
     s = cache.struct()
     check(lib().yoco_cross_attn_prefill(_ptr(q), _dt(q), q_start, t, hq, ctypes.byref(s), seq,
                                         scale, _ptr(out), _dt(out), _ptr(lse), _stream(stream)))
-    return (out, lse) if want_lse else out
+    return (out, lse) if (want_lse or lse_out is not None) else out
 
 
 def prefill_bwd_workspace_bytes(t: int, n_q_heads: int) -> int:
@@ -246,15 +364,20 @@ def cross_attn_prefill_bwd(q: torch.Tensor, o: torch.Tensor, d_o: torch.Tensor, 
     not given), so passing the same tensors for every cross layer sums the
     layers' shares of the shared cache's gradient."""
     _on_device(q, o, d_o, lse)
+    if q.dim() != 3 or q.shape[2] != cache.head_dim:
+        raise ValueError(f"q must be [t, H_q, {cache.head_dim}], got {tuple(q.shape)}")
     t, hq, dh = q.shape
-    scale = 1.0 / math.sqrt(dh) if softmax_scale is None else softmax_scale
+    _check_shape("o", o, (t, hq, dh))
+    _check_shape("d_o", d_o, (t, hq, dh))
+    scale = _scale(softmax_scale, dh)
     rows = q_start + t
-    if d_q is None:
-        d_q = torch.empty((t, hq, dh), dtype=torch.float32, device=q.device)
-    if d_k is None:
-        d_k = torch.zeros((rows, cache.n_kv_heads, dh), dtype=torch.float32, device=q.device)
-    if d_v is None:
-        d_v = torch.zeros((rows, cache.n_kv_heads, dh), dtype=torch.float32, device=q.device)
+    with _on(stream):
+        if d_q is None:
+            d_q = torch.empty((t, hq, dh), dtype=torch.float32, device=q.device)
+        if d_k is None:
+            d_k = torch.zeros((rows, cache.n_kv_heads, dh), dtype=torch.float32, device=q.device)
+        if d_v is None:
+            d_v = torch.zeros((rows, cache.n_kv_heads, dh), dtype=torch.float32, device=q.device)
     for name, x in (("d_q", d_q), ("d_k", d_k), ("d_v", d_v)):
         if x.dtype != torch.float32 or not x.is_contiguous():
             raise TypeError(f"{name} must be a contiguous float32 tensor")
@@ -264,7 +387,8 @@ def cross_attn_prefill_bwd(q: torch.Tensor, o: torch.Tensor, d_o: torch.Tensor, 
         raise ValueError("lse must be the forward's float32 [t, H_q]")
     nbytes = prefill_bwd_workspace_bytes(t, hq)
     if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+        with _on(stream):
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     s = cache.struct()
     check(lib().yoco_cross_attn_prefill_bwd(_ptr(q), _ptr(o), _dt(o), _ptr(d_o), _ptr(lse), q_start, t, hq,
                                             ctypes.byref(s), seq, scale, _ptr(d_q), _ptr(d_k), _ptr(d_v),
@@ -279,14 +403,15 @@ def project_bwd_workspace_bytes(n: int, d_model: int, n_cols: int, n_out: int) -
     return int(out.value)
 
 
-def _grad_buffers(x, ws_bytes, weights, d_x, d_ws, d_gain, want_gain, workspace):
+def _grad_buffers(x, ws_bytes, weights, d_x, d_ws, d_gain, want_gain, workspace, stream):
     n, d = x.shape
-    if d_x is None:
-        d_x = torch.empty((n, d), dtype=torch.float32, device=x.device)
-    d_ws = [torch.zeros(w.shape, dtype=torch.float32, device=x.device) if g is None else g
-            for w, g in zip(weights, d_ws)]
-    if d_gain is None and want_gain:
-        d_gain = torch.zeros(d, dtype=torch.float32, device=x.device)
+    with _on(stream):
+        if d_x is None:
+            d_x = torch.empty((n, d), dtype=torch.float32, device=x.device)
+        d_ws = [torch.zeros(w.shape, dtype=torch.float32, device=x.device) if g is None else g
+                for w, g in zip(weights, d_ws)]
+        if d_gain is None and want_gain:
+            d_gain = torch.zeros(d, dtype=torch.float32, device=x.device)
     for name, t in [("d_x", d_x), ("d_gain", d_gain)] + [("d_w", g) for g in d_ws]:
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
             raise TypeError(f"{name} must be a contiguous float32 tensor")
@@ -295,7 +420,8 @@ def _grad_buffers(x, ws_bytes, weights, d_x, d_ws, d_gain, want_gain, workspace)
     if d_gain is not None and d_gain.shape != (d,):
         raise ValueError("d_gain must be [d_model]")
     if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+        with _on(stream):
+            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
     return d_x, d_ws, d_gain, workspace
 
 
@@ -317,7 +443,7 @@ def kv_project_bwd(m: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor, dz_k: 
         raise ValueError(f"dz_k, dz_v must hold [n, {ncols}] values")
     ws_bytes = project_bwd_workspace_bytes(n, d, ncols, 2)
     d_m, (d_w_k, d_w_v), d_gain, workspace = _grad_buffers(m, ws_bytes, (w_k, w_v), d_m, (d_w_k, d_w_v), d_gain,
-                                                           want_gain, workspace)
+                                                           want_gain, workspace, stream)
     check(lib().yoco_kv_project_bwd(_ptr(m), _dt(m), n, d, _ptr(gain), eps, _ptr(w_k), _ptr(w_v), _dt(w_k),
                                     n_kv_heads, head_dim, _ptr(dz_k), _ptr(dz_v), _dt(dz_k), _ptr(d_m),
                                     _ptr(d_w_k), _ptr(d_w_v), _ptr(d_gain), _ptr(workspace),
@@ -338,7 +464,7 @@ def q_project_bwd(x: torch.Tensor, w_q: torch.Tensor, dz_q: torch.Tensor, n_q_he
         raise ValueError(f"dz_q must hold [n, {ncols}] values")
     ws_bytes = project_bwd_workspace_bytes(n, d, ncols, 1)
     d_x, (d_w_q,), d_gain, workspace = _grad_buffers(x, ws_bytes, (w_q,), d_x, (d_w_q,), d_gain, want_gain,
-                                                     workspace)
+                                                     workspace, stream)
     check(lib().yoco_q_project_bwd(_ptr(x), _dt(x), n, d, _ptr(gain), eps, _ptr(w_q), _dt(w_q), n_q_heads,
                                    head_dim, _ptr(dz_q), _dt(dz_q), _ptr(d_x), _ptr(d_w_q), _ptr(d_gain),
                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -364,12 +490,13 @@ def gret_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate_logits:
         raise ValueError("q, k, v must be matching [n, H, D] tensors")
     if gate_logits.dtype != torch.float32 or gate_logits.shape != (n, heads):
         raise ValueError("gate_logits must be float32 [n, H]")
-    if out is None:
-        out = torch.empty((n, heads, dh), dtype=torch.float32, device=q.device)
-    state_out = torch.empty((heads, dh, dh), dtype=torch.float32, device=q.device) if want_state else None
     nbytes = gret_prefill_workspace_bytes(n, heads, dh, q.dtype)
-    if workspace is None and nbytes > 0:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((n, heads, dh), dtype=torch.float32, device=q.device)
+        state_out = torch.empty((heads, dh, dh), dtype=torch.float32, device=q.device) if want_state else None
+        if workspace is None and nbytes > 0:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(lib().yoco_gret_prefill(_ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(gate_logits), float(tau), n, heads, dh,
                                   _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(workspace), ws_bytes,
@@ -386,7 +513,8 @@ def gret_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate_logits: 
     if state.dtype != torch.float32 or state.shape != (b, heads, dh, dh):
         raise ValueError("state must be float32 [B, H, D, D]")
     if out is None:
-        out = torch.empty((b, heads, dh), dtype=torch.float32, device=q.device)
+        with _on(stream):
+            out = torch.empty((b, heads, dh), dtype=torch.float32, device=q.device)
     check(lib().yoco_gret_decode(_ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(gate_logits), float(tau), b, heads, dh,
                                  _ptr(state), _ptr(out), _stream(stream)))
     return out
@@ -400,27 +528,37 @@ def decode_workspace_bytes(cache: KVCache, n_q_heads: int, rows_per_split: int =
     return int(out.value)
 
 
-def decode_workspace(cache: KVCache, n_q_heads: int, rows_per_split: int = 0) -> torch.Tensor:
+def decode_workspace(cache: KVCache, n_q_heads: int, rows_per_split: int = 0, stream=None) -> torch.Tensor:
     """A zero-filled workspace large enough for any length up to capacity."""
     nbytes = decode_workspace_bytes(cache, n_q_heads, rows_per_split)
-    return torch.zeros(nbytes, dtype=torch.uint8, device=cache.k.device)
+    with _on(stream):
+        return torch.zeros(nbytes, dtype=torch.uint8, device=cache.k.device)
 
 
 def cross_attn_decode(q: torch.Tensor, cache: KVCache, softmax_scale: Optional[float] = None,
                       workspace: Optional[torch.Tensor] = None, rows_per_split: int = 0,
-                      out: Optional[torch.Tensor] = None, want_lse: bool = False, stream=None):
+                      out: Optional[torch.Tensor] = None, want_lse: bool = False, stream=None,
+                      lse_out: Optional[torch.Tensor] = None):
     """One decode step of one cross layer: q ``[n_seq, H_q, d_h]`` at position
-    len-1 of every sequence.  Returns o ``[n_seq, H_q, d_h]`` fp32 (and lse)."""
-    _on_device(q)
+    len-1 of every sequence.  Returns o ``[n_seq, H_q, d_h]`` fp32 (and lse).
+    The scale defaults to the library's 1/sqrt(d_h)."""
+    if q.dim() != 3 or q.shape[0] != cache.n_seq or q.shape[2] != cache.head_dim:
+        raise ValueError(f"q must be [{cache.n_seq}, H_q, {cache.head_dim}], got {tuple(q.shape)}")
     n_seq, hq, dh = q.shape
-    scale = 1.0 / math.sqrt(dh) if softmax_scale is None else softmax_scale
-    if workspace is None:
-        workspace = decode_workspace(cache, hq, rows_per_split)
-    if out is None:
-        out = torch.empty((n_seq, hq, dh), dtype=torch.float32, device=q.device)
-    lse = torch.empty((n_seq, hq), dtype=torch.float32, device=q.device) if want_lse else None
+    _check_shape("out", out, (n_seq, hq, dh), torch.float32)
+    _check_shape("lse_out", lse_out, (n_seq, hq), torch.float32)
+    _on_device(q, out, lse_out, workspace)
+    scale = _scale(softmax_scale, dh)
+    with _on(stream):
+        if workspace is None:
+            workspace = decode_workspace(cache, hq, rows_per_split)
+        if out is None:
+            out = torch.empty((n_seq, hq, dh), dtype=torch.float32, device=q.device)
+        lse = lse_out
+        if lse is None and want_lse:
+            lse = torch.empty((n_seq, hq), dtype=torch.float32, device=q.device)
     s = cache.struct()
     check(lib().yoco_cross_attn_decode(_ptr(q), _dt(q), hq, ctypes.byref(s), scale, _ptr(out),
-                                       _ptr(lse), _ptr(workspace), workspace.numel(),
+                                       _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                        rows_per_split, _stream(stream)))
-    return (out, lse) if want_lse else out
+    return (out, lse) if (want_lse or lse_out is not None) else out

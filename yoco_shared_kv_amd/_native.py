@@ -16,6 +16,7 @@ YOCO_DT_F32 = 0
 YOCO_DT_BF16 = 1
 YOCO_MAX_SEQ = 256
 YOCO_DECODE_COUNTER_BYTES = YOCO_MAX_SEQ * 64 * 4
+YOCO_PROJECT_COUNTER_BYTES = 4096
 
 STATUS = {
     0: "YOCO_OK", 1: "YOCO_ERR_NULL_POINTER", 2: "YOCO_ERR_BAD_SHAPE", 3: "YOCO_ERR_BAD_DTYPE",
@@ -62,18 +63,23 @@ def _declare(lib):
     lib.yoco_kv_cache_row_stride.restype = st
     lib.yoco_kv_cache_row_stride.argtypes = [i32, i32, i32, ctypes.POINTER(i64)]
     lib.yoco_kv_project.restype = st
-    lib.yoco_kv_project.argtypes = [vp, i32, i64, i32, vp, f32, vp, vp, i32, cp, i32, i64, vp]
+    lib.yoco_kv_project.argtypes = [vp, i32, i64, i32, vp, f32, vp, vp, i32, cp, i32, i64, vp, sz, vp]
     lib.yoco_kv_append.restype = st
-    lib.yoco_kv_append.argtypes = [vp, i32, i32, vp, f32, vp, vp, i32, cp, vp]
+    lib.yoco_kv_append.argtypes = [vp, i32, i32, vp, f32, vp, vp, i32, cp, vp, sz, vp]
     lib.yoco_q_project.restype = st
-    lib.yoco_q_project.argtypes = [vp, i32, i64, i32, vp, f32, vp, i32, i32, i32, vp, i32, vp]
+    lib.yoco_q_project.argtypes = [vp, i32, i64, i32, vp, f32, vp, i32, i32, i32, vp, i32, vp, sz, vp]
+    lib.yoco_project_workspace.restype = st
+    lib.yoco_project_workspace.argtypes = [i64, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.yoco_default_softmax_scale.restype = st
+    lib.yoco_default_softmax_scale.argtypes = [i32, ctypes.POINTER(f32)]
     f64 = ctypes.c_double
     lib.yoco_kv_project_rope.restype = st
-    lib.yoco_kv_project_rope.argtypes = [vp, i32, i64, i32, vp, f32, vp, vp, i32, cp, i32, i64, f64, vp]
+    lib.yoco_kv_project_rope.argtypes = [vp, i32, i64, i32, vp, f32, vp, vp, i32, cp, i32, i64, f64, vp, sz, vp]
     lib.yoco_kv_append_rope.restype = st
-    lib.yoco_kv_append_rope.argtypes = [vp, i32, i32, vp, f32, vp, vp, i32, cp, f64, vp]
+    lib.yoco_kv_append_rope.argtypes = [vp, i32, i32, vp, f32, vp, vp, i32, cp, f64, vp, sz, vp]
     lib.yoco_q_project_rope.restype = st
-    lib.yoco_q_project_rope.argtypes = [vp, i32, i64, i32, vp, f32, vp, i32, i32, i32, vp, i32, vp, i64, f64, vp]
+    lib.yoco_q_project_rope.argtypes = [vp, i32, i64, i32, vp, f32, vp, i32, i32, i32, vp, i32, vp, i64, f64, vp,
+                                        sz, vp]
     lib.yoco_cross_attn_prefill.restype = st
     lib.yoco_cross_attn_prefill.argtypes = [vp, i32, i64, i64, i32, cp, i32, f32, vp, i32, vp, vp]
     lib.yoco_cross_attn_prefill_bwd_workspace.restype = st

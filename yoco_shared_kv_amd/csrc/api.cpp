@@ -248,6 +248,35 @@ yoco_status check_rope(const RopeSpec &r) {
   return YOCO_OK;
 }
 
+// The few-row path (project_rows.hip) runs when the caller passes a
+// workspace and the shapes allow it; without a workspace the strip kernel of
+// project.hip takes the same rows.  A workspace that is given but too small
+// for a call that would use it is an error.
+struct RowsChoice {
+  bool use = false;
+  yoco::ProjRowsPlan plan{};
+};
+
+yoco_status choose_rows_path(int64_t n, int32_t d, int32_t ncols, int32_t n_out, int32_t w_dtype,
+                             const void *workspace, size_t workspace_bytes, RowsChoice *c) {
+  c->use = false;
+  if (check_aligned({{workspace, "workspace"}}, 16) != YOCO_OK) return YOCO_ERR_ALIGNMENT;
+  if (workspace == nullptr || n < 1 || n > yoco::kProjRowsMaxRows) return YOCO_OK;
+  if (!yoco::project_rows_plan(d, ncols, n_out, w_dtype, &c->plan)) return YOCO_OK;
+  const size_t need = yoco::project_rows_workspace_bytes(c->plan);
+  if (workspace_bytes < need)
+    return fail(YOCO_ERR_WORKSPACE, "workspace %zu bytes < %zu (yoco_project_workspace)", workspace_bytes, need);
+  c->use = true;
+  return YOCO_OK;
+}
+
+yoco_status launch_projection(const yoco::ProjArgs &a, const RowsChoice &rows, int x_dt, int w_dt, int o_dt,
+                              void *workspace, void *stream, const char *what) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (rows.use) return launched(yoco::launch_project_rows(a, rows.plan, x_dt, w_dt, o_dt, workspace, s), what);
+  return launched(yoco::launch_project(a, x_dt, w_dt, o_dt, s), what);
+}
+
 void set_rope(yoco::ProjArgs &a, const RopeSpec &r, int head_dim) {
   if (r.theta == 0.0) return;
   a.rope_out = 0;
@@ -258,7 +287,7 @@ void set_rope(yoco::ProjArgs &a, const RopeSpec &r, int head_dim) {
 yoco_status kv_project_impl(const void *m, int32_t m_dtype, int64_t n, int32_t d_model, const float *gain,
                             float eps, const void *w_k, const void *w_v, int32_t w_dtype,
                             yoco_kv_cache *cache, int32_t seq, int64_t row_start, const RopeSpec &rope,
-                            void *stream) {
+                            void *workspace, size_t workspace_bytes, void *stream) {
   yoco_status st = check_cache(cache);
   if (st != YOCO_OK) return st;
   if (m == nullptr || w_k == nullptr || w_v == nullptr) return fail(YOCO_ERR_NULL_POINTER, "m, w_k or w_v is NULL");
@@ -271,6 +300,10 @@ yoco_status kv_project_impl(const void *m, int32_t m_dtype, int64_t n, int32_t d
   if (n < 0 || row_start < 0 || row_start > cache->seq_capacity - n)
     return fail(YOCO_ERR_OUT_OF_RANGE, "rows [%lld, %lld) outside capacity %lld", (long long)row_start,
                 (long long)(row_start + n), (long long)cache->seq_capacity);
+  RowsChoice rows;
+  if ((st = choose_rows_path(n, d_model, cache->n_kv_heads * cache->head_dim, 2, w_dtype, workspace,
+                             workspace_bytes, &rows)) != YOCO_OK)
+    return st;
   if (n == 0) return ok();
   if ((st = check_device()) != YOCO_OK) return st;
 
@@ -291,8 +324,7 @@ yoco_status kv_project_impl(const void *m, int32_t m_dtype, int64_t n, int32_t d
   a.eps = eps;
   set_rope(a, rope, cache->head_dim);  // K^ only; row r at position row_start + r
   a.pos_base = row_start;
-  st = launched(yoco::launch_project(a, m_dtype, w_dtype, cache->dtype, static_cast<hipStream_t>(stream)),
-                "kv_project");
+  st = launch_projection(a, rows, m_dtype, w_dtype, cache->dtype, workspace, stream, "kv_project");
   if (st != YOCO_OK) return st;
   if (cache->len_host[seq] < row_start + n) cache->len_host[seq] = row_start + n;
   return ok();
@@ -300,7 +332,7 @@ yoco_status kv_project_impl(const void *m, int32_t m_dtype, int64_t n, int32_t d
 
 yoco_status kv_append_impl(const void *m_new, int32_t m_dtype, int32_t d_model, const float *gain, float eps,
                            const void *w_k, const void *w_v, int32_t w_dtype, yoco_kv_cache *cache,
-                           const RopeSpec &rope, void *stream) {
+                           const RopeSpec &rope, void *workspace, size_t workspace_bytes, void *stream) {
   yoco_status st = check_cache(cache);
   if (st != YOCO_OK) return st;
   if (m_new == nullptr || w_k == nullptr || w_v == nullptr)
@@ -316,6 +348,10 @@ yoco_status kv_append_impl(const void *m_new, int32_t m_dtype, int32_t d_model, 
       return fail(YOCO_ERR_OUT_OF_RANGE, "sequence %d: length %lld leaves no room under capacity %lld", b,
                   (long long)len, (long long)cache->seq_capacity);
   }
+  RowsChoice rows;
+  if ((st = choose_rows_path(cache->n_seq, d_model, cache->n_kv_heads * cache->head_dim, 2, w_dtype, workspace,
+                             workspace_bytes, &rows)) != YOCO_OK)
+    return st;
   if ((st = check_device()) != YOCO_OK) return st;
 
   yoco::ProjArgs a{};
@@ -337,8 +373,7 @@ yoco_status kv_append_impl(const void *m_new, int32_t m_dtype, int32_t d_model, 
   set_rope(a, rope, cache->head_dim);  // the new row of sequence b sits at position len_b
   a.pos_indexed = 1;
   a.pos_stride = cache->seq_capacity;
-  st = launched(yoco::launch_project(a, m_dtype, w_dtype, cache->dtype, static_cast<hipStream_t>(stream)),
-                "kv_append");
+  st = launch_projection(a, rows, m_dtype, w_dtype, cache->dtype, workspace, stream, "kv_append");
   if (st != YOCO_OK) return st;
   for (int b = 0; b < cache->n_seq; ++b) cache->len_host[b] += 1;
   return ok();
@@ -346,7 +381,8 @@ yoco_status kv_append_impl(const void *m_new, int32_t m_dtype, int32_t d_model, 
 
 yoco_status q_project_impl(const void *x, int32_t x_dtype, int64_t n, int32_t d_model, const float *gain,
                            float eps, const void *w_q, int32_t w_dtype, int32_t n_q_heads, int32_t head_dim,
-                           void *q_out, int32_t q_dtype, const RopeSpec &rope, void *stream) {
+                           void *q_out, int32_t q_dtype, const RopeSpec &rope, void *workspace,
+                           size_t workspace_bytes, void *stream) {
   if (x == nullptr || w_q == nullptr || q_out == nullptr) return fail(YOCO_ERR_NULL_POINTER, "x, w_q or q_out is NULL");
   if (check_aligned({{x, "x"}, {w_q, "w_q"}, {gain, "gain"}, {q_out, "q_out"}}, 16) != YOCO_OK)
     return YOCO_ERR_ALIGNMENT;
@@ -369,6 +405,10 @@ yoco_status q_project_impl(const void *x, int32_t x_dtype, int64_t n, int32_t d_
       return fail(YOCO_ERR_OUT_OF_RANGE, "pos0 %lld is negative", (long long)rope.pos0);
     }
   }
+  RowsChoice rows;
+  if ((st = choose_rows_path(n, d_model, n_q_heads * head_dim, 1, w_dtype, workspace, workspace_bytes, &rows)) !=
+      YOCO_OK)
+    return st;
   if (n == 0) return ok();
   if ((st = check_device()) != YOCO_OK) return st;
 
@@ -396,64 +436,87 @@ yoco_status q_project_impl(const void *x, int32_t x_dtype, int64_t n, int32_t d_
   } else {
     a.pos_base = rope.pos0;
   }
-  return launched(yoco::launch_project(a, x_dtype, w_dtype, q_dtype, static_cast<hipStream_t>(stream)),
-                  "q_project");
+  return launch_projection(a, rows, x_dtype, w_dtype, q_dtype, workspace, stream, "q_project");
 }
 
 }  // namespace
 
 extern "C" {
 
+yoco_status yoco_project_workspace(int64_t n, int32_t d_model, int32_t n_cols, int32_t n_out, int32_t w_dtype,
+                                   size_t *bytes) {
+  if (bytes == nullptr) return fail(YOCO_ERR_NULL_POINTER, "bytes is NULL");
+  if (n < 0 || d_model < 1 || n_cols < 1 || (n_out != 1 && n_out != 2))
+    return fail(YOCO_ERR_BAD_SHAPE, "n %lld, d_model %d, n_cols %d, n_out %d", (long long)n, d_model, n_cols, n_out);
+  if (!dtype_ok(w_dtype)) return fail(YOCO_ERR_BAD_DTYPE, "w dtype %d unknown", w_dtype);
+  yoco::ProjRowsPlan plan{};
+  *bytes = (n >= 1 && n <= yoco::kProjRowsMaxRows && yoco::project_rows_plan(d_model, n_cols, n_out, w_dtype, &plan))
+               ? yoco::project_rows_workspace_bytes(plan)
+               : 0;
+  return ok();
+}
+
+yoco_status yoco_default_softmax_scale(int32_t head_dim, float *scale) {
+  if (scale == nullptr) return fail(YOCO_ERR_NULL_POINTER, "scale is NULL");
+  if (head_dim < 1) return fail(YOCO_ERR_BAD_SHAPE, "head_dim %d < 1", head_dim);
+  *scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(head_dim)));
+  return ok();
+}
+
 yoco_status yoco_kv_project(const void *m, int32_t m_dtype, int64_t n, int32_t d_model, const float *gain,
                             float eps, const void *w_k, const void *w_v, int32_t w_dtype,
-                            yoco_kv_cache *cache, int32_t seq, int64_t row_start, void *stream) {
+                            yoco_kv_cache *cache, int32_t seq, int64_t row_start, void *workspace,
+                            size_t workspace_bytes, void *stream) {
   return kv_project_impl(m, m_dtype, n, d_model, gain, eps, w_k, w_v, w_dtype, cache, seq, row_start, RopeSpec{},
-                         stream);
+                         workspace, workspace_bytes, stream);
 }
 
 yoco_status yoco_kv_project_rope(const void *m, int32_t m_dtype, int64_t n, int32_t d_model, const float *gain,
                                  float eps, const void *w_k, const void *w_v, int32_t w_dtype,
                                  yoco_kv_cache *cache, int32_t seq, int64_t row_start, double rope_theta,
-                                 void *stream) {
+                                 void *workspace, size_t workspace_bytes, void *stream) {
   RopeSpec r;
   r.theta = rope_theta;
   if (rope_theta == 0.0) return fail(YOCO_ERR_BAD_VALUE, "rope_theta must be finite and > 1");
-  return kv_project_impl(m, m_dtype, n, d_model, gain, eps, w_k, w_v, w_dtype, cache, seq, row_start, r, stream);
+  return kv_project_impl(m, m_dtype, n, d_model, gain, eps, w_k, w_v, w_dtype, cache, seq, row_start, r, workspace,
+                         workspace_bytes, stream);
 }
 
 yoco_status yoco_kv_append(const void *m_new, int32_t m_dtype, int32_t d_model, const float *gain, float eps,
                            const void *w_k, const void *w_v, int32_t w_dtype, yoco_kv_cache *cache,
-                           void *stream) {
-  return kv_append_impl(m_new, m_dtype, d_model, gain, eps, w_k, w_v, w_dtype, cache, RopeSpec{}, stream);
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  return kv_append_impl(m_new, m_dtype, d_model, gain, eps, w_k, w_v, w_dtype, cache, RopeSpec{}, workspace,
+                        workspace_bytes, stream);
 }
 
 yoco_status yoco_kv_append_rope(const void *m_new, int32_t m_dtype, int32_t d_model, const float *gain, float eps,
                                 const void *w_k, const void *w_v, int32_t w_dtype, yoco_kv_cache *cache,
-                                double rope_theta, void *stream) {
+                                double rope_theta, void *workspace, size_t workspace_bytes, void *stream) {
   RopeSpec r;
   r.theta = rope_theta;
   if (rope_theta == 0.0) return fail(YOCO_ERR_BAD_VALUE, "rope_theta must be finite and > 1");
-  return kv_append_impl(m_new, m_dtype, d_model, gain, eps, w_k, w_v, w_dtype, cache, r, stream);
+  return kv_append_impl(m_new, m_dtype, d_model, gain, eps, w_k, w_v, w_dtype, cache, r, workspace, workspace_bytes,
+                        stream);
 }
 
 yoco_status yoco_q_project(const void *x, int32_t x_dtype, int64_t n, int32_t d_model, const float *gain,
                            float eps, const void *w_q, int32_t w_dtype, int32_t n_q_heads, int32_t head_dim,
-                           void *q_out, int32_t q_dtype, void *stream) {
+                           void *q_out, int32_t q_dtype, void *workspace, size_t workspace_bytes, void *stream) {
   return q_project_impl(x, x_dtype, n, d_model, gain, eps, w_q, w_dtype, n_q_heads, head_dim, q_out, q_dtype,
-                        RopeSpec{}, stream);
+                        RopeSpec{}, workspace, workspace_bytes, stream);
 }
 
 yoco_status yoco_q_project_rope(const void *x, int32_t x_dtype, int64_t n, int32_t d_model, const float *gain,
                                 float eps, const void *w_q, int32_t w_dtype, int32_t n_q_heads, int32_t head_dim,
                                 void *q_out, int32_t q_dtype, const int64_t *pos_host, int64_t pos0,
-                                double rope_theta, void *stream) {
+                                double rope_theta, void *workspace, size_t workspace_bytes, void *stream) {
   RopeSpec r;
   r.theta = rope_theta;
   r.pos_host = pos_host;
   r.pos0 = pos0;
   if (rope_theta == 0.0) return fail(YOCO_ERR_BAD_VALUE, "rope_theta must be finite and > 1");
   return q_project_impl(x, x_dtype, n, d_model, gain, eps, w_q, w_dtype, n_q_heads, head_dim, q_out, q_dtype, r,
-                        stream);
+                        workspace, workspace_bytes, stream);
 }
 
 yoco_status yoco_cross_attn_prefill(const void *q, int32_t q_dtype, int64_t q_start, int64_t t, int32_t n_q_heads,

@@ -10,7 +10,7 @@
 
 namespace yoco {
 
-constexpr int kMaxKvHeads = 64;        // counters are laid out [YOCO_MAX_SEQ][kMaxKvHeads]
+constexpr int kMaxKvHeads = 64;        // counters are laid out [kMaxKvHeads][YOCO_MAX_SEQ]
 constexpr int kDecodeSplitQuantum = 256;   // caller-chosen split sizes are multiples of this
 constexpr int kDecodeAutoQuantum = 64;     // library-chosen split sizes are multiples of this
 constexpr int kDecodeMinSplitRows = 256;   // library-chosen split sizes are at least this
@@ -25,7 +25,7 @@ struct DecodeArgs {
   const void *q;          // [n_seq][n_q_heads][head_dim]
   float *o;               // [n_seq][n_q_heads][head_dim]
   float *lse;             // [n_seq][n_q_heads] or null
-  unsigned int *counters; // [YOCO_MAX_SEQ][kMaxKvHeads]
+  unsigned int *counters; // [kMaxKvHeads][YOCO_MAX_SEQ]
   float *part_ml;         // [total_splits][n_kv_heads][G][2]
   float *part_acc;        // [total_splits][n_kv_heads][G][head_dim]
   int64_t seq_stride;     // elements between sequence slabs (capacity * row_stride)

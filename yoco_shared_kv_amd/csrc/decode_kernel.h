@@ -34,7 +34,7 @@
 //   stores and read with agent-scope atomic loads (they bypass the
 //   per-XCD caches, so no cache write-back or invalidate is needed); every
 //   wave waits for its stores, then thread 0 increments the (b, g) arrival
-//   counter with an agent-scope acquire-release RMW.  The workgroup that
+//   counter with an agent-scope RMW.  The workgroup that
 //   arrives last merges the group's partials: each task combines a fixed
 //   subset of the splits in one round trip, and the subsets are combined in a
 //   fixed order through LDS, so results are bitwise reproducible.  It writes
@@ -222,6 +222,13 @@ __device__ __forceinline__ float4 load_agent4(const float4 *p) {
                      __uint_as_float(static_cast<uint32_t>(hi)), __uint_as_float(static_cast<uint32_t>(hi >> 32)));
 }
 
+// The (m, l) pair of a partial row (its first 8 bytes), agent scope.
+__device__ __forceinline__ float2 load_agent2(const float *p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(static_cast<uint32_t>(v)), __uint_as_float(static_cast<uint32_t>(v >> 32)));
+}
+
 // Log-sum-exp merge weight of a state with reference max `ms` into `mnew`.
 __device__ __forceinline__ float merge_weight(float ms, float mnew) {
   return (ms == -INFINITY) ? 0.f : fast_exp2(ms - mnew);
@@ -389,14 +396,21 @@ __global__ __launch_bounds__(TUNE::NW * 64) void decode_kernel(const DecodeArgs 
     }
   }
 
-  // Every wave waits until its partial stores are performed, then thread 0
-  // counts this workgroup's arrival for (b, g).
+  // Every wave waits until its partial stores are performed at agent scope,
+  // then thread 0 counts this workgroup's arrival for (b, g).  The partials
+  // travel only through agent-scope atomic stores and loads, which the
+  // per-XCD caches do not hold, so the count needs no release or acquire
+  // fence (each would write back or invalidate this XCD's L2, once per
+  // workgroup): the wait orders the stores before the count, and the last
+  // arriver's loads are issued after its count has returned.  The counters
+  // of one sequence's KV heads are YOCO_MAX_SEQ words apart, on separate
+  // 128-byte lines, so the heads' arrivals do not queue on one line.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   __shared__ int s_is_last;
-  unsigned int *counter = a.counters + b * kMaxKvHeads + g;
+  unsigned int *counter = a.counters + g * YOCO_MAX_SEQ + b;
   if (tid == 0) {
-    const unsigned int prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned int prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_is_last = (prev == static_cast<unsigned int>(n_splits - 1)) ? 1 : 0;
   }
   __syncthreads();
@@ -421,16 +435,26 @@ __global__ __launch_bounds__(TUNE::NW * 64) void decode_kernel(const DecodeArgs 
     float mr = -INFINITY, lr = 0.f;
     float4 ar = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s0 = sub; s0 < n_splits; s0 += NSUB * MAXS) {
-      float4 vv[MAXS], mm[MAXS];
+      // Every load of the batch is issued at a clamped split (a load under a
+      // branch would be waited for before the branch joins: one round trip
+      // per split), then the splits past the last are replaced by the
+      // empty state.
+      // (Only the 8 bytes of (m, l) are loaded: a loaded value left unused
+      // would also force a wait, since its register is then reused while
+      // the load is still in flight.)
+      float4 vv[MAXS];
+      float2 mm[MAXS];
 #pragma unroll
       for (int k = 0; k < MAXS; ++k) {
-        const int s = s0 + k * NSUB;
-        if (s < n_splits) {
-          vv[k] = load_agent4(parts + s * split_stride4 + oc);
-          mm[k] = load_agent4(parts + s * split_stride4 + ml_chunk);
-        } else {
+        const int s = min(s0 + k * NSUB, n_splits - 1);
+        vv[k] = load_agent4(parts + s * split_stride4 + oc);
+        mm[k] = load_agent2(reinterpret_cast<const float *>(parts + s * split_stride4 + ml_chunk));
+      }
+#pragma unroll
+      for (int k = 0; k < MAXS; ++k) {
+        if (s0 + k * NSUB >= n_splits) {
           vv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-          mm[k] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
+          mm[k] = make_float2(-INFINITY, 0.f);
         }
       }
       float mb = mr;

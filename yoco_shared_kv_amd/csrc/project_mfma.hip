@@ -189,8 +189,11 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
     }
     if constexpr (kGain) {
       // 64 gains of this slice (lanes 16..63 fetch the next ones, unused).
+      // The slice offset goes into the per-lane offset, not the scalar one:
+      // the range check of a raw buffer load sees only the per-lane offset,
+      // so past the last slice those lanes read zeros, never past the gains.
       if (wave == 0) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(g_rsrc, (lds_void_t *)gdst, 16, lane * 16u, k0 * 4, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(g_rsrc, (lds_void_t *)gdst, 16, lane * 16u + k0 * 4, 0, 0, 0);
       }
     }
   };

@@ -49,6 +49,27 @@ __device__ __forceinline__ int64_t proj_row_pos(const ProjArgs &a, int64_t r) {
 }
 
 hipError_t launch_project(const ProjArgs &a, int x_dt, int w_dt, int o_dt, hipStream_t s);
+
+// Few-row projection split over W's reduction rows (project_rows.hip).  The
+// caller's workspace holds kProjRowsCounterBytes of arrival counters (zero
+// between calls) and then the partials of one launch of up to 8 input rows.
+constexpr int kProjRowsCounterBytes = YOCO_PROJECT_COUNTER_BYTES;
+constexpr int kProjRowsCounterStride = 32;  // words between counters: one 128-byte line each
+constexpr int kProjRowsMaxBlocks = kProjRowsCounterBytes / (4 * kProjRowsCounterStride);  // column blocks
+constexpr int kProjRowsMaxRows = 32;                           // input rows per call on this path
+struct ProjRowsPlan {
+  int32_t n_cb;          // column blocks over all outputs
+  int32_t splits;        // S: splits of W's d rows
+  int32_t split_rows;    // R: rows per split (multiple of 16, <= 256)
+  int32_t block_cols;    // CB: 128 (bf16 W) or 64 (fp32 W)
+  int64_t part_floats;   // partial storage for one launch
+};
+// Plan for these shapes; false when the path does not apply (columns not a
+// multiple of the block width, or more blocks than counters).
+bool project_rows_plan(int32_t d, int32_t ncols, int32_t n_out, int w_dt, ProjRowsPlan *p);
+size_t project_rows_workspace_bytes(const ProjRowsPlan &p);
+hipError_t launch_project_rows(const ProjArgs &a, const ProjRowsPlan &p, int x_dt, int w_dt, int o_dt,
+                               void *workspace, hipStream_t s);
 // Matrix-core path for prompt-sized bf16 projections (d_model % 64 == 0,
 // columns % 256 == 0, contiguous destination rows).
 bool project_mfma_applies(const ProjArgs &a, int x_dt, int w_dt, int o_dt);
