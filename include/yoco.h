@@ -420,6 +420,31 @@ yoco_status yoco_cross_attn_decode(const void *q, int32_t q_dtype, int32_t n_q_h
                                    float *lse, void *workspace, size_t workspace_bytes,
                                    int64_t rows_per_split, void *stream);
 
+/* yoco_cross_attn_decode for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It takes no workspace: the counters and partials live in a
+ * library array of YOCO_DECODE_NOALLOC_SCRATCH_BYTES in device memory (laid
+ * out as the workspace above), one per device, which each device holds until
+ * the process ends.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); the caller still passes q, o and lse.  The
+ * first call on a device looks the array up and clears its counters with a
+ * kernel on `stream`; every completed call leaves them zero.  Every call on
+ * a device shares that device's array, so calls that overlap in time on one
+ * device (different streams, or threads without synchronization) race.
+ * Results are the bits yoco_cross_attn_decode gives for the same cache,
+ * query, scale and rows_per_split.  Errors as yoco_cross_attn_decode, and
+ * WORKSPACE when this call's split plan needs more than the array holds:
+ * it has room for 15,763 partial rows of head_dim 128 (one per split, KV
+ * head and query head), e.g. 656 splits at 8 KV heads x 3 query heads; the
+ * library's split size (rows_per_split 0) plans at most
+ * (CUs x resident workgroups) / n_kv_heads + n_seq splits, and a caller's
+ * larger rows_per_split needs fewer. */
+#define YOCO_DECODE_NOALLOC_SCRATCH_BYTES (8 * 1024 * 1024)
+yoco_status yoco_cross_attn_decode_noalloc(const void *q, int32_t q_dtype, int32_t n_q_heads,
+                                           const yoco_kv_cache *cache, float softmax_scale,
+                                           float *o, float *lse, int64_t rows_per_split,
+                                           void *stream);
+
 /* ---- Gated retention (gRet), the self-decoder's token mixer -------------
  * [Notes] "YOCO：You Only Cache Once 中文精读笔记" section 2.2, Eq. 4-5 and
  * section 2.3 (chunkwise form); [Deep] section 3.1.  The self-decoder output

@@ -37,6 +37,7 @@ __all__ = [
     "kv_cache_row_stride", "lib", "project_workspace_bytes", "default_softmax_scale",
     "cross_attn_prefill_bwd", "prefill_bwd_workspace_bytes", "kv_project_bwd", "q_project_bwd",
     "project_bwd_workspace_bytes", "gret_prefill", "gret_decode", "gret_prefill_workspace_bytes",
+    "cross_attn_decode_noalloc",
 ]
 
 _DT = {torch.float32: YOCO_DT_F32, torch.bfloat16: YOCO_DT_BF16}
@@ -562,3 +563,22 @@ def cross_attn_decode(q: torch.Tensor, cache: KVCache, softmax_scale: Optional[f
                                        _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                        rows_per_split, _stream(stream)))
     return (out, lse) if (want_lse or lse_out is not None) else out
+
+
+def cross_attn_decode_noalloc(q: torch.Tensor, cache: KVCache, out: torch.Tensor,
+                              softmax_scale: Optional[float] = None, rows_per_split: int = 0,
+                              lse_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """``cross_attn_decode`` through ``yoco_cross_attn_decode_noalloc``: no
+    workspace, and nothing allocated here either (the caller passes ``out``
+    ``[n_seq, H_q, d_h]`` fp32 and optionally ``lse_out`` ``[n_seq, H_q]``).
+    Calls that overlap in time on one device race on the library's scratch."""
+    if q.dim() != 3 or q.shape[0] != cache.n_seq or q.shape[2] != cache.head_dim:
+        raise ValueError(f"q must be [{cache.n_seq}, H_q, {cache.head_dim}], got {tuple(q.shape)}")
+    n_seq, hq, dh = q.shape
+    _check_shape("out", out, (n_seq, hq, dh), torch.float32)
+    _check_shape("lse_out", lse_out, (n_seq, hq), torch.float32)
+    _on_device(q, out, lse_out)
+    s = cache.struct()
+    check(lib().yoco_cross_attn_decode_noalloc(_ptr(q), _dt(q), hq, ctypes.byref(s), _scale(softmax_scale, dh),
+                                               _ptr(out), _ptr(lse_out), rows_per_split, _stream(stream)))
+    return out

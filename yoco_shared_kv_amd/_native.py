@@ -16,7 +16,7 @@ YOCO_DT_F32 = 0
 YOCO_DT_BF16 = 1
 YOCO_MAX_SEQ = 256
 YOCO_DECODE_COUNTER_BYTES = YOCO_MAX_SEQ * 64 * 4
-YOCO_PROJECT_COUNTER_BYTES = 4096
+YOCO_DECODE_NOALLOC_SCRATCH_BYTES = 8 * 1024 * 1024
 
 STATUS = {
     0: "YOCO_OK", 1: "YOCO_ERR_NULL_POINTER", 2: "YOCO_ERR_BAD_SHAPE", 3: "YOCO_ERR_BAD_DTYPE",
@@ -105,6 +105,8 @@ def _declare(lib):
     lib.yoco_cross_attn_decode_workspace.argtypes = [cp, i32, i64, ctypes.POINTER(sz)]
     lib.yoco_cross_attn_decode.restype = st
     lib.yoco_cross_attn_decode.argtypes = [vp, i32, i32, cp, f32, vp, vp, vp, sz, i64, vp]
+    lib.yoco_cross_attn_decode_noalloc.restype = st
+    lib.yoco_cross_attn_decode_noalloc.argtypes = [vp, i32, i32, cp, f32, vp, vp, i64, vp]
     return lib
 
 

@@ -570,12 +570,20 @@ yoco_status yoco_cross_attn_decode_workspace(const yoco_kv_cache *cache, int32_t
   return ok();
 }
 
-yoco_status yoco_cross_attn_decode(const void *q, int32_t q_dtype, int32_t n_q_heads, const yoco_kv_cache *cache,
-                                   float softmax_scale, float *o, float *lse, void *workspace,
-                                   size_t workspace_bytes, int64_t rows_per_split, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the decode with a caller's workspace and the variant that uses
+// the library's static scratch (noalloc): the caller's workspace must hold
+// the bound over every length up to capacity; the scratch only this call's
+// split plan, within its fixed size.
+yoco_status decode_impl(const void *q, int32_t q_dtype, int32_t n_q_heads, const yoco_kv_cache *cache,
+                        float softmax_scale, float *o, float *lse, void *workspace, size_t workspace_bytes,
+                        int64_t rows_per_split, void *stream, bool noalloc) {
   yoco_status st = check_cache(cache);
   if (st != YOCO_OK) return st;
-  if (q == nullptr || o == nullptr || workspace == nullptr)
+  if (q == nullptr || o == nullptr || (!noalloc && workspace == nullptr))
     return fail(YOCO_ERR_NULL_POINTER, "q, o or workspace is NULL");
   if ((st = check_aligned({{q, "q"}, {o, "o"}, {workspace, "workspace"}}, 16)) != YOCO_OK) return st;
   if ((st = check_aligned({{lse, "lse"}}, 4)) != YOCO_OK) return st;
@@ -589,12 +597,13 @@ yoco_status yoco_cross_attn_decode(const void *q, int32_t q_dtype, int32_t n_q_h
       return fail(YOCO_ERR_OUT_OF_RANGE, "sequence %d: length %lld outside [1, %lld]", b, (long long)len,
                   (long long)cache->seq_capacity);
   }
-  const size_t bound = decode_workspace_bytes(cache, n_q_heads, max_total_splits(cache, rows_per_split));
-  if (workspace_bytes < bound)
-    return fail(YOCO_ERR_WORKSPACE, "workspace %zu bytes < %zu (yoco_cross_attn_decode_workspace)",
-                workspace_bytes, bound);
+  if (!noalloc) {
+    const size_t bound = decode_workspace_bytes(cache, n_q_heads, max_total_splits(cache, rows_per_split));
+    if (workspace_bytes < bound)
+      return fail(YOCO_ERR_WORKSPACE, "workspace %zu bytes < %zu (yoco_cross_attn_decode_workspace)",
+                  workspace_bytes, bound);
+  }
   const int group = n_q_heads / cache->n_kv_heads;
-  if ((st = check_device()) != YOCO_OK) return st;
   const int64_t rows = rows_per_split != 0
                            ? rows_per_split
                            : auto_split_rows(cache->len_host, cache->n_seq, cache->n_kv_heads,
@@ -607,10 +616,22 @@ yoco_status yoco_cross_attn_decode(const void *q, int32_t q_dtype, int32_t n_q_h
     total += (cache->len_host[b] + rows - 1) / rows;
   }
   a.split_begin[cache->n_seq] = static_cast<int32_t>(total);
-  if (decode_workspace_bytes(cache, n_q_heads, total) > workspace_bytes)
+  const size_t need = decode_workspace_bytes(cache, n_q_heads, total);
+  if (noalloc && need > YOCO_DECODE_NOALLOC_SCRATCH_BYTES)
+    return fail(YOCO_ERR_WORKSPACE,
+                "this call's split plan needs %zu bytes of scratch, more than the %d the no-allocation decode has "
+                "(use yoco_cross_attn_decode with a workspace, or larger rows_per_split)",
+                need, YOCO_DECODE_NOALLOC_SCRATCH_BYTES);
+  if (need > (noalloc ? size_t(YOCO_DECODE_NOALLOC_SCRATCH_BYTES) : workspace_bytes))
     return fail(YOCO_ERR_WORKSPACE, "split plan exceeds the workspace (internal bound violated)");
   if (total * cache->n_kv_heads > (int64_t(1) << 31) - 1)
     return fail(YOCO_ERR_BAD_VALUE, "too many splits (%lld)", (long long)total);
+  if ((st = check_device()) != YOCO_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (noalloc) {
+    const hipError_t e = yoco::decode_noalloc_scratch(&workspace, s);
+    if (e != hipSuccess) return fail(YOCO_ERR_HIP, "no-allocation decode scratch: %s", hipGetErrorString(e));
+  }
 
   a.k = cache->k;
   a.v = cache->v;
@@ -628,8 +649,25 @@ yoco_status yoco_cross_attn_decode(const void *q, int32_t q_dtype, int32_t n_q_h
   a.split_rows = static_cast<int32_t>(rows);
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.total_splits = static_cast<int32_t>(total);
-  return launched(yoco::launch_decode(a, cache->dtype, cache->head_dim, group, static_cast<hipStream_t>(stream)),
-                  "cross_attn_decode");
+  return launched(yoco::launch_decode(a, cache->dtype, cache->head_dim, group, s),
+                  noalloc ? "cross_attn_decode_noalloc" : "cross_attn_decode");
+}
+
+}  // namespace
+
+extern "C" {
+
+yoco_status yoco_cross_attn_decode(const void *q, int32_t q_dtype, int32_t n_q_heads, const yoco_kv_cache *cache,
+                                   float softmax_scale, float *o, float *lse, void *workspace,
+                                   size_t workspace_bytes, int64_t rows_per_split, void *stream) {
+  return decode_impl(q, q_dtype, n_q_heads, cache, softmax_scale, o, lse, workspace, workspace_bytes, rows_per_split,
+                     stream, false);
+}
+
+yoco_status yoco_cross_attn_decode_noalloc(const void *q, int32_t q_dtype, int32_t n_q_heads,
+                                           const yoco_kv_cache *cache, float softmax_scale, float *o, float *lse,
+                                           int64_t rows_per_split, void *stream) {
+  return decode_impl(q, q_dtype, n_q_heads, cache, softmax_scale, o, lse, nullptr, 0, rows_per_split, stream, true);
 }
 
 

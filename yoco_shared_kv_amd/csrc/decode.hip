@@ -4,9 +4,60 @@
 // 8 passes per tile for bf16 and 4 for fp32, no register double buffering;
 // measured on MI355X as the fastest of the swept shapes for the 128 Ki-row
 // workload when the grid is one resident round.
+#include <atomic>
+#include <mutex>
+
 #include "decode_kernel.h"
 
 namespace yoco {
+
+// Scratch of the decode variant that allocates nothing
+// (yoco_cross_attn_decode_noalloc): arrival counters, then partial rows,
+// laid out as the caller's workspace of yoco_cross_attn_decode.  Each device
+// holds its own copy until the process ends.  Host code never uses the
+// array's name as an address (on the host it is only a stand-in): the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[YOCO_DECODE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void *> g_scratch_ptr[kScratchDevices];
+std::mutex g_scratch_mutex;
+
+__global__ void zero_words_kernel(unsigned int *p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+}  // namespace
+
+hipError_t decode_noalloc_scratch(void **ptr, hipStream_t s) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      // The counters must start at zero (every completed call leaves them
+      // zero): clear them once, in stream order before the first decode,
+      // with a kernel rather than a memset (a caller may be capturing the
+      // stream into a graph).
+      const int words = YOCO_DECODE_COUNTER_BYTES / 4;
+      hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, s,
+                         static_cast<unsigned int *>(p), words);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 template <typename T>
 using ProdTune = DecodeTune<8, 8, (sizeof(T) == 2 ? 8 : 4), false>;

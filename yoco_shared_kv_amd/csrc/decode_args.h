@@ -41,6 +41,9 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int head_dim, int group, hipStream_t s);
+// Device address of this device's no-allocation decode scratch
+// (YOCO_DECODE_NOALLOC_SCRATCH_BYTES), set up on the first call on a device.
+hipError_t decode_noalloc_scratch(void **ptr, hipStream_t s);
 // Resident workgroups per CU of the decode kernel for this shape (0 on error).
 int decode_blocks_per_cu(int dtype, int head_dim, int group);
 
