@@ -68,6 +68,9 @@ def parse_args():
     p.add_argument("--copy-calibration", action="store_true")
     p.add_argument("--dense-rows", action="store_true",
                    help="decode cache with dense rows instead of the library's padded row stride (for comparison)")
+    p.add_argument("--no-extra-decodes", action="store_true",
+                   help="skip the ragged-16 and 2^20-row decode workloads reported beside the headline")
+    p.add_argument("--extra-steps", type=int, default=10, help="timed steps of each extra decode workload")
     return p.parse_args()
 
 
@@ -649,6 +652,51 @@ def bench_gret(args, torch, y, W):
                 decode_us=davg * 1e3, decode_p50_us=pct(dms, 50) * 1e3, case=c)
 
 
+def needle_cosines(torch, dec):
+    """cos(o, V^ row of the needle) for every layer and query head of the last
+    timed step of the 2^20-row workload (the needle reading of the pages'
+    long-context test: the output points along the needle's value row)."""
+    case, cache, outs = dec["case"], dec["cache"], dec["outs"]
+    g_size = case.n_q_heads // case.n_kv_heads
+    cos = []
+    for h in range(case.n_q_heads):
+        g = h // g_size
+        v = cache.v[0, int(case.needle_pos[0, g]), g].float()
+        for o in outs:
+            oh = o[0, h]
+            cos.append(float((oh @ v) / (oh.norm() * v.norm())))
+    return cos
+
+
+def bench_extra_decodes(args, torch, y, W):
+    """The ragged 16-sequence and the 2^20-row (planted needle) decode
+    workloads through the same step as the headline (one append per sequence
+    and 13 decode calls), fewer steps each."""
+    res = {}
+    for wl in ("ragged16", "decode1m"):
+        sub = argparse.Namespace(**vars(args))
+        sub.workload, sub.steps, sub.warmup, sub.cold_steps = wl, args.extra_steps, 2, 0
+        d = bench_decode(sub, torch, y, W)
+        entry = {
+            "workload": WORKLOADS[wl][2],
+            "us_per_token_layer": round(d["us_per_token_layer"], 2),
+            "ms_per_step": round(d["ms_per_step"], 4),
+            "steps": args.extra_steps,
+            "roofline": {"bound": "hbm", "achieved": round(d["achieved_gbps"], 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(d["achieved_gbps"] / HBM_PEAK_GBPS, 4),
+                         "avg_launch_us": round(d["kern_avg_us"], 2), "bytes_per_launch": d["bytes_per_launch"]},
+        }
+        if wl == "decode1m":
+            cos = needle_cosines(torch, d)
+            entry["needle_cos_min"] = round(min(cos), 5)
+            entry["needle_check"] = "min over 13 layers x 24 heads of cos(o, V^ needle row) >= 0.99"
+            log(f"decode1m needle: min cos {min(cos):.5f} over {len(cos)} (layer, head) outputs")
+        res[wl] = entry
+        del d
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(dec, W):
     import oracle
     case = dec["case"]
@@ -687,6 +735,7 @@ def main():
     bwd = None if args.no_prefill else bench_backward(args, torch, y, W)
     pbwd = None if args.no_prefill else bench_project_bwd(args, torch, y, W)
     gret = None if args.no_prefill else bench_gret(args, torch, y, W)
+    extra = None if (args.no_extra_decodes or args.workload != "decode128k") else bench_extra_decodes(args, torch, y, W)
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec, W)
     pre_cpu = gret_cpu = None
     if not args.no_cpu_baseline and pre is not None:
@@ -757,6 +806,8 @@ def main():
             "GBps": round(dec["cold"]["GBps"], 1), "launches": dec["cold"]["launches"]},
         "cpu_baseline": cpu,
     }
+    if extra is not None:
+        result.update(extra)
     if pre is not None:
         busy, busy_why = prefill_mfma_busy()
         if busy_why:

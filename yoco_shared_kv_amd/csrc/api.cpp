@@ -3,6 +3,7 @@
 // enqueued and no host length changes.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -159,19 +160,46 @@ int decode_target_blocks(int dtype, int head_dim, int group) {
   return static_cast<int>(target < yoco::kDecodeMaxTargetBlocks ? target : yoco::kDecodeMaxTargetBlocks);
 }
 
-int64_t auto_split_rows(const int64_t *lens, int n_seq, int n_kv_heads, int64_t target_blocks) {
-  int64_t total = 0;
-  for (int b = 0; b < n_seq; ++b) total += lens[b];
-  const int64_t work = total * n_kv_heads;
-  int64_t rows = (work + target_blocks - 1) / target_blocks;
-  rows = ((rows + yoco::kDecodeAutoQuantum - 1) / yoco::kDecodeAutoQuantum) * yoco::kDecodeAutoQuantum;
-  if (rows < yoco::kDecodeMinSplitRows) rows = yoco::kDecodeMinSplitRows;
-  return rows;
+// Library split plan: the smallest split size R (a multiple of
+// kDecodeAutoQuantum, at least kDecodeMinSplitRows) whose splits
+// n_b = ceil(len_b / R) number at most target_blocks / n_kv_heads over the
+// sequences (or one per sequence when there are more sequences than that),
+// so the grid is one resident round; each sequence then cuts its rows into
+// n_b equal splits (rounded up to the quantum), which keeps a ragged batch's
+// workgroups close to the same length.  A single sequence of 131072 rows at
+// 8 KV heads and 256 workgroups gets 32 splits of 4096 rows.
+void auto_split_plan(const int64_t *lens, int n_seq, int n_kv_heads, int64_t target_blocks, int32_t *rows_out) {
+  const int64_t budget = std::max<int64_t>(1, target_blocks / n_kv_heads);
+  int64_t longest = 0;
+  for (int b = 0; b < n_seq; ++b) longest = std::max(longest, lens[b]);
+  auto splits_at = [&](int64_t r) {
+    int64_t n = 0;
+    for (int b = 0; b < n_seq; ++b) n += (lens[b] + r - 1) / r;
+    return n;
+  };
+  const int64_t q = yoco::kDecodeAutoQuantum;
+  int64_t lo = std::max<int64_t>(yoco::kDecodeMinSplitRows, q), hi = std::max(lo, ((longest + q - 1) / q) * q);
+  if (splits_at(lo) <= budget) {
+    hi = lo;
+  } else {
+    while (hi - lo > q) {  // splits_at(hi) <= max(budget, n_seq), splits_at(lo) > budget
+      const int64_t mid = ((lo + hi) / 2 / q) * q;
+      if (mid <= lo) break;
+      if (splits_at(mid) <= budget) hi = mid; else lo = mid;
+    }
+  }
+  for (int b = 0; b < n_seq; ++b) {
+    const int64_t n = std::max<int64_t>(1, (lens[b] + hi - 1) / hi);
+    int64_t r = (lens[b] + n - 1) / n;
+    r = std::max<int64_t>(yoco::kDecodeMinSplitRows, ((r + q - 1) / q) * q);
+    rows_out[b] = static_cast<int32_t>(std::min(r, hi));
+  }
 }
 
 // Upper bound of total splits over every length <= capacity for a split size.
-// Library choice: rows >= total*H/target, so splits <= target/H + n_seq, and
-// rows >= kDecodeMinSplitRows bounds it by n_seq*ceil(cap/kDecodeMinSplitRows).
+// Library choice: at most max(target/H, n_seq) <= target/H + n_seq splits,
+// and every split is at least kDecodeMinSplitRows rows (unless it is its
+// sequence's only one), which bounds them by n_seq*ceil(cap/kDecodeMinSplitRows).
 int64_t max_total_splits(const yoco_kv_cache *c, int64_t rows_per_split) {
   if (rows_per_split == 0) {
     const int64_t fixed_bound =
@@ -604,16 +632,18 @@ yoco_status decode_impl(const void *q, int32_t q_dtype, int32_t n_q_heads, const
                   workspace_bytes, bound);
   }
   const int group = n_q_heads / cache->n_kv_heads;
-  const int64_t rows = rows_per_split != 0
-                           ? rows_per_split
-                           : auto_split_rows(cache->len_host, cache->n_seq, cache->n_kv_heads,
-                                             decode_target_blocks(cache->dtype, cache->head_dim, group));
   yoco::DecodeArgs a{};
+  if (rows_per_split != 0) {
+    for (int b = 0; b < cache->n_seq; ++b) a.split_rows[b] = static_cast<int32_t>(rows_per_split);
+  } else {
+    auto_split_plan(cache->len_host, cache->n_seq, cache->n_kv_heads,
+                    decode_target_blocks(cache->dtype, cache->head_dim, group), a.split_rows);
+  }
   int64_t total = 0;
   for (int b = 0; b < cache->n_seq; ++b) {
     a.split_begin[b] = static_cast<int32_t>(total);
     a.len[b] = static_cast<int32_t>(cache->len_host[b]);
-    total += (cache->len_host[b] + rows - 1) / rows;
+    total += (cache->len_host[b] + a.split_rows[b] - 1) / a.split_rows[b];
   }
   a.split_begin[cache->n_seq] = static_cast<int32_t>(total);
   const size_t need = decode_workspace_bytes(cache, n_q_heads, total);
@@ -646,7 +676,6 @@ yoco_status decode_impl(const void *q, int32_t q_dtype, int32_t n_q_heads, const
   a.n_seq = cache->n_seq;
   a.n_kv_heads = cache->n_kv_heads;
   a.n_q_heads = n_q_heads;
-  a.split_rows = static_cast<int32_t>(rows);
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.total_splits = static_cast<int32_t>(total);
   return launched(yoco::launch_decode(a, cache->dtype, cache->head_dim, group, s),

@@ -33,11 +33,11 @@ struct DecodeArgs {
   int32_t n_seq;
   int32_t n_kv_heads;
   int32_t n_q_heads;
-  int32_t split_rows;
   float scale_log2;       // softmax_scale * log2(e)
   int32_t total_splits;
   int32_t len[YOCO_MAX_SEQ];
   int32_t split_begin[YOCO_MAX_SEQ + 1];  // prefix sums of splits per sequence
+  int32_t split_rows[YOCO_MAX_SEQ];       // rows per split of each sequence (its last split may be shorter)
 };
 
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int head_dim, int group, hipStream_t s);

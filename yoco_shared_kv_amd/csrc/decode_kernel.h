@@ -12,8 +12,8 @@
 //   blockIdx.x = split_index * H_kv + g.  Consecutive blocks go to
 //   consecutive XCDs, so with H_kv = 8 every split of KV head g runs on one
 //   XCD and the merge reads partials from that XCD's L2.
-//   A workgroup of NW waves streams rows [split*split_rows, +split_rows) of
-//   (b, g).  Each lane owns EPL elements of a head row in 16-byte pieces;
+//   A workgroup of NW waves streams rows [split*split_rows_b, +split_rows_b)
+//   of (b, g), with a split size per sequence.  Each lane owns EPL elements of a head row in 16-byte pieces;
 //   LPR = head_dim / EPL lanes cover a row, and piece j of lane c holds
 //   elements j*LPR*VE + c*VE .. +VE (VE elements per 16 bytes), so each load
 //   instruction reads whole contiguous segments of the rows.  A wave covers
@@ -253,8 +253,9 @@ __global__ __launch_bounds__(TUNE::NW * 64) void decode_kernel(const DecodeArgs 
   const int b = lo;
   const int first_split = a.split_begin[b];
   const int n_splits = a.split_begin[b + 1] - first_split;
-  const int row_begin = (ws - first_split) * a.split_rows;
-  const int nrows = min(a.split_rows, a.len[b] - row_begin);
+  const int split_rows = a.split_rows[b];
+  const int row_begin = (ws - first_split) * split_rows;
+  const int nrows = min(split_rows, a.len[b] - row_begin);
 
   const int64_t row_stride = a.row_stride;
   const T *kbase = static_cast<const T *>(a.k) + b * a.seq_stride + row_begin * row_stride + g * DH;
