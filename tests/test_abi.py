@@ -389,13 +389,13 @@ def test_gret_rejects_and_sizes_workspace():
     assert pre(ws_bytes=100) == _status("YOCO_ERR_WORKSPACE")
     assert pre(n=0) == 0
     out = ctypes.c_size_t(0)
-    # chunkwise path, 256-byte aligned regions: cumulative gates, per-chunk and per-group log decays,
-    # group-local states per chunk (bf16), group totals and group start states (fp32); 3 chunks, 1 group
+    # chunkwise path, 256-byte aligned regions: cumulative gates, per-group log decays, group totals
+    # and group start states (fp32); 3 chunks, 1 group
     assert L.yoco_gret_prefill_workspace(300, 3, 128, 1, ctypes.byref(out)) == 0
     up = lambda b: (b + 255) // 256 * 256
-    assert out.value == up(300 * 3 * 4) + up(3 * 3 * 4) + up(1 * 3 * 4) + 3 * 3 * 128 * 128 * 2 + 2 * 3 * 128 * 128 * 4
+    assert out.value == up(300 * 3 * 4) + up(1 * 3 * 4) + 2 * 1 * 3 * 128 * 128 * 4
     assert L.yoco_gret_prefill_workspace(2049, 1, 128, 1, ctypes.byref(out)) == 0  # 17 chunks, 3 groups
-    assert out.value == up(2049 * 4) + up(17 * 4) + up(3 * 4) + 17 * 128 * 128 * 2 + 2 * 3 * 128 * 128 * 4
+    assert out.value == up(2049 * 4) + up(3 * 4) + 2 * 3 * 1 * 128 * 128 * 4
     assert L.yoco_gret_prefill_workspace(300, 3, 128, 0, ctypes.byref(out)) == 0 and out.value == 0
     assert L.yoco_gret_prefill_workspace(300, 3, 64, 1, ctypes.byref(out)) == 0 and out.value == 0
     assert pre(dt=0, ws=None, ws_bytes=0) != _status("YOCO_ERR_WORKSPACE")

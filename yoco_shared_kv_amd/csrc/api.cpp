@@ -912,28 +912,22 @@ yoco_status yoco_q_project_bwd(const void *x, int32_t x_dtype, int64_t n, int32_
 namespace {
 
 // Workspace of the chunkwise gated-retention prefill, 256-byte aligned
-// regions: cumulative log gates, per-chunk and per-group log decays,
-// group-local states before each chunk (bf16), group totals and the states
-// entering each group (fp32).
+// regions: cumulative log gates, per-group log decays, group totals and the
+// states entering each group (fp32).
 struct GretLayout {
-  size_t lcum = 0, cdec = 0, gdec = 0, rl = 0, tg = 0, sg = 0, total = 0;
+  size_t lcum = 0, gdec = 0, tg = 0, sg = 0, total = 0;
 };
 
 GretLayout gret_layout(int64_t n, int32_t heads, int32_t head_dim, int32_t dtype) {
   GretLayout L;
   if (!yoco::gret_chunked_applies(dtype, head_dim) || n <= 0) return L;
-  const size_t chunks = static_cast<size_t>(yoco::gret_n_chunks(n));
   const size_t groups = static_cast<size_t>(yoco::gret_n_groups(n));
   const size_t state = static_cast<size_t>(head_dim) * head_dim;
   size_t off = 0;
   L.lcum = off;
   off = align256(off + static_cast<size_t>(n) * heads * 4);
-  L.cdec = off;
-  off = align256(off + chunks * heads * 4);
   L.gdec = off;
   off = align256(off + groups * heads * 4);
-  L.rl = off;
-  off = align256(off + chunks * heads * state * 2);
   L.tg = off;
   off = align256(off + groups * heads * state * 4);
   L.sg = off;
@@ -998,9 +992,7 @@ yoco_status yoco_gret_prefill(const void *q, const void *k, const void *v, int32
   if (L.total > 0) {
     char *ws = static_cast<char *>(workspace);
     a.lcum = reinterpret_cast<float *>(ws + L.lcum);
-    a.cdec = reinterpret_cast<float *>(ws + L.cdec);
     a.gdec = reinterpret_cast<float *>(ws + L.gdec);
-    a.rl = reinterpret_cast<uint16_t *>(ws + L.rl);
     a.tg = reinterpret_cast<float *>(ws + L.tg);
     a.sg = reinterpret_cast<float *>(ws + L.sg);
     return launched(yoco::launch_gret_chunked(a, s), "gret_prefill");

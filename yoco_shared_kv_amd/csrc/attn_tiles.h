@@ -52,7 +52,6 @@ struct PrefillShape {
   static constexpr int kTileBytes = pf::kKeyTile * kRowBytes;
   static constexpr int kRowsPerLoad = 64 / kChunks;         // rows per wave-wide 1 KiB load
   static constexpr int kLoadsPerTile = pf::kKeyTile / kRowsPerLoad;    // per K (or V) tile
-  static constexpr int kLoadsPerWave = kLoadsPerTile / pf::kWaves;
   static constexpr int KSTEPS = DH / 16;                    // S^T k-steps over head_dim
   static constexpr int DSUB = DH / 32;                      // O^T 32-row tiles over head_dim
 };
@@ -89,14 +88,16 @@ __device__ __forceinline__ int swz(int row, int dim) {
 // load i of the wave fills 1 KiB block blk = wave * kLoadsPerWave + i, lane
 // L writes LDS bytes blk*1024 + L*16 = (row, slot) and so reads global chunk
 // slot ^ row_xor(row) of that row.
-template <int DH, int SWZ>
+// NW: waves of the workgroup that share the staging of a tile.
+template <int DH, int SWZ, int NW = pf::kWaves>
 struct StageOffsets {
   using S = PrefillShape<DH>;
-  uint32_t boff[S::kLoadsPerWave];  // (row * row_stride + chunk * 8) * 2
+  static constexpr int kLoadsPerWave = S::kLoadsPerTile / NW;
+  uint32_t boff[kLoadsPerWave];  // (row * row_stride + chunk * 8) * 2
   __device__ __forceinline__ void init(int wave, int lane, int row_stride) {
 #pragma unroll
-    for (int i = 0; i < S::kLoadsPerWave; ++i) {
-      const int row = (wave * S::kLoadsPerWave + i) * S::kRowsPerLoad + lane / S::kChunks;
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+      const int row = (wave * kLoadsPerWave + i) * S::kRowsPerLoad + lane / S::kChunks;
       const int chunk = (lane % S::kChunks) ^ row_xor<DH, SWZ>(row);
       boff[i] = static_cast<uint32_t>(row * row_stride + chunk * 8) * 2u;
     }
@@ -110,10 +111,10 @@ struct StageOffsets {
 // outside the cache.  `wave` is wave-uniform (an SGPR), so the LDS address
 // in M0 is scalar arithmetic.
 constexpr int32_t kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
-template <int DH, int SWZ>
+template <int DH, int SWZ, int NW>
 __device__ __forceinline__ void stage_tile(char *lds_dst, const bf16_t *src, int row_stride, int key0, int kv_len,
-                                           int wave, const StageOffsets<DH, SWZ> &so) {
-  using S = PrefillShape<DH>;
+                                           int wave, const StageOffsets<DH, SWZ, NW> &so) {
+  constexpr int kLoadsPerWave = StageOffsets<DH, SWZ, NW>::kLoadsPerWave;
   // Bytes from the tile start to the end of row kv_len-1 of this head; a
   // staged tile always starts at or before that row.
   // (64-bit: the distance to the last row can pass 2 GiB in long slabs.)
@@ -123,8 +124,8 @@ __device__ __forceinline__ void stage_tile(char *lds_dst, const bf16_t *src, int
       const_cast<bf16_t *>(src + (int64_t)key0 * row_stride), 0, static_cast<int>(min(valid, tile_bytes)),
       kBufferFlags);
 #pragma unroll
-  for (int i = 0; i < S::kLoadsPerWave; ++i) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)(lds_dst + (wave * S::kLoadsPerWave + i) * 1024), 16,
+  for (int i = 0; i < kLoadsPerWave; ++i) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t *)(lds_dst + (wave * kLoadsPerWave + i) * 1024), 16,
                                              so.boff[i], 0, 0, 0);
   }
 }

@@ -24,30 +24,32 @@
 //   U_c     = sum_k exp(l_C - l_k) k_k^T v_k                  (chunk's own state)
 //   R_{c+1} = exp(l_C) R_c + U_c,  R_0 = the start state       (state entering chunk c+1)
 //   O_j     = sum_{k<=j} exp(l_j - l_k) (q_j . k_k) v_k + exp(l_j) q_j R_c
-// The pass over chunks is split in two levels, so no per-chunk fp32 state
-// ever goes to memory: chunks form groups of kGroup; inside group g the
-// same recurrence started from zero gives A_c, the group's total T_g and
-// its decay Lambda_g, and then S_{g+1} = exp(Lambda_g) S_g + T_g (S_0 the
-// start state) gives R_c = A_c + exp(delta_c) S_g, delta_c the log decay
-// from the group's start to chunk c.
+// The pass over chunks is split in two levels, so no per-chunk state ever
+// goes to memory: chunks form groups of kGroup; inside group g the same
+// recurrence started from zero gives the group's total T_g and its decay
+// Lambda_g, and S_{g+1} = exp(Lambda_g) S_g + T_g (S_0 the start state)
+// gives the state entering each group.
 //   * gret_group_state_kernel: one workgroup per (group, head) walks the
-//     group's chunks with A in the MFMA accumulators: l for the chunk (a
-//     wave scan), A_c out in bf16, then A <- exp(l_C) A + K'^T V with
-//     K' = exp(l_C - l_k) k_k rounded to bf16 (weights applied to the
-//     transposed K fragments), both operands from row-major LDS tiles.
+//     group's chunks with the state in the MFMA accumulators: l for the
+//     chunk (a wave scan, also stored for the output kernel), then
+//     A <- exp(l_C) A + K'^T V with K' = exp(l_C - l_k) k_k rounded to bf16
+//     (weights applied to the transposed K fragments), both operands from
+//     row-major LDS tiles; T_g = A after the group's last chunk, in fp32.
 //   * gret_group_scan_kernel: the short pass over groups, elementwise over
 //     the state (S_g in fp32, the last state to state_out).
-//   * gret_chunk_out_kernel: 4 waves x 32 query rows of a chunk.  R_c is
-//     formed in fp32 from A_c and S_g and rounded to bf16 into LDS; the
-//     carried term O^T = R^T Q^T comes first (then each lane scales its
-//     query row by exp(l_j)), then per 32-key half S^T = K Q^T,
+//   * gret_group_out_kernel: one workgroup per (group, head) walks the
+//     group's chunks again, with A started at S_g, so before chunk c it
+//     holds R_c.  Per chunk, 4 waves x 32 query rows: R_c is rounded to bf16
+//     into LDS; the carried term O^T = R^T Q^T comes first (then each lane
+//     scales its query row by exp(l_j)), then per 32-key half S^T = K Q^T,
 //     P = S exp(l_j - l_k) masked to k <= j and rounded to bf16 (formed
 //     while V loads into the buffer R_c held), then O^T += V^T P^T -- the
 //     layout of the causal prefill kernel (one query row per lane, Q^T in
-//     registers).
-// The stored states are transposed ([value dim][key dim]): the output
-// kernel then reads R^T rows with plain 16-byte LDS reads, and the state
-// kernel writes four consecutive key dims per lane.
+//     registers) -- and last the state update of the chunk, as in the state
+//     kernel.  Each chunk's k and v are read twice in all (once per
+//     kernel); no state goes to memory per chunk.
+// The stored states are transposed ([value dim][key dim]): the accumulator
+// layout writes and reads four consecutive key dims per lane.
 #include "attn_tiles.h"
 
 namespace yoco {
@@ -62,6 +64,11 @@ constexpr int kTileBytes = kChunk * kRowBytes;       // 32 KiB: [128][128] bf16
 constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // 8 one-KiB loads
 constexpr int kGroup = 8;          // chunks per group of the state kernel
 constexpr int kScanAhead = 8;      // group states in flight per thread in the scan
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// in 6:4, lgkmcnt in 11:8) that wait for vector memory only, down to 4 or 8
+// outstanding operations.
+constexpr int kVmcnt4 = 4 | (7 << 4) | (15 << 8);
+constexpr int kVmcnt8 = 8 | (7 << 4) | (15 << 8);
 }  // namespace gr
 
 // log gamma = logsigmoid(g) / tau = (min(g, 0) - log1p(exp(-|g|))) / tau.
@@ -231,26 +238,90 @@ struct TrFrag {
     return read_at(tile, off[0][dt], off[1][dt], ks);
   }
 };
+
+// One chunk's step of a state held in the MFMA accumulators (wave w: key
+// dims 32w .. 32w+31, acc[t] value dims 32t .. 32t+31):
+//   A <- exp(l_C) A + K'^T V,  K' = exp(l_C - l_k) k_k rounded to bf16,
+// with K and V as row-major [128][128] LDS tiles and the key weights
+// exp(l_C - l_k) in w (zero past the chunk's rows).  ka0/ka1: this wave's
+// K^T fragment offsets; fr: V's offsets in the same k order.
+__device__ __forceinline__ void state_step(floatx16 (&acc)[4], const char *lds_k, const char *lds_v, const float *w,
+                                           int ka0, int ka1, const TrFrag &fr, float dec, int half) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[t][e] *= dec;
+  }
+#pragma unroll
+  for (int ks = 0; ks < kChunk / 16; ++ks) {
+    // The K^T fragment holds key rows ks*16 + half*8 + i (i = 0..7) of
+    // key dim 32*wave + col; each is weighted and rounded to bf16.
+    Frag8 af;
+    af.v = TrFrag::read_at(lds_k, ka0, ka1, ks);
+    const float4 w0 = *reinterpret_cast<const float4 *>(w + ks * 16 + half * 8);
+    const float4 w1 = *reinterpret_cast<const float4 *>(w + ks * 16 + half * 8 + 4);
+    af.w[0] = cvt_pk_bf16(bf16_lo(af.w[0]) * w0.x, bf16_hi(af.w[0]) * w0.y);
+    af.w[1] = cvt_pk_bf16(bf16_lo(af.w[1]) * w0.z, bf16_hi(af.w[1]) * w0.w);
+    af.w[2] = cvt_pk_bf16(bf16_lo(af.w[2]) * w1.x, bf16_hi(af.w[2]) * w1.y);
+    af.w[3] = cvt_pk_bf16(bf16_lo(af.w[3]) * w1.z, bf16_hi(af.w[3]) * w1.w);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af.v, fr.read(lds_v, t, ks), acc[t], 0, 0, 0);
+  }
+}
 }  // namespace gr
 
 // ---------------------------------------------------------------------------
-// Per (group of kGroup chunks, head), walking the group's chunks in order:
-// l (inclusive cumulative log gamma inside each chunk) and the log decay
-// from the group's start to each chunk (delta_c) go to the workspace; the
-// group-local state A_c (state before chunk c, counted from zero at the
-// group's start) goes out in bf16 for every chunk but the group's first,
-// A_{c+1} = exp(l_C) A_c + K'^T V with K' = exp(l_C - l_k) k_k rounded to
-// bf16, and the group's total T_g = A after its last chunk in fp32, with
-// its log decay Lambda_g.  A lives in the MFMA accumulators: wave w owns
-// rows (key dims) 32w .. 32w+31, all 128 value dims.  States are stored
-// transposed ([value dim][key dim]), the layout the output kernel reads.
+// Per (group of kGroup chunks, head): the group's total
+//   T_g = sum_k exp(L_G - L_k) k_k^T v_k
+// over its positions, L the inclusive cumulative log gamma from the group's
+// start and L_G its value at the group's end (Lambda_g) -- the recurrence
+// A <- exp(l_C) A + U_c over the group's chunks from A = 0, summed in one
+// pass: no step depends on the previous one, so K and V stream through LDS
+// in 64-row sub-tiles, two stages deep.  Wave 0 first scans the group's
+// gates: 16 consecutive positions per lane, lane totals scanned over the
+// wave for L and over each 8-lane segment (one chunk) for the chunk-local
+// cumulative sums l that go to the workspace for the output kernel; the key
+// weights exp(L_G - L_k) go to LDS.  The weighted K^T fragments are rounded
+// to bf16.  T_g lives in the MFMA accumulators: wave w owns rows (key dims)
+// 32w .. 32w+31, all 128 value dims; it is stored transposed ([value
+// dim][key dim]).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(gr::kThreads, 2) void gret_group_state_kernel(const GretArgs a) {
   using namespace gr;
-  __shared__ __attribute__((aligned(1024))) char lds_k[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_v[kTileBytes];
-  __shared__ __attribute__((aligned(16))) float s_w[kChunk];
-  __shared__ float s_lc;
+  constexpr int kSubRows = 32;                           // rows per streamed sub-tile
+  constexpr int kSubBytes = kSubRows * kRowBytes;        // 8 KiB of K (and of V)
+  constexpr int kStages = 4;                             // ring of sub-tiles: three in flight
+  constexpr int kLoadsPerStage = 2 * kSubBytes / 1024 / kWaves;  // vector memory ops per wave per stage (K and V)
+  constexpr int kGroupRows = kGroup * kChunk;            // 1024 positions
+  constexpr int kPerLane = kGroupRows / 64;              // 16 positions per lane of the scan
+  static_assert(kChunk / kPerLane == 8, "one chunk = 8 lanes of the scan");
+  static_assert(kLoadsPerStage == 4, "the counted waits below assume 4 loads per wave per stage");
+  // One array per ring slot, selected at compile time: the compiler can then
+  // tell that reads of one slot do not alias the direct-to-LDS loads still
+  // landing in the others, and waits only as the counted waits below say.
+  __shared__ __attribute__((aligned(1024))) char lds_k0[kSubBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_k1[kSubBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_k2[kSubBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_k3[kSubBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v0[kSubBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v1[kSubBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v2[kSubBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v3[kSubBytes];
+  __shared__ __attribute__((aligned(16))) float s_w[kGroupRows];
+  auto kslot = [&](auto b_c) __attribute__((always_inline)) -> char * {
+    constexpr int B = decltype(b_c)::value;
+    if constexpr (B == 0) return lds_k0;
+    else if constexpr (B == 1) return lds_k1;
+    else if constexpr (B == 2) return lds_k2;
+    else return lds_k3;
+  };
+  auto vslot = [&](auto b_c) __attribute__((always_inline)) -> char * {
+    constexpr int B = decltype(b_c)::value;
+    if constexpr (B == 0) return lds_v0;
+    else if constexpr (B == 1) return lds_v1;
+    else if constexpr (B == 2) return lds_v2;
+    else return lds_v3;
+  };
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -258,10 +329,81 @@ __global__ __launch_bounds__(gr::kThreads, 2) void gret_group_state_kernel(const
   const int col = lane & 31;
   const int g = blockIdx.x / a.heads;
   const int h = blockIdx.x % a.heads;
-  const int n_chunks = static_cast<int>((a.n_tokens + kChunk - 1) / kChunk);
-  const int c_begin = g * kGroup;
-  const int c_end = c_begin + kGroup < n_chunks ? c_begin + kGroup : n_chunks;
+  const int64_t t0 = static_cast<int64_t>(g) * kGroupRows;
+  const int rows = a.n_tokens - t0 < kGroupRows ? static_cast<int>(a.n_tokens - t0) : kGroupRows;
+  const int n_sub = (rows + kSubRows - 1) / kSubRows;
   const int stride = a.heads * kD;
+  const bf16_t *kg = static_cast<const bf16_t *>(a.k) + (t0 * a.heads + h) * kD;
+  const bf16_t *vg = static_cast<const bf16_t *>(a.v) + (t0 * a.heads + h) * kD;
+  // Sub-tile j: rows 32j .. 32j+31 of the group; wave w loads rows 8w ..
+  // 8w+7 of K and of V (two 1-KiB loads of 4 rows each); rows past the
+  // group's end land as zeros.
+  auto stage = [&](auto b_c, int j) __attribute__((always_inline)) {
+    char *dk = kslot(b_c);
+    char *dv = vslot(b_c);
+    const int r0 = j * kSubRows;
+    const int valid = rows - r0 < kSubRows ? rows - r0 : kSubRows;
+    const int bytes = ((valid - 1) * stride + kD) * 2;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t *>(kg + static_cast<int64_t>(r0) * stride), 0, bytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t *>(vg + static_cast<int64_t>(r0) * stride), 0, bytes, kBufferFlags);
+#pragma unroll
+    for (int i = 0; i < kSubBytes / 1024 / kWaves; ++i) {
+      const int blk = wave * (kSubBytes / 1024 / kWaves) + i;
+      const int row = blk * 4 + (lane >> 4);
+      const uint32_t off = static_cast<uint32_t>(row * stride * 2 + (((lane & 15) ^ row_xor<kD, kSwz>(row)) * 16));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t *)(dk + blk * 1024), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t *)(dv + blk * 1024), 16, off, 0, 0, 0);
+    }
+  };
+  // Wave 0 loads the group's gates first (every load issued at once, at
+  // clamped positions), then every wave starts the first three sub-tiles.
+  float lg[kPerLane];
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+      const int p = min(lane * kPerLane + i, rows - 1);
+      lg[i] = a.gate[(t0 + p) * a.heads + h];
+    }
+  }
+  stage(std::integral_constant<int, 0>(), 0);
+  if (n_sub > 1) stage(std::integral_constant<int, 1>(), 1);
+  if (n_sub > 2) stage(std::integral_constant<int, 2>(), 2);
+
+  // Wave 0, while the first sub-tiles load: the group's cumulative gates.
+  if (wave == 0) {
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+      const int p = lane * kPerLane + i;
+      lg[i] = p < rows ? gret_log_gate(lg[i], a.inv_tau) : 0.f;
+      tot += lg[i];
+    }
+    // Inclusive scans of the lane totals: over the wave (L) and over each
+    // 8-lane segment (the chunk).
+    float incl = tot, seg = tot;
+#pragma unroll
+    for (int sft = 1; sft < 64; sft <<= 1) {
+      const float o = __shfl_up(incl, sft, 64);
+      if (lane >= sft) incl += o;
+      if (sft < 8) {
+        const float os = __shfl_up(seg, sft, 64);
+        if ((lane & 7) >= sft) seg += os;
+      }
+    }
+    const float total = __shfl(incl, 63, 64);  // L_G (positions past the group add 0)
+    float big = incl - tot, loc = seg - tot;   // exclusive prefixes
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+      const int p = lane * kPerLane + i;
+      big += lg[i];
+      loc += lg[i];
+      s_w[p] = p < rows ? expf(total - big) : 0.f;
+      if (p < rows) a.lcum[(t0 + p) * a.heads + h] = loc;
+    }
+    if (lane == 0) a.gdec[static_cast<int64_t>(g) * a.heads + h] = total;
+  }
 
   TrFrag fr;  // both operands of K'^T V in the same k order
   fr.init(lane, kSplitHalves);
@@ -275,82 +417,58 @@ __global__ __launch_bounds__(gr::kThreads, 2) void gret_group_state_kernel(const
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
   }
-  float delta = 0.f;  // log decay from the group's start to chunk c
-  for (int c = c_begin; c < c_end; ++c) {
-    const int64_t t0 = static_cast<int64_t>(c) * kChunk;
-    const int rows = a.n_tokens - t0 < kChunk ? static_cast<int>(a.n_tokens - t0) : kChunk;
-    stage_rows(lds_k, static_cast<const bf16_t *>(a.k) + (t0 * a.heads + h) * kD, stride, rows, wave, lane);
-    stage_rows(lds_v, static_cast<const bf16_t *>(a.v) + (t0 * a.heads + h) * kD, stride, rows, wave, lane);
-    // Wave 0, while the tiles load: the chunk's cumulative log gates (lane
-    // holds positions 2L, 2L+1) and the key weights exp(l_C - l_k).
-    if (wave == 0) {
-      float l0 = 0.f, l1 = 0.f;
-      const int p0 = 2 * lane, p1 = 2 * lane + 1;
-      if (p0 < rows) l0 = gret_log_gate(a.gate[(t0 + p0) * a.heads + h], a.inv_tau);
-      if (p1 < rows) l1 = gret_log_gate(a.gate[(t0 + p1) * a.heads + h], a.inv_tau);
-      l1 += l0;
-      float incl = l1;  // inclusive scan of the pair sums over lanes
-#pragma unroll
-      for (int sft = 1; sft < 64; sft <<= 1) {
-        const float o = __shfl_up(incl, sft, 64);
-        if (lane >= sft) incl += o;
-      }
-      const float excl = incl - l1;
-      const float c0v = excl + l0, c1v = excl + l1;
-      const float last = __shfl(incl, 63, 64);  // l_C (rows past the chunk add 0)
-      if (p0 < rows) a.lcum[(t0 + p0) * a.heads + h] = c0v;
-      if (p1 < rows) a.lcum[(t0 + p1) * a.heads + h] = c1v;
-      s_w[p0] = p0 < rows ? expf(last - c0v) : 0.f;
-      s_w[p1] = p1 < rows ? expf(last - c1v) : 0.f;
-      if (lane == 0) {
-        s_lc = last;
-        a.cdec[static_cast<int64_t>(c) * a.heads + h] = delta;
-      }
+  // Sub-tile j sits in ring slot j % 4; the loop runs four sub-tiles per
+  // pass so that every slot is a compile-time choice.
+  auto step = [&](auto b_c, int j) __attribute__((always_inline)) {
+    constexpr int B = decltype(b_c)::value;
+    // Sub-tile j has landed for every wave: this wave waits until only the
+    // loads of the (up to two) later sub-tiles it has issued are
+    // outstanding (the first pass waits for everything, the gates
+    // included), then the barrier.  Every wave is then also done with
+    // sub-tile j-1, whose slot sub-tile j+3 takes.
+    const int later = n_sub - 1 - j;
+    if (j == 0 || later == 0) {
+      __builtin_amdgcn_s_waitcnt(0);
+    } else if (later == 1) {
+      __builtin_amdgcn_s_waitcnt(kVmcnt4);
+    } else {
+      __builtin_amdgcn_s_waitcnt(kVmcnt8);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    const float lc = s_lc;
-    // A_c out (bf16, transposed): acc[t] element e is A row (key dim)
-    // 32*wave + (e/4)*8 + half*4 + e%4, column (value dim) t*32 + col, so a
-    // lane's four consecutive e are four consecutive key dims: 8-byte stores.
-    if (c > c_begin) {
-      uint16_t *rl = a.rl + (static_cast<int64_t>(c) * a.heads + h) * kD * kD;
+    // A plain barrier: __syncthreads() adds a workgroup release fence, which
+    // would wait for every load still landing in LDS.  LDS is one memory for
+    // the workgroup, so the counted wait above is what orders this wave's
+    // landed sub-tile before the others' reads; the empty asm statements keep
+    // the compiler from moving memory accesses across the barrier.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (j + kStages - 1 < n_sub) stage(std::integral_constant<int, (B + kStages - 1) % kStages>(), j + kStages - 1);
+    const char *tk = kslot(b_c);
+    const char *tv = vslot(b_c);
+    const float *w = s_w + j * kSubRows;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          uint2 pk;
-          pk.x = cvt_pk_bf16(acc[t][q4 * 4 + 0], acc[t][q4 * 4 + 1]);
-          pk.y = cvt_pk_bf16(acc[t][q4 * 4 + 2], acc[t][q4 * 4 + 3]);
-          *reinterpret_cast<uint2 *>(rl + (t * 32 + col) * kD + wave * 32 + q4 * 8 + half * 4) = pk;
-        }
-      }
-    }
-    const float dec = expf(lc);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[t][e] *= dec;
-    }
-    delta += lc;
-#pragma unroll
-    for (int ks = 0; ks < kChunk / 16; ++ks) {
-      // The K^T fragment holds key rows ks*16 + half*8 + i (i = 0..7) of
-      // key dim 32*wave + col; each is weighted and rounded to bf16.
+    for (int ks = 0; ks < kSubRows / 16; ++ks) {
+      // The K^T fragment holds rows ks*16 + half*8 + i (i = 0..7) of the
+      // sub-tile for key dim 32*wave + col; each is weighted and rounded to bf16.
       Frag8 af;
-      af.v = TrFrag::read_at(lds_k, ka0, ka1, ks);
-      const float4 w0 = *reinterpret_cast<const float4 *>(s_w + ks * 16 + half * 8);
-      const float4 w1 = *reinterpret_cast<const float4 *>(s_w + ks * 16 + half * 8 + 4);
+      af.v = TrFrag::read_at(tk, ka0, ka1, ks);
+      const float4 w0 = *reinterpret_cast<const float4 *>(w + ks * 16 + half * 8);
+      const float4 w1 = *reinterpret_cast<const float4 *>(w + ks * 16 + half * 8 + 4);
       af.w[0] = cvt_pk_bf16(bf16_lo(af.w[0]) * w0.x, bf16_hi(af.w[0]) * w0.y);
       af.w[1] = cvt_pk_bf16(bf16_lo(af.w[1]) * w0.z, bf16_hi(af.w[1]) * w0.w);
       af.w[2] = cvt_pk_bf16(bf16_lo(af.w[2]) * w1.x, bf16_hi(af.w[2]) * w1.y);
       af.w[3] = cvt_pk_bf16(bf16_lo(af.w[3]) * w1.z, bf16_hi(af.w[3]) * w1.w);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af.v, fr.read(lds_v, t, ks), acc[t], 0, 0, 0);
+      for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af.v, fr.read(tv, t, ks), acc[t], 0, 0, 0);
     }
-    __syncthreads();  // the next chunk's tiles take the buffers
+  };
+  for (int j = 0; j < n_sub; j += kStages) {
+    step(std::integral_constant<int, 0>(), j);
+    if (j + 1 < n_sub) step(std::integral_constant<int, 1>(), j + 1);
+    if (j + 2 < n_sub) step(std::integral_constant<int, 2>(), j + 2);
+    if (j + 3 < n_sub) step(std::integral_constant<int, 3>(), j + 3);
   }
-  // T_g (fp32, transposed) and Lambda_g.
+  // T_g (fp32, transposed).
   float *tg = a.tg + (static_cast<int64_t>(g) * a.heads + h) * kD * kD;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -360,7 +478,6 @@ __global__ __launch_bounds__(gr::kThreads, 2) void gret_group_state_kernel(const
           make_float4(acc[t][q4 * 4 + 0], acc[t][q4 * 4 + 1], acc[t][q4 * 4 + 2], acc[t][q4 * 4 + 3]);
     }
   }
-  if (tid == 0) a.gdec[static_cast<int64_t>(g) * a.heads + h] = delta;
 }
 
 // ---------------------------------------------------------------------------
@@ -424,156 +541,197 @@ __global__ __launch_bounds__(256) void gret_group_scan_kernel(const GretArgs a, 
 }
 
 // ---------------------------------------------------------------------------
-// Outputs of one chunk of one head: wave w owns query rows 32w .. 32w+31.
-// 64 KiB of LDS (two workgroups per CU): the carried state R_c is formed in
-// the buffer that V takes afterwards, so V loads while the scores of the
-// chunk are formed.
+// Outputs of a group of chunks of one head, walking the group's chunks in
+// order with the state in the MFMA accumulators (the state kernel's layout),
+// started at S_g, so that before chunk c it holds R_c.  Wave w owns query
+// rows 32w .. 32w+31 of each chunk.  64 KiB of LDS (two workgroups per CU):
+// R_c is rounded to bf16 into the buffer that V takes afterwards, so V loads
+// while the scores of the chunk are formed.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(gr::kThreads, 2) void gret_chunk_out_kernel(const GretArgs a) {
+__global__ __launch_bounds__(gr::kThreads, 2) void gret_group_out_kernel(const GretArgs a) {
   using namespace gr;
   __shared__ __attribute__((aligned(1024))) char lds_k[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_rv[kTileBytes];  // R_c, then V
-  __shared__ float s_l[kChunk];
+  __shared__ __attribute__((aligned(1024))) char lds_rv[kTileBytes];  // R_c, then V_c
+  __shared__ __attribute__((aligned(16))) float s_l[kChunk];
+  __shared__ __attribute__((aligned(16))) float s_w[kChunk];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int col = lane & 31;
-  // Chunks in reverse order, so the ragged last chunk does not run last.
-  const int n_chunks = static_cast<int>((a.n_tokens + kChunk - 1) / kChunk);
-  const int chunk = n_chunks - 1 - static_cast<int>(blockIdx.x / a.heads);
+  const int g = blockIdx.x / a.heads;
   const int h = blockIdx.x % a.heads;
-  const int64_t t0 = static_cast<int64_t>(chunk) * kChunk;
-  const int rows = a.n_tokens - t0 < kChunk ? static_cast<int>(a.n_tokens - t0) : kChunk;
+  const int n_chunks = static_cast<int>((a.n_tokens + kChunk - 1) / kChunk);
+  const int c_begin = g * kGroup;
+  const int c_end = c_begin + kGroup < n_chunks ? c_begin + kGroup : n_chunks;
   const int stride = a.heads * kD;
-  const bf16_t *kg = static_cast<const bf16_t *>(a.k) + (t0 * a.heads + h) * kD;
-  const bf16_t *vg = static_cast<const bf16_t *>(a.v) + (t0 * a.heads + h) * kD;
-  stage_rows(lds_k, kg, stride, rows, wave, lane);
-  if (tid < kChunk) s_l[tid] = tid < rows ? a.lcum[(t0 + tid) * a.heads + h] : 0.f;
-  // R_c = A_c + exp(delta_c) S_g (transposed: row = value dim), formed in
-  // fp32 and rounded to bf16 into LDS; A_c is zero for a group's first chunk.
+
+  // S_g (fp32, transposed: element (value v, key k) at v * 128 + k) into
+  // the accumulators: acc[t] element e is key dim 32*wave + (e/4)*8 +
+  // half*4 + e%4, value dim t*32 + col.
+  floatx16 acc[4];
   {
-    const int g = chunk / kGroup;
-    const bool first = chunk == g * kGroup;
-    const float dec = expf(a.cdec[static_cast<int64_t>(chunk) * a.heads + h]);
     const float *sg = a.sg + (static_cast<int64_t>(g) * a.heads + h) * kD * kD;
-    const uint16_t *rl = a.rl + (static_cast<int64_t>(chunk) * a.heads + h) * kD * kD;
 #pragma unroll
-    for (int i = 0; i < kD * 16 / kThreads; ++i) {
-      const int piece = i * kThreads + tid;
-      const int row = piece >> 4;
-      const int ch = piece & 15;
-      const float4 s0 = *reinterpret_cast<const float4 *>(sg + row * kD + ch * 8);
-      const float4 s1 = *reinterpret_cast<const float4 *>(sg + row * kD + ch * 8 + 4);
-      Frag8 r;
-      r.u = first ? make_uint4(0, 0, 0, 0) : ld16(reinterpret_cast<const bf16_t *>(rl) + row * kD + ch * 8);
-      r.w[0] = cvt_pk_bf16(fmaf(dec, s0.x, bf16_lo(r.w[0])), fmaf(dec, s0.y, bf16_hi(r.w[0])));
-      r.w[1] = cvt_pk_bf16(fmaf(dec, s0.z, bf16_lo(r.w[1])), fmaf(dec, s0.w, bf16_hi(r.w[1])));
-      r.w[2] = cvt_pk_bf16(fmaf(dec, s1.x, bf16_lo(r.w[2])), fmaf(dec, s1.y, bf16_hi(r.w[2])));
-      r.w[3] = cvt_pk_bf16(fmaf(dec, s1.z, bf16_lo(r.w[3])), fmaf(dec, s1.w, bf16_hi(r.w[3])));
-      *reinterpret_cast<uint4 *>(lds_rv + swz<kD, kSwz>(row, ch * 8)) = r.u;
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 v = *reinterpret_cast<const float4 *>(sg + (t * 32 + col) * kD + wave * 32 + q4 * 8 + half * 4);
+        acc[t][q4 * 4 + 0] = v.x;
+        acc[t][q4 * 4 + 1] = v.y;
+        acc[t][q4 * 4 + 2] = v.z;
+        acc[t][q4 * 4 + 3] = v.w;
+      }
     }
   }
 
-  // Q^T as the B operand: lane holds query row 32*wave + col, dims ks*16 + half*8 .. +8.
   const int my_row = wave * 32 + col;
-  const bool row_valid = my_row < rows;
+  // Q^T of a chunk as the B operand: lane holds query row my_row, dims
+  // ks*16 + half*8 .. +8.  The next chunk's rows load while the current
+  // chunk's state step runs.
   Frag8 qf[kD / 16];
-  {
-    const bf16_t *qp = static_cast<const bf16_t *>(a.q) + ((t0 + (row_valid ? my_row : 0)) * a.heads + h) * kD + half * 8;
+  auto load_q = [&](int c) __attribute__((always_inline)) {
+    const int64_t t0 = static_cast<int64_t>(c) * kChunk;
+    const bool ok = t0 + my_row < a.n_tokens;
+    const bf16_t *qp = static_cast<const bf16_t *>(a.q) + ((t0 + (ok ? my_row : 0)) * a.heads + h) * kD + half * 8;
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks) qf[ks].u = row_valid ? ld16(qp + ks * 16) : make_uint4(0, 0, 0, 0);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+    for (int ks = 0; ks < kD / 16; ++ks) qf[ks].u = ok ? ld16(qp + ks * 16) : make_uint4(0, 0, 0, 0);
+  };
+  load_q(c_begin);
 
-  TrFrag fv;
-  fv.init(lane, kInterleave);   // V^T against P^T (the score accumulator order)
-  int koff[kD / 16];            // 16-byte reads of a row-major [.][128] tile: row col, dims ks*16 + half*8
+  for (int c = c_begin; c < c_end; ++c) {
+    // LDS read offsets are derived inside each chunk from an opaque copy of
+    // the lane index, so the compiler cannot keep them in registers across
+    // the whole loop (the state, O and P take most of them).
+    int lane_o = lane;
+    asm volatile("" : "+v"(lane_o));
+    int koff[kD / 16];  // 16-byte reads of a row-major [.][128] tile: row col, dims ks*16 + half*8
 #pragma unroll
-  for (int ks = 0; ks < kD / 16; ++ks) koff[ks] = swz<kD, kSwz>(col, ks * 16 + half * 8);
-  floatx16 oacc[4];
+    for (int ks = 0; ks < kD / 16; ++ks) koff[ks] = swz<kD, kSwz>(lane_o & 31, ks * 16 + (lane_o >> 5) * 8);
+    const int64_t t0 = static_cast<int64_t>(c) * kChunk;
+    const int rows = a.n_tokens - t0 < kChunk ? static_cast<int>(a.n_tokens - t0) : kChunk;
+    const bf16_t *kg = static_cast<const bf16_t *>(a.k) + (t0 * a.heads + h) * kD;
+    const bf16_t *vg = static_cast<const bf16_t *>(a.v) + (t0 * a.heads + h) * kD;
+    // Every wave is done with the previous chunk's K, V and key weights.
+    __syncthreads();
+    stage_rows(lds_k, kg, stride, rows, wave, lane);
+    if (tid < kChunk) s_l[tid] = tid < rows ? a.lcum[(t0 + tid) * a.heads + h] : 0.f;
+    // R_c (bf16, transposed: row = value dim) into LDS: four consecutive key
+    // dims per lane and (t, q4), 8-byte writes.
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
+    for (int t = 0; t < 4; ++t) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) oacc[d][e] = 0.f;
-  }
-  // Carried state: O^T = R^T Q^T (R^T rows d*32 + col from 16-byte reads),
-  // then row j times exp(l_j).
-#pragma unroll
-  for (int ks = 0; ks < kD / 16; ++ks) {
+      for (int q4 = 0; q4 < 4; ++q4) {
+        uint2 pk;
+        pk.x = cvt_pk_bf16(acc[t][q4 * 4 + 0], acc[t][q4 * 4 + 1]);
+        pk.y = cvt_pk_bf16(acc[t][q4 * 4 + 2], acc[t][q4 * 4 + 3]);
+        *reinterpret_cast<uint2 *>(lds_rv + swz<kD, kSwz>(t * 32 + col, wave * 32 + q4 * 8 + half * 4)) = pk;
+      }
+    }
+    const bool row_valid = my_row < rows;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // Key weights of the state step, exp(l_C - l_k) (read after a later barrier).
+    const float lc = s_l[rows - 1];
+    if (tid < kChunk) s_w[tid] = tid < rows ? expf(lc - s_l[tid]) : 0.f;
+
+    floatx16 oacc[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      Frag8 rf;
-      rf.u = *reinterpret_cast<const uint4 *>(lds_rv + d * 32 * kRowBytes + koff[ks]);
-      oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf.v, qf[ks].v, oacc[d], 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[d][e] = 0.f;
     }
-  }
-  const float l_row = s_l[row_valid ? my_row : 0];
-  const float carry = expf(l_row);
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) oacc[d][e] *= carry;
-  }
-  __syncthreads();  // every wave is done with R_c; V takes its buffer
-  stage_rows(lds_rv, vg, stride, rows, wave, lane);
-
-  // Scores of the chunk while V loads: 32-key halves u = 0 .. wave (keys <=
-  // the wave's rows), P = S exp(l_j - l_k) masked to k <= j, in bf16.
-  Frag8 p[kWaves][2];
-#pragma unroll
-  for (int u = 0; u < kWaves; ++u) {
-    if (u > wave) break;
-    floatx16 s;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) s[e] = 0.f;
-    const char *tk = lds_k + u * 32 * kRowBytes;
+    // Carried state: O^T = R^T Q^T (R^T rows d*32 + col from 16-byte reads),
+    // then row j times exp(l_j).
 #pragma unroll
     for (int ks = 0; ks < kD / 16; ++ks) {
-      Frag8 kf;
-      kf.u = *reinterpret_cast<const uint4 *>(tk + koff[ks]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v, qf[ks].v, s, 0, 0, 0);
-    }
-    // S^T element e is key 32u + (e/4)*8 + half*4 + e%4 of query row my_row.
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float pv[2];
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const int e = kk * 8 + 2 * j + x;
-          const int key = u * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
-          pv[x] = (key <= my_row) ? s[e] * expf(l_row - s_l[key]) : 0.f;
-        }
-        p[u][kk].w[j] = cvt_pk_bf16(pv[0], pv[1]);
-      }
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();  // V has landed for every wave
-  // O^T += V^T P^T over each half's two 16-key steps.
-#pragma unroll
-  for (int u = 0; u < kWaves; ++u) {
-    if (u > wave) break;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv.read(lds_rv + u * 32 * kRowBytes, d, kk), p[u][kk].v, oacc[d], 0, 0, 0);
+        Frag8 rf;
+        rf.u = *reinterpret_cast<const uint4 *>(lds_rv + d * 32 * kRowBytes + koff[ks]);
+        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf.v, qf[ks].v, oacc[d], 0, 0, 0);
       }
     }
-  }
-  if (!row_valid) return;
-  // oacc[d] element e is value dim d*32 + (e/4)*8 + half*4 + e%4 of row my_row.
-  float *op = a.o + ((t0 + my_row) * a.heads + h) * kD;
+    const float l_row = s_l[row_valid ? my_row : 0];
+    const float carry = expf(l_row);
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
+    for (int d = 0; d < 4; ++d) {
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      *reinterpret_cast<float4 *>(op + d * 32 + i4 * 8 + half * 4) =
-          make_float4(oacc[d][i4 * 4 + 0], oacc[d][i4 * 4 + 1], oacc[d][i4 * 4 + 2], oacc[d][i4 * 4 + 3]);
+      for (int e = 0; e < 16; ++e) oacc[d][e] *= carry;
+    }
+    __syncthreads();  // every wave is done with R_c; V takes its buffer
+    stage_rows(lds_rv, vg, stride, rows, wave, lane);
+
+    // Per 32-key half u = 0 .. wave (keys <= the wave's rows): S^T = K Q^T,
+    // P = S exp(l_j - l_k) masked to k <= j, in bf16, then O^T += V^T P^T
+    // over the half's two 16-key steps.  The first half's scores are formed
+    // while V loads.
+    TrFrag fv;
+    fv.init(lane_o, kInterleave);  // V^T against P^T (the score accumulator order)
+#pragma unroll
+    for (int u = 0; u < kWaves; ++u) {
+      if (u > wave) break;
+      floatx16 sc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[e] = 0.f;
+      const char *tk = lds_k + u * 32 * kRowBytes;
+#pragma unroll
+      for (int ks = 0; ks < kD / 16; ++ks) {
+        Frag8 kf;
+        kf.u = *reinterpret_cast<const uint4 *>(tk + koff[ks]);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.v, qf[ks].v, sc, 0, 0, 0);
+      }
+      // S^T element e is key 32u + (e/4)*8 + half*4 + e%4 of query row my_row.
+      Frag8 pf[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float pv[2];
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const int e = kk * 8 + 2 * j + x;
+            const int key = u * 32 + (e >> 2) * 8 + half * 4 + (e & 3);
+            pv[x] = (key <= my_row) ? sc[e] * expf(l_row - s_l[key]) : 0.f;
+          }
+          pf[kk].w[j] = cvt_pk_bf16(pv[0], pv[1]);
+        }
+      }
+      if (u == 0) {
+        // Every wave runs half 0: V has landed for every wave and the key
+        // weights are in place.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fv.read(lds_rv + u * 32 * kRowBytes, d, kk), pf[kk].v,
+                                                            oacc[d], 0, 0, 0);
+        }
+      }
+    }
+    if (row_valid) {
+      // oacc[d] element e is value dim d*32 + (e/4)*8 + half*4 + e%4 of row my_row.
+      float *op = a.o + ((t0 + my_row) * a.heads + h) * kD;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          *reinterpret_cast<float4 *>(op + d * 32 + i4 * 8 + half * 4) =
+              make_float4(oacc[d][i4 * 4 + 0], oacc[d][i4 * 4 + 1], oacc[d][i4 * 4 + 2], oacc[d][i4 * 4 + 3]);
+        }
+      }
+    }
+    // R_{c+1}; the state after the group's last chunk is the scan's.
+    if (c + 1 < c_end) {
+      load_q(c + 1);
+      TrFrag fr;
+      fr.init(lane_o, kSplitHalves);  // V against K'^T
+      const int ka0 = TrFrag::offset(lane_o, kSplitHalves, 0, wave);
+      const int ka1 = TrFrag::offset(lane_o, kSplitHalves, 1, wave);
+      state_step(acc, lds_k, lds_rv, s_w, ka0, ka1, fr, expf(lc), half);
     }
   }
 }
@@ -599,19 +757,17 @@ hipError_t launch_gret_recurrent(const GretArgs &a, int dtype, int head_dim, int
 }
 
 hipError_t launch_gret_chunked(const GretArgs &a, hipStream_t s) {
-  const int64_t n_chunks = gret_n_chunks(a.n_tokens);
   const int64_t n_groups = gret_n_groups(a.n_tokens);
-  const int64_t blocks = n_chunks * a.heads;
+  const int64_t blocks = n_groups * a.heads;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gret_group_state_kernel, dim3(static_cast<unsigned>(n_groups * a.heads)), dim3(gr::kThreads), 0,
-                     s, a);
+  hipLaunchKernelGGL(gret_group_state_kernel, dim3(static_cast<unsigned>(blocks)), dim3(gr::kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t scan_threads = static_cast<int64_t>(a.heads) * gr::kD * gr::kD / 4;
   hipLaunchKernelGGL(gret_group_scan_kernel, dim3(static_cast<unsigned>((scan_threads + 255) / 256)), dim3(256), 0, s,
                      a, static_cast<int>(n_groups));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(gret_chunk_out_kernel, dim3(static_cast<unsigned>(blocks)), dim3(gr::kThreads), 0, s, a);
+  hipLaunchKernelGGL(gret_group_out_kernel, dim3(static_cast<unsigned>(blocks)), dim3(gr::kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -52,9 +52,16 @@
 
 namespace yoco {
 
-template <int DH, int SWZ>
-__global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const PrefillArgs a) {
+// RB: 32-row blocks of query rows per wave (1: 8 waves, two per SIMD; 2: 4
+// waves of 64 rows, one per SIMD, every K and V operand read from LDS feeding
+// two MFMAs).  Each row block keeps its own Q^T, S^T, P^T, O^T and softmax
+// state and runs exactly the arithmetic of RB = 1, so results do not depend
+// on RB.
+template <int DH, int SWZ, int RB>
+__global__ __launch_bounds__(pf::kThreads / RB, 1) void prefill_bf16_kernel(const PrefillArgs a) {
   using S = PrefillShape<DH>;
+  constexpr int NW = pf::kWaves / RB;          // waves per workgroup
+  constexpr int kWaveRows = pf::kRowsPerWave * RB;
   // K and V tiles, two buffers each, as four separate arrays: the compiler
   // can then tell that reads of one buffer do not alias the direct-to-LDS
   // loads into another, and need not wait for those loads to land.  Every
@@ -70,7 +77,7 @@ __global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const Pre
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int half = lane >> 5;       // 0 or 1
-  const int col = lane & 31;        // the query row this lane owns (within the wave)
+  const int col = lane & 31;        // the query row this lane owns in each row block
 
   // Block -> (query tile, query head): units (qtile, g) longest first; the G
   // heads of a unit get consecutive slots on the same XCD.
@@ -96,12 +103,17 @@ __global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const Pre
   const int q_start = static_cast<int>(a.q_start);
   const int kv_len = static_cast<int>(a.kv_len);
   const int blk_row0 = qtile * pf::kBlockRows;
-  const int wave_row_first = blk_row0 + wave * pf::kRowsPerWave;
-  const int my_row = wave_row_first + col;
-  const bool row_valid = my_row < t;
-  const int my_pos = q_start + (row_valid ? my_row : (t - 1));
+  const int wave_row_first = blk_row0 + wave * kWaveRows;
+  int my_row[RB], my_pos[RB];
+  bool row_valid[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    my_row[rb] = wave_row_first + rb * 32 + col;
+    row_valid[rb] = my_row[rb] < t;
+    my_pos[rb] = q_start + (row_valid[rb] ? my_row[rb] : (t - 1));
+  }
   const bool wave_active = wave_row_first < t;
-  const int wave_last_row = min(wave_row_first + pf::kRowsPerWave, t) - 1;
+  const int wave_last_row = min(wave_row_first + kWaveRows, t) - 1;
   const int wave_pos_last = q_start + wave_last_row;
   const int wave_pos_first = q_start + wave_row_first;
   const int blk_last_row = min(blk_row0 + pf::kBlockRows, t) - 1;
@@ -109,17 +121,19 @@ __global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const Pre
   // 32-key halves this wave needs: 0 .. n_half-1 (keys up to its last row).
   const int n_half = wave_active ? wave_pos_last / 32 + 1 : 0;
 
-  StageOffsets<DH, SWZ> so;
+  StageOffsets<DH, SWZ, NW> so;
   so.init(wave, lane, row_stride_kv);
   // Start loading key tile 0 before touching Q.
-  stage_tile<DH, SWZ>(lds_k0, kg, row_stride_kv, 0, kv_len, wave, so);
+  stage_tile<DH, SWZ, NW>(lds_k0, kg, row_stride_kv, 0, kv_len, wave, so);
 
-  // Q^T as the MFMA B operand: lane holds row `col`, dims ks*16 + half*8 .. +8.
-  Frag8 qf[S::KSTEPS];
-  {
-    const bf16_t *qp = qg + (int64_t)(row_valid ? my_row : 0) * row_stride_q + (int64_t)h * DH + half * 8;
+  // Q^T as the MFMA B operand: lane holds row `col` of each row block, dims
+  // ks*16 + half*8 .. +8.
+  Frag8 qf[RB][S::KSTEPS];
 #pragma unroll
-    for (int ks = 0; ks < S::KSTEPS; ++ks) qf[ks].u = row_valid ? ld16(qp + ks * 16) : make_uint4(0, 0, 0, 0);
+  for (int rb = 0; rb < RB; ++rb) {
+    const bf16_t *qp = qg + (int64_t)(row_valid[rb] ? my_row[rb] : 0) * row_stride_q + (int64_t)h * DH + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < S::KSTEPS; ++ks) qf[rb][ks].u = row_valid[rb] ? ld16(qp + ks * 16) : make_uint4(0, 0, 0, 0);
   }
 
   // LDS read offsets within a tile.  K (A operand of S^T): row col of the
@@ -146,18 +160,23 @@ __global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const Pre
     for (int d = 0; d < S::DSUB; ++d) voff[r][d] = swz<DH, SWZ>(vrow + 8 * r, d * 32 + dcol);
   }
 
-  floatx16 oacc[S::DSUB];
-  float l_run;  // this lane's share of sum(p), from the bf16 p the MFMA uses
-  // Reference maximum (log2 units) of this lane's query row.  It is fixed
-  // from the row's first 32 keys, so O never needs rescaling: later
+  floatx16 oacc[RB][S::DSUB];
+  float l_run[RB];  // this lane's share of sum(p) per row block, from the bf16 p the MFMA uses
+  // Reference maximum (log2 units) of each of this lane's query rows.  It is
+  // fixed from the row's first 32 keys, so O never needs rescaling: later
   // probabilities may exceed 1.  A row whose probabilities sum to 2^60 or
   // more (or to inf/NaN) may have lost range, which makes the workgroup run
   // a pass that finds each row's largest maximum and then a final pass in
   // which that row's reference is its largest maximum (every probability of
   // the row is then <= 1); the other rows repeat their arithmetic.
-  float m_ref = -INFINITY;
-  float m_seen = -INFINITY;  // largest half maximum of this row (generic steps)
-  bool row_ovf = false;      // this row's sum reached the limit in the first pass
+  float m_ref[RB], m_seen[RB];
+  bool row_ovf[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_ref[rb] = -INFINITY;
+    m_seen[rb] = -INFINITY;  // largest half maximum of the row (generic steps)
+    row_ovf[rb] = false;     // the row's sum reached the limit in the first pass
+  }
   const uint32_t kOnesBf16x2 = 0x3F803F80u;  // (1.0, 1.0) in bf16
   __shared__ int redo_flag;
   if (tid == 0) redo_flag = 0;  // ordered before any update by the first barrier below
@@ -166,11 +185,12 @@ __global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const Pre
   //   PV(u-1): O^T += V^T P^T for half u-1      (MFMA)
   //   S(u+1):  S^T = K Q^T for half u+1          (MFMA)
   //   softmax of half u: P(u) from S(u)          (VALU)
-  // so the exps of one half run while the matrix cores work on its
-  // neighbours.  Halves 2p-1 and 2p form period p, which reads K tile p and
-  // V tile p-1 from LDS while K tile p+1 and V tile p are being loaded.
-  floatx16 sa, sb;     // S of the half being normalised / being computed
-  Frag8 pa[2], pb[2];  // P of the half being multiplied / being formed
+  // for every row block, so the exps of one half run while the matrix cores
+  // work on its neighbours.  Halves 2p-1 and 2p form period p, which reads K
+  // tile p and V tile p-1 from LDS while K tile p+1 and V tile p are being
+  // loaded.
+  floatx16 sa[RB], sb[RB];       // S of the half being normalised / being computed
+  Frag8 pa[RB][2], pb[RB][2];    // P of the half being multiplied / being formed
 
   // Operands of the step's MFMAs.  PV MFMA i (i < 2*DSUB) is dim tile i/2,
   // key step i%2 of the V half; S MFMA ks reads K rows of the K half.
@@ -189,16 +209,17 @@ __global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const Pre
   // P for accumulator pair j of key step kk: k-slot j of lane half `half`
   // in step kk is key kk*16 + (j/4)*8 + half*4 + (j%4), which is S^T
   // accumulator element kk*8 + j.
-  auto make_p_pair = [&](const floatx16 &s, Frag8 (&p)[2], int kk, int j) __attribute__((always_inline)) {
-    const float p0 = fast_exp2(fmaf(s[kk * 8 + 2 * j], a.scale_log2, -m_ref));
-    const float p1 = fast_exp2(fmaf(s[kk * 8 + 2 * j + 1], a.scale_log2, -m_ref));
+  auto make_p_pair = [&](const floatx16 &sv, Frag8 (&p)[2], float mref, int kk, int j) __attribute__((always_inline)) {
+    const float p0 = fast_exp2(fmaf(sv[kk * 8 + 2 * j], a.scale_log2, -mref));
+    const float p1 = fast_exp2(fmaf(sv[kk * 8 + 2 * j + 1], a.scale_log2, -mref));
     p[kk].w[j] = cvt_pk_bf16(p0, p1);
   };
 
-  // One step of the pipeline, scheduled by hand: chunk i issues MFMA i (the
-  // PV MFMAs, then the S MFMAs), the LDS reads of MFMA i+4 and one piece of
-  // the softmax of half u, with a scheduling fence between chunks, so the
-  // VALU work runs under the matrix work and few operands are in flight.
+  // One step of the pipeline, scheduled by hand: chunk i issues MFMA i of
+  // every row block (the PV MFMAs, then the S MFMAs), the LDS reads of the
+  // operand of MFMA i+4 and one piece of each row block's softmax of half u,
+  // with a scheduling fence between chunks, so the VALU work runs under the
+  // matrix work and few operands are in flight.
   // The generic form (first, causal-diagonal and last halves) adds only
   // selects, never branches, so O and S stay in fixed registers:
   //  * the causal mask;
@@ -211,30 +232,34 @@ __global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const Pre
   // the second's first kAhead MFMAs in its last chunks (into `carry`), so
   // the second starts without waiting for LDS.  link_c: 0 none, 1 fill
   // carry from tv + one half, 2 start from carry.
-  constexpr int kAhead = 4;  // LDS reads run this many MFMAs ahead
+  constexpr int kAhead = 4;  // LDS reads run this many operands ahead
   constexpr int kHalfBytes = 32 * S::kRowBytes;
   Frag8 carry[kAhead];
-  auto step = [&](auto generic_c, auto link_c, int u, const char *tk, const char *tv, floatx16 &s_cur,
-                  floatx16 &s_next, Frag8 (&p_prev)[2], Frag8 (&p_cur)[2]) __attribute__((always_inline)) {
+  auto step = [&](auto generic_c, auto link_c, int u, const char *tk, const char *tv, floatx16 (&s_cur)[RB],
+                  floatx16 (&s_next)[RB], Frag8 (&p_prev)[RB][2], Frag8 (&p_cur)[RB][2]) __attribute__((always_inline)) {
     constexpr bool kGeneric = decltype(generic_c)::value;
     constexpr int kLink = decltype(link_c)::value;
     constexpr int NPV = 2 * S::DSUB;
     constexpr int NM = NPV + S::KSTEPS;
-    // Softmax pieces: (generic only) the row maximum (4 pieces of 4
-    // elements) and its cross-lane exchange, then the probabilities (8
-    // pieces of one packed pair) and the running sum of P(u-1) (2 pieces).
-    // The fast form needs no maximum: the reference is fixed, and range is
-    // checked once, from the row sum, at the end of the pass.
+    // Softmax pieces of each row block: (generic only) the row maximum (4
+    // pieces of 4 elements) and its cross-lane exchange, then the
+    // probabilities (8 pieces of one packed pair) and the running sum of
+    // P(u-1) (2 pieces).  The fast form needs no maximum: the reference is
+    // fixed, and range is checked once, from the row sum, at the end of the
+    // pass.
     constexpr int kMax0 = 0, kXchg = kGeneric ? 4 : -1;
     constexpr int kP0 = kGeneric ? 5 : 0, kL0 = kP0 + 8, kPieces = kL0 + 2;
     const bool do_pv = !kGeneric || (u >= 1 && u - 1 < n_half);
     const bool do_soft = !kGeneric || (u >= 0 && u < n_half);
     if constexpr (kGeneric) {
       // Causal mask: accumulator element i is key 32u + (i/4)*8 + half*4 +
-      // (i%4) of query row `col` (a no-op below the wave's diagonal).
-      const int rel = min(my_pos - u * 32 - half * 4, 32);
+      // (i%4) of query row `col` of the block (a no-op below its diagonal).
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s_cur[i] = (i >> 2) * 8 + (i & 3) > rel ? -INFINITY : s_cur[i];
+      for (int rb = 0; rb < RB; ++rb) {
+        const int rel = min(my_pos[rb] - u * 32 - half * 4, 32);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s_cur[rb][i] = (i >> 2) * 8 + (i & 3) > rel ? -INFINITY : s_cur[rb][i];
+      }
     }
     Frag8 opnd[NM];
     auto issue_read = [&](int i) __attribute__((always_inline)) {
@@ -245,23 +270,27 @@ __global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const Pre
         opnd[i] = read_k(tk, i - NPV);
       }
     };
-    float tmax = s_cur[0];
-    float tmax_other = 0.f;
-    float l_add = 0.f;
-    auto piece = [&](int i) __attribute__((always_inline)) {
+    float tmax[RB], tmax_other[RB], l_add[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      tmax[rb] = s_cur[rb][0];
+      tmax_other[rb] = 0.f;
+      l_add[rb] = 0.f;
+    }
+    auto piece = [&](int rb, int i) __attribute__((always_inline)) {
       if (kGeneric && i >= kMax0 && i < kMax0 + 4) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, s_cur[(i - kMax0) * 4 + e]);
+        for (int e = 0; e < 4; ++e) tmax[rb] = fmaxf(tmax[rb], s_cur[rb][(i - kMax0) * 4 + e]);
       } else if (kGeneric && i == kXchg) {
-        tmax_other = shfl_xor_f(tmax, 32);
+        tmax_other[rb] = shfl_xor_f(tmax[rb], 32);
         // The row's first half (key 0 is always visible) sets the reference.
-        const float t = fmaxf(tmax, tmax_other) * a.scale_log2;
-        m_ref = (do_soft && m_ref == -INFINITY) ? t : m_ref;
+        const float tt = fmaxf(tmax[rb], tmax_other[rb]) * a.scale_log2;
+        m_ref[rb] = (do_soft && m_ref[rb] == -INFINITY) ? tt : m_ref[rb];
       } else if (i >= kP0 && i < kP0 + 8) {
-        make_p_pair(s_cur, p_cur, (i - kP0) >> 2, (i - kP0) & 3);
+        make_p_pair(s_cur[rb], p_cur[rb], m_ref[rb], (i - kP0) >> 2, (i - kP0) & 3);
       } else if (i >= kL0 && i < kL0 + 2) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) l_add = dot2_bf16_f32(p_prev[i - kL0].w[j], kOnesBf16x2, l_add);
+        for (int j = 0; j < 4; ++j) l_add[rb] = dot2_bf16_f32(p_prev[rb][i - kL0].w[j], kOnesBf16x2, l_add[rb]);
       }
     };
 #pragma unroll
@@ -279,30 +308,40 @@ __global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const Pre
       } else if constexpr (kLink == 1) {
         carry[i + kAhead - NM] = read_v(tv + kHalfBytes, i + kAhead - NM);
       }
-      if (i < NPV) {
-        oacc[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[i].v, p_prev[i & 1].v, oacc[i >> 1], 0, 0, 0);
-      } else {
-        if (i == NPV) {
 #pragma unroll
-          for (int e = 0; e < 16; ++e) s_next[e] = 0.f;
+      for (int rb = 0; rb < RB; ++rb) {
+        if (i < NPV) {
+          oacc[rb][i >> 1] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[i].v, p_prev[rb][i & 1].v, oacc[rb][i >> 1], 0, 0, 0);
+        } else {
+          if (i == NPV) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s_next[rb][e] = 0.f;
+          }
+          s_next[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[i].v, qf[rb][i - NPV].v, s_next[rb], 0, 0, 0);
         }
-        s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[i].v, qf[i - NPV].v, s_next, 0, 0, 0);
+        piece(rb, i);
       }
-      piece(i);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int i = NM; i < kPieces; ++i) piece(i);  // head_dim 64: fewer MFMAs than pieces
-    if constexpr (kGeneric) {
-      const float t = fmaxf(tmax, tmax_other) * a.scale_log2;
-      l_run += do_pv ? l_add : 0.f;
-      m_seen = do_soft ? fmaxf(m_seen, t) : m_seen;
+    for (int i = NM; i < kPieces; ++i) {  // head_dim 64: fewer MFMAs than pieces
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        if (!do_soft) p_cur[kk].u = make_uint4(0, 0, 0, 0);
+      for (int rb = 0; rb < RB; ++rb) piece(rb, i);
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if constexpr (kGeneric) {
+        const float tt = fmaxf(tmax[rb], tmax_other[rb]) * a.scale_log2;
+        l_run[rb] += do_pv ? l_add[rb] : 0.f;
+        m_seen[rb] = do_soft ? fmaxf(m_seen[rb], tt) : m_seen[rb];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          if (!do_soft) p_cur[rb][kk].u = make_uint4(0, 0, 0, 0);
+        }
+      } else {
+        l_run[rb] += l_add[rb];
       }
-    } else {
-      l_run += l_add;
     }
   };
 
@@ -320,9 +359,9 @@ __global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const Pre
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (decltype(inner_c)::value || p + 1 < n_ktiles)
-      stage_tile<DH, SWZ>(kbuf(kb ^ 1), kg, row_stride_kv, (p + 1) * pf::kKeyTile, kv_len, wave, so);
+      stage_tile<DH, SWZ, NW>(kbuf(kb ^ 1), kg, row_stride_kv, (p + 1) * pf::kKeyTile, kv_len, wave, so);
     if (decltype(inner_c)::value || p < n_ktiles)
-      stage_tile<DH, SWZ>(vbuf(kb), vg, row_stride_kv, p * pf::kKeyTile, kv_len, wave, so);
+      stage_tile<DH, SWZ, NW>(vbuf(kb), vg, row_stride_kv, p * pf::kKeyTile, kv_len, wave, so);
   };
   auto period_fast = [&](auto buf_c, int p) __attribute__((always_inline)) {
     constexpr int KB = decltype(buf_c)::value;  // K tile p sits in buffer p % 2
@@ -355,22 +394,25 @@ __global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const Pre
 
   for (int pass = 0;; ++pass) {
 #pragma unroll
-    for (int d = 0; d < S::DSUB; ++d) {
+    for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[d][i] = 0.f;
-    }
+      for (int d = 0; d < S::DSUB; ++d) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sa[i] = 0.f;
-      sb[i] = 0.f;
-    }
+        for (int i = 0; i < 16; ++i) oacc[rb][d][i] = 0.f;
+      }
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      pa[kk].u = make_uint4(0, 0, 0, 0);
-      pb[kk].u = make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < 16; ++i) {
+        sa[rb][i] = 0.f;
+        sb[rb][i] = 0.f;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        pa[rb][kk].u = make_uint4(0, 0, 0, 0);
+        pb[rb][kk].u = make_uint4(0, 0, 0, 0);
+      }
+      l_run[rb] = 0.f;
     }
-    l_run = 0.f;
-    if (pass > 0) stage_tile<DH, SWZ>(lds_k0, kg, row_stride_kv, 0, kv_len, wave, so);
+    if (pass > 0) stage_tile<DH, SWZ, NW>(lds_k0, kg, row_stride_kv, 0, kv_len, wave, so);
     period_generic(0);
     int p = 1;
     // The maximum-finding pass runs every period in the generic form.
@@ -383,57 +425,67 @@ __global__ __launch_bounds__(pf::kThreads, 1) void prefill_bf16_kernel(const Pre
     if (pass == 2) break;
     if (pass == 0) {
       // Range check: every probability of a row is below its sum.
-      const float l_sum = l_run + shfl_xor_f(l_run, 32);
-      row_ovf = !(l_sum < pf::kSumLimit);
-      if (__any(row_ovf) && lane == 0) redo_flag = 1;
+      bool any_ovf = false;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float l_sum = l_run[rb] + shfl_xor_f(l_run[rb], 32);
+        row_ovf[rb] = !(l_sum < pf::kSumLimit);
+        any_ovf |= row_ovf[rb];
+      }
+      if (__any(any_ovf) && lane == 0) redo_flag = 1;
       __syncthreads();
       if (redo_flag == 0) break;
-      m_seen = -INFINITY;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) m_seen[rb] = -INFINITY;
     } else {
       // Each row that overflowed takes its largest maximum as the reference
       // for the final pass; the other rows keep theirs and repeat the same
       // arithmetic, so a row's result never depends on the other rows of its
       // workgroup.
-      m_ref = row_ovf ? m_seen : m_ref;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) m_ref[rb] = row_ovf[rb] ? m_seen[rb] : m_ref[rb];
       __syncthreads();
     }
     // The barrier above also retires every read of the LDS tiles the next
     // pass overwrites.
   }
 
-  const float l_tot = l_run + shfl_xor_f(l_run, 32);
-  if (!row_valid) return;
-  const float inv = 1.0f / l_tot;
-  // O^T accumulator element i of tile d is dim d*32 + (i/4)*8 + half*4 + (i%4)
-  // of query row `col`.
-  if (a.o_bf16) {
-    bf16_t *op = static_cast<bf16_t *>(a.o) + (int64_t)my_row * row_stride_q + (int64_t)h * DH;
 #pragma unroll
-    for (int d = 0; d < S::DSUB; ++d) {
+  for (int rb = 0; rb < RB; ++rb) {
+    const float l_tot = l_run[rb] + shfl_xor_f(l_run[rb], 32);
+    if (!row_valid[rb]) continue;
+    const float inv = 1.0f / l_tot;
+    // O^T accumulator element i of tile d is dim d*32 + (i/4)*8 + half*4 + (i%4)
+    // of query row `col` of the block.
+    if (a.o_bf16) {
+      bf16_t *op = static_cast<bf16_t *>(a.o) + (int64_t)my_row[rb] * row_stride_q + (int64_t)h * DH;
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int dim = d * 32 + i4 * 8 + half * 4;
-        uint2 packed;
-        packed.x = cvt_pk_bf16(oacc[d][i4 * 4 + 0] * inv, oacc[d][i4 * 4 + 1] * inv);
-        packed.y = cvt_pk_bf16(oacc[d][i4 * 4 + 2] * inv, oacc[d][i4 * 4 + 3] * inv);
-        *reinterpret_cast<uint2 *>(op + dim) = packed;
+      for (int d = 0; d < S::DSUB; ++d) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int dim = d * 32 + i4 * 8 + half * 4;
+          uint2 packed;
+          packed.x = cvt_pk_bf16(oacc[rb][d][i4 * 4 + 0] * inv, oacc[rb][d][i4 * 4 + 1] * inv);
+          packed.y = cvt_pk_bf16(oacc[rb][d][i4 * 4 + 2] * inv, oacc[rb][d][i4 * 4 + 3] * inv);
+          *reinterpret_cast<uint2 *>(op + dim) = packed;
+        }
+      }
+    } else {
+      float *op = static_cast<float *>(a.o) + (int64_t)my_row[rb] * row_stride_q + (int64_t)h * DH;
+#pragma unroll
+      for (int d = 0; d < S::DSUB; ++d) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int dim = d * 32 + i4 * 8 + half * 4;
+          float4 v = make_float4(oacc[rb][d][i4 * 4 + 0] * inv, oacc[rb][d][i4 * 4 + 1] * inv,
+                                 oacc[rb][d][i4 * 4 + 2] * inv, oacc[rb][d][i4 * 4 + 3] * inv);
+          *reinterpret_cast<float4 *>(op + dim) = v;
+        }
       }
     }
-  } else {
-    float *op = static_cast<float *>(a.o) + (int64_t)my_row * row_stride_q + (int64_t)h * DH;
-#pragma unroll
-    for (int d = 0; d < S::DSUB; ++d) {
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int dim = d * 32 + i4 * 8 + half * 4;
-        float4 v = make_float4(oacc[d][i4 * 4 + 0] * inv, oacc[d][i4 * 4 + 1] * inv,
-                               oacc[d][i4 * 4 + 2] * inv, oacc[d][i4 * 4 + 3] * inv);
-        *reinterpret_cast<float4 *>(op + dim) = v;
-      }
+    if (a.lse != nullptr && half == 0) {
+      a.lse[(int64_t)my_row[rb] * a.n_q_heads + h] = (m_ref[rb] + log2f(l_tot)) * kLn2;
     }
-  }
-  if (a.lse != nullptr && half == 0) {
-    a.lse[(int64_t)my_row * a.n_q_heads + h] = (m_ref + log2f(l_tot)) * kLn2;
   }
 }
 
@@ -496,6 +548,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillArgs a) {
   if (a.lse != nullptr) a.lse[row * a.n_q_heads + h] = (m + log2f(l)) * kLn2;
 }
 
+constexpr int kPrefillRowBlocks = 1;  // 32-row blocks per wave
 constexpr int kPrefillSwizzle = 2;  // modes 1 and 2 both remove the 2-way V-read bank conflicts; 2 measured fastest
 
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, int head_dim, hipStream_t s) {
@@ -506,9 +559,11 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, int head_dim, hipStre
     const unsigned int blocks =
         static_cast<unsigned int>(((n_units + pf::kXcds - 1) / pf::kXcds) * pf::kXcds * group);
     if (head_dim == 128) {
-      hipLaunchKernelGGL((prefill_bf16_kernel<128, kPrefillSwizzle>), dim3(blocks), dim3(pf::kThreads), 0, s, a);
+      hipLaunchKernelGGL((prefill_bf16_kernel<128, kPrefillSwizzle, kPrefillRowBlocks>), dim3(blocks),
+                         dim3(pf::kThreads / kPrefillRowBlocks), 0, s, a);
     } else if (head_dim == 64) {
-      hipLaunchKernelGGL((prefill_bf16_kernel<64, kPrefillSwizzle>), dim3(blocks), dim3(pf::kThreads), 0, s, a);
+      hipLaunchKernelGGL((prefill_bf16_kernel<64, kPrefillSwizzle, kPrefillRowBlocks>), dim3(blocks),
+                         dim3(pf::kThreads / kPrefillRowBlocks), 0, s, a);
     } else {
       return hipErrorInvalidValue;
     }

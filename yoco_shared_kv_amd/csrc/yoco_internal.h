@@ -161,8 +161,8 @@ hipError_t launch_project_bwd(const ProjBwdArgs &a, hipStream_t s);
 // element (b * n_tokens + t) of q, k, v ([..][heads][D]), gate ([..][heads])
 // and o; one of n_seq and n_tokens is 1.  States are [n_seq][heads][D][D]
 // fp32 (state_in may be null: zero; state_out may be null; they may alias).
-// Chunkwise path workspace: lcum [n_tokens][heads] fp32, u [chunks][heads]
-// [D][D] fp32, rb [chunks][heads][D][D] bf16.
+// Chunkwise path workspace: lcum [n_tokens][heads], gdec [groups][heads],
+// tg and sg [groups][heads][D][D], all fp32.
 struct GretArgs {
   const void *q;
   const void *k;
@@ -172,9 +172,7 @@ struct GretArgs {
   float *state_out;
   float *o;
   float *lcum;      // [n][heads] inclusive cumulative log gates inside each chunk
-  float *cdec;      // [chunks][heads] log decay from the chunk's group start to the chunk
   float *gdec;      // [groups][heads] log decay over each group
-  uint16_t *rl;     // [chunks][heads][D][D] bf16 group-local state before each chunk (transposed)
   float *tg;        // [groups][heads][D][D] group-local state after each group (transposed)
   float *sg;        // [groups][heads][D][D] state entering each group (transposed)
   int64_t n_tokens;
