@@ -62,7 +62,7 @@ constexpr int kSwz = 2;
 constexpr int kRowBytes = kD * 2;                    // 256
 constexpr int kTileBytes = kChunk * kRowBytes;       // 32 KiB: [128][128] bf16
 constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // 8 one-KiB loads
-constexpr int kGroup = 8;          // chunks per group of the state kernel
+constexpr int kGroup = 8;          // chunks per group
 constexpr int kScanAhead = 8;      // group states in flight per thread in the scan
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // in 6:4, lgkmcnt in 11:8) that wait for vector memory only, down to 4 or 8
@@ -277,9 +277,10 @@ __device__ __forceinline__ void state_step(floatx16 (&acc)[4], const char *lds_k
 // start and L_G its value at the group's end (Lambda_g) -- the recurrence
 // A <- exp(l_C) A + U_c over the group's chunks from A = 0, summed in one
 // pass: no step depends on the previous one, so K and V stream through LDS
-// in 64-row sub-tiles, two stages deep.  Wave 0 first scans the group's
-// gates: 16 consecutive positions per lane, lane totals scanned over the
-// wave for L and over each 8-lane segment (one chunk) for the chunk-local
+// in 32-row sub-tiles, a ring of four with three in flight.  Wave 0 first
+// scans the group's
+// gates: kGroup * 2 consecutive positions per lane, lane totals scanned over
+// the wave for L and over each lane segment of one chunk for the chunk-local
 // cumulative sums l that go to the workspace for the output kernel; the key
 // weights exp(L_G - L_k) go to LDS.  The weighted K^T fragments are rounded
 // to bf16.  T_g lives in the MFMA accumulators: wave w owns rows (key dims)
@@ -292,9 +293,10 @@ __global__ __launch_bounds__(gr::kThreads, 2) void gret_group_state_kernel(const
   constexpr int kSubBytes = kSubRows * kRowBytes;        // 8 KiB of K (and of V)
   constexpr int kStages = 4;                             // ring of sub-tiles: three in flight
   constexpr int kLoadsPerStage = 2 * kSubBytes / 1024 / kWaves;  // vector memory ops per wave per stage (K and V)
-  constexpr int kGroupRows = kGroup * kChunk;            // 1024 positions
-  constexpr int kPerLane = kGroupRows / 64;              // 16 positions per lane of the scan
-  static_assert(kChunk / kPerLane == 8, "one chunk = 8 lanes of the scan");
+  constexpr int kGroupRows = kGroup * kChunk;            // positions per group
+  constexpr int kPerLane = kGroupRows / 64;              // positions per lane of the scan
+  constexpr int kChunkLanes = kChunk / kPerLane;         // lanes of the scan per chunk
+  static_assert(kGroupRows % 64 == 0 && kChunk % kPerLane == 0, "whole chunks per lane segment");
   static_assert(kLoadsPerStage == 4, "the counted waits below assume 4 loads per wave per stage");
   // One array per ring slot, selected at compile time: the compiler can then
   // tell that reads of one slot do not alias the direct-to-LDS loads still
@@ -381,15 +383,15 @@ __global__ __launch_bounds__(gr::kThreads, 2) void gret_group_state_kernel(const
       tot += lg[i];
     }
     // Inclusive scans of the lane totals: over the wave (L) and over each
-    // 8-lane segment (the chunk).
+    // segment of kChunkLanes lanes (the chunk).
     float incl = tot, seg = tot;
 #pragma unroll
     for (int sft = 1; sft < 64; sft <<= 1) {
       const float o = __shfl_up(incl, sft, 64);
       if (lane >= sft) incl += o;
-      if (sft < 8) {
+      if (sft < kChunkLanes) {
         const float os = __shfl_up(seg, sft, 64);
-        if ((lane & 7) >= sft) seg += os;
+        if ((lane & (kChunkLanes - 1)) >= sft) seg += os;
       }
     }
     const float total = __shfl(incl, 63, 64);  // L_G (positions past the group add 0)
