@@ -233,6 +233,9 @@ __global__ __launch_bounds__(pf::kThreads / RB, 1) void prefill_bf16_kernel(cons
   // the second starts without waiting for LDS.  link_c: 0 none, 1 fill
   // carry from tv + one half, 2 start from carry.
   constexpr int kAhead = 4;  // LDS reads run this many operands ahead
+  // The linked steps carry the next step's first kAhead operands, which must
+  // all be V operands.
+  static_assert(kAhead <= 2 * S::DSUB, "read-ahead deeper than one step's V operands");
   constexpr int kHalfBytes = 32 * S::kRowBytes;
   Frag8 carry[kAhead];
   auto step = [&](auto generic_c, auto link_c, int u, const char *tk, const char *tv, floatx16 (&s_cur)[RB],
