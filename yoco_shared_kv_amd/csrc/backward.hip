@@ -225,22 +225,34 @@ __global__ __launch_bounds__(pf::kThreads, 1) void bwd_dq_kernel(const BwdArgs a
 #pragma unroll
         for (int ks = 0; ks < S::KSTEPS; ++ks) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows(tv, ks).v, of[ks].v, dp, 0, 0, 0);
         // Element i is key 32u + (i/4)*8 + half*4 + (i%4) of query row `col`.
-        const int rel = min(my_pos - u * 32 - half * 4, 32);
+        // kMask: the half reaches past the first row of the wave (near the
+        // diagonal) or the wave has rows past the block; the other halves
+        // skip the per-element test.
         Frag8 dsf[2];
+        auto soft = [&](auto mask_c) __attribute__((always_inline)) {
+          const int rel = min(my_pos - u * 32 - half * 4, 32);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+          for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float ds[2];
+            for (int j = 0; j < 4; ++j) {
+              float ds[2];
 #pragma unroll
-            for (int e2 = 0; e2 < 2; ++e2) {
-              const int e = kk * 8 + 2 * j + e2;
-              const bool vis = (e >> 2) * 8 + (e & 3) <= rel;
-              const float p = vis ? fast_exp2(fmaf(s[e], a.scale_log2, -lse2)) : 0.f;
-              ds[e2] = p * (dp[e] - dterm);
+              for (int e2 = 0; e2 < 2; ++e2) {
+                const int e = kk * 8 + 2 * j + e2;
+                float p = fast_exp2(fmaf(s[e], a.scale_log2, -lse2));
+                if constexpr (decltype(mask_c)::value) p = (e >> 2) * 8 + (e & 3) <= rel ? p : 0.f;
+                ds[e2] = p * (dp[e] - dterm);
+              }
+              dsf[kk].w[j] = cvt_pk_bf16(ds[0], ds[1]);
             }
-            dsf[kk].w[j] = cvt_pk_bf16(ds[0], ds[1]);
           }
+        };
+        // Every row of the wave is a row of the block at a position at or
+        // past the half's last key (wave-uniform).
+        if (wave_row_first + 31 < t && q_start + wave_row_first >= u * 32 + 31) {
+          soft(std::false_type());
+        } else {
+          soft(std::true_type());
         }
 #pragma unroll
         for (int i = 0; i < 2 * S::DSUB; ++i) {
