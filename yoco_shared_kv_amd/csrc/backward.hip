@@ -198,8 +198,12 @@ __global__ __launch_bounds__(pf::kThreads, 1) void bwd_dq_kernel(const BwdArgs a
   }
   constexpr int kHalfBytes = 32 * S::kRowBytes;
 
-  for (int kt = 0; kt < n_ktiles; ++kt) {
-    const int b = kt & 1;
+  // Tile kt sits in buffers kt % 2; the loop runs two tiles per pass so the
+  // buffer of each is a compile-time choice: the compiler can then tell
+  // that the reads of tile kt do not alias the loads of tile kt+1 still
+  // landing in the other buffers, and does not wait for them.
+  auto tile = [&](auto b_c, int kt) __attribute__((always_inline)) {
+    constexpr int b = decltype(b_c)::value;
     // Tile kt has landed for every wave, and every wave is done with tile
     // kt-1, whose buffers the next loads overwrite.
     __builtin_amdgcn_s_waitcnt(0);
@@ -261,6 +265,10 @@ __global__ __launch_bounds__(pf::kThreads, 1) void bwd_dq_kernel(const BwdArgs a
         }
       }
     }
+  };
+  for (int kt = 0; kt < n_ktiles; kt += 2) {
+    tile(std::integral_constant<int, 0>(), kt);
+    if (kt + 1 < n_ktiles) tile(std::integral_constant<int, 1>(), kt + 1);
   }
   if (!row_valid) return;
   // dQ^T element i of tile d is dim d*32 + (i/4)*8 + half*4 + (i%4) of row `col`.
