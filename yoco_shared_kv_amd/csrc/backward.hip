@@ -198,6 +198,77 @@ __global__ __launch_bounds__(pf::kThreads, 1) void bwd_dq_kernel(const BwdArgs a
   }
   constexpr int kHalfBytes = 32 * S::kRowBytes;
 
+  // A whole tile without masks, scheduled by hand: the products of both
+  // halves in the order S0, dP0, S1, dP1, dQ0, dQ1 (each half's dQ products
+  // in the order of the per-half form, so the sums are the same), with the
+  // LDS reads three products ahead and one piece of a half's dS work between
+  // products: half 0's while S1 and dP1 run, half 1's while dQ0 runs.
+  auto pair_step = [&](const char *tk, const char *tv) __attribute__((always_inline)) {
+    constexpr int KS = S::KSTEPS;        // S (or dP) products per half
+    constexpr int NS = 2 * KS;           // S and dP products per half
+    constexpr int NQ = 2 * S::DSUB;      // dQ products per half
+    constexpr int NM = 2 * NS + 2 * NQ;  // products of the tile
+    constexpr int kAhead = 3;          // 4 spills at two waves per SIMD
+    floatx16 sv[2], dpv[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sv[h][i] = 0.f;
+        dpv[h][i] = 0.f;
+      }
+    }
+    Frag8 dsf[2][2];
+    auto read = [&](int i) __attribute__((always_inline)) {
+      if (i < 2 * NS) {
+        const int h = i / NS, r = i % NS;
+        return read_rows((r < KS ? tk : tv) + h * kHalfBytes, r % KS);
+      }
+      const int h = (i - 2 * NS) / NQ, r = (i - 2 * NS) % NQ;
+      return read_tr(tk + h * kHalfBytes, r >> 1, r & 1);
+    };
+    auto product = [&](int i, const Frag8 &op) __attribute__((always_inline)) {
+      if (i < 2 * NS) {
+        const int h = i / NS, r = i % NS;
+        if (r < KS) {
+          sv[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op.v, qf[r].v, sv[h], 0, 0, 0);
+        } else {
+          dpv[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op.v, of[r - KS].v, dpv[h], 0, 0, 0);
+        }
+      } else {
+        const int h = (i - 2 * NS) / NQ, r = (i - 2 * NS) % NQ;
+        dqacc[r >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op.v, dsf[h][r & 1].v, dqacc[r >> 1], 0, 0, 0);
+      }
+    };
+    // Piece k (0..7) of half h: accumulator elements kk*8 + 2j, +1 with
+    // kk = k / 4, j = k % 4 (k-slot j of key step kk).
+    auto piece = [&](int h, int k) __attribute__((always_inline)) {
+      const int kk = k >> 2, j = k & 3;
+      float ds[2];
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        const int e = kk * 8 + 2 * j + e2;
+        const float p = fast_exp2(fmaf(sv[h][e], a.scale_log2, -lse2));
+        ds[e2] = p * (dpv[h][e] - dterm);
+      }
+      dsf[h][kk].w[j] = cvt_pk_bf16(ds[0], ds[1]);
+    };
+    Frag8 opnd[NM];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) opnd[i] = read(i);
+#pragma clang loop unroll(full)
+    for (int i = 0; i < NM; ++i) {
+      if (i + kAhead < NM) opnd[i + kAhead] = read(i + kAhead);
+      product(i, opnd[i]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (i == NS + ((k + 1) * NS) / 8 - 1) piece(0, k);  // during S1, dP1
+        if (i == 2 * NS + (k * NQ) / 8) piece(1, k);        // during dQ0
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   // Tile kt sits in buffers kt % 2; the loop runs two tiles per pass so the
   // buffer of each is a compile-time choice: the compiler can then tell
   // that the reads of tile kt do not alias the loads of tile kt+1 still
@@ -211,6 +282,12 @@ __global__ __launch_bounds__(pf::kThreads, 1) void bwd_dq_kernel(const BwdArgs a
     if (kt + 1 < n_ktiles) {
       stage_tile<DH, SWZ>(kbuf(b ^ 1), kg, row_stride_kv, (kt + 1) * pf::kKeyTile, kv_len, wave, so);
       stage_tile<DH, SWZ>(vbuf(b ^ 1), vg, row_stride_kv, (kt + 1) * pf::kKeyTile, kv_len, wave, so);
+    }
+    // Both halves in range and every row of the wave a row of the block at
+    // or past the tile's last key (wave-uniform): the pipelined pair.
+    if (2 * kt + 1 < n_half && wave_row_first + 31 < t && q_start + wave_row_first >= kt * pf::kKeyTile + 63) {
+      pair_step(kbuf(b), vbuf(b));
+      return;
     }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
