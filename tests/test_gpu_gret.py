@@ -52,6 +52,10 @@ def _dev(c):
     (2049, 1, 128, W.BF16, 16.0, False),  # 17 chunks: the last group is one chunk of one position
     (3000, 2, 128, W.BF16, 1.0, False),   # strong decay across groups
     (128, 2, 128, W.BF16, 16.0, False),   # exactly one chunk
+    (1024, 2, 128, W.BF16, 16.0, True),   # exactly one group of 8 chunks (32 whole 32-row sub-tiles)
+    (1025, 1, 128, W.BF16, 4.0, True),    # one group and a second group of one position
+    (4096, 3, 128, W.BF16, 16.0, True),   # four whole groups chained through the scan
+    (1100, 2, 128, W.BF16, 16.0, False),  # second group of 76 positions: 3 sub-tiles, the last ragged
     (1, 2, 128, W.BF16, 16.0, True),      # one position
     (257, 2, 64, W.BF16, 16.0, True),     # head dim 64: recurrent path on bf16 values
     (200, 2, 128, W.F32, 16.0, True),     # fp32: recurrent path
