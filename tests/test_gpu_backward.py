@@ -79,6 +79,10 @@ def _forward(c, o_dtype=torch.float32):
     (130, 24, 8, 128, 0),     # the 3B head layout
     (1, 6, 2, 128, 0),        # one row, one key
     (257, 3, 1, 128, 256),    # one row at position 256 (last prompt token)
+    (600, 8, 4, 128, 0),      # G = 2; the dQ kernel's unmasked tile pairs below the diagonal
+    (520, 16, 4, 64, 0),      # G = 4, head_dim 64 (unmasked tile pairs at 4 products per half)
+    (400, 12, 2, 128, 37),    # G = 6 with q_start > 0
+    (330, 16, 2, 128, 0),     # G = 8
 ])
 def test_backward_matches_oracle(n, hq, hkv, dh, q_start):
     c = W.make_prefill(n=n, n_q_heads=hq, n_kv_heads=hkv, head_dim=dh, seed=51, q_start=q_start)
