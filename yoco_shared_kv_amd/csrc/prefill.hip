@@ -551,7 +551,9 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const PrefillArgs a) {
   if (a.lse != nullptr) a.lse[row * a.n_q_heads + h] = (m + log2f(l)) * kLn2;
 }
 
-constexpr int kPrefillRowBlocks = 1;  // 32-row blocks per wave
+// 32-row blocks per wave.  2 (4 waves of 64 rows, one per SIMD) gives the same
+// bits and halves the LDS reads per product, but ran slower.
+constexpr int kPrefillRowBlocks = 1;
 constexpr int kPrefillSwizzle = 2;  // modes 1 and 2 both remove the 2-way V-read bank conflicts; 2 measured fastest
 
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, int head_dim, hipStream_t s) {
