@@ -25,11 +25,14 @@
 //
 // A workgroup is 8 waves and computes 256 input rows x 256 output columns of
 // one weight, in wave tiles of 64 x 128 (32 x 256 with a gain).  The
-// reduction runs in slices of 64, staged global -> LDS with 16-byte buffer
-// loads to LDS, two stages deep: x slice [256][64] (128-byte rows, chunk
-// index XOR row%8), W slice [64][256] as two [64][128] halves (256-byte rows,
-// chunk index XOR a 4-bit function of the row).  The x descriptor ends at the
-// last input row, so rows past it load as zeros and are not stored.
+// reduction runs in slices of 32, staged global -> LDS with 16-byte buffer
+// loads to LDS through a ring of four slots, three slices in flight while
+// the fourth is read: x slice [256][32] (64-byte rows, chunk index XOR
+// (row/4)%4), W slice [32][256] as two [32][128] halves (256-byte rows,
+// chunk index XOR a 4-bit function of the row).  The x descriptor ends at
+// the last input row, so rows past it load as zeros and are not stored.
+#include <type_traits>
+
 #include "device_common.h"
 #include "rope.h"
 #include "yoco_internal.h"
@@ -49,11 +52,13 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRows = 256;                      // input rows per workgroup
 constexpr int kCols = 256;                      // output columns per workgroup
-constexpr int kK = 64;                          // reduction slice per stage
-constexpr int kXRowBytes = kK * 2;              // 128
-constexpr int kXTileBytes = kRows * kXRowBytes;  // 32 KiB
+constexpr int kK = 32;                          // reduction slice per stage
+constexpr int kStages = 4;                      // LDS ring slots (three slices in flight)
+constexpr int kXRowBytes = kK * 2;              // 64
+constexpr int kXTileBytes = kRows * kXRowBytes;  // 16 KiB
 constexpr int kWRowBytes = 128 * 2;             // one half: 128 columns
-constexpr int kWHalfBytes = kK * kWRowBytes;    // 16 KiB
+constexpr int kWHalfBytes = kK * kWRowBytes;    // 8 KiB
+constexpr int kWHalfBlocks = kWHalfBytes / 1024;         // 1 KiB load blocks per W half
 constexpr int kXLoads = kXTileBytes / 1024 / kWaves;     // 1 KiB loads per wave per stage
 constexpr int kXcds = 8;
 constexpr int64_t kNarrowBelowTiles = 256;      // 256-column tiles fill the device from this many
@@ -74,6 +79,15 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
+
+// Chunk-index XOR of an x tile row (4 chunks of 16 bytes): 16 consecutive
+// rows read at one chunk index fall on 16 different 16-byte bank groups.
+__device__ __forceinline__ int x_xor(int row) { return (row >> 2) & 3; }
+
+// s_waitcnt immediate that waits for vector memory only, down to n
+// outstanding operations (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// in 6:4, lgkmcnt in 11:8).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // Chunk-index XOR of a W half-tile row (16 chunks of 16 bytes).
 __device__ __forceinline__ int w_xor(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
@@ -112,13 +126,45 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
   constexpr int kWaveCols = Sh::kWaveCols;
   constexpr int NT = Sh::NT;
   constexpr int kRB = Sh::kRB;
+  // One array per ring slot, selected at compile time: the compiler can then
+  // tell that reads of one slot do not alias the direct-to-LDS loads still
+  // landing in the others, and waits only as the counted waits below say.
   __shared__ __attribute__((aligned(1024))) char lds_x0[kXTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_x1[kXTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_x2[kXTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_x3[kXTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_w0[kHalves * kWHalfBytes];
   __shared__ __attribute__((aligned(1024))) char lds_w1[kHalves * kWHalfBytes];
-  __shared__ __attribute__((aligned(1024))) float lds_g0[256];
-  __shared__ __attribute__((aligned(1024))) float lds_g1[256];
+  __shared__ __attribute__((aligned(1024))) char lds_w2[kHalves * kWHalfBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_w3[kHalves * kWHalfBytes];
+  // Gains of a slice: each wave stages its own copy (64 floats, of which the
+  // slice's 32 are read), so every wave issues the same loads.
+  __shared__ __attribute__((aligned(1024))) float lds_g0[kWaves * 64];
+  __shared__ __attribute__((aligned(1024))) float lds_g1[kWaves * 64];
+  __shared__ __attribute__((aligned(1024))) float lds_g2[kWaves * 64];
+  __shared__ __attribute__((aligned(1024))) float lds_g3[kWaves * 64];
   __shared__ double lds_rev[64];  // RoPE turns per position, per pair of a head
+  auto xslot = [&](auto b_c) __attribute__((always_inline)) -> char * {
+    constexpr int B = decltype(b_c)::value;
+    if constexpr (B == 0) return lds_x0;
+    else if constexpr (B == 1) return lds_x1;
+    else if constexpr (B == 2) return lds_x2;
+    else return lds_x3;
+  };
+  auto wslot = [&](auto b_c) __attribute__((always_inline)) -> char * {
+    constexpr int B = decltype(b_c)::value;
+    if constexpr (B == 0) return lds_w0;
+    else if constexpr (B == 1) return lds_w1;
+    else if constexpr (B == 2) return lds_w2;
+    else return lds_w3;
+  };
+  auto gslot = [&](auto b_c) __attribute__((always_inline)) -> float * {
+    constexpr int B = decltype(b_c)::value;
+    if constexpr (B == 0) return lds_g0;
+    else if constexpr (B == 1) return lds_g1;
+    else if constexpr (B == 2) return lds_g2;
+    else return lds_g3;
+  };
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -150,11 +196,17 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
       __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(wg), 0, d * a.ncols * 2, kBufferFlags);
   __amdgpu_buffer_rsrc_t g_rsrc;
   if constexpr (kGain) g_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.gain), 0, d * 4, kBufferFlags);
+  // Descriptors of zero size for the slices past the last one: every lane is
+  // out of range, so those loads touch no memory (they land zeros in a slot
+  // nobody reads).  Issuing them keeps the staging unconditional, and with it
+  // the count of loads in flight the same at every step.
+  const __amdgpu_buffer_rsrc_t x_none = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(xg), 0, 0, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t w_none = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t *>(wg), 0, 0, kBufferFlags);
 
-  // Per-lane byte offsets of this wave's staging loads.  x block b (8 rows):
-  // lane L -> row b*8 + L/8, LDS slot L%8 holding global chunk slot^(row%8).
-  // W block b (4 rows of half b/16): lane L -> row (b%16)*4 + L/16, slot
-  // L%16 holding global chunk slot^w_xor(row).
+  // Per-lane byte offsets of this wave's staging loads.  x block b (16
+  // rows): lane L -> row b*16 + L/4, LDS slot L%4 holding global chunk
+  // slot^x_xor(row).  W block b (4 rows of half b/8): lane L -> row
+  // (b%8)*4 + L/16, slot L%16 holding global chunk slot^w_xor(row).
   // (wsoff has its 256-column size for both widths: host compilation drops
   // the kernel's instantiation when the buffer-load builtins below see an
   // operand whose type depends on NCOLS.)
@@ -162,49 +214,57 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
   uint32_t xsoff[kXLoads], wsoff[kWLoadsMax];
 #pragma unroll
   for (int i = 0; i < kXLoads; ++i) {
-    const int row = (wave * kXLoads + i) * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ (row & 7);
+    const int row = (wave * kXLoads + i) * 16 + (lane >> 2);
+    const int chunk = (lane & 3) ^ x_xor(row);
     xsoff[i] = static_cast<uint32_t>(row * d * 2 + chunk * 16);
   }
 #pragma unroll
   for (int i = 0; i < kWLoadsMax; ++i) {
     const int blk = wave * Sh::kWLoadsT + (i < Sh::kWLoadsT ? i : 0);
-    const int k = (blk & 15) * 4 + (lane >> 4);
+    const int k = (blk % kWHalfBlocks) * 4 + (lane >> 4);
     const int chunk = (lane & 15) ^ w_xor(k);
-    wsoff[i] = static_cast<uint32_t>((k * a.ncols + (blk >> 4) * 128) * 2 + chunk * 16);
+    wsoff[i] = static_cast<uint32_t>((k * a.ncols + (blk / kWHalfBlocks) * 128) * 2 + chunk * 16);
   }
-  auto stage = [&](char *xdst, char *wdst, float *gdst, int s) __attribute__((always_inline)) {
-    const uint32_t k0 = static_cast<uint32_t>(s * kK);
+  auto stage = [&](auto b_c, int s) __attribute__((always_inline)) {
+    char *xdst = xslot(b_c);
+    char *wdst = wslot(b_c);
+    float *gdst = gslot(b_c);
+    const bool live = s < n_stages;  // block-uniform
+    const int sl = live ? s : 0;
+    const uint32_t k0 = static_cast<uint32_t>(sl * kK);
+    const __amdgpu_buffer_rsrc_t xr = live ? x_rsrc : x_none;
+    const __amdgpu_buffer_rsrc_t wr_ = live ? w_rsrc : w_none;
 #pragma unroll
     for (int i = 0; i < kXLoads; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, (lds_void_t *)(xdst + (wave * kXLoads + i) * 1024), 16, xsoff[i],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t *)(xdst + (wave * kXLoads + i) * 1024), 16, xsoff[i],
                                                k0 * 2, 0, 0);
     }
     const uint32_t wbase = (k0 * a.ncols + col0) * 2;
 #pragma unroll
     for (int i = 0; i < kWLoadsMax; ++i) {
       if (i >= Sh::kWLoadsT) break;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_t *)(wdst + (wave * Sh::kWLoadsT + i) * 1024), 16, wsoff[i],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr_, (lds_void_t *)(wdst + (wave * Sh::kWLoadsT + i) * 1024), 16, wsoff[i],
                                                wbase, 0, 0);
     }
     if constexpr (kGain) {
-      // 64 gains of this slice (lanes 16..63 fetch the next ones, unused).
-      // The slice offset goes into the per-lane offset, not the scalar one:
-      // the range check of a raw buffer load sees only the per-lane offset,
-      // so past the last slice those lanes read zeros, never past the gains.
-      if (wave == 0) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(g_rsrc, (lds_void_t *)gdst, 16, lane * 16u + k0 * 4, 0, 0, 0);
-      }
+      // The 32 gains of this slice, 4 bytes per lane (lanes 32..63 fetch the
+      // next ones, unused).  The slice offset goes into the per-lane offset,
+      // not the scalar one: the range check of a raw buffer load sees only
+      // the per-lane offset, so past the last slice those lanes read zeros,
+      // never past the gains.
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(g_rsrc, (lds_void_t *)(gdst + wave * 64), 4, lane * 4u + k0 * 4, 0, 0, 0);
     }
   };
 
   // Wave tile: rows wr*kWaveRows + s*32 (s < kRB), columns wc*kWaveCols + t*32 (t < NT).
   const int wr = wave % Sh::kWavesR;
   const int wc = wave / Sh::kWavesR;
-  // B (x^T) read: row wr*kWaveRows + s*32 + col, chunk 2*ks + half; row % 8 = col % 8.
-  int xoff[4];
+  // B (x^T) read: row wr*kWaveRows + s*32 + col, chunk 2*ks + half;
+  // x_xor(row) = x_xor(col) (wave rows start at multiples of 32).
+  constexpr int kKSteps = kK / 16;
+  int xoff[kKSteps];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) xoff[ks] = (wr * Sh::kWaveRows + col) * kXRowBytes + (((2 * ks + half) ^ (col & 7)) << 4);
+  for (int ks = 0; ks < kKSteps; ++ks) xoff[ks] = (wr * Sh::kWaveRows + col) * kXRowBytes + (((2 * ks + half) ^ x_xor(col)) << 4);
   // A (W^T) reads: in each 16-lane group, source lane a + 4j points at k row
   // kb + j, columns cb + 4a .. +3, and lane i of the group receives k rows
   // kb..kb+3 of column cb + i.  Lanes 0..31 take k rows 0..7 of the step (two
@@ -240,7 +300,7 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
 
   auto compute = [&](const char *xt, const char *wt, const float *gt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < kKSteps; ++ks) {
       Frag8 b[kRB];
 #pragma unroll
       for (int s2 = 0; s2 < kRB; ++s2) b[s2].u = *reinterpret_cast<const uint4 *>(xt + xoff[ks] + s2 * 32 * kXRowBytes);
@@ -256,8 +316,8 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
         for (int j = 0; j < 4; ++j) sumsq[s2] = dot2_bf16(b[s2].w[j], b[s2].w[j], sumsq[s2]);
       }
       if constexpr (kGain) {
-        const float4 g0 = *reinterpret_cast<const float4 *>(gt + ks * 16 + half * 8);
-        const float4 g1 = *reinterpret_cast<const float4 *>(gt + ks * 16 + half * 8 + 4);
+        const float4 g0 = *reinterpret_cast<const float4 *>(gt + wave * 64 + ks * 16 + half * 8);
+        const float4 g1 = *reinterpret_cast<const float4 *>(gt + wave * 64 + ks * 16 + half * 8 + 4);
         const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
         for (int s2 = 0; s2 < kRB; ++s2) {
@@ -290,21 +350,42 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
     }
   };
 
-  // n_stages is even (d_model % 128 == 0), so the loop runs whole pairs and
-  // the accumulators never leave it from two places.
-  stage(lds_x0, lds_w0, lds_g0, 0);
-  for (int s = 0; s < n_stages; s += 2) {
-    // Stage s has landed for every wave and every wave is done with stage
-    // s-1, whose buffers the next loads overwrite.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    stage(lds_x1, lds_w1, lds_g1, s + 1);
-    compute(lds_x0, lds_w0, lds_g0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (s + 2 < n_stages) stage(lds_x0, lds_w0, lds_g0, s + 2);
-    compute(lds_x1, lds_w1, lds_g1);
+  // Vector memory operations per wave per slice, for the counted waits.
+  constexpr int kLoads = kXLoads + Sh::kWLoadsT + (kGain ? 1 : 0);
+  // Slice s sits in ring slot s % 4; n_stages is a multiple of 4 (d_model %
+  // 128 == 0), so the loop runs four slices per pass and every slot is a
+  // compile-time choice.  Every step stages a slice (the last three steps
+  // stage empty ones), so the compiler's own wait tracking sees the same
+  // loads in flight on every path and needs no wait of its own.
+  auto step = [&](auto b_c, int s) __attribute__((always_inline)) {
+    constexpr int B = decltype(b_c)::value;
+    // Slice s has landed for every wave: this wave waits until only the
+    // loads of the two later slices it has issued are outstanding, then the
+    // barrier.  Every wave is then also done with slice s-1, whose slot
+    // slice s+3 takes.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoads));
+    // A plain barrier: __syncthreads() adds a workgroup release fence, which
+    // would wait for every load still landing in LDS.  LDS is one memory for
+    // the workgroup, so the counted wait above is what orders this wave's
+    // landed slice before the others' reads; the empty asm statements keep
+    // the compiler from moving memory accesses across the barrier.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    stage(std::integral_constant<int, (B + kStages - 1) % kStages>(), s + kStages - 1);
+    compute(xslot(b_c), wslot(b_c), gslot(b_c));
+  };
+  stage(std::integral_constant<int, 0>(), 0);
+  stage(std::integral_constant<int, 1>(), 1);
+  stage(std::integral_constant<int, 2>(), 2);
+  for (int s = 0; s < n_stages; s += kStages) {
+    step(std::integral_constant<int, 0>(), s);
+    step(std::integral_constant<int, 1>(), s + 1);
+    step(std::integral_constant<int, 2>(), s + 2);
+    step(std::integral_constant<int, 3>(), s + 3);
   }
+  // The empty slices' loads land before the workgroup's LDS is released.
+  __builtin_amdgcn_s_waitcnt(0);
 
   // Epilogue: acc[t][s2] element i is output column
   //   col0 + wc*kWaveCols + t*32 + (i/4)*8 + half*4 + (i%4)
@@ -346,7 +427,7 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
 
 bool project_mfma_applies(const ProjArgs &a, int x_dt, int w_dt, int o_dt) {
   return x_dt == YOCO_DT_BF16 && w_dt == YOCO_DT_BF16 && o_dt == YOCO_DT_BF16 && !a.indexed && a.n > 0 &&
-         a.d % (2 * pm::kK) == 0 && a.ncols % pm::kCols == 0 &&
+         a.d % (pm::kStages * pm::kK) == 0 && a.ncols % pm::kCols == 0 &&
          static_cast<int64_t>(a.d) * a.ncols * 2 < (int64_t(1) << 31) &&
          static_cast<int64_t>(pm::kRows) * a.d * 2 < (int64_t(1) << 31);
 }
