@@ -64,11 +64,10 @@ constexpr int kTileBytes = kChunk * kRowBytes;       // 32 KiB: [128][128] bf16
 constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // 8 one-KiB loads
 constexpr int kGroup = 8;          // chunks per group
 constexpr int kScanAhead = 8;      // group states in flight per thread in the scan
-// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
-// in 6:4, lgkmcnt in 11:8) that wait for vector memory only, down to 4 or 8
+// s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// in 6:4, lgkmcnt in 11:8) that waits for vector memory only, down to 4
 // outstanding operations.
 constexpr int kVmcnt4 = 4 | (7 << 4) | (15 << 8);
-constexpr int kVmcnt8 = 8 | (7 << 4) | (15 << 8);
 }  // namespace gr
 
 // log gamma = logsigmoid(g) / tau = (min(g, 0) - log1p(exp(-|g|))) / tau.
@@ -287,11 +286,11 @@ __device__ __forceinline__ void state_step(floatx16 (&acc)[4], const char *lds_k
 // 32w .. 32w+31, all 128 value dims; it is stored transposed ([value
 // dim][key dim]).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(gr::kThreads, 2) void gret_group_state_kernel(const GretArgs a) {
+__global__ __launch_bounds__(gr::kThreads, 3) void gret_group_state_kernel(const GretArgs a) {
   using namespace gr;
   constexpr int kSubRows = 32;                           // rows per streamed sub-tile
   constexpr int kSubBytes = kSubRows * kRowBytes;        // 8 KiB of K (and of V)
-  constexpr int kStages = 4;                             // ring of sub-tiles: three in flight
+  constexpr int kStages = 3;                             // ring of sub-tiles: two in flight
   constexpr int kLoadsPerStage = 2 * kSubBytes / 1024 / kWaves;  // vector memory ops per wave per stage (K and V)
   constexpr int kGroupRows = kGroup * kChunk;            // positions per group
   constexpr int kPerLane = kGroupRows / 64;              // positions per lane of the scan
@@ -301,29 +300,18 @@ __global__ __launch_bounds__(gr::kThreads, 2) void gret_group_state_kernel(const
   // One array per ring slot, selected at compile time: the compiler can then
   // tell that reads of one slot do not alias the direct-to-LDS loads still
   // landing in the others, and waits only as the counted waits below say.
-  __shared__ __attribute__((aligned(1024))) char lds_k0[kSubBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_k1[kSubBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_k2[kSubBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_k3[kSubBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_v0[kSubBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_v1[kSubBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_v2[kSubBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_v3[kSubBytes];
+  // (Each slot holds the K sub-tile and, after it, the V sub-tile.)
+  __shared__ __attribute__((aligned(1024))) char lds_kv0[2 * kSubBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_kv1[2 * kSubBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_kv2[2 * kSubBytes];
   __shared__ __attribute__((aligned(16))) float s_w[kGroupRows];
   auto kslot = [&](auto b_c) __attribute__((always_inline)) -> char * {
     constexpr int B = decltype(b_c)::value;
-    if constexpr (B == 0) return lds_k0;
-    else if constexpr (B == 1) return lds_k1;
-    else if constexpr (B == 2) return lds_k2;
-    else return lds_k3;
+    if constexpr (B == 0) return lds_kv0;
+    else if constexpr (B == 1) return lds_kv1;
+    else return lds_kv2;
   };
-  auto vslot = [&](auto b_c) __attribute__((always_inline)) -> char * {
-    constexpr int B = decltype(b_c)::value;
-    if constexpr (B == 0) return lds_v0;
-    else if constexpr (B == 1) return lds_v1;
-    else if constexpr (B == 2) return lds_v2;
-    else return lds_v3;
-  };
+  auto vslot = [&](auto b_c) __attribute__((always_inline)) -> char * { return kslot(b_c) + kSubBytes; };
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -339,13 +327,18 @@ __global__ __launch_bounds__(gr::kThreads, 2) void gret_group_state_kernel(const
   const bf16_t *vg = static_cast<const bf16_t *>(a.v) + (t0 * a.heads + h) * kD;
   // Sub-tile j: rows 32j .. 32j+31 of the group; wave w loads rows 8w ..
   // 8w+7 of K and of V (two 1-KiB loads of 4 rows each); rows past the
-  // group's end land as zeros.
+  // group's end land as zeros.  Sub-tiles past the group's last one are
+  // staged too, through descriptors of zero size (no memory access; zeros
+  // land in a slot nobody reads), so every step issues the same loads and
+  // the compiler's own wait tracking never merges paths with different
+  // loads in flight (where it does, it waits for all of them).
   auto stage = [&](auto b_c, int j) __attribute__((always_inline)) {
     char *dk = kslot(b_c);
     char *dv = vslot(b_c);
     const int r0 = j * kSubRows;
     const int valid = rows - r0 < kSubRows ? rows - r0 : kSubRows;
-    const int bytes = ((valid - 1) * stride + kD) * 2;
+    // (valid <= 0 gives a negative span: stride >= kD.)
+    const int bytes = max(0, ((valid - 1) * stride + kD) * 2);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<bf16_t *>(kg + static_cast<int64_t>(r0) * stride), 0, bytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
@@ -370,8 +363,7 @@ __global__ __launch_bounds__(gr::kThreads, 2) void gret_group_state_kernel(const
     }
   }
   stage(std::integral_constant<int, 0>(), 0);
-  if (n_sub > 1) stage(std::integral_constant<int, 1>(), 1);
-  if (n_sub > 2) stage(std::integral_constant<int, 2>(), 2);
+  stage(std::integral_constant<int, 1>(), 1);
 
   // Wave 0, while the first sub-tiles load: the group's cumulative gates.
   if (wave == 0) {
@@ -419,22 +411,19 @@ __global__ __launch_bounds__(gr::kThreads, 2) void gret_group_state_kernel(const
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
   }
-  // Sub-tile j sits in ring slot j % 4; the loop runs four sub-tiles per
+  // Sub-tile j sits in ring slot j % 3; the loop runs three sub-tiles per
   // pass so that every slot is a compile-time choice.
   auto step = [&](auto b_c, int j) __attribute__((always_inline)) {
     constexpr int B = decltype(b_c)::value;
     // Sub-tile j has landed for every wave: this wave waits until only the
-    // loads of the (up to two) later sub-tiles it has issued are
-    // outstanding (the first pass waits for everything, the gates
-    // included), then the barrier.  Every wave is then also done with
-    // sub-tile j-1, whose slot sub-tile j+3 takes.
-    const int later = n_sub - 1 - j;
-    if (j == 0 || later == 0) {
+    // loads of the next sub-tile it has issued are outstanding (the first
+    // pass waits for everything, the gates included), then the barrier.
+    // Every wave is then also done with sub-tile j-1, whose slot sub-tile
+    // j+2 takes.
+    if (j == 0) {
       __builtin_amdgcn_s_waitcnt(0);
-    } else if (later == 1) {
-      __builtin_amdgcn_s_waitcnt(kVmcnt4);
     } else {
-      __builtin_amdgcn_s_waitcnt(kVmcnt8);
+      __builtin_amdgcn_s_waitcnt(kVmcnt4);
     }
     // A plain barrier: __syncthreads() adds a workgroup release fence, which
     // would wait for every load still landing in LDS.  LDS is one memory for
@@ -444,7 +433,9 @@ __global__ __launch_bounds__(gr::kThreads, 2) void gret_group_state_kernel(const
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (j + kStages - 1 < n_sub) stage(std::integral_constant<int, (B + kStages - 1) % kStages>(), j + kStages - 1);
+    stage(std::integral_constant<int, (B + kStages - 1) % kStages>(), j + kStages - 1);
+    __builtin_amdgcn_sched_barrier(0);  // the loads go out before this sub-tile's reads
+    if (j >= n_sub) return;  // a step past the end only keeps the staging uniform
     const char *tk = kslot(b_c);
     const char *tv = vslot(b_c);
     const float *w = s_w + j * kSubRows;
@@ -464,12 +455,15 @@ __global__ __launch_bounds__(gr::kThreads, 2) void gret_group_state_kernel(const
       for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af.v, fr.read(tv, t, ks), acc[t], 0, 0, 0);
     }
   };
+  // Whole passes of three steps (steps past the last sub-tile stage and
+  // wait like the others), so no step sits under a branch.
   for (int j = 0; j < n_sub; j += kStages) {
     step(std::integral_constant<int, 0>(), j);
-    if (j + 1 < n_sub) step(std::integral_constant<int, 1>(), j + 1);
-    if (j + 2 < n_sub) step(std::integral_constant<int, 2>(), j + 2);
-    if (j + 3 < n_sub) step(std::integral_constant<int, 3>(), j + 3);
+    step(std::integral_constant<int, 1>(), j + 1);
+    step(std::integral_constant<int, 2>(), j + 2);
   }
+  // The loads of the sub-tiles past the end land before the LDS is released.
+  __builtin_amdgcn_s_waitcnt(0);
   // T_g (fp32, transposed).
   float *tg = a.tg + (static_cast<int64_t>(g) * a.heads + h) * kD * kD;
 #pragma unroll
