@@ -68,6 +68,7 @@ constexpr int kScanAhead = 8;      // group states in flight per thread in the s
 // in 6:4, lgkmcnt in 11:8) that waits for vector memory only, down to 4
 // outstanding operations.
 constexpr int kVmcnt4 = 4 | (7 << 4) | (15 << 8);
+constexpr int kLgkm0 = 0xF | (7 << 4) | (3 << 14);  // LDS/scalar counter only, down to 0
 }  // namespace gr
 
 // log gamma = logsigmoid(g) / tau = (min(g, 0) - log1p(exp(-|g|))) / tau.
@@ -594,6 +595,15 @@ __global__ __launch_bounds__(gr::kThreads, 2) void gret_group_out_kernel(const G
     for (int ks = 0; ks < kD / 16; ++ks) qf[ks].u = ok ? ld16(qp + ks * 16) : make_uint4(0, 0, 0, 0);
   };
   load_q(c_begin);
+  // The chunk-local cumulative gate of this thread's position (threads <
+  // 128), loaded a chunk ahead like the queries (its load is not waited for
+  // at the chunk's start).
+  auto load_l = [&](int c) __attribute__((always_inline)) {
+    const int64_t t0 = static_cast<int64_t>(c) * kChunk;
+    const int64_t p = t0 + (tid < kChunk ? tid : 0);
+    return p < a.n_tokens ? a.lcum[p * a.heads + h] : 0.f;
+  };
+  float l_next = load_l(c_begin);
 
   for (int c = c_begin; c < c_end; ++c) {
     // LDS read offsets are derived inside each chunk from an opaque copy of
@@ -610,8 +620,7 @@ __global__ __launch_bounds__(gr::kThreads, 2) void gret_group_out_kernel(const G
     const bf16_t *vg = static_cast<const bf16_t *>(a.v) + (t0 * a.heads + h) * kD;
     // Every wave is done with the previous chunk's K, V and key weights.
     __syncthreads();
-    stage_rows(lds_k, kg, stride, rows, wave, lane);
-    if (tid < kChunk) s_l[tid] = tid < rows ? a.lcum[(t0 + tid) * a.heads + h] : 0.f;
+    if (tid < kChunk) s_l[tid] = l_next;  // zero past the last position
     // R_c (bf16, transposed: row = value dim) into LDS: four consecutive key
     // dims per lane and (t, q4), 8-byte writes.
 #pragma unroll
@@ -624,9 +633,18 @@ __global__ __launch_bounds__(gr::kThreads, 2) void gret_group_out_kernel(const G
         *reinterpret_cast<uint2 *>(lds_rv + swz<kD, kSwz>(t * 32 + col, wave * 32 + q4 * 8 + half * 4)) = pk;
       }
     }
+    // The K tile loads go out after this wave's LDS writes (an LDS write
+    // issued after them would wait for them).
+    asm volatile("" ::: "memory");
+    stage_rows(lds_k, kg, stride, rows, wave, lane);
     const bool row_valid = my_row < rows;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // R_c and s_l are in LDS for every wave.  A plain barrier after the LDS
+    // writes only: the K tile keeps loading under the carried term, which
+    // does not read it (__syncthreads() would wait for those loads too).
+    __builtin_amdgcn_s_waitcnt(kLgkm0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     // Key weights of the state step, exp(l_C - l_k) (read after a later barrier).
     const float lc = s_l[rows - 1];
     if (tid < kChunk) s_w[tid] = tid < rows ? expf(lc - s_l[tid]) : 0.f;
@@ -655,7 +673,10 @@ __global__ __launch_bounds__(gr::kThreads, 2) void gret_group_out_kernel(const G
 #pragma unroll
       for (int e = 0; e < 16; ++e) oacc[d][e] *= carry;
     }
-    __syncthreads();  // every wave is done with R_c; V takes its buffer
+    // Every wave is done with R_c (V takes its buffer), and the K tile has
+    // landed for every wave.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     stage_rows(lds_rv, vg, stride, rows, wave, lane);
 
     // Per 32-key half u = 0 .. wave (keys <= the wave's rows): S^T = K Q^T,
@@ -722,6 +743,7 @@ __global__ __launch_bounds__(gr::kThreads, 2) void gret_group_out_kernel(const G
     }
     // R_{c+1}; the state after the group's last chunk is the scan's.
     if (c + 1 < c_end) {
+      l_next = load_l(c + 1);
       load_q(c + 1);
       TrFrag fr;
       fr.init(lane_o, kSplitHalves);  // V against K'^T
