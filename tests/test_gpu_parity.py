@@ -340,6 +340,8 @@ def test_kv_project_parity(dtype, n, d):
     (600, 256, 2, 128, True),     # 3 row tiles with a ragged tail, unit gain (NULL)
     (600, 256, 2, 128, False),    # same rows, fp32 gain (hi/lo split)
     (257, 1024, 4, 64, False),    # one full row tile plus one row
+    (300, 128, 2, 128, False),    # d_model 128: four reduction slices, one pass of the staging ring
+    (40, 384, 2, 128, True),      # d_model 384: three passes; fewer rows than one tile
     (96, 192, 2, 128, False),     # d_model % 128 != 0: the fp32-FMA tiled kernel
 ])
 def test_prompt_projection_paths(n, d, hkv, dh, unit_gain):
