@@ -29,19 +29,20 @@
 // recurrence started from zero gives the group's total T_g and its decay
 // Lambda_g, and S_{g+1} = exp(Lambda_g) S_g + T_g (S_0 the start state)
 // gives the state entering each group.
-//   * gret_group_state_kernel: one workgroup per (group, head) walks the
-//     group's chunks with the state in the MFMA accumulators: l for the
-//     chunk (a wave scan, also stored for the output kernel), then
-//     A <- exp(l_C) A + K'^T V with K' = exp(l_C - l_k) k_k rounded to bf16
-//     (weights applied to the transposed K fragments), both operands from
-//     row-major LDS tiles; T_g = A after the group's last chunk, in fp32.
+//   * gret_group_state_kernel: one workgroup per (group, head) forms the
+//     group's total in one pass, T_g = K'^T V over the group's positions
+//     with K' = exp(L_G - L_k) k_k rounded to bf16 (the same value as the
+//     chunk recurrence from zero; weights applied to the transposed K
+//     fragments), both operands from row-major LDS tiles, in fp32; it also
+//     stores the chunk-local cumulative gates l for the output kernel.
 //   * gret_group_scan_kernel: the short pass over groups, elementwise over
 //     the state (S_g in fp32, the last state to state_out).
 //   * gret_group_out_kernel: one workgroup per (group, head) walks the
 //     group's chunks again, with A started at S_g, so before chunk c it
 //     holds R_c.  Per chunk, 4 waves x 32 query rows: R_c is rounded to bf16
-//     into LDS; the carried term O^T = R^T Q^T comes first (then each lane
-//     scales its query row by exp(l_j)), then per 32-key half S^T = K Q^T,
+//     into LDS; the carried term O^T = R^T Q^T comes first, while the
+//     chunk's K loads (then each lane scales its query row by exp(l_j)),
+//     then per 32-key half S^T = K Q^T,
 //     P = S exp(l_j - l_k) masked to k <= j and rounded to bf16 (formed
 //     while V loads into the buffer R_c held), then O^T += V^T P^T -- the
 //     layout of the causal prefill kernel (one query row per lane, Q^T in
@@ -277,7 +278,7 @@ __device__ __forceinline__ void state_step(floatx16 (&acc)[4], const char *lds_k
 // start and L_G its value at the group's end (Lambda_g) -- the recurrence
 // A <- exp(l_C) A + U_c over the group's chunks from A = 0, summed in one
 // pass: no step depends on the previous one, so K and V stream through LDS
-// in 32-row sub-tiles, a ring of four with three in flight.  Wave 0 first
+// in 32-row sub-tiles, a ring of three with two in flight.  Wave 0 first
 // scans the group's
 // gates: kGroup * 2 consecutive positions per lane, lane totals scanned over
 // the wave for L and over each lane segment of one chunk for the chunk-local
