@@ -501,14 +501,17 @@ __global__ __launch_bounds__(256) void gret_group_scan_kernel(const GretArgs a, 
   auto t_at = [&](int gg) __attribute__((always_inline)) {
     return reinterpret_cast<const float4 *>(a.tg + (static_cast<int64_t>(gg) * a.heads + h) * kD * kD)[e4];
   };
+  // kScanAhead groups' totals in flight.  Every load is issued at a clamped
+  // group index, never under a branch (a load under a branch makes the
+  // compiler wait for it where the branch joins, which would leave one load
+  // in flight).
   float4 ring[kScanAhead];
   float lring[kScanAhead];
 #pragma unroll
   for (int j = 0; j < kScanAhead; ++j) {
-    if (j < n_groups) {
-      ring[j] = t_at(j);
-      lring[j] = a.gdec[static_cast<int64_t>(j) * a.heads + h];
-    }
+    const int gj = min(j, n_groups - 1);
+    ring[j] = t_at(gj);
+    lring[j] = a.gdec[static_cast<int64_t>(gj) * a.heads + h];
   }
   for (int g0 = 0; g0 < n_groups; g0 += kScanAhead) {
 #pragma unroll
@@ -522,11 +525,10 @@ __global__ __launch_bounds__(256) void gret_group_scan_kernel(const GretArgs a, 
         r.y = fmaf(dec, r.y, t.y);
         r.z = fmaf(dec, r.z, t.z);
         r.w = fmaf(dec, r.w, t.w);
-        if (gg + kScanAhead < n_groups) {
-          ring[j] = t_at(gg + kScanAhead);
-          lring[j] = a.gdec[static_cast<int64_t>(gg + kScanAhead) * a.heads + h];
-        }
       }
+      const int gn = min(gg + kScanAhead, n_groups - 1);
+      ring[j] = t_at(gn);
+      lring[j] = a.gdec[static_cast<int64_t>(gn) * a.heads + h];
     }
   }
   if (a.state_out) {
