@@ -345,8 +345,10 @@ __global__ __launch_bounds__(pm::kThreads, 1) void project_mfma_kernel(const Pro
         }
       }
       // One k-step's operands in flight at a time (the accumulators take
-      // half the registers).
-      __builtin_amdgcn_sched_barrier(0);
+      // half the registers).  The 128-column tiles (half the accumulators)
+      // leave the compiler free to read ahead across k-steps, which measured
+      // faster there and slower for the 256-column tiles.
+      if constexpr (NCOLS == 256) __builtin_amdgcn_sched_barrier(0);
     }
   };
 
