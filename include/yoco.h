@@ -260,6 +260,24 @@ yoco_status yoco_q_project_rope(const void *x, int32_t x_dtype, int64_t n, int32
                                 double rope_theta, void *workspace, size_t workspace_bytes,
                                 void *stream);
 
+/* Weight preparation, run once per model (not per token): the RMSNorm gain
+ * of [Notes] Eq. 2 / Eq. 3 folded into the weights of the projection that
+ * follows it.  LN(x) W = (x * gain / r) W = (x / r) (diag(gain) W), so
+ *   w_out[c][j] = RNE_bf16(fp32(w[c][j]) * gain[c])   (fp32 product)
+ * given to yoco_kv_project / yoco_kv_append / yoco_q_project (and their
+ * _rope forms) with a NULL gain computes LN(x) W with the gain rounded into
+ * each weight once, instead of applied to every activation.  Prompt-sized
+ * calls then take the unit-gain matrix-core path (one bf16 product per
+ * fragment; an fp32 gain on the activations takes two, x*gain entering as a
+ * bf16 hi + lo pair); the price is one bf16 rounding of gain*w per weight.
+ * w: [d_model][n_cols] in w_dtype (f32 or bf16); gain: [d_model] fp32;
+ * w_out: [d_model][n_cols] bf16, written.  w_out may be w itself when
+ * w_dtype is bf16; any other overlap of the two is BAD_VALUE.
+ * Errors: NULL w/gain/w_out -> NULL_POINTER; d_model < 1 or n_cols < 1 ->
+ * BAD_SHAPE; dtype code -> BAD_DTYPE; ALIGNMENT; BAD_VALUE; HIP. */
+yoco_status yoco_fold_norm_gain(const void *w, int32_t w_dtype, const float *gain, int32_t d_model,
+                                int32_t n_cols, void *w_out, void *stream);
+
 /* Host-only helper: the softmax scale 1/sqrt(head_dim) of [Blog] section 2
  * (o_t = softmax(q_t K^T / sqrt(d_h)) V), the scale the attention calls below
  * use in the pages' method; the calls take the scale explicitly.  Errors:

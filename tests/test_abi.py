@@ -27,7 +27,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = _lib()
     names = _declared_functions()
-    assert len(names) == 24, names
+    assert len(names) == 25, names
     for name in names:
         assert hasattr(lib, name), f"{name} declared in yoco.h but not exported"
 
@@ -509,6 +509,43 @@ def test_project_workspace_sizes_and_rules():
     assert lens.tolist() == [10, 20]
     assert L.yoco_q_project(FAKE, 1, 4, 32, None, 1e-6, FAKE, 1, 4, 64, FAKE, 1, FAKE, 16, None) == \
         _status("YOCO_ERR_WORKSPACE")
+
+
+def test_fold_norm_gain_rejects():
+    L = _lib()
+    OUT = ctypes.c_void_p(0x100000)
+    fold = lambda w=FAKE, dt=1, g=FAKE, d=4, n=8, out=OUT: L.yoco_fold_norm_gain(w, dt, g, d, n, out, None)
+    assert fold(w=None) == _status("YOCO_ERR_NULL_POINTER")
+    assert fold(g=None) == _status("YOCO_ERR_NULL_POINTER")
+    assert fold(out=None) == _status("YOCO_ERR_NULL_POINTER")
+    assert fold(d=0) == _status("YOCO_ERR_BAD_SHAPE")
+    assert fold(n=-8) == _status("YOCO_ERR_BAD_SHAPE")
+    assert fold(dt=2) == _status("YOCO_ERR_BAD_DTYPE")
+    assert fold(w=MIS) == _status("YOCO_ERR_ALIGNMENT")
+    assert fold(out=MIS) == _status("YOCO_ERR_ALIGNMENT")
+    # bf16 4 x 8 spans 64 bytes: an output 16 bytes further on overlaps it
+    assert fold(out=ctypes.c_void_p(0x1010)) == _status("YOCO_ERR_BAD_VALUE")
+    assert "overlaps" in L.yoco_last_error().decode()
+    # fp32 weights to bf16 in the same array would overwrite unread weights
+    assert fold(dt=0, out=FAKE) == _status("YOCO_ERR_BAD_VALUE")
+    assert fold(dt=0, out=ctypes.c_void_p(0x1000 + 4 * 4 * 8)) != _status("YOCO_ERR_BAD_VALUE")  # just past it
+    if not gpu_available():
+        assert fold(out=FAKE) == _status("YOCO_ERR_HIP")   # in place, bf16: valid, so it reaches the device check
+
+
+def test_fold_binding_checks_shapes():
+    import torch
+    import yoco_shared_kv_amd as y
+    with pytest.raises(ValueError, match="gain must"):
+        y.fold_norm_gain(torch.zeros(32, 64, dtype=torch.bfloat16), torch.ones(16))
+    with pytest.raises(TypeError, match="gain must"):
+        y.fold_norm_gain(torch.zeros(32, 64, dtype=torch.bfloat16), torch.ones(32, dtype=torch.float64))
+    with pytest.raises(TypeError, match="out must"):
+        y.fold_norm_gain(torch.zeros(32, 64), torch.ones(32), out=torch.zeros(32, 64))
+    with pytest.raises(ValueError, match="gain is required"):
+        y.fold_norm_gain(torch.zeros(32, 64), None)
+    with pytest.raises(ValueError, match="device"):
+        y.fold_norm_gain(torch.zeros(32, 64), torch.ones(32))
 
 
 def test_default_softmax_scale():

@@ -37,7 +37,7 @@ __all__ = [
     "kv_cache_row_stride", "lib", "project_workspace_bytes", "default_softmax_scale",
     "cross_attn_prefill_bwd", "prefill_bwd_workspace_bytes", "kv_project_bwd", "q_project_bwd",
     "project_bwd_workspace_bytes", "gret_prefill", "gret_decode", "gret_prefill_workspace_bytes",
-    "cross_attn_decode_noalloc",
+    "cross_attn_decode_noalloc", "fold_norm_gain",
 ]
 
 _DT = {torch.float32: YOCO_DT_F32, torch.bfloat16: YOCO_DT_BF16}
@@ -315,6 +315,27 @@ def q_project(x: torch.Tensor, w_q: torch.Tensor, n_q_heads: int, head_dim: int,
         pos_ptr = None if pos is None else pos.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
         check(lib().yoco_q_project_rope(*args, pos_ptr, int(pos0), float(rope_theta), ws, ws_bytes,
                                         _stream(stream)))
+    return out
+
+
+def fold_norm_gain(w: torch.Tensor, gain: torch.Tensor, out: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """diag(gain) W in bf16 (``[d_model, n_cols]``), each element the fp32
+    product gain[c] * w[c][j] rounded once: the projections given it and no
+    gain compute RMSNorm(x) W.  ``out`` may be ``w`` itself for a bf16 ``w``."""
+    if w.dim() != 2:
+        raise ValueError("w must be [d_model, n_cols]")
+    d, ncols = w.shape
+    if gain is None:
+        raise ValueError("gain is required")
+    _check_shape("gain", gain, (d,), torch.float32)
+    if out is not None:
+        _check_shape("out", out, (d, ncols), torch.bfloat16)
+    _on_device(w, gain, out)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((d, ncols), dtype=torch.bfloat16, device=w.device)
+    check(lib().yoco_fold_norm_gain(_ptr(w), _dt(w), _ptr(gain), d, ncols, _ptr(out), _stream(stream)))
     return out
 
 

@@ -70,6 +70,8 @@ def _declare(lib):
     lib.yoco_q_project.argtypes = [vp, i32, i64, i32, vp, f32, vp, i32, i32, i32, vp, i32, vp, sz, vp]
     lib.yoco_project_workspace.restype = st
     lib.yoco_project_workspace.argtypes = [i64, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.yoco_fold_norm_gain.restype = st
+    lib.yoco_fold_norm_gain.argtypes = [vp, i32, vp, i32, i32, vp, vp]
     lib.yoco_default_softmax_scale.restype = st
     lib.yoco_default_softmax_scale.argtypes = [i32, ctypes.POINTER(f32)]
     f64 = ctypes.c_double

@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libyoco.so")
 ROOT = os.path.dirname(HERE)
 
-SOURCES = ["api.cpp", "backward.hip", "decode.hip", "prefill.hip", "project.hip", "project_mfma.hip", "project_rows.hip", "project_bwd.hip", "gret.hip"]
+SOURCES = ["api.cpp", "backward.hip", "decode.hip", "prefill.hip", "project.hip", "project_mfma.hip", "project_rows.hip", "project_bwd.hip", "gret.hip", "fold_gain.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -484,6 +484,27 @@ yoco_status yoco_project_workspace(int64_t n, int32_t d_model, int32_t n_cols, i
   return ok();
 }
 
+yoco_status yoco_fold_norm_gain(const void *w, int32_t w_dtype, const float *gain, int32_t d_model, int32_t n_cols,
+                                void *w_out, void *stream) {
+  if (w == nullptr || gain == nullptr || w_out == nullptr)
+    return fail(YOCO_ERR_NULL_POINTER, "w, gain or w_out is NULL");
+  if (d_model < 1 || n_cols < 1) return fail(YOCO_ERR_BAD_SHAPE, "d_model %d and n_cols %d must be >= 1", d_model, n_cols);
+  if (!dtype_ok(w_dtype)) return fail(YOCO_ERR_BAD_DTYPE, "w dtype %d unknown", w_dtype);
+  if (check_aligned({{w, "w"}, {gain, "gain"}, {w_out, "w_out"}}, 16) != YOCO_OK) return YOCO_ERR_ALIGNMENT;
+  // In place only as the same bf16 array: any other overlap would let one
+  // lane overwrite weights another lane has yet to read.
+  const size_t n_elems = static_cast<size_t>(d_model) * static_cast<size_t>(n_cols);
+  const uintptr_t in0 = reinterpret_cast<uintptr_t>(w), in1 = in0 + n_elems * dtype_size(w_dtype);
+  const uintptr_t out0 = reinterpret_cast<uintptr_t>(w_out), out1 = out0 + n_elems * 2;
+  const bool same = in0 == out0 && w_dtype == YOCO_DT_BF16;
+  if (!same && in0 < out1 && out0 < in1)
+    return fail(YOCO_ERR_BAD_VALUE, "w_out overlaps w (in place only as the same bf16 array)");
+  yoco_status st = check_device();
+  if (st != YOCO_OK) return st;
+  return launched(yoco::launch_fold_gain(w, w_dtype, gain, d_model, n_cols, w_out, static_cast<hipStream_t>(stream)),
+                  "fold_norm_gain");
+}
+
 yoco_status yoco_default_softmax_scale(int32_t head_dim, float *scale) {
   if (scale == nullptr) return fail(YOCO_ERR_NULL_POINTER, "scale is NULL");
   if (head_dim < 1) return fail(YOCO_ERR_BAD_SHAPE, "head_dim %d < 1", head_dim);

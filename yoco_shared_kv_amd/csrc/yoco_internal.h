@@ -50,6 +50,10 @@ __device__ __forceinline__ int64_t proj_row_pos(const ProjArgs &a, int64_t r) {
 
 hipError_t launch_project(const ProjArgs &a, int x_dt, int w_dt, int o_dt, hipStream_t s);
 
+// w_out[c][j] = bf16(w[c][j] * gain[c]) over d x n_cols (fold_gain.hip).
+hipError_t launch_fold_gain(const void *w, int w_dt, const float *gain, int32_t d, int32_t n_cols, void *out,
+                            hipStream_t s);
+
 // Few-row projection split over W's reduction rows (project_rows.hip).  The
 // caller's workspace holds kProjRowsCounterBytes of arrival counters (zero
 // between calls) and then the partials of one launch of up to 8 input rows.
