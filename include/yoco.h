@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define YOCO_ABI_VERSION 8
+#define YOCO_ABI_VERSION 9
 #define YOCO_MAX_SEQ 256
 
 /* Storage types. */
