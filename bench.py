@@ -68,6 +68,8 @@ def parse_args():
     p.add_argument("--copy-calibration", action="store_true")
     p.add_argument("--dense-rows", action="store_true",
                    help="decode cache with dense rows instead of the library's padded row stride (for comparison)")
+    p.add_argument("--no-graph-step", action="store_true",
+                   help="skip the step replayed from a HIP graph (reported beside the headline)")
     p.add_argument("--no-extra-decodes", action="store_true",
                    help="skip the ragged-16 and 2^20-row decode workloads reported beside the headline")
     p.add_argument("--extra-steps", type=int, default=10, help="timed steps of each extra decode workload")
@@ -298,8 +300,36 @@ def bench_decode(args, torch, y, W):
                     GBps=bytes_per_launch / (float(np.mean(cold_ms)) * 1e-3) / 1e9, launches=len(cold_ms))
         log(f"cold decode (512 MiB flush before each launch): avg {cold['avg_launch_us']:.2f} us "
             f"-> {cold['GBps']:.0f} GB/s")
+    # The same step captured once in a HIP graph and replayed (how a serving
+    # loop removes host work between launches): every replay appends the
+    # captured row and decodes at the captured lengths, the same work as a
+    # step.  Reported beside the headline, never as it.
+    graph_ms = None
+    if not args.no_graph_step:
+        def graph_step():
+            cache.len[:] = lens - 1
+            i0 = args.warmup * n_seq
+            y.kv_append(cache, m_rows[i0:i0 + n_seq], w_k, w_v, gain, 1e-6, workspace=pws)
+            for l in range(layers):
+                y.cross_attn_decode(q_layers[l], cache, workspace=ws, out=outs[l])
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            graph_step()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        g_ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        g_ev[0].record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        g_ev[1].record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g_ev[0].elapsed_time(g_ev[1]) / args.steps
+        del graph
+        log(f"decode step as a HIP graph replay: {graph_ms:.3f} ms ({graph_ms * 1e3 / layers:.2f} us/token/layer)")
     return dict(case=case, cache=cache, q_layers=q_layers, outs=outs, ms_per_step=ms_per_step,
-                gpu_ms_per_step=gpu_ms_per_step,
+                gpu_ms_per_step=gpu_ms_per_step, graph_ms_per_step=graph_ms,
+                graph_us_per_token_layer=None if graph_ms is None else graph_ms * 1e3 / layers,
                 us_per_token_layer=us_per_token_layer, kern_avg_us=kern_avg_ms * 1e3,
                 kern_p10_us=pct(kern_ms, 10) * 1e3, kern_p50_us=pct(kern_ms, 50) * 1e3,
                 kern_p90_us=pct(kern_ms, 90) * 1e3,
@@ -692,6 +722,7 @@ def bench_extra_decodes(args, torch, y, W):
     for wl in ("ragged16", "decode1m"):
         sub = argparse.Namespace(**vars(args))
         sub.workload, sub.steps, sub.warmup, sub.cold_steps = wl, args.extra_steps, 2, 0
+        sub.no_graph_step = True
         d = bench_decode(sub, torch, y, W)
         entry = {
             "workload": WORKLOADS[wl][2],
@@ -815,6 +846,12 @@ def main():
                              "avg over steps of elapsed / 13 (percentiles over steps)",
             "bytes_per_launch": dec["bytes_per_launch"],
         },
+        "decode_graph": None if dec["graph_ms_per_step"] is None else {
+            "what": "the same step (append + 13 decodes) captured once in a HIP graph and replayed "
+                    "--steps times between two events; each replay appends the captured row and decodes at "
+                    "the captured lengths",
+            "ms_per_step": round(dec["graph_ms_per_step"], 4),
+            "us_per_token_layer": round(dec["graph_us_per_token_layer"], 3)},
         "decode_cold": None if dec["cold"] is None else {
             "what": "a 512 MiB device copy before every decode launch (evicts L2 and the 256 MB MALL)",
             "avg_launch_us": round(dec["cold"]["avg_launch_us"], 2),
