@@ -13,8 +13,9 @@ benchmark times (library-chosen split size, fp32 outputs):
   and oracle parity for all 13 layers; a prefill block of
   the last 64 positions over the same cache (the decode's row and the oracle);
 * K^/V^ projection of 32768 rows at 3B-like widths (3072 -> 2 x 1024, matrix
-  cores): a seeded sample of rows against the fp64 projection, every value
-  finite, and the cache rows outside the range untouched.
+  cores), with unit gain and with an fp32 gain: two seeded rows in every
+  256-row tile against the fp64 projection, every value finite, and the
+  cache rows outside the range untouched.
 """
 import math
 import sys
@@ -184,7 +185,11 @@ def test_kv_project_3b_sampled_rows():
     assert cache.len.tolist() == [n + 4]
     assert torch.all(cache.k[0, :4] == 7.0) and torch.all(cache.v[0, n + 4:] == 7.0)
     assert torch.isfinite(cache.k[0, 4:n + 4].float()).all() and torch.isfinite(cache.v[0, 4:n + 4].float()).all()
-    rows = np.unique(np.concatenate([[0, 1, 255, 256, n - 1], np.random.default_rng(7).integers(0, n, 59)]))
+    # Two seeded rows in every 256-row tile of the matrix-core kernel (every
+    # workgroup: each row spans all of its column tiles) plus the tile edges.
+    r = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, n - 1]] +
+                                    [t * 256 + r.choice(256, 2, replace=False) for t in range(n // 256)]))
     m_s = p.m[rows]
     ynorm = np.abs(oracle.rmsnorm(m_s, None, p.eps))
     for got, w, name in ((cache.k, p.w_k, "K^"), (cache.v, p.w_v, "V^")):
@@ -192,3 +197,12 @@ def test_kv_project_3b_sampled_rows():
         ref = oracle.project(m_s, w, None, p.eps)
         assert_projection_bf16(stored, ref, ynorm @ np.abs(W.as_f32(w).astype(np.float64)), d, name)
     say(f"kv_project 3B: {len(rows)} sampled rows of {n} within one ulp + fp32 bound")
+    # The same rows through the fp32-gain path (its own wave tiles, x*g as a bf16 hi + lo pair).
+    gain = (1.0 + 0.1 * np.random.default_rng(8).standard_normal(d)).astype(np.float32)
+    y.kv_project(cache, to_dev(p.m), to_dev(p.w_k), to_dev(p.w_v), torch.from_numpy(gain).cuda(), p.eps, row_start=4)
+    ynorm_g = np.abs(oracle.rmsnorm(m_s, gain, p.eps))
+    for got, w, name in ((cache.k, p.w_k, "K^"), (cache.v, p.w_v, "V^")):
+        stored = to_stored(got[0, torch.from_numpy(4 + rows).cuda()]).reshape(len(rows), -1)
+        ref = oracle.project(m_s, w, gain, p.eps)
+        assert_projection_bf16(stored, ref, ynorm_g @ np.abs(W.as_f32(w).astype(np.float64)), d, name + " (gain)")
+    say(f"kv_project 3B with an fp32 gain: the same {len(rows)} rows within one ulp + fp32 bound")
