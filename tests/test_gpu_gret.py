@@ -126,7 +126,7 @@ def test_gret_prefill_blocks_chain():
 
 def test_gret_prefill_full_size_sampled():
     """32768 positions, 24 heads of 128 (the 3B self-decoder shapes), bf16:
-    sampled rows and the final state against the oracle."""
+    a row of every 128-position chunk and the final state against the oracle."""
     cfg = W.GRET_32K
     print(f"gret_prefill full size {cfg}", flush=True)
     c = W.make_gret(**cfg, dtype=W.BF16, seed=0)
@@ -134,8 +134,11 @@ def test_gret_prefill_full_size_sampled():
     o, s = y.gret_prefill(q, k, v, g, c.tau, want_state=True)
     torch.cuda.synchronize()
     n = cfg["n"]
+    # One seeded row in every 128-position chunk (every chunk step of every
+    # group's output pass, all heads) plus chunk and group edges.
     rng = np.random.default_rng(2)
-    rows = np.concatenate([[0, 127, 128, n - 1], rng.choice(n, 60, replace=False)]).astype(np.int64)
+    rows = np.unique(np.concatenate([[0, 127, 128, 1023, 1024, n - 1]] +
+                                    [[c0 * 128 + int(rng.integers(128))] for c0 in range(n // 128)])).astype(np.int64)
     gamma = oracle.gret_gate(c.gate, c.tau)
     ref_o, ref_s = oracle.gret(c.q, c.k, c.v, gamma, rows=rows, want_state=True)
     assert_close(o.cpu().numpy()[rows], ref_o, "sampled rows", **TOL_BF16)
